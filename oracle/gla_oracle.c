@@ -1,0 +1,308 @@
+/*
+ * gla_oracle.c -- plain, slow, fp64 CPU oracle for the DiG token mixer:
+ * the Gated Linear Attention (GLA) forward scanned in one SREM direction,
+ * the 3x3 depthwise conv of the SREM block with its direction remap, and
+ * the adaLN modulation that feeds the block.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product (the HIP library and its
+ * Python binding) may include, link, load or call this file.  Only the tests,
+ * the smoke check and the CPU-baseline leg of the benchmark use it.  It shares
+ * no code, header, table or constant with the GPU path.
+ *
+ * Every value is computed in IEEE fp64, token by token, with no chunking,
+ * blocking, factorisation or reordering beyond the plain definitions below.
+ * Inputs arrive as fp64 arrays (bf16 and fp32 inputs convert to fp64 exactly).
+ *
+ * Sources (web pages; cited by title and section):
+ *  [DiG-notes]  "DiG: Scalable and Efficient Diffusion Models with Gated Linear
+ *               Attention", Paper-Notes (CVPR 2025): sections 关键设计 / SREM
+ *               (scan-direction control, transpose + flip, 3x3 DWConv2d with
+ *               identity init), 关键设计 / DiG Block设计 (block order: adaLN ->
+ *               GLA -> adaLN -> FFN -> reshape to 2D -> DWConv2d -> direction
+ *               change), 关键设计 / 硬件友好的效率设计 (chunk-wise GLA).
+ *  [GLA-issue]  "DiG: Scalable and Efficient Diffusion Models with Gated Linear
+ *               Attention", diffusers issue #20: description bullets (per-head
+ *               head_dim x head_dim recurrent state; data-dependent forget gate
+ *               on that state) and the draft recurrence (gate applied over the
+ *               key rows of the state, current token written before the read,
+ *               readout q . state, zero initial state).  Its feature map, its
+ *               sigmoid(q*k) gate and its normaliser are NOT part of the
+ *               operator computed here.
+ *  [DiT-notes]  "Scalable Diffusion Models with Transformers" notes, section
+ *               3.2 DiT Block 设计 (adaLN: scale and shift regressed from the
+ *               conditioning; adaLN-Zero identity-at-init convention).
+ *  [ZigMa-notes] "ZigMa: A DiT-style Zigzag Mamba Diffusion Model",
+ *               Paper-Notes (ECCV 2024), 关键设计 / 异构逐层扫描 (arrange ->
+ *               scan -> arrange back, one scan order per layer).
+ *
+ * Readings where the pages leave a step open are stated at each function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Scan directions, in the order [DiG-notes] SREM lists them. */
+enum { OR_L2R = 0, OR_R2L = 1, OR_T2B = 2, OR_B2T = 3 };
+
+/*
+ * Canonical grid index visited at scan position p.
+ *
+ * The canonical order is the row-major order of the (gh x gw) token grid.
+ * [DiG-notes] SREM names four scans (left->right, right->left, top->bottom,
+ * bottom->top) obtained with a transpose of the 2D token matrix and a flip of
+ * the sequence.  Reading: the flip reverses the whole sequence, so
+ *   left->right : row-major order;
+ *   right->left : row-major order reversed;
+ *   top->bottom : column-major order (row-major order of the transpose);
+ *   bottom->top : column-major order reversed.
+ * Returns -1 for an unknown direction.
+ */
+int64_t oracle_scan_index(int dir, int64_t gh, int64_t gw, int64_t p)
+{
+    const int64_t T = gh * gw;
+    int64_t r, c, s;
+    if (p < 0 || p >= T) return -1;
+    switch (dir) {
+    case OR_L2R:
+        return p;
+    case OR_R2L:
+        return T - 1 - p;
+    case OR_T2B:
+        c = p / gh;          /* column being walked */
+        r = p - c * gh;      /* row inside that column */
+        return r * gw + c;
+    case OR_B2T:
+        s = T - 1 - p;
+        c = s / gh;
+        r = s - c * gh;
+        return r * gw + c;
+    default:
+        return -1;
+    }
+}
+
+/* Fill perm[p] = canonical index of scan position p, for p in [0, T). */
+int oracle_scan_perm(int dir, int64_t gh, int64_t gw, int64_t *perm)
+{
+    const int64_t T = gh * gw;
+    for (int64_t p = 0; p < T; ++p) {
+        perm[p] = oracle_scan_index(dir, gh, gw, p);
+        if (perm[p] < 0) return -1;
+    }
+    return 0;
+}
+
+/*
+ * GLA forward, token by token, per (batch, head).
+ *
+ * Layouts (contiguous, fp64):
+ *   q, k, log_alpha : [B, T, H, dk]   canonical token order
+ *   v               : [B, T, H, dv]   canonical token order
+ *   s0 (nullable)   : [B, H, dk, dv]  initial state; NULL means zero
+ *   o               : [B, T, H, dv]   written in SCAN order (position p)
+ *   s_final (nullable): [B, H, dk, dv] state after the last scanned token
+ *
+ * For each (b, h), with S := s0[b, h] (dk x dv), and for p = 0 .. T-1 with
+ * n = canonical index at scan position p:
+ *   a_i      = exp(log_alpha[b, n, h, i])                (forget gate)
+ *   S_ij    := a_i * S_ij + k[b, n, h, i] * v[b, n, h, j] (decay, then write)
+ *   o[b,p,h,j] = sum_i q[b, n, h, i] * S_ij               (inclusive readout)
+ * This is the recurrence of [GLA-issue] (state of head_dim x head_dim, gate
+ * over the key rows, write before read, q . state readout, zero start) with
+ * the per-key-channel gate supplied as an input in log space, and without the
+ * draft's feature map and normaliser.  [DiG-notes] 硬件友好的效率设计 states
+ * that the chunk-wise form computes the same thing, so no chunks appear here.
+ *
+ * nthreads <= 0 means "let OpenMP decide".  Returns 0, or -1 on bad args.
+ */
+int oracle_gla_fwd(const double *q, const double *k, const double *v,
+                   const double *log_alpha, int64_t B, int64_t T, int64_t H,
+                   int64_t dk, int64_t dv, int64_t gh, int64_t gw, int dir,
+                   const double *s0, double *o, double *s_final, int nthreads)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (gh <= 0 || gw <= 0 || gh * gw != T) return -1;
+    if (dir < OR_L2R || dir > OR_B2T) return -1;
+
+    int64_t *perm = (int64_t *)malloc((size_t)T * sizeof(int64_t));
+    if (!perm) return -1;
+    oracle_scan_perm(dir, gh, gw, perm);
+
+    const int64_t units = B * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t b = u / H, h = u % H;
+        double *S = (double *)malloc((size_t)(dk * dv) * sizeof(double));
+        double *a = (double *)malloc((size_t)dk * sizeof(double));
+        if (!S || !a) {
+            failed = 1;
+            free(S);
+            free(a);
+            continue;
+        }
+        if (s0)
+            memcpy(S, s0 + (b * H + h) * dk * dv, (size_t)(dk * dv) * sizeof(double));
+        else
+            memset(S, 0, (size_t)(dk * dv) * sizeof(double));
+
+        for (int64_t p = 0; p < T; ++p) {
+            const int64_t n = perm[p];
+            const double *qn = q + ((b * T + n) * H + h) * dk;
+            const double *kn = k + ((b * T + n) * H + h) * dk;
+            const double *gn = log_alpha + ((b * T + n) * H + h) * dk;
+            const double *vn = v + ((b * T + n) * H + h) * dv;
+            double *op = o + ((b * T + p) * H + h) * dv;
+
+            for (int64_t i = 0; i < dk; ++i) a[i] = exp(gn[i]);
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] = a[i] * S[i * dv + j] + kn[i] * vn[j];
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dk; ++i) acc += qn[i] * S[i * dv + j];
+                op[j] = acc;
+            }
+        }
+        if (s_final)
+            memcpy(s_final + (b * H + h) * dk * dv, S, (size_t)(dk * dv) * sizeof(double));
+        free(S);
+        free(a);
+    }
+    free(perm);
+    return failed ? -1 : 0;
+}
+
+/*
+ * SREM 3x3 depthwise conv with the direction remap to canonical order.
+ *
+ *   x : [B, T, C]  the mixer output in SCAN order of direction `dir`
+ *   w : [C, 3, 3]  one 3x3 kernel per channel
+ *   y : [B, T, C]  CANONICAL (row-major grid) order
+ *
+ * [DiG-notes] DiG Block设计 step (4) reshapes the sequence to 2D and applies a
+ * DWConv2d; step (5) changes the scan direction.  Readings: the reshape is of
+ * the scan-ordered sequence into its scan frame, (R, Q) = (gh, gw) for the
+ * row scans and (gw, gh) for the column scans, X[r][c] = x[r*Q + c]; the conv
+ * is a cross-correlation with zero padding 1, stride 1 and no bias
+ *   Y[r][c] = sum_{a,e in 0..2} w[ch][a][e] * X[r+a-1][c+e-1];
+ * the direction change is the exact permutation back to canonical order,
+ * y[canon(p)] = Y[p / Q][p % Q], the arrange-back step of [ZigMa-notes].
+ */
+int oracle_srem_dwconv(const double *x, int64_t B, int64_t T, int64_t C,
+                       const double *w, int64_t gh, int64_t gw, int dir,
+                       double *y, int nthreads)
+{
+    if (B <= 0 || T <= 0 || C <= 0 || gh <= 0 || gw <= 0 || gh * gw != T) return -1;
+    if (dir < OR_L2R || dir > OR_B2T) return -1;
+    const int64_t R = (dir == OR_L2R || dir == OR_R2L) ? gh : gw;
+    const int64_t Q = (dir == OR_L2R || dir == OR_R2L) ? gw : gh;
+    int64_t *perm = (int64_t *)malloc((size_t)T * sizeof(int64_t));
+    if (!perm) return -1;
+    oracle_scan_perm(dir, gh, gw, perm);
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+#endif
+    for (int64_t bp = 0; bp < B * T; ++bp) {
+        const int64_t b = bp / T, p = bp % T;
+        const int64_t r = p / Q, c = p % Q;
+        double *yo = y + (b * T + perm[p]) * C;
+        for (int64_t ch = 0; ch < C; ++ch) {
+            double acc = 0.0;
+            for (int a = 0; a < 3; ++a) {
+                const int64_t rr = r + a - 1;
+                if (rr < 0 || rr >= R) continue;
+                for (int e = 0; e < 3; ++e) {
+                    const int64_t cc = c + e - 1;
+                    if (cc < 0 || cc >= Q) continue;
+                    acc += w[ch * 9 + a * 3 + e] * x[(b * T + rr * Q + cc) * C + ch];
+                }
+            }
+            yo[ch] = acc;
+        }
+    }
+    free(perm);
+    return 0;
+}
+
+/*
+ * Exact permutation between two scan orders of the same grid:
+ * x is in scan order `from`, y in scan order `to`; the token at canonical
+ * index n moves from position inv_from(n) to position inv_to(n).
+ * ([DiG-notes] SREM transpose + flip; [ZigMa-notes] arrange / arrange back.)
+ */
+int oracle_remap(const double *x, int64_t B, int64_t C, int64_t gh, int64_t gw,
+                 int from, int to, double *y)
+{
+    const int64_t T = gh * gw;
+    if (B <= 0 || C <= 0 || gh <= 0 || gw <= 0) return -1;
+    if (from < OR_L2R || from > OR_B2T || to < OR_L2R || to > OR_B2T) return -1;
+    int64_t *pf = (int64_t *)malloc((size_t)T * sizeof(int64_t));
+    int64_t *inv = (int64_t *)malloc((size_t)T * sizeof(int64_t));
+    if (!pf || !inv) {
+        free(pf);
+        free(inv);
+        return -1;
+    }
+    oracle_scan_perm(from, gh, gw, pf);
+    for (int64_t p = 0; p < T; ++p) inv[pf[p]] = p;   /* canonical -> from-position */
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t p2 = 0; p2 < T; ++p2) {
+            const int64_t n = oracle_scan_index(to, gh, gw, p2);
+            memcpy(y + (b * T + p2) * C, x + (b * T + inv[n]) * C, (size_t)C * sizeof(double));
+        }
+    free(pf);
+    free(inv);
+    return 0;
+}
+
+/*
+ * adaLN modulation of each token, over its C channels:
+ *   y = ((x - mean) / sqrt(var + eps) * (1 + scale) + shift) * out_scale
+ * with the population variance.  [DiG-notes] DiG Block设计 step (2) (adaLN
+ * before the GLA); [DiT-notes] 3.2 (adaLN regresses the norm's scale and
+ * shift; adaLN-Zero starts from the identity, hence the 1 + scale form).
+ * out_scale is the fixed 1/sqrt(head_dim) pre-scaling of the synthetic q/k/v.
+ */
+int oracle_adaln_modulate(const double *x, int64_t N, int64_t C,
+                          const double *scale, const double *shift, double eps,
+                          double out_scale, double *y, int nthreads)
+{
+    if (N <= 0 || C <= 0) return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        const double *xr = x + n * C;
+        double *yr = y + n * C;
+        double mean = 0.0, var = 0.0;
+        for (int64_t c = 0; c < C; ++c) mean += xr[c];
+        mean /= (double)C;
+        for (int64_t c = 0; c < C; ++c) var += (xr[c] - mean) * (xr[c] - mean);
+        var /= (double)C;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int64_t c = 0; c < C; ++c)
+            yr[c] = ((xr[c] - mean) * inv * (1.0 + scale[c]) + shift[c]) * out_scale;
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads the oracle would use by default (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,154 @@
+"""Python entry to the fp64 CPU oracle in ``gla_oracle.c``.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``.  The product package never imports
+it, and it never imports the product package.
+
+The arithmetic lives in ``gla_oracle.c`` (plain loops, fp64).  This module only
+builds that file with gcc, converts arrays to contiguous float64 numpy arrays
+and calls it through ctypes.  See the C file for the definitions and the
+passages of the pages each one follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+DIRS = {"l2r": 0, "r2l": 1, "t2b": 2, "b2t": 3}
+
+
+def build(force: bool = False) -> str:
+    """Compile gla_oracle.c into liboracle.so (gcc -O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Werror",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            d, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+            lib.oracle_gla_fwd.argtypes = [d, d, d, d, i64, i64, i64, i64, i64, i64, i64, i32, d, d, d, i32]
+            lib.oracle_gla_fwd.restype = i32
+            lib.oracle_srem_dwconv.argtypes = [d, i64, i64, i64, d, i64, i64, i32, d, i32]
+            lib.oracle_srem_dwconv.restype = i32
+            lib.oracle_remap.argtypes = [d, i64, i64, i64, i64, i32, i32, d]
+            lib.oracle_remap.restype = i32
+            lib.oracle_adaln_modulate.argtypes = [d, i64, i64, d, d, ctypes.c_double, ctypes.c_double, d, i32]
+            lib.oracle_adaln_modulate.restype = i32
+            lib.oracle_scan_perm.argtypes = [i32, i64, i64, d]
+            lib.oracle_scan_perm.restype = i32
+            lib.oracle_max_threads.argtypes = []
+            lib.oracle_max_threads.restype = i32
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    """Contiguous float64 copy/view of a numpy array or CPU torch tensor (exact for bf16/fp32)."""
+    if hasattr(a, "detach"):  # torch tensor: bf16 has no numpy dtype, widen in torch first
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dir(d) -> int:
+    return DIRS[d] if isinstance(d, str) else int(d)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def scan_perm(direction, gh: int, gw: int) -> np.ndarray:
+    """perm[p] = canonical (row-major) grid index visited at scan position p."""
+    out = np.empty(gh * gw, dtype=np.int64)
+    rc = _load().oracle_scan_perm(_dir(direction), gh, gw, _ptr(out))
+    if rc != 0:
+        raise ValueError("bad direction")
+    return out
+
+
+def gla_fwd(q, k, v, log_alpha, grid, direction, s0=None, nthreads: int = 0):
+    """Token-by-token fp64 GLA forward.
+
+    q, k, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; canonical token order.
+    Returns (o_scan [B, T, H, dv] in scan order, s_final [B, H, dk, dv]).
+    """
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(log_alpha)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H):
+        raise ValueError("shape mismatch")
+    gh, gw = grid
+    o = np.empty((B, T, H, dv), dtype=np.float64)
+    sf = np.empty((B, H, dk, dv), dtype=np.float64)
+    s0a = None if s0 is None else _f64(s0)
+    if s0a is not None and s0a.shape != (B, H, dk, dv):
+        raise ValueError("s0 shape")
+    rc = _load().oracle_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), B, T, H, dk, dv, gh, gw,
+                                _dir(direction), None if s0a is None else _ptr(s0a),
+                                _ptr(o), _ptr(sf), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gla_fwd rejected its arguments")
+    return o, sf
+
+
+def srem_dwconv(x_scan, w, grid, direction, nthreads: int = 0):
+    """x_scan [B, T, C] in scan order, w [C, 3, 3] -> y [B, T, C] canonical order."""
+    x, wf = _f64(x_scan), _f64(w)
+    B, T, C = x.shape
+    if wf.shape != (C, 3, 3):
+        raise ValueError("w shape")
+    y = np.empty_like(x)
+    rc = _load().oracle_srem_dwconv(_ptr(x), B, T, C, _ptr(wf), grid[0], grid[1],
+                                    _dir(direction), _ptr(y), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_srem_dwconv rejected its arguments")
+    return y
+
+
+def remap(x, grid, src, dst):
+    """x [B, T, C] in scan order `src` -> y in scan order `dst` (exact permutation)."""
+    xf = _f64(x)
+    B, T, C = xf.shape
+    y = np.empty_like(xf)
+    rc = _load().oracle_remap(_ptr(xf), B, C, grid[0], grid[1], _dir(src), _dir(dst), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_remap rejected its arguments")
+    return y
+
+
+def adaln_modulate(x, scale, shift, eps: float = 1e-6, out_scale: float = 1.0, nthreads: int = 0):
+    """x [..., C] -> LN over C, then * (1 + scale) + shift, then * out_scale."""
+    xf = _f64(x)
+    C = xf.shape[-1]
+    N = xf.size // C
+    sc, sh = _f64(scale).reshape(C), _f64(shift).reshape(C)
+    y = np.empty_like(xf)
+    rc = _load().oracle_adaln_modulate(_ptr(xf), N, C, _ptr(sc), _ptr(sh), float(eps),
+                                       float(out_scale), _ptr(y), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_adaln_modulate rejected its arguments")
+    return y

@@ -1,0 +1,332 @@
+"""Pins of the fp64 CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against something it does not share code with:
+values worked by hand (tests/golden), closed forms written from the
+mathematics, textbook special cases computed with numpy/torch library
+routines, and exact permutation identities.  All CPU, no GPU.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gated_linear_attention_gla_amd import inputs as gen
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _rand(B, T, H, dk, dv, seed, gate_mu=0.0, gate_div=16.0, scale=0.5):
+    d = gen.gla_inputs(B, T, H, dk, dv, dtype="f32", seed=seed, qkv_scale=scale,
+                       gate_mu=gate_mu, gate_div=gate_div)
+    return {k_: v_.double().numpy() for k_, v_ in d.items()}
+
+
+def _relerr(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- hand-worked
+
+def test_golden_hand_3tok(orc):
+    g = _load("gla_hand_3tok.json")
+    q = np.array(g["q"], float)[None, :, None, :]
+    k = np.array(g["k"], float)[None, :, None, :]
+    v = np.array(g["v"], float)[None, :, None, :]
+    la = np.log(np.array(g["alpha"], float))[None, :, None, :]
+    for case in g["cases"]:
+        s0 = None if case["s0"] is None else np.array(case["s0"], float)[None, None]
+        o, sf = orc.gla_fwd(q, k, v, la, tuple(g["grid"]), g["dir"], s0=s0)
+        np.testing.assert_allclose(o[0, :, 0, :], np.array(case["o"], float), rtol=1e-14, atol=0)
+        np.testing.assert_allclose(sf[0, 0], np.array(case["s_final"], float), rtol=1e-14, atol=0)
+
+
+def test_golden_scan_orders(orc):
+    g = _load("scan_orders_2x3.json")
+    gh, gw = g["grid"]
+    for d, perm in g["perm"].items():
+        assert orc.scan_perm(d, gh, gw).tolist() == perm, d
+
+
+def test_golden_dwconv_hand(orc):
+    g = _load("dwconv_hand_2x3.json")
+    gh, gw = g["grid"]
+    w = np.array(g["w"], float)[None]
+    x_canon = np.array(g["x_frame_l2r"], float).reshape(1, gh * gw, 1)
+    y = orc.srem_dwconv(x_canon, w, (gh, gw), "l2r")
+    assert y.reshape(gh, gw).tolist() == g["y_canon_l2r"]
+    x_scan = x_canon[:, ::-1, :].copy()       # r2l scan order of the same image
+    y = orc.srem_dwconv(x_scan, w, (gh, gw), "r2l")
+    assert y.reshape(-1).tolist() == g["y_canon_r2l"]
+
+
+# ------------------------------------------------------------- closed forms
+
+def _closed_form(q, k, v, la, perm, s0=None):
+    """o_t = sum_{s<=t} (q_t * prod_{r=s+1..t} alpha_r) . k_s^T v_s  (+ s0 term), brute force."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    a = np.exp(la)
+    o = np.zeros((B, T, H, dv))
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                nt = perm[t]
+                acc = np.zeros(dv)
+                for s in range(t + 1):
+                    ns = perm[s]
+                    dec = np.ones(dk)
+                    for r in range(s + 1, t + 1):
+                        dec = dec * a[b, perm[r], h]
+                    acc += np.dot(q[b, nt, h] * dec, k[b, ns, h]) * v[b, ns, h]
+                if s0 is not None:
+                    dec = np.ones(dk)
+                    for r in range(0, t + 1):
+                        dec = dec * a[b, perm[r], h]
+                    acc += (q[b, nt, h] * dec) @ s0[b, h]
+                o[b, t, h] = acc
+    return o
+
+
+@pytest.mark.parametrize("direction", ["l2r", "r2l", "t2b", "b2t"])
+def test_closed_form_quadratic(orc, direction):
+    gh, gw = 3, 5
+    x = _rand(2, gh * gw, 2, 3, 4, seed=11, gate_div=2.0)   # dk != dv catches transposes
+    o, _ = orc.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], (gh, gw), direction)
+    ref = _closed_form(x["q"], x["k"], x["v"], x["log_alpha"], orc.scan_perm(direction, gh, gw))
+    assert _relerr(o, ref) < 1e-12
+
+
+def test_closed_form_with_initial_state(orc):
+    gh, gw = 4, 4
+    x = _rand(1, 16, 2, 4, 3, seed=12, gate_div=1.0)
+    s0 = np.random.default_rng(5).standard_normal((1, 2, 4, 3))
+    o, _ = orc.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], (gh, gw), "t2b", s0=s0)
+    ref = _closed_form(x["q"], x["k"], x["v"], x["log_alpha"], orc.scan_perm("t2b", gh, gw), s0=s0)
+    assert _relerr(o, ref) < 1e-12
+
+
+def test_c0_shape_closed_form(orc):
+    """The tiny fp32 workload (B=1, H=2, 8x8 grid, d=16) against the quadratic form."""
+    d = gen.make_inputs("C0")
+    q, k, v, la = (d[n].double().numpy() for n in ("q", "k", "v", "log_alpha"))
+    o, _ = orc.gla_fwd(q, k, v, la, (8, 8), "l2r")
+    ref = _closed_form(q, k, v, la, np.arange(64))
+    assert _relerr(o, ref) < 1e-12
+
+
+def test_alpha_one_is_causal_linear_attention(orc):
+    """alpha == 1: o = tril(Q K^T) V, a plain masked matmul."""
+    x = _rand(2, 24, 3, 5, 7, seed=13)
+    la = np.zeros_like(x["log_alpha"])
+    o, sf = orc.gla_fwd(x["q"], x["k"], x["v"], la, (4, 6), "l2r")
+    for b in range(2):
+        for h in range(3):
+            Q, K, V = x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h]
+            ref = np.tril(Q @ K.T) @ V
+            assert _relerr(o[b, :, h], ref) < 1e-12
+            assert _relerr(sf[b, h], K.T @ V) < 1e-12
+
+
+def test_alpha_zero_keeps_only_current_token(orc):
+    """log alpha = -1e4 (alpha underflows to 0): o_t = (q_t . k_t) v_t (up to summation order), S_final = k_T^T v_T exactly."""
+    x = _rand(1, 12, 2, 4, 3, seed=14)
+    la = np.full_like(x["log_alpha"], -1e4)
+    o, sf = orc.gla_fwd(x["q"], x["k"], x["v"], la, (3, 4), "b2t")
+    perm = orc.scan_perm("b2t", 3, 4)
+    for h in range(2):
+        for t in range(12):
+            n = perm[t]
+            ref = np.dot(x["q"][0, n, h], x["k"][0, n, h]) * x["v"][0, n, h]
+            np.testing.assert_allclose(o[0, t, h], ref, rtol=1e-14, atol=0)
+        n = perm[-1]
+        assert np.array_equal(sf[0, h], np.outer(x["k"][0, n, h], x["v"][0, n, h]))
+
+
+@pytest.mark.parametrize("a", [0.5, 0.9, 0.999])
+def test_scalar_geometric_series(orc, a):
+    """d=1, q=k=v=1, alpha=a: o_t = (1 - a^(t+1)) / (1 - a)."""
+    T = 50
+    ones = np.ones((1, T, 1, 1))
+    la = np.full((1, T, 1, 1), math.log(a))
+    o, sf = orc.gla_fwd(ones, ones, ones, la, (5, 10), "l2r")
+    t = np.arange(T)
+    ref = (1 - a ** (t + 1)) / (1 - a)
+    np.testing.assert_allclose(o[0, :, 0, 0], ref, rtol=1e-13)
+    np.testing.assert_allclose(sf[0, 0, 0, 0], ref[-1], rtol=1e-13)
+
+
+# ------------------------------------------------------ structural identities
+
+def test_state_chaining_resume(orc):
+    """Two calls with s0 = S_final of the first equal one call over the whole scan."""
+    T1, T2 = 17, 23
+    x = _rand(2, T1 + T2, 2, 4, 5, seed=15, gate_div=4.0)
+    o, sf = orc.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], (1, T1 + T2), "l2r")
+    part = lambda a, s, e: np.ascontiguousarray(a[:, s:e])
+    o1, s1 = orc.gla_fwd(*(part(x[n], 0, T1) for n in ("q", "k", "v", "log_alpha")), (1, T1), "l2r")
+    o2, s2 = orc.gla_fwd(*(part(x[n], T1, T1 + T2) for n in ("q", "k", "v", "log_alpha")),
+                         (1, T2), "l2r", s0=s1)
+    assert _relerr(np.concatenate([o1, o2], 1), o) < 1e-13
+    assert _relerr(s2, sf) < 1e-13
+
+
+def test_linearity_in_v(orc):
+    x = _rand(1, 20, 2, 3, 4, seed=16)
+    v2 = np.random.default_rng(3).standard_normal(x["v"].shape)
+    oa, _ = orc.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], (4, 5), "t2b")
+    ob, _ = orc.gla_fwd(x["q"], x["k"], v2, x["log_alpha"], (4, 5), "t2b")
+    oc, _ = orc.gla_fwd(x["q"], x["k"], x["v"] + v2, x["log_alpha"], (4, 5), "t2b")
+    assert _relerr(oa + ob, oc) < 1e-12
+
+
+def test_scan_perm_library_forms(orc):
+    """Permutations vs numpy reshapes/transposes: row-major, reversed, transposed."""
+    for gh, gw in [(4, 4), (3, 7), (1, 9), (8, 1)]:
+        T = gh * gw
+        grid = np.arange(T).reshape(gh, gw)
+        l2r = orc.scan_perm("l2r", gh, gw)
+        t2b = orc.scan_perm("t2b", gh, gw)
+        assert np.array_equal(l2r, grid.ravel())
+        assert np.array_equal(orc.scan_perm("r2l", gh, gw), grid.ravel()[::-1])
+        assert np.array_equal(t2b, grid.T.ravel())
+        assert np.array_equal(orc.scan_perm("b2t", gh, gw), grid.T.ravel()[::-1])
+        for d in gen.DIRS:
+            assert np.array_equal(np.sort(orc.scan_perm(d, gh, gw)), np.arange(T))
+
+
+@pytest.mark.parametrize("direction", ["r2l", "t2b", "b2t"])
+def test_direction_equals_arranged_l2r(orc, direction):
+    """gla(x, dir) == gla(arrange_dir(x), l2r) exactly: the scan is the only thing dir changes."""
+    gh, gw = 4, 6
+    x = _rand(2, gh * gw, 2, 4, 4, seed=17)
+    perm = orc.scan_perm(direction, gh, gw)
+    o, sf = orc.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], (gh, gw), direction)
+    arr = {n: np.ascontiguousarray(x[n][:, perm]) for n in ("q", "k", "v", "log_alpha")}
+    o2, sf2 = orc.gla_fwd(arr["q"], arr["k"], arr["v"], arr["log_alpha"], (gh, gw), "l2r")
+    assert np.array_equal(o, o2) and np.array_equal(sf, sf2)
+
+
+def test_remap_is_exact_permutation(orc):
+    gh, gw = 5, 3
+    x = np.random.default_rng(7).standard_normal((2, gh * gw, 4))
+    for src in gen.DIRS:
+        for dst in gen.DIRS:
+            y = orc.remap(x, (gh, gw), src, dst)
+            ps, pd = orc.scan_perm(src, gh, gw), orc.scan_perm(dst, gh, gw)
+            canon = np.empty_like(x)
+            canon[:, ps] = x
+            assert np.array_equal(y, canon[:, pd])
+    # the four-step crisscross cycle returns the input
+    y = x
+    for i in range(4):
+        y = orc.remap(y, (gh, gw), gen.DIRS[i], gen.DIRS[(i + 1) % 4])
+    assert np.array_equal(y, x)
+
+
+# ---------------------------------------------------------------------- conv
+
+def test_dwconv_identity_is_exact(orc):
+    gh, gw, C = 6, 7, 5
+    x = np.random.default_rng(8).standard_normal((2, gh * gw, C))
+    w = np.zeros((C, 3, 3))
+    w[:, 1, 1] = 1.0
+    for d in gen.DIRS:
+        y = orc.srem_dwconv(x, w, (gh, gw), d)
+        assert np.array_equal(y, orc.remap(x, (gh, gw), d, "l2r"))
+
+
+@pytest.mark.parametrize("tap", [(0, 0), (0, 2), (2, 1), (1, 0)])
+def test_dwconv_one_hot_tap_is_shift(orc, tap):
+    gh, gw, C = 4, 5, 3
+    a, e = tap
+    x = np.random.default_rng(9).standard_normal((1, gh * gw, C))
+    w = np.zeros((C, 3, 3))
+    w[:, a, e] = 1.0
+    y = orc.srem_dwconv(x, w, (gh, gw), "l2r").reshape(gh, gw, C)
+    X = x.reshape(gh, gw, C)
+    ref = np.zeros_like(X)
+    for r in range(gh):
+        for c in range(gw):
+            rr, cc = r + a - 1, c + e - 1
+            if 0 <= rr < gh and 0 <= cc < gw:
+                ref[r, c] = X[rr, cc]
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("direction", ["l2r", "r2l", "t2b", "b2t"])
+def test_dwconv_vs_torch_conv2d(orc, direction):
+    """Against torch's grouped conv2d (fp64 CPU) applied in the scan frame."""
+    gh, gw, C, B = 5, 7, 6, 2
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((B, gh * gw, C))
+    w = rng.standard_normal((C, 3, 3))
+    y = orc.srem_dwconv(x, w, (gh, gw), direction)
+    R, Q = (gh, gw) if direction in ("l2r", "r2l") else (gw, gh)
+    X = torch.from_numpy(x).reshape(B, R, Q, C).permute(0, 3, 1, 2)
+    Y = torch.nn.functional.conv2d(X, torch.from_numpy(w)[:, None], padding=1, groups=C)
+    y_scan = Y.permute(0, 2, 3, 1).reshape(B, R * Q, C).numpy()
+    perm = orc.scan_perm(direction, gh, gw)
+    ref = np.empty_like(y_scan)
+    ref[:, perm] = y_scan
+    assert _relerr(y, ref) < 1e-13
+
+
+# --------------------------------------------------------------------- adaLN
+
+def test_adaln_vs_torch_layer_norm(orc):
+    rng = np.random.default_rng(11)
+    N, C = 37, 48
+    x = rng.standard_normal((N, C)) * 3 + 1
+    sc, sh = rng.standard_normal(C) * 0.1, rng.standard_normal(C) * 0.1
+    y = orc.adaln_modulate(x, sc, sh, eps=1e-6, out_scale=0.25)
+    ln = torch.nn.functional.layer_norm(torch.from_numpy(x), (C,), eps=1e-6).numpy()
+    ref = (ln * (1 + sc) + sh) * 0.25
+    assert _relerr(y, ref) < 1e-12
+
+
+def test_adaln_zero_modulation_is_standardisation(orc):
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((9, 64)) * 5 - 2
+    y = orc.adaln_modulate(x, np.zeros(64), np.zeros(64), eps=0.0, out_scale=1.0)
+    np.testing.assert_allclose(y.mean(1), 0, atol=1e-13)
+    np.testing.assert_allclose(y.var(1), 1, rtol=1e-12)
+
+
+# ------------------------------------------------------- planted mistakes
+
+def test_pins_reject_planted_mistakes(orc):
+    """Plausible slips in the recurrence must fail the closed form: check that they would."""
+    gh, gw = 3, 4
+    x = _rand(1, 12, 1, 3, 2, seed=18, gate_div=2.0)
+    perm = orc.scan_perm("t2b", gh, gw)
+    ref = _closed_form(x["q"], x["k"], x["v"], x["log_alpha"], perm)
+    a = np.exp(x["log_alpha"])
+
+    def run(variant):
+        S = np.zeros((3, 2))
+        o = np.zeros((12, 2))
+        for p in range(12):
+            n = perm[p]
+            qn, kn, vn, an = x["q"][0, n, 0], x["k"][0, n, 0], x["v"][0, n, 0], a[0, n, 0]
+            if variant == "read_before_write":
+                o[p] = qn @ (an[:, None] * S)
+                S = an[:, None] * S + np.outer(kn, vn)
+                continue
+            if variant == "gate_after_write":
+                S = an[:, None] * (S + np.outer(kn, vn))
+            else:
+                S = an[:, None] * S + np.outer(kn, vn)
+            o[p] = qn @ S
+        return o
+
+    assert _relerr(run("correct"), ref[0, :, 0]) < 1e-12
+    for bad in ("read_before_write", "gate_after_write"):
+        assert _relerr(run(bad), ref[0, :, 0]) > 1e-3
