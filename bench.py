@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the DiG token-mixer hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config C2] [--gpus 1]
+
+One step = one pass of the whole path over one batch of synthetic input:
+gla_fwd (chunk-wise GLA forward in the step's scan direction, directions
+cycled step by step) followed by srem_dwconv (3x3 depthwise conv in the scan
+frame, stored back to canonical order = the direction remap); the full
+2048^2 step (--config C4) also runs the adaLN modulation first.  Inputs are
+resident in HBM before timing starts; input sets rotate so that consecutive
+steps do not find their inputs in the 256 MB Infinity Cache.
+
+Prints ONE JSON line with the throughput (tokens/s), the roofline of the
+dominant kernel (gla_fwd, HBM-bound) measured with HIP events on the stream
+it runs on, and the fp64 CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "GLA fwd tokens/sec + % MFMA/HBM roofline, DiG-XL/2 shape T=4096 d=72"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gla_alg_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one gla_fwd call: read q, k, v, log_alpha, write o (bf16) + fp32 final state."""
+    el = 2 if cfg.dtype == "bf16" else 4
+    return cfg.B * cfg.H * cfg.T * cfg.d * el * 5 + cfg.B * cfg.H * cfg.d * cfg.d * 4
+
+
+def gla_alg_flops(cfg, M=64) -> int:
+    """Chunk-wise algorithmic flops: B*H*T*(4*M*d + 4*d^2) (QK^T, PV, Q~S, K^T V tiles)."""
+    return cfg.B * cfg.H * cfg.T * (4 * M * cfg.d + 4 * cfg.d * cfg.d)
+
+
+def conv_alg_bytes(cfg) -> int:
+    el = 2 if cfg.dtype == "bf16" else 4
+    return 2 * cfg.B * cfg.T * cfg.C * el + cfg.C * 9 * 4
+
+
+def traffic_record(cfg_key: str):
+    """Measured HBM bytes per gla_fwd launch from a committed rocprofv3 PMC summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"gla_fwd_{cfg_key.lower()}_traffic.json")
+    src = os.path.join(ROOT, "gated_linear_attention_gla_amd", "csrc", "gla_bf16.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("kernel_src_sha256") != sha:
+            return None
+        return float(rec["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(cfg, x_cpu, budget_s: float = 20.0):
+    """The fp64 oracle (as it stands) on this host: GLA + conv over a bounded sample of (b, h)
+    units of the same workload, scaled to tokens/s of the whole batch."""
+    import numpy as np
+    from oracle import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    units = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    direction = cfg.direction(0)
+    grid = (cfg.gh, cfg.gw)
+
+    def run(sample):
+        t0 = time.perf_counter()
+        bs = sorted({b for b, _ in sample})
+        for b in bs:
+            hs = [h for bb, h in sample if bb == b]
+            sl = lambda t: t[b:b + 1][:, :, hs].contiguous()
+            if cfg.adaln:
+                m = oracle.adaln_modulate(x_cpu["x_qkv"][:, b:b + 1], x_cpu["ada_scale"], x_cpu["ada_shift"],
+                                          1e-6, x_cpu["ada_out_scale"], nthreads=threads)
+                m = m.reshape(3, 1, cfg.T, cfg.H, cfg.d)[:, :, :, hs]
+                q, k, v = (np.ascontiguousarray(m[i]) for i in range(3))
+            else:
+                q, k, v = sl(x_cpu["q"]), sl(x_cpu["k"]), sl(x_cpu["v"])
+            o, _ = oracle.gla_fwd(q, k, v, sl(x_cpu["log_alpha"]), grid, direction, nthreads=threads)
+            ch = np.concatenate([np.arange(h * cfg.d, (h + 1) * cfg.d) for h in hs])
+            oracle.srem_dwconv(o.reshape(1, cfg.T, len(hs) * cfg.d), x_cpu["w"][ch], grid, direction,
+                               nthreads=threads)
+        return time.perf_counter() - t0
+
+    # probe with as many units as threads, then size the sample to the budget
+    probe = units[:min(len(units), threads)]
+    tp = run(probe)
+    n = len(probe)
+    if tp < budget_s / 4 and n < len(units):
+        want = int(n * (budget_s * 0.6) / max(tp, 1e-3) / threads) * threads
+        want = max(n, min(len(units), want))
+        if want > n:
+            sample = units[:want]
+            tp = run(sample)
+            n = want
+    est_full = tp * len(units) / n
+    return {
+        "value": cfg.B * cfg.T / est_full,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} of {len(units)} (batch, head) units of {cfg.key} "
+                  f"({'adaLN + ' if cfg.adaln else ''}GLA fwd + conv, dir {direction}, fp64, "
+                  f"{threads} OpenMP threads): {tp:.2f} s, scaled to the whole batch",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4"])
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 512 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {a.gpus} is not supported "
+              "(head/batch sharding needs no communication; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from gated_linear_attention_gla_amd import binding as dg
+    from gated_linear_attention_gla_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dg.lib()
+    dev = torch.device("cuda:0")
+    cfg = gen.CONFIGS[a.config]
+    B, T, H, d, C = cfg.B, cfg.T, cfg.H, cfg.d, cfg.C
+    grid = (cfg.gh, cfg.gw)
+
+    ws_bytes = gla_alg_bytes(cfg) + conv_alg_bytes(cfg)
+    nsets = a.sets or max(1, math.ceil(512e6 / ws_bytes))
+    log(f"[bench] {cfg.key} {cfg.name}: B={B} H={H} T={T} ({cfg.gh}x{cfg.gw}) d={d}; {nsets} input sets")
+    sets = []
+    for i in range(nsets):
+        x = gen.make_inputs(cfg.key, set_index=i, device=dev)
+        bufs = {"o": torch.empty(B, T, H, d, dtype=torch.bfloat16, device=dev),
+                "sf": torch.empty(B, H, d, d, dtype=torch.float32, device=dev),
+                "y": torch.empty(B, T, C, dtype=torch.bfloat16, device=dev)}
+        if cfg.adaln:
+            bufs["m"] = torch.empty_like(x["x_qkv"])
+        sets.append((x, bufs))
+    nbytes = dg.workspace_bytes(dg.DIG_BF16, B, T, H, d, d, cfg.chunk)
+    ws = dg.get_workspace(dev, nbytes)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = []
+
+    def step(i, timed=False):
+        x, bf = sets[i % nsets]
+        direction = cfg.direction(i)
+        if cfg.adaln:
+            m = dg.adaln_modulate(x["x_qkv"], x["ada_scale"], x["ada_shift"], 1e-6, x["ada_out_scale"], out=bf["m"])
+            q, k, v = (m[j].view(B, T, H, d) for j in range(3))
+        else:
+            q, k, v = x["q"], x["k"], x["v"]
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        dg.gla_fwd(q, k, v, x["log_alpha"], grid, direction, chunk=cfg.chunk, out=bf["o"], s_final=bf["sf"],
+                   workspace=ws)
+        if timed:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(stream)
+            ev.append((e0, e1))
+        dg.srem_dwconv(bf["o"].view(B, T, C), x["w"], grid, direction, out=bf["y"])
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, bracketed by synchronisation
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(a.warmup + i, timed=True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / a.steps
+    gla_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    gla_avg_ms = sum(gla_ms) / len(gla_ms)
+    gla_sorted = sorted(gla_ms)
+
+    tokens = B * T
+    value = tokens / (ms_step * 1e-3)
+    abytes = gla_alg_bytes(cfg)
+    aflops = gla_alg_flops(cfg)
+    achieved = abytes / (gla_avg_ms * 1e-3) / 1e9
+    traffic = traffic_record(cfg.key)
+    log(f"[bench] step {ms_step * 1e3:.1f} us, gla_fwd avg {gla_avg_ms * 1e3:.1f} us "
+        f"(p10 {gla_sorted[len(gla_sorted) // 10] * 1e3:.1f}, p90 {gla_sorted[(9 * len(gla_sorted)) // 10] * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s, wall {wall:.3f} s")
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle on a bounded sample ...")
+        x_cpu = {k_: (v_.cpu() if isinstance(v_, torch.Tensor) else v_) for k_, v_ in sets[0][0].items()}
+        cpu = cpu_baseline(cfg, x_cpu)
+        log(f"[bench] cpu oracle: {cpu['value']:.3e} tokens/s on {cpu['cores']} cores")
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian activations of the DiG latent-grid shape; no dataset or weights)",
+        "config": {"workload": f"{cfg.key} {cfg.name}: GLA fwd (chunk {cfg.chunk}, fp32 state) + "
+                               f"SREM 3x3 dwconv/remap{', adaLN prologue' if cfg.adaln else ''}",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "grid": list(grid),
+                   "directions": list(cfg.dirs), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gla_fwd_bf16_kernel", "alg_bytes_per_launch": abytes,
+                     "avg_launch_us": gla_avg_ms * 1e3},
+        "gla_fwd": {"tokens_per_s": tokens / (gla_avg_ms * 1e-3), "tflops_alg": aflops / (gla_avg_ms * 1e-3) / 1e12,
+                    "mfma_frac": aflops / (gla_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "p10_us": gla_sorted[len(gla_sorted) // 10] * 1e3,
+                    "p90_us": gla_sorted[(9 * len(gla_sorted)) // 10] * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

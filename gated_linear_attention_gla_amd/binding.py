@@ -1,0 +1,194 @@
+"""Thin ctypes binding over libdig_gla.so (include/dig_gla.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback of any kind: if the library is missing or a call fails,
+an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdig_gla.so")
+
+DIG_F32, DIG_BF16 = 0, 1
+DIRS = {"l2r": 0, "r2l": 1, "t2b": 2, "b2t": 3}
+_lock = threading.Lock()
+_lib = None
+_ws_cache: dict = {}
+
+
+class DigError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdig_gla.so (built in-tree); raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise DigError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m gated_linear_attention_gla_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            p, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+            L.gla_fwd.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
+                                  i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                  p, p, i64, i64, i64, p, p, sz, p]
+            L.gla_fwd.restype = i32
+            L.gla_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+            L.gla_fwd_workspace_size.restype = sz
+            L.srem_dwconv.argtypes = [p, i32, i32, i32, i32, i64, i64, p, i32, i32, i32, p, i64, i64, p]
+            L.srem_dwconv.restype = i32
+            L.srem_remap.argtypes = [p, i32, i32, i32, i32, i32, i32, i32, i32, p, p]
+            L.srem_remap.restype = i32
+            L.dig_adaln_modulate.argtypes = [p, i32, i64, i32, i64, p, p, f32, f32, p, i64, p]
+            L.dig_adaln_modulate.restype = i32
+            L.dig_last_error.argtypes = []
+            L.dig_last_error.restype = ctypes.c_char_p
+            L.dig_version.argtypes = []
+            L.dig_version.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        msg = lib().dig_last_error().decode(errors="replace")
+        raise DigError(f"{what} failed ({rc}): {msg}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DIG_BF16
+    if t.dtype == torch.float32:
+        return DIG_F32
+    raise DigError(f"unsupported dtype {t.dtype}")
+
+
+def _dir(d) -> int:
+    return DIRS[d] if isinstance(d, str) else int(d)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_bytes(dtype_code: int, B: int, T: int, H: int, dk: int, dv: int, chunk: int = 0) -> int:
+    n = lib().gla_fwd_workspace_size(dtype_code, B, T, H, dk, dv, chunk)
+    if n == ctypes.c_size_t(-1).value:
+        raise DigError("gla_fwd_workspace_size: invalid sizes: " + lib().dig_last_error().decode())
+    return int(n)
+
+
+def get_workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
+    """A cached, zero-initialised workspace of at least nbytes on `device` (grown on demand)."""
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def gla_fwd(q, k, v, log_alpha, grid, direction, chunk: int = 0, s0=None, out=None,
+            s_final: bool | torch.Tensor = True, workspace=None):
+    """GLA forward over one scan direction.
+
+    q, k, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; canonical token order,
+    innermost dim contiguous, all on one GPU, same dtype (bf16 or fp32).
+    Returns (o [B, T, H, dv] in SCAN order, s_final [B, H, dk, dv] fp32 or None).
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or log_alpha.shape != q.shape or tuple(v.shape[:3]) != (B, T, H):
+        raise DigError("gla_fwd: shape mismatch")
+    for t in (q, k, v, log_alpha):
+        if t.stride(3) != 1 or t.dtype != q.dtype or t.device != q.device:
+            raise DigError("gla_fwd: tensors must share dtype/device and have a contiguous last dim")
+    if k.stride() != q.stride() or log_alpha.stride() != q.stride():
+        raise DigError("gla_fwd: q, k, log_alpha must share strides")
+    dc = _dtype_code(q)
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, T, H, dv, dtype=q.dtype, device=dev)
+    sf = None
+    if isinstance(s_final, torch.Tensor):
+        sf = s_final
+    elif s_final:
+        sf = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    if s0 is not None:
+        if s0.dtype != torch.float32 or tuple(s0.shape) != (B, H, dk, dv) or not s0.is_contiguous():
+            raise DigError("gla_fwd: s0 must be contiguous fp32 [B, H, dk, dv]")
+    if workspace is None:
+        workspace = get_workspace(dev, workspace_bytes(dc, B, T, H, dk, dv, chunk))
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    gh, gw = grid
+    rc = lib().gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), dc,
+                       q.stride(0), q.stride(1), q.stride(2), v.stride(0), v.stride(1), v.stride(2),
+                       B, T, H, dk, dv, gh, gw, _dir(direction), chunk,
+                       _ptr(s0), _ptr(out), out.stride(0), out.stride(1), out.stride(2),
+                       _ptr(sf), _ptr(workspace), wsb, _stream(dev))
+    _check(rc, "gla_fwd")
+    return out, sf
+
+
+def srem_dwconv(x_scan, w, grid, direction, out=None):
+    """x_scan [B, T, C] (scan order of `direction`), w fp32 [C, 3, 3] -> y [B, T, C] canonical order."""
+    B, T, C = x_scan.shape
+    if x_scan.stride(2) != 1:
+        raise DigError("srem_dwconv: channels must be contiguous")
+    if w.dtype != torch.float32 or tuple(w.shape) != (C, 3, 3) or not w.is_contiguous():
+        raise DigError("srem_dwconv: w must be contiguous fp32 [C, 3, 3]")
+    if out is None:
+        out = torch.empty(B, T, C, dtype=x_scan.dtype, device=x_scan.device)
+    rc = lib().srem_dwconv(_ptr(x_scan), _dtype_code(x_scan), B, T, C, x_scan.stride(0), x_scan.stride(1),
+                           _ptr(w), grid[0], grid[1], _dir(direction), _ptr(out), out.stride(0),
+                           out.stride(1), _stream(x_scan.device))
+    _check(rc, "srem_dwconv")
+    return out
+
+
+def srem_remap(x, grid, src, dst, out=None):
+    """Contiguous x [B, T, C] in scan order `src` -> y in scan order `dst`."""
+    B, T, C = x.shape
+    if not x.is_contiguous():
+        raise DigError("srem_remap: x must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib().srem_remap(_ptr(x), _dtype_code(x), B, T, C, grid[0], grid[1], _dir(src), _dir(dst),
+                          _ptr(out), _stream(x.device))
+    _check(rc, "srem_remap")
+    return out
+
+
+def adaln_modulate(x, scale, shift, eps: float = 1e-6, out_scale: float = 1.0, out=None):
+    """x [..., C] (rows contiguous) -> LN over C, * (1 + scale) + shift, * out_scale."""
+    C = x.shape[-1]
+    if not x.is_contiguous():
+        raise DigError("adaln_modulate: x must be contiguous")
+    N = x.numel() // C
+    if out is None:
+        out = torch.empty_like(x)
+    for t in (scale, shift):
+        if t.dtype != torch.float32 or t.numel() != C or not t.is_contiguous():
+            raise DigError("adaln_modulate: scale/shift must be contiguous fp32 [C]")
+    rc = lib().dig_adaln_modulate(_ptr(x), _dtype_code(x), N, C, C, _ptr(scale), _ptr(shift),
+                                  float(eps), float(out_scale), _ptr(out), C, _stream(x.device))
+    _check(rc, "dig_adaln_modulate")
+    return out
+
+
+def version() -> str:
+    return lib().dig_version().decode()

@@ -1,0 +1,229 @@
+// api.cpp -- the C ABI of libdig_gla.so (declared in include/dig_gla.h):
+// argument validation (before any HIP call), device checks, dispatch to the
+// kernel launchers, error codes and the thread-local error message.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/dig_gla.h"
+#include "dig_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(DIG_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device facts, looked up once per device.
+struct DevInfo {
+  bool ok = false;
+  int num_cu = 0;
+};
+constexpr int kMaxDev = 64;
+DevInfo g_dev[kMaxDev];
+std::once_flag g_dev_once[kMaxDev];
+
+int current_device(DevInfo &out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) return fail(DIG_ENODEV, "device index %d out of range", dev);
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    g_dev[dev].ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev[dev].num_cu = prop.multiProcessorCount;
+  });
+  out = g_dev[dev];
+  if (!out.ok) return fail(DIG_ENODEV, "device %d is not a gfx950 (MI355X) GPU", dev);
+  return DIG_OK;
+}
+
+std::atomic<uint32_t> g_epoch{1};
+
+int auto_chunk(int dtype, int chunk) {
+  if (chunk != 0) return chunk;
+  return dtype == DIG_BF16 ? 64 : 16;
+}
+
+int check_gla_sizes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+  if (dtype != DIG_F32 && dtype != DIG_BF16) return fail(DIG_EINVAL, "gla_fwd: dtype must be DIG_F32 or DIG_BF16");
+  if (B <= 0 || T <= 0 || H <= 0) return fail(DIG_EINVAL, "gla_fwd: B, T, H must be positive");
+  if (dk <= 0 || dv <= 0 || dk > 128 || dv > 128)
+    return fail(DIG_EINVAL, "gla_fwd: dk and dv must be in [1, 128] (got %d, %d)", dk, dv);
+  if ((int64_t)B * H > (int64_t)1 << 30) return fail(DIG_EINVAL, "gla_fwd: B*H too large");
+  const int M = auto_chunk(dtype, chunk);
+  if (dtype == DIG_BF16) {
+    if (dk % 8 || dv % 8) return fail(DIG_EINVAL, "gla_fwd: bf16 path needs dk, dv multiples of 8");
+    if (M != 16 && M != 32 && M != 64) return fail(DIG_EINVAL, "gla_fwd: bf16 chunk must be 0, 16, 32 or 64");
+  } else {
+    if (M != 16 && M != 32) return fail(DIG_EINVAL, "gla_fwd: fp32 chunk must be 0, 16 or 32");
+  }
+  return DIG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dig_last_error(void) { return g_err.c_str(); }
+
+const char *dig_version(void) { return "dig_gla 0.1.0 (gfx950)"; }
+
+size_t gla_fwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+  if (check_gla_sizes(dtype, B, T, H, dk, dv, chunk) != DIG_OK) return (size_t)-1;
+  if (dtype == DIG_F32) return 0;
+  DevInfo di;
+  const int num_cu = (current_device(di) == DIG_OK) ? di.num_cu : 256;
+  return dig_gla_bf16_workspace(B, T, H, dk, dv, auto_chunk(dtype, chunk), num_cu);
+}
+
+int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+            int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+            int B, int T, int H, int dk, int dv, int gh, int gw, int dir, int chunk,
+            const float *s0, void *o, int64_t o_sb, int64_t o_st, int64_t o_sh, float *s_final,
+            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    int rc = check_gla_sizes(dtype, B, T, H, dk, dv, chunk);
+    if (rc) return rc;
+    if (!q || !k || !v || !log_alpha || !o) return fail(DIG_EINVAL, "gla_fwd: q, k, v, log_alpha and o are required");
+    if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
+      return fail(DIG_EINVAL, "gla_fwd: grid %dx%d does not hold T=%d tokens", gh, gw, T);
+    if (dir < DIG_L2R || dir > DIG_B2T) return fail(DIG_EINVAL, "gla_fwd: dir must be 0..3");
+    if (qk_sb < 0 || qk_st < 0 || qk_sh < 0 || v_sb < 0 || v_st < 0 || v_sh < 0 || o_sb < 0 || o_st < 0 || o_sh < 0)
+      return fail(DIG_EINVAL, "gla_fwd: negative stride");
+    if (o == q || o == k || o == v || o == log_alpha) return fail(DIG_EINVAL, "gla_fwd: o aliases an input");
+    const int M = auto_chunk(dtype, chunk);
+    if (dtype == DIG_BF16) {
+      if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(o))
+        return fail(DIG_EINVAL, "gla_fwd: bf16 path needs 16-byte aligned q, k, v, log_alpha, o");
+      if ((qk_sb | qk_st | qk_sh | v_sb | v_st | v_sh) % 8)
+        return fail(DIG_EINVAL, "gla_fwd: bf16 input strides must be multiples of 8 elements");
+      if ((o_sb | o_st | o_sh) % 4) return fail(DIG_EINVAL, "gla_fwd: bf16 output strides must be multiples of 4");
+    } else {
+      if (dig_gla_f32_lds_bytes(dk, dv, M) > 160 * 1024)
+        return fail(DIG_EINVAL, "gla_fwd: fp32 path LDS need exceeds 160 KiB for dk=%d dv=%d chunk=%d", dk, dv, M);
+    }
+    DevInfo di;
+    rc = current_device(di);
+    if (rc) return rc;
+    const size_t need = dtype == DIG_BF16 ? dig_gla_bf16_workspace(B, T, H, dk, dv, M, di.num_cu) : 0;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(DIG_EWORKSPACE, "gla_fwd: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      return fail(DIG_EINVAL, "gla_fwd: workspace must be 256-byte aligned");
+
+    DigGlaArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = log_alpha;
+    a.qk_sb = qk_sb; a.qk_st = qk_st; a.qk_sh = qk_sh;
+    a.v_sb = v_sb; a.v_st = v_st; a.v_sh = v_sh;
+    a.o_sb = o_sb; a.o_st = o_st; a.o_sh = o_sh;
+    a.o = o; a.s0 = s0; a.s_final = s_final;
+    a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.gh = gh; a.gw = gw; a.dir = dir; a.chunk = M;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    a.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) & 0x3fffffffu;
+    a.num_cu = di.num_cu;
+    const hipError_t e = dtype == DIG_BF16 ? dig_launch_gla_bf16(a, stream) : dig_launch_gla_f32(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "gla_fwd launch");
+    return DIG_OK;
+  } catch (...) {
+    return fail(DIG_EHIP, "gla_fwd: unexpected C++ exception");
+  }
+}
+
+int srem_dwconv(const void *x_scan, int dtype, int B, int T, int C, int64_t x_sb, int64_t x_st,
+                const float *w, int gh, int gw, int dir, void *y, int64_t y_sb, int64_t y_st,
+                hipStream_t stream) {
+  try {
+    if (dtype != DIG_F32 && dtype != DIG_BF16) return fail(DIG_EINVAL, "srem_dwconv: bad dtype");
+    if (!x_scan || !w || !y) return fail(DIG_EINVAL, "srem_dwconv: x_scan, w and y are required");
+    if (B <= 0 || T <= 0 || C <= 0) return fail(DIG_EINVAL, "srem_dwconv: B, T, C must be positive");
+    if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
+      return fail(DIG_EINVAL, "srem_dwconv: grid %dx%d does not hold T=%d tokens", gh, gw, T);
+    if (dir < DIG_L2R || dir > DIG_B2T) return fail(DIG_EINVAL, "srem_dwconv: dir must be 0..3");
+    const int vec = dtype == DIG_BF16 ? 8 : 4;
+    if (C % vec) return fail(DIG_EINVAL, "srem_dwconv: C must be a multiple of %d", vec);
+    if (!aligned16(x_scan) || !aligned16(y)) return fail(DIG_EINVAL, "srem_dwconv: x and y must be 16-byte aligned");
+    if ((x_sb | x_st | y_sb | y_st) % vec || x_sb < 0 || x_st < C || y_sb < 0 || y_st < C)
+      return fail(DIG_EINVAL, "srem_dwconv: strides must be multiples of %d and token strides >= C", vec);
+    if (x_scan == y) return fail(DIG_EINVAL, "srem_dwconv: in-place is not allowed");
+    DevInfo di;
+    int rc = current_device(di);
+    if (rc) return rc;
+    const hipError_t e = dig_launch_dwconv(x_scan, dtype, B, T, C, x_sb, x_st, w, gh, gw, dir, y, y_sb, y_st,
+                                           di.num_cu, stream);
+    if (e != hipSuccess) return hip_fail(e, "srem_dwconv launch");
+    return DIG_OK;
+  } catch (...) {
+    return fail(DIG_EHIP, "srem_dwconv: unexpected C++ exception");
+  }
+}
+
+int srem_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw, int from, int to, void *y,
+               hipStream_t stream) {
+  try {
+    if (dtype != DIG_F32 && dtype != DIG_BF16) return fail(DIG_EINVAL, "srem_remap: bad dtype");
+    if (!x || !y) return fail(DIG_EINVAL, "srem_remap: x and y are required");
+    if (B <= 0 || T <= 0 || C <= 0) return fail(DIG_EINVAL, "srem_remap: B, T, C must be positive");
+    if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
+      return fail(DIG_EINVAL, "srem_remap: grid %dx%d does not hold T=%d tokens", gh, gw, T);
+    if (from < DIG_L2R || from > DIG_B2T || to < DIG_L2R || to > DIG_B2T)
+      return fail(DIG_EINVAL, "srem_remap: directions must be 0..3");
+    const int vec = dtype == DIG_BF16 ? 8 : 4;
+    if (C % vec) return fail(DIG_EINVAL, "srem_remap: C must be a multiple of %d", vec);
+    if (!aligned16(x) || !aligned16(y)) return fail(DIG_EINVAL, "srem_remap: x and y must be 16-byte aligned");
+    if (x == y) return fail(DIG_EINVAL, "srem_remap: in-place is not allowed");
+    DevInfo di;
+    int rc = current_device(di);
+    if (rc) return rc;
+    const hipError_t e = dig_launch_remap(x, dtype, B, T, C, gh, gw, from, to, y, di.num_cu, stream);
+    if (e != hipSuccess) return hip_fail(e, "srem_remap launch");
+    return DIG_OK;
+  } catch (...) {
+    return fail(DIG_EHIP, "srem_remap: unexpected C++ exception");
+  }
+}
+
+int dig_adaln_modulate(const void *x, int dtype, int64_t N, int C, int64_t x_sn, const float *scale,
+                       const float *shift, float eps, float out_scale, void *y, int64_t y_sn,
+                       hipStream_t stream) {
+  try {
+    if (dtype != DIG_F32 && dtype != DIG_BF16) return fail(DIG_EINVAL, "dig_adaln_modulate: bad dtype");
+    if (!x || !scale || !shift || !y) return fail(DIG_EINVAL, "dig_adaln_modulate: x, scale, shift, y are required");
+    const int vec = dtype == DIG_BF16 ? 8 : 4;
+    if (N <= 0 || C <= 0 || C % vec || C / vec > 2048)
+      return fail(DIG_EINVAL, "dig_adaln_modulate: need N > 0 and C a multiple of %d with C/%d <= 2048", vec, vec);
+    if (!aligned16(x) || !aligned16(y)) return fail(DIG_EINVAL, "dig_adaln_modulate: x and y must be 16-byte aligned");
+    if (x_sn < C || y_sn < C || x_sn % vec || y_sn % vec)
+      return fail(DIG_EINVAL, "dig_adaln_modulate: row strides must be >= C and multiples of %d", vec);
+    if (!(eps >= 0.f)) return fail(DIG_EINVAL, "dig_adaln_modulate: eps must be >= 0");
+    DevInfo di;
+    int rc = current_device(di);
+    if (rc) return rc;
+    const hipError_t e = dig_launch_adaln(x, dtype, N, C, x_sn, scale, shift, eps, out_scale, y, y_sn, stream);
+    if (e != hipSuccess) return hip_fail(e, "dig_adaln_modulate launch");
+    return DIG_OK;
+  } catch (...) {
+    return fail(DIG_EHIP, "dig_adaln_modulate: unexpected C++ exception");
+  }
+}
+
+}  // extern "C"

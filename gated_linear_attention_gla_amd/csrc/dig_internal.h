@@ -1,0 +1,101 @@
+// dig_internal.h -- internal declarations shared by the HIP sources of
+// libdig_gla.so (kernels, launchers and the C ABI layer).  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dig {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Scan order over a (gh x gw) grid, canonical order row-major (n = r*gw + c).
+// DiG paper notes, 关键设计 / SREM: left->right, right->left, top->bottom and
+// bottom->top scans made by transposing the 2D token matrix and flipping the
+// sequence (flip = reversal of the whole sequence).
+//   0 L2R: n = p            1 R2L: n = T-1-p
+//   2 T2B: n = (p % gh) * gw + p / gh
+//   3 B2T: T2B index of T-1-p
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int scan_to_canon(int dir, int gh, int gw, int T, int p) {
+  const int s = (dir & 1) ? (T - 1 - p) : p;   // R2L and B2T walk backwards
+  if (dir < 2) return s;
+  const int col = (int)((unsigned)s / (unsigned)gh);
+  const int row = s - col * gh;
+  return row * gw + col;
+}
+
+// Inverse: the scan position at which canonical index n is visited.
+__host__ __device__ __forceinline__ int canon_to_scan(int dir, int gh, int gw, int T, int n) {
+  int s = n;
+  if (dir >= 2) {
+    const int row = (int)((unsigned)n / (unsigned)gw);
+    const int col = n - row * gw;
+    s = col * gh + row;
+  }
+  return (dir & 1) ? (T - 1 - s) : s;
+}
+
+// Frame of the scan-ordered sequence: (R, Q) = (gh, gw) for the row scans,
+// (gw, gh) for the column scans.
+__host__ __device__ __forceinline__ void scan_frame(int dir, int gh, int gw, int &R, int &Q) {
+  if (dir < 2) { R = gh; Q = gw; } else { R = gw; Q = gh; }
+}
+
+// XCD-aware workgroup order: MI355X deals workgroups round-robin over its 8
+// XCDs (each with its own L2), so workgroup i runs on XCD i % 8.  This maps
+// blockIdx.x to a logical index such that each XCD receives a contiguous
+// range of logical indices (neighbouring heads / tokens share cache lines and
+// L2 on one XCD).  grid must be a multiple of 8.
+__device__ __forceinline__ int xcd_linear_block(int bid, int grid) {
+  const int per = grid >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// ------------------------------- bf16 bits ---------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 round-to-nearest-even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+}  // namespace dig
+
+// ----------------------------- launchers -----------------------------------
+// Each returns hipSuccess or the launch error; arguments are validated by the
+// ABI layer before these are called.
+struct DigGlaArgs {
+  const void *q, *k, *v, *g;
+  int64_t qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
+  void *o;
+  const float *s0;
+  float *s_final;
+  int B, T, H, dk, dv, gh, gw, dir, chunk;
+  void *workspace;
+  size_t workspace_bytes;
+  uint32_t epoch;
+  int num_cu;
+};
+
+hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s);
+size_t dig_gla_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk, int num_cu);
+hipError_t dig_launch_gla_f32(const DigGlaArgs &a, hipStream_t s);
+size_t dig_gla_f32_lds_bytes(int dk, int dv, int chunk);
+
+hipError_t dig_launch_dwconv(const void *x, int dtype, int B, int T, int C, int64_t x_sb, int64_t x_st,
+                             const float *w, int gh, int gw, int dir, void *y, int64_t y_sb,
+                             int64_t y_st, int num_cu, hipStream_t s);
+hipError_t dig_launch_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw, int from,
+                            int to, void *y, int num_cu, hipStream_t s);
+hipError_t dig_launch_adaln(const void *x, int dtype, int64_t N, int C, int64_t x_sn, const float *scale,
+                            const float *shift, float eps, float out_scale, void *y, int64_t y_sn,
+                            hipStream_t s);

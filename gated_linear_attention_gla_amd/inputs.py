@@ -81,8 +81,8 @@ def torch_dtype(name: str) -> torch.dtype:
     return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
 
 
-def _gen(seed: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
+def _gen(seed: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     return g
 
@@ -92,12 +92,12 @@ def gate_from_normal(x: torch.Tensor) -> torch.Tensor:
     return F.logsigmoid(x) / 16.0
 
 
-def conv_weight(C: int, perturb: float, gen: torch.Generator | None) -> torch.Tensor:
+def conv_weight(C: int, perturb: float, gen: torch.Generator | None, device="cpu") -> torch.Tensor:
     """[C, 3, 3] fp32: identity 3x3 (centre 1, rest 0), plus N(0, perturb) if perturb > 0."""
-    w = torch.zeros(C, 3, 3, dtype=torch.float32)
+    w = torch.zeros(C, 3, 3, dtype=torch.float32, device=device)
     w[:, 1, 1] = 1.0
     if perturb > 0:
-        w += torch.randn(C, 3, 3, generator=gen, dtype=torch.float32) * perturb
+        w += torch.randn(C, 3, 3, generator=gen, dtype=torch.float32, device=device) * perturb
     return w
 
 
@@ -114,31 +114,32 @@ def gla_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", se
     return {"q": q, "k": k, "v": v, "log_alpha": g}
 
 
-def make_inputs(key: str, set_index: int = 0) -> dict:
-    """Materialise the inputs of one named workload on the CPU.
+def make_inputs(key: str, set_index: int = 0, device="cpu") -> dict:
+    """Materialise the inputs of one named workload.
 
     Draw order: q (or raw x_q), k (x_k), v (x_v), gate x, then the full-step
     extras (adaLN scale, shift, conv-weight perturbation).  `set_index` > 0
-    gives an independent set of the same shapes (rotating buffers).
+    gives an independent set of the same shapes (rotating buffers).  With
+    device="cuda" the draws come from the seeded device generator (a
+    different, equally seeded stream; used for large benchmark sets).
     """
     cfg = CONFIGS[key]
-    gen = _gen(cfg.seed + 7919 * set_index)
+    gen = _gen(cfg.seed + 7919 * set_index, device)
     B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.d
     td = torch_dtype(cfg.dtype)
     out = {"cfg": cfg}
     if cfg.adaln:
         # raw activations [3, B, T, C] (x_q, x_k, x_v), modulated on the path
-        xs = [torch.randn(B, T, H * d, generator=gen) for _ in range(3)]
+        xs = [torch.randn(B, T, H * d, generator=gen, device=device) for _ in range(3)]
         out["x_qkv"] = torch.stack(xs, 0).to(td)
     else:
-        out["q"] = (torch.randn(B, T, H, d, generator=gen) * cfg.qkv_scale).to(td)
-        out["k"] = (torch.randn(B, T, H, d, generator=gen) * cfg.qkv_scale).to(td)
-        out["v"] = (torch.randn(B, T, H, d, generator=gen) * cfg.qkv_scale).to(td)
-    x = torch.randn(B, T, H, d, generator=gen) + cfg.gate_mu
+        for n in ("q", "k", "v"):
+            out[n] = torch.randn(B, T, H, d, generator=gen, device=device).mul_(cfg.qkv_scale).to(td)
+    x = torch.randn(B, T, H, d, generator=gen, device=device).add_(cfg.gate_mu)
     out["log_alpha"] = gate_from_normal(x).to(td)
     if cfg.adaln:
-        out["ada_scale"] = torch.randn(H * d, generator=gen) * 0.1
-        out["ada_shift"] = torch.randn(H * d, generator=gen) * 0.1
+        out["ada_scale"] = torch.randn(H * d, generator=gen, device=device) * 0.1
+        out["ada_shift"] = torch.randn(H * d, generator=gen, device=device) * 0.1
         out["ada_out_scale"] = cfg.qkv_scale
-    out["w"] = conv_weight(H * d, cfg.conv_perturb, gen)
+    out["w"] = conv_weight(H * d, cfg.conv_perturb, gen, device)
     return out

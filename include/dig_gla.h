@@ -1,0 +1,195 @@
+/*
+ * dig_gla.h -- C ABI of the MI355X (gfx950) GLA forward + SREM library
+ *              (libdig_gla.so).
+ *
+ * The library computes the token mixer of a DiG block on one GPU:
+ *   gla_fwd       chunk-wise Gated Linear Attention forward, scanned in one
+ *                 of four SREM directions, output in scan order + final state;
+ *   srem_dwconv   3x3 depthwise conv in the scan frame, stored back to the
+ *                 canonical token order (the fused direction remap);
+ *   srem_remap    the exact permutation between two scan orders;
+ *   dig_adaln_modulate  the adaLN modulation that feeds the mixer.
+ *
+ * Sources (web pages, cited by title and section):
+ *   "DiG: Scalable and Efficient Diffusion Models with Gated Linear
+ *   Attention" paper notes (CVPR 2025): 关键设计 / SREM, 关键设计 / DiG
+ *   Block设计, 关键设计 / 硬件友好的效率设计;
+ *   the diffusers issue #20 of the same title: description bullets and the
+ *   draft recurrence (state orientation, gate over key rows, readout q.S);
+ *   "Scalable Diffusion Models with Transformers" notes, 3.2 (adaLN);
+ *   "ZigMa" paper notes (ECCV 2024), 关键设计 / 异构逐层扫描 (arrange, scan,
+ *   arrange back).
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch-owned
+ *     device memory) unless stated otherwise.  The caller owns every buffer
+ *     and keeps it alive until the work queued on `stream` has finished.
+ *   - The library never allocates or frees device memory and never
+ *     synchronises the stream.  Work is queued on `stream` (NULL = the
+ *     default stream of the current device); errors raised by a kernel while
+ *     it runs surface at the caller's next synchronisation.
+ *   - Strides are in ELEMENTS; the innermost (channel) dimension is contiguous.
+ *   - Return value: 0 on success; DIG_EINVAL for invalid arguments (checked
+ *     before any HIP call, nothing is queued); DIG_EWORKSPACE when the
+ *     workspace is too small; DIG_EHIP when a HIP call or launch fails;
+ *     DIG_ENODEV when the current device is not a gfx950.  After a non-zero
+ *     return, dig_last_error() describes it.  No C++ exception crosses the ABI.
+ *   - Calls on different streams are thread-safe, except that two calls in
+ *     flight at the same time must not share a gla_fwd workspace.
+ */
+#ifndef DIG_GLA_H
+#define DIG_GLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIG_OK 0
+#define DIG_EINVAL (-1)
+#define DIG_EWORKSPACE (-2)
+#define DIG_EHIP (-3)
+#define DIG_ENODEV (-4)
+
+/* Element types. */
+#define DIG_F32 0
+#define DIG_BF16 1
+
+/* Scan directions over a (gh x gw) token grid whose canonical order is
+ * row-major, n = r*gw + c.  Scan position p visits canonical index
+ *   DIG_L2R: n = p                                  (row-major)
+ *   DIG_R2L: n = T-1-p                              (row-major, reversed)
+ *   DIG_T2B: n = (p mod gh)*gw + floor(p / gh)      (column-major)
+ *   DIG_B2T: the DIG_T2B index of T-1-p             (column-major, reversed)
+ * (DiG paper notes, 关键设计 / SREM: four scans made with a transpose of the
+ * 2D token matrix and a flip of the sequence, the flip read as a reversal of
+ * the whole sequence.)  A DiG stack uses direction i mod 4 in block i. */
+#define DIG_L2R 0
+#define DIG_R2L 1
+#define DIG_T2B 2
+#define DIG_B2T 3
+
+/*
+ * gla_fwd -- Gated Linear Attention forward over one scan direction.
+ *
+ * For each batch b and head h, with S = s0[b,h] (or 0) a dk x dv fp32 state,
+ * and for scan positions p = 0..T-1 visiting canonical token n (see DIG_*):
+ *     S   = diag(exp(log_alpha[b,n,h,:])) * S + k[b,n,h,:]^T v[b,n,h,:]
+ *     o[b,p,h,:] = q[b,n,h,:] * S
+ * (the diffusers issue #20 recurrence: head_dim x head_dim state, forget
+ * gate over the key rows, current token written before the read; no feature
+ * map, normaliser or internal 1/sqrt(d)).  It is evaluated chunk-wise as the
+ * DiG notes (硬件友好的效率设计) describe: chunks of `chunk` tokens, causal
+ * intra-chunk products on bf16 MFMA with fp32 accumulation, the state kept
+ * in fp32 and handed from chunk to chunk and from segment to segment.
+ *
+ * Arguments
+ *   q, k, log_alpha  [B, T, H, dk] in CANONICAL token order, strides
+ *                    (qk_sb, qk_st, qk_sh) shared by the three tensors.
+ *   v                [B, T, H, dv] canonical order, strides (v_sb, v_st, v_sh).
+ *   dtype            DIG_BF16: q, k, v, log_alpha and o are bf16, the state
+ *                    and all accumulation are fp32 (MFMA path);
+ *                    DIG_F32: all fp32, evaluated on the vector ALUs.
+ *   B, T, H, dk, dv  sizes; T = gh*gw; 1 <= dk, dv <= 128.  The bf16 path
+ *                    needs dk and dv multiples of 8, 16-byte aligned q/k/v/
+ *                    log_alpha/o pointers and strides that are multiples of 8
+ *                    elements; the fp32 path takes any layout.
+ *   gh, gw, dir      the token grid and the scan direction.
+ *   chunk            tokens per chunk: 0 = automatic (64 for bf16, 16 for
+ *                    fp32); else 16, 32 or 64 (bf16) or 16, 32 (fp32).  The
+ *                    chunk size changes rounding only, never the result.
+ *   s0               nullable; [B, H, dk, dv] contiguous fp32 initial state.
+ *   o                [B, T, H, dv] written in SCAN order (row p is scan
+ *                    position p), strides (o_sb, o_st, o_sh).  Must not
+ *                    overlap any input.
+ *   s_final          nullable; [B, H, dk, dv] contiguous fp32, the state after
+ *                    scan position T-1.  Passing it as s0 of a later call
+ *                    continues the scan (state hand-off).
+ *   workspace        device memory of at least gla_fwd_workspace_size(...)
+ *                    bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST
+ *                    USE; the library keeps it consistent afterwards, so it
+ *                    can be reused by later calls of any size up to the one
+ *                    it was sized for (not by two calls in flight at once).
+ *                    May be NULL when the size function returns 0.
+ *   stream           HIP stream to queue on.
+ */
+int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
+            int dtype,
+            int64_t qk_sb, int64_t qk_st, int64_t qk_sh,
+            int64_t v_sb, int64_t v_st, int64_t v_sh,
+            int B, int T, int H, int dk, int dv,
+            int gh, int gw, int dir, int chunk,
+            const float *s0,
+            void *o, int64_t o_sb, int64_t o_st, int64_t o_sh,
+            float *s_final,
+            void *workspace, size_t workspace_bytes,
+            hipStream_t stream);
+
+/* Bytes of workspace gla_fwd needs for these sizes on the current device
+ * (state hand-off records between sequence segments, their flags and a
+ * ticket counter).  Returns 0 when no workspace is needed; (size_t)-1 for
+ * invalid sizes. */
+size_t gla_fwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+
+/*
+ * srem_dwconv -- SREM 3x3 depthwise conv with the direction remap fused in.
+ *
+ * x_scan is the mixer output in SCAN order of `dir` ([B, T, C], strides
+ * (x_sb, x_st), channels contiguous).  Its sequence is reshaped to the scan
+ * frame, (R, Q) = (gh, gw) for L2R/R2L and (gw, gh) for T2B/B2T, X[r][c] =
+ * x_scan[r*Q + c]; each channel is cross-correlated with its 3x3 kernel w[ch]
+ * (fp32 [C, 3, 3], contiguous) with zero padding and no bias; the result of
+ * scan position p = r*Q + c is stored at the CANONICAL index of p in y
+ * ([B, T, C], strides (y_sb, y_st)).  (DiG notes, 关键设计 / DiG Block设计
+ * steps 4-5 and 关键设计 / SREM; arrange-back of the ZigMa notes.)
+ * Accumulation is fp32; y has the dtype of x.  With the identity kernel
+ * (centre tap 1) y is exactly the canonical reordering of x.
+ * Constraints: C >= 1; bf16 needs C % 8 == 0 and 16-byte aligned pointers and
+ * strides; fp32 needs C % 4 == 0 and 16-byte alignment.  y must not overlap x.
+ */
+int srem_dwconv(const void *x_scan, int dtype, int B, int T, int C,
+                int64_t x_sb, int64_t x_st,
+                const float *w, int gh, int gw, int dir,
+                void *y, int64_t y_sb, int64_t y_st,
+                hipStream_t stream);
+
+/*
+ * srem_remap -- exact permutation of a [B, T, C] token tensor from scan order
+ * `from` to scan order `to` (the transpose/flip of DiG's SREM): the token at
+ * canonical index n moves from position inv_from(n) to position inv_to(n).
+ * Contiguous [B, T, C] in and out; bitwise copy; element size from dtype.
+ * Constraints as for srem_dwconv; y must not overlap x.
+ */
+int srem_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw,
+               int from, int to, void *y, hipStream_t stream);
+
+/*
+ * dig_adaln_modulate -- adaLN modulation of N rows (tokens) of C channels:
+ *   y = ((x - mean) / sqrt(var + eps) * (1 + scale) + shift) * out_scale
+ * with the population mean and variance of the row, computed in fp32.
+ * (DiG notes, 关键设计 / DiG Block设计 step 2: adaLN before the GLA; DiT notes,
+ * 3.2: scale/shift regressed from the conditioning, identity at init.)
+ * x, y: [N, C] with row strides x_sn, y_sn (elements), same dtype; scale and
+ * shift: fp32 [C].  Constraints: C % 8 == 0 (bf16) or C % 4 == 0 (fp32),
+ * 16-byte alignment, C <= 16384.  y may equal x (in place) but may not
+ * partially overlap it.
+ */
+int dig_adaln_modulate(const void *x, int dtype, int64_t N, int C, int64_t x_sn,
+                       const float *scale, const float *shift, float eps, float out_scale,
+                       void *y, int64_t y_sn, hipStream_t stream);
+
+/* Thread-local description of the last non-zero return on this thread. */
+const char *dig_last_error(void);
+
+/* Library version string. */
+const char *dig_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIG_GLA_H */

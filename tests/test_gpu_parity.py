@@ -1,0 +1,295 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Every test feeds the same materialised, seeded tensors to both sides.  Sizes
+the oracle finishes in seconds are compared element by element over whole
+outputs; the full-size workloads run in the benchmark's launch configuration
+and are compared on sampled (batch, head) units computed by the oracle one
+by one.  Tolerances (normwise per slice, see helpers.py): 1e-4 for the fp32
+path, 2e-2 for bf16 inputs with fp32 state; permutations and identity convs
+are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_linear_attention_gla_amd import binding as dg
+from gated_linear_attention_gla_amd import inputs as gen
+from helpers import (TOL_BF16, TOL_F32, assert_conv_close, assert_o_close, assert_state_close, to_np)
+
+pytestmark = pytest.mark.gpu
+DIRS = gen.DIRS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dg.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def np_perm(direction, gh, gw):
+    """Scan order from numpy reshapes (independent of both implementations)."""
+    grid = np.arange(gh * gw).reshape(gh, gw)
+    return {"l2r": grid.ravel(), "r2l": grid.ravel()[::-1], "t2b": grid.T.ravel(),
+            "b2t": grid.T.ravel()[::-1]}[direction].copy()
+
+
+def run_gla(x, grid, direction, chunk=0, s0=None):
+    o, sf = dg.gla_fwd(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["log_alpha"]), grid, direction,
+                       chunk=chunk, s0=None if s0 is None else dev(s0))
+    torch.cuda.synchronize()
+    return o.cpu(), sf.cpu()
+
+
+def oracle_gla(orc, x, grid, direction, s0=None, units=None):
+    q, k, v, g = x["q"], x["k"], x["v"], x["log_alpha"]
+    if units is not None:
+        outs = []
+        for b, h in units:
+            sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous()
+            outs.append(orc.gla_fwd(sl(q), sl(k), sl(v), sl(g), grid, direction,
+                                    s0=None if s0 is None else s0[b:b + 1, h:h + 1]))
+        return outs
+    return orc.gla_fwd(q, k, v, g, grid, direction, s0=s0)
+
+
+# ------------------------------------------------------------------ fp32 path
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_c0_fp32_vs_oracle(orc, direction, chunk):
+    x = gen.make_inputs("C0")
+    o, sf = run_gla(x, (8, 8), direction, chunk=chunk)
+    ro, rs = oracle_gla(orc, x, (8, 8), direction)
+    assert_o_close(o, ro, TOL_F32)
+    assert_state_close(sf, rs, TOL_F32)
+
+
+def test_fp32_ragged_dk_ne_dv_with_s0(orc):
+    x = gen.gla_inputs(2, 35, 3, 24, 40, dtype="f32", seed=21, qkv_scale=0.3, gate_div=4.0)
+    s0 = torch.randn(2, 3, 24, 40, generator=torch.Generator().manual_seed(3))
+    for d in DIRS:
+        o, sf = run_gla(x, (5, 7), d, s0=s0)
+        ro, rs = oracle_gla(orc, x, (5, 7), d, s0=s0.double().numpy())
+        assert_o_close(o, ro, TOL_F32, f"o[{d}]")
+        assert_state_close(sf, rs, TOL_F32, f"s[{d}]")
+
+
+# ------------------------------------------------------------------ bf16 path
+
+BF16_SHAPES = [
+    # B, H, gh, gw, dk, dv, chunk
+    (2, 3, 10, 13, 64, 64, 64),     # ragged tail: T=130
+    (1, 2, 9, 9, 72, 72, 64),       # DiG-XL head dim, ragged
+    (2, 2, 8, 12, 16, 16, 16),
+    (1, 3, 12, 11, 128, 128, 32),   # maximum head dim
+    (2, 2, 7, 9, 48, 80, 64),       # dk != dv
+    (1, 2, 1, 1, 8, 8, 64),         # a single token
+    (3, 1, 16, 16, 32, 32, 0),      # automatic chunk
+]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_shapes_vs_oracle(orc, shape):
+    B, H, gh, gw, dk, dv, chunk = shape
+    x = gen.gla_inputs(B, gh * gw, H, dk, dv, dtype="bf16", seed=sum(shape),
+                       qkv_scale=1.0 / np.sqrt(dk), gate_mu=0.0)
+    for d in DIRS:
+        o, sf = run_gla(x, (gh, gw), d, chunk=chunk)
+        ro, rs = oracle_gla(orc, x, (gh, gw), d)
+        assert_o_close(o, ro, TOL_BF16, f"o[{d}]")
+        assert_state_close(sf, rs, TOL_BF16, f"s[{d}]")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_bf16_chunk_invariance(orc, chunk):
+    x = gen.gla_inputs(2, 200, 2, 64, 64, dtype="bf16", seed=5, qkv_scale=0.125)
+    o, sf = run_gla(x, (10, 20), "t2b", chunk=chunk)
+    ro, rs = oracle_gla(orc, x, (10, 20), "t2b")
+    assert_o_close(o, ro, TOL_BF16)
+    assert_state_close(sf, rs, TOL_BF16)
+
+
+def test_bf16_state_handoff(orc):
+    """Scan [0, T1) then [T1, T) with s0 = s_final of the first call == one call."""
+    T1, T2 = 96, 160
+    x = gen.gla_inputs(2, T1 + T2, 2, 72, 72, dtype="bf16", seed=6, qkv_scale=0.12)
+    part = lambda s, e: {n: x[n][:, s:e].contiguous() for n in ("q", "k", "v", "log_alpha")}
+    o1, s1 = run_gla(part(0, T1), (1, T1), "l2r")
+    o2, s2 = run_gla(part(T1, T1 + T2), (1, T2), "l2r", s0=s1)
+    ro, rs = oracle_gla(orc, x, (1, T1 + T2), "l2r")
+    assert_o_close(torch.cat([o1, o2], 1), ro, TOL_BF16)
+    assert_state_close(s2, rs, TOL_BF16)
+
+
+@pytest.mark.parametrize("direction", ["r2l", "t2b", "b2t"])
+def test_bf16_direction_is_permuted_read_bitwise(direction):
+    """gla(x, dir) == gla(arrange_dir(x), l2r) bit for bit: the direction only permutes reads."""
+    gh, gw = 12, 10
+    x = gen.gla_inputs(2, gh * gw, 3, 72, 72, dtype="bf16", seed=7, qkv_scale=0.12)
+    perm = torch.from_numpy(np_perm(direction, gh, gw))
+    arr = {n: x[n][:, perm].contiguous() for n in ("q", "k", "v", "log_alpha")}
+    o, sf = run_gla(x, (gh, gw), direction)
+    o2, sf2 = run_gla(arr, (gh, gw), "l2r")
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(sf.view(torch.int32), sf2.view(torch.int32))
+
+
+def test_bf16_deterministic():
+    x = gen.make_inputs("C1")
+    a = run_gla(x, (16, 16), "t2b")
+    b = run_gla(x, (16, 16), "t2b")
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("case", ["all_zero_alpha", "mixed_extreme", "alpha_one", "long_memory"])
+def test_bf16_gate_extremes(orc, case):
+    """alpha -> 0 (log alpha = -1e4), chunks mixing extreme and mild gates (the pairwise
+    intra-chunk path), alpha == 1 (causal linear attention) and very slow decay."""
+    gh, gw = 10, 16
+    x = gen.gla_inputs(2, gh * gw, 2, 64, 64, dtype="bf16", seed=8, qkv_scale=0.125)
+    g = x["log_alpha"].float()
+    if case == "all_zero_alpha":
+        g = torch.full_like(g, -1e4)
+    elif case == "mixed_extreme":
+        g[:, 40:44] = -1e4             # inside the first chunk of l2r
+        g[:, 100, :, :8] = -300.0      # one token, a few channels
+    elif case == "alpha_one":
+        g = torch.zeros_like(g)
+    elif case == "long_memory":
+        g = g / 64.0
+    x["log_alpha"] = g.to(torch.bfloat16)
+    for d in ("l2r", "b2t"):
+        o, sf = run_gla(x, (gh, gw), d)
+        ro, rs = oracle_gla(orc, x, (gh, gw), d)
+        assert_o_close(o, ro, TOL_BF16, f"o[{case},{d}]")
+        assert_state_close(sf, rs, TOL_BF16, f"s[{case},{d}]")
+
+
+# -------------------------------------------------------- named workloads
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_c1_full_vs_oracle(orc, direction):
+    x = gen.make_inputs("C1")
+    o, sf = run_gla(x, (16, 16), direction, chunk=64)
+    ro, rs = oracle_gla(orc, x, (16, 16), direction)
+    assert_o_close(o, ro, TOL_BF16)
+    assert_state_close(sf, rs, TOL_BF16)
+
+
+def _sampled(orc, key, directions, units):
+    cfg = gen.CONFIGS[key]
+    x = gen.make_inputs(key)
+    for d in directions:
+        o, sf = run_gla(x, (cfg.gh, cfg.gw), d, chunk=cfg.chunk)
+        assert torch.isfinite(o.float()).all() and torch.isfinite(sf).all()
+        for (b, h), (ro, rs) in zip(units, oracle_gla(orc, x, (cfg.gh, cfg.gw), d, units=units)):
+            assert_o_close(o[b:b + 1, :, h:h + 1], ro, TOL_BF16, f"{key} o[{d}] unit {(b, h)}")
+            assert_state_close(sf[b:b + 1, h:h + 1], rs, TOL_BF16, f"{key} s[{d}] unit {(b, h)}")
+
+
+def test_c2_full_size_sampled(orc):
+    _sampled(orc, "C2", DIRS, [(0, 0), (3, 7), (7, 15)])
+
+
+def test_c3_full_size_sampled(orc):
+    _sampled(orc, "C3", ("t2b", "b2t"), [(0, 0), (2, 3), (3, 5)])
+
+
+# ------------------------------------------------------------------- SREM
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_dwconv_identity_is_exact_remap(orc, direction):
+    gh, gw, C = 12, 9, 64
+    x = torch.randn(2, gh * gw, C, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    w = gen.conv_weight(C, 0.0, None)
+    y = dg.srem_dwconv(dev(x), dev(w), (gh, gw), direction).cpu()
+    r = dg.srem_remap(dev(x), (gh, gw), direction, "l2r").cpu()
+    ref = orc.remap(x, (gh, gw), direction, "l2r")
+    assert torch.equal(y.view(torch.int16), r.view(torch.int16))
+    assert np.array_equal(to_np(y), ref)
+
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dwconv_vs_oracle(orc, direction, dtype):
+    gh, gw, C = 11, 14, 48
+    g = torch.Generator().manual_seed(10)
+    x = torch.randn(2, gh * gw, C, generator=g).to(gen.torch_dtype(dtype))
+    w = gen.conv_weight(C, 0.3, g)
+    y = dg.srem_dwconv(dev(x), dev(w), (gh, gw), direction).cpu()
+    ref = orc.srem_dwconv(x, w, (gh, gw), direction)
+    assert_conv_close(y, ref, 1e-2 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("tap", [(0, 0), (0, 1), (1, 2), (2, 2)])
+def test_dwconv_one_hot_tap_exact(orc, tap):
+    gh, gw, C = 6, 10, 16
+    x = torch.randn(1, gh * gw, C, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16)
+    w = torch.zeros(C, 3, 3)
+    w[:, tap[0], tap[1]] = 1.0
+    for d in DIRS:
+        y = dg.srem_dwconv(dev(x), dev(w), (gh, gw), d).cpu()
+        assert np.array_equal(to_np(y), orc.srem_dwconv(x, w, (gh, gw), d))
+
+
+def test_remap_bitwise_all_pairs(orc):
+    gh, gw, C = 7, 13, 24
+    x = torch.randn(2, gh * gw, C, generator=torch.Generator().manual_seed(12)).to(torch.bfloat16)
+    xd = dev(x)
+    for s in DIRS:
+        for t in DIRS:
+            y = dg.srem_remap(xd, (gh, gw), s, t).cpu()
+            assert np.array_equal(to_np(y), orc.remap(x, (gh, gw), s, t)), (s, t)
+    y = xd
+    for i in range(4):
+        y = dg.srem_remap(y, (gh, gw), DIRS[i], DIRS[(i + 1) % 4])
+    assert torch.equal(y.cpu().view(torch.int16), x.view(torch.int16))
+
+
+# ------------------------------------------------------------------ adaLN
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_adaln_vs_oracle(orc, dtype):
+    g = torch.Generator().manual_seed(13)
+    x = (torch.randn(3, 37, 1152, generator=g) * 2 + 0.5).to(gen.torch_dtype(dtype))
+    sc, sh = torch.randn(1152, generator=g) * 0.1, torch.randn(1152, generator=g) * 0.1
+    y = dg.adaln_modulate(dev(x), dev(sc), dev(sh), eps=1e-6, out_scale=0.125).cpu()
+    ref = orc.adaln_modulate(x, sc, sh, eps=1e-6, out_scale=0.125).reshape(3 * 37, 1152)
+    e = np.max(np.abs(to_np(y).reshape(-1, 1152) - ref), axis=1) / np.max(np.abs(ref), axis=1)
+    assert e.max() <= (1e-2 if dtype == "bf16" else 1e-5), e.max()
+
+
+# ------------------------------------------------- full token-mixer step (C4)
+
+def test_c4_mixer_step_sampled(orc):
+    """adaLN modulate -> GLA (scan dir) -> fused DWConv + remap at 2048^2, sampled heads."""
+    cfg = gen.CONFIGS["C4"]
+    x = gen.make_inputs("C4")
+    B, T, H, d, C = cfg.B, cfg.T, cfg.H, cfg.d, cfg.C
+    direction = "t2b"
+    xq = dev(x["x_qkv"])
+    m = dg.adaln_modulate(xq, dev(x["ada_scale"]), dev(x["ada_shift"]), eps=1e-6, out_scale=x["ada_out_scale"])
+    q, k, v = (m[i].view(B, T, H, d) for i in range(3))
+    o, sf = dg.gla_fwd(q, k, v, dev(x["log_alpha"]), (cfg.gh, cfg.gw), direction, chunk=cfg.chunk)
+    y = dg.srem_dwconv(o.view(B, T, C), dev(x["w"]), (cfg.gh, cfg.gw), direction)
+    torch.cuda.synchronize()
+    y, o = y.cpu(), o.cpu()
+    # oracle: its own adaLN over full rows, then sampled heads through GLA and conv
+    mo = orc.adaln_modulate(x["x_qkv"], x["ada_scale"], x["ada_shift"], eps=1e-6, out_scale=x["ada_out_scale"])
+    mo = mo.reshape(3, B, T, H, d)
+    la = to_np(x["log_alpha"])
+    for h in (0, 9):
+        sl = lambda a: np.ascontiguousarray(a[:, :, h:h + 1])
+        ro, rs = orc.gla_fwd(sl(mo[0]), sl(mo[1]), sl(mo[2]), sl(la), (cfg.gh, cfg.gw), direction)
+        assert_o_close(o[:, :, h:h + 1], ro, TOL_BF16, f"C4 o head {h}")
+        assert_state_close(sf.cpu()[:, h:h + 1], rs, TOL_BF16, f"C4 s head {h}")
+        wh = x["w"][h * d:(h + 1) * d]
+        ry = orc.srem_dwconv(ro.reshape(B, T, d), wh, (cfg.gh, cfg.gw), direction)
+        assert_conv_close(y[:, :, h * d:(h + 1) * d], ry, TOL_BF16, f"C4 y head {h}")
