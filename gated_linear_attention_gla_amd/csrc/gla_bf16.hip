@@ -24,9 +24,11 @@
 //   * the scan permutation is applied in the loads: scan position p reads
 //     canonical token scan_to_canon(p), whole 16-byte channel groups per lane,
 //     so no transposed or flipped copy of the inputs is ever written;
-//   * v_mfma_f32_16x16x32_bf16 (plus 16x16x16 for a 16-wide remainder) with
-//     fp32 accumulation; operands staged in LDS in the two orders the
-//     products need (token-major q~, k~; channel-major k^, v);
+//   * v_mfma_f32_16x16x32_bf16 with fp32 accumulation, the only MFMA shape
+//     used: key channels are zero-padded to a multiple of 32 and an odd
+//     16-token tile count pads its last token block with zeros;
+//     operands staged in LDS in the two orders the products need
+//     (token-major q~, k~; channel-major k^, v);
 //   * the next chunk's loads are issued before this chunk's MFMA work.
 //
 // Operand layout facts used (CDNA3/CDNA4 MFMA 16x16xK): lane l supplies row
@@ -41,7 +43,6 @@ namespace dig {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -50,10 +51,6 @@ constexpr float kFastRange = 64.0f;   // |cumulative log2 gate| bound of the fac
 __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ uint2 pack4(f32x4_t x) {
   return make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
@@ -101,8 +98,8 @@ gla_fwd_bf16_kernel(Params P) {
   constexpr int R = (ITEMS + NT - 1) / NT;   // 16-byte items per thread per tensor
   constexpr int MT = M / 16;                 // token tiles per chunk
   constexpr int DT = DP / 16;                // channel tiles
-  constexpr int K32 = DP / 32;               // full 32-wide channel blocks
-  constexpr bool KT = (DP % 32) != 0;        // one 16-wide channel remainder
+  constexpr int K32 = DP / 32;               // 32-wide channel blocks (DP is a multiple of 32)
+  static_assert(DP % 32 == 0, "key channels are padded to a multiple of 32");
   constexpr int QS = Lds<DP, M>::QS, TS = Lds<DP, M>::TS;
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -272,15 +269,13 @@ gla_fwd_bf16_kernel(Params P) {
       for (int jp = 0; jp < MT / 2; ++jp)
         vf[jp] = cat(lds2(sVT + (n0 + l16) * TS + 32 * jp + 4 * g4),
                      lds2(sVT + (n0 + l16) * TS + 32 * jp + 16 + 4 * g4));
-      if (MT & 1) vf[MT / 2] = make_uint4(0, 0, 0, 0);
-      uint2 vtail = make_uint2(0, 0);
-      if (MT & 1) vtail = lds2(sVT + (n0 + l16) * TS + 16 * (MT - 1) + 4 * g4);
+      if (MT & 1)   // odd tile count (16-token chunks): zero upper half of the last K block
+        vf[MT / 2] = cat(lds2(sVT + (n0 + l16) * TS + 16 * (MT - 1) + 4 * g4), make_uint2(0, 0));
 
       // S^T as the A operand of the inter-chunk product (bf16)
-      uint4 sa[K32 > 0 ? K32 : 1];
+      uint4 sa[K32];
 #pragma unroll
       for (int kb = 0; kb < K32; ++kb) sa[kb] = cat(pack4(S[2 * kb]), pack4(S[2 * kb + 1]));
-      const uint2 satail = KT ? pack4(S[DT - 1]) : make_uint2(0, 0);
 
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
@@ -289,17 +284,15 @@ gla_fwd_bf16_kernel(Params P) {
         // intra-chunk weights P^T[s][t] for the s-tiles j <= i
         uint2 pt[MT];
         if (!pairwise) {
-          uint4 qn[K32 > 0 ? K32 : 1];
+          uint4 qn[K32];
 #pragma unroll
           for (int kb = 0; kb < K32; ++kb) qn[kb] = lds4(qrow + 32 * kb + 8 * g4);
-          const uint2 qnt = KT ? lds2(qrow + 32 * K32 + 4 * g4) : make_uint2(0, 0);
 #pragma unroll
           for (int j = 0; j <= i; ++j) {
             const uint16_t *krow = sKt + (16 * j + l16) * QS;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < K32; ++kb) acc = mfma32(lds4(krow + 32 * kb + 8 * g4), qn[kb], acc);
-            if (KT) acc = mfma16(lds2(krow + 32 * K32 + 4 * g4), qnt, acc);
             if (j == i) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
@@ -320,12 +313,11 @@ gla_fwd_bf16_kernel(Params P) {
             O = mfma32(vf[jp], cat(pt[j0], hi), O);
           }
         }
-        if ((MT & 1) && i == MT - 1) O = mfma16(vtail, pt[MT - 1], O);
+        if ((MT & 1) && i == MT - 1) O = mfma32(vf[MT / 2], cat(pt[MT - 1], make_uint2(0, 0)), O);
         // O^T += S^T q~^T
 #pragma unroll
         for (int kb = 0; kb < K32; ++kb)
           O = mfma32(sa[kb], cat(lds2(qrow + 32 * kb + 4 * g4), lds2(qrow + 32 * kb + 16 + 4 * g4)), O);
-        if (KT) O = mfma16(satail, lds2(qrow + 32 * K32 + 4 * g4), O);
         // store o[t][n0 + 4g4 .. +4], t = c*M + 16i + l16 (scan position)
         const int p = c * M + 16 * i + l16;
         const int n = n0 + 4 * g4;
@@ -342,7 +334,8 @@ gla_fwd_bf16_kernel(Params P) {
 #pragma unroll
         for (int jp = 0; jp < MT / 2; ++jp)
           S[r] = mfma32(cat(lds2(krow + 32 * jp + 4 * g4), lds2(krow + 32 * jp + 16 + 4 * g4)), vf[jp], S[r]);
-        if (MT & 1) S[r] = mfma16(lds2(krow + 16 * (MT - 1) + 4 * g4), vtail, S[r]);
+        if (MT & 1)
+          S[r] = mfma32(cat(lds2(krow + 16 * (MT - 1) + 4 * g4), make_uint2(0, 0)), vf[MT / 2], S[r]);
       }
     }
     __syncthreads();
@@ -406,15 +399,11 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   p.nchunks = (a.T + M - 1) / M;
   p.units = a.B * a.H;
   const int d = a.dk > a.dv ? a.dk : a.dv;
-  const int DP = ((d + 15) / 16) * 16;
+  const int DP = ((d + 31) / 32) * 32;
   switch (DP) {
-    case 16: return launch_m<16>(p, M, s);
     case 32: return launch_m<32>(p, M, s);
-    case 48: return launch_m<48>(p, M, s);
     case 64: return launch_m<64>(p, M, s);
-    case 80: return launch_m<80>(p, M, s);
     case 96: return launch_m<96>(p, M, s);
-    case 112: return launch_m<112>(p, M, s);
     case 128: return launch_m<128>(p, M, s);
     default: return hipErrorInvalidValue;
   }
