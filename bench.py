@@ -128,6 +128,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 512 MB)")
+    ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = the workload's, 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     a = ap.parse_args(argv)
 
@@ -149,6 +150,7 @@ def main(argv=None) -> int:
     cfg = gen.CONFIGS[a.config]
     B, T, H, d, C = cfg.B, cfg.T, cfg.H, cfg.d, cfg.C
     grid = (cfg.gh, cfg.gw)
+    chunk = a.chunk or cfg.chunk
 
     ws_bytes = gla_alg_bytes(cfg) + conv_alg_bytes(cfg)
     nsets = a.sets or max(1, math.ceil(512e6 / ws_bytes))
@@ -162,7 +164,7 @@ def main(argv=None) -> int:
         if cfg.adaln:
             bufs["m"] = torch.empty_like(x["x_qkv"])
         sets.append((x, bufs))
-    nbytes = dg.workspace_bytes(dg.DIG_BF16, B, T, H, d, d, cfg.chunk)
+    nbytes = dg.workspace_bytes(dg.DIG_BF16, B, T, H, d, d, chunk)
     ws = dg.get_workspace(dev, nbytes)
     torch.cuda.synchronize()
 
@@ -180,7 +182,7 @@ def main(argv=None) -> int:
         if timed:
             e0 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        dg.gla_fwd(q, k, v, x["log_alpha"], grid, direction, chunk=cfg.chunk, out=bf["o"], s_final=bf["sf"],
+        dg.gla_fwd(q, k, v, x["log_alpha"], grid, direction, chunk=chunk, out=bf["o"], s_final=bf["sf"],
                    workspace=ws)
         if timed:
             e1 = torch.cuda.Event(enable_timing=True)
@@ -239,7 +241,7 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian activations of the DiG latent-grid shape; no dataset or weights)",
-        "config": {"workload": f"{cfg.key} {cfg.name}: GLA fwd (chunk {cfg.chunk}, fp32 state) + "
+        "config": {"workload": f"{cfg.key} {cfg.name}: GLA fwd (chunk {chunk}, fp32 state) + "
                                f"SREM 3x3 dwconv/remap{', adaLN prologue' if cfg.adaln else ''}",
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "grid": list(grid),
                    "directions": list(cfg.dirs), "parallelism": "single GPU"},

@@ -91,10 +91,12 @@ def workspace_bytes(dtype_code: int, B: int, T: int, H: int, dk: int, dv: int, c
 
 
 def get_workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
-    """A cached, zero-initialised workspace of at least nbytes on `device` (grown on demand)."""
+    """A cached, zero-initialised workspace of at least nbytes for `device` and its current
+    stream (grown on demand).  Calls in flight at the same time must not share a workspace,
+    so the cache is per stream."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index)
+    key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)

@@ -139,7 +139,8 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, 
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.gh = gh; a.gw = gw; a.dir = dir; a.chunk = M;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
-    a.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) & 0x3fffffffu;
+    // launch tag for the workspace flags: 1 .. 2^29-1 (never 0, the zero-filled state)
+    a.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) % 0x1fffffffu + 1u;
     a.num_cu = di.num_cu;
     const hipError_t e = dtype == DIG_BF16 ? dig_launch_gla_bf16(a, stream) : dig_launch_gla_f32(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gla_fwd launch");

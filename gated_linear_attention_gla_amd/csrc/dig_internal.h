@@ -57,16 +57,14 @@ __device__ __forceinline__ int xcd_linear_block(int bid, int grid) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 round-to-nearest-even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16, round to nearest even, NaN kept quiet: gfx950's
+// v_cvt_pk_bf16_f32 (two values per instruction).
+typedef __bf16 dig_bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f2bf(lo) | (f2bf(hi) << 16);
+  const dig_bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint32_t f2bf(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 }  // namespace dig
 

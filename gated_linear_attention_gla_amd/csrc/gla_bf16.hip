@@ -3,40 +3,54 @@
 // Method (DiG paper notes, 关键设计 / 硬件友好的效率设计: chunk-wise parallel
 // GLA computed on chip; diffusers issue #20 for the recurrence itself):
 // the scan-ordered sequence of one (batch, head) is cut into chunks of M
-// tokens.  Inside chunk c, with b_t the inclusive cumulative log-gate from the
+// tokens.  Inside a chunk, with b_t the inclusive cumulative log-gate from the
 // chunk start (per key channel) and S the state entering the chunk,
-//   o_t = sum_{s<=t, s in chunk} [ sum_i q_ti k_si e^{b_ti - b_si} ] v_s      (intra)
+//   o_t = sum_{s<=t in chunk} [ sum_i q_ti k_si e^{b_ti - b_si} ] v_s        (intra)
 //       + (q_t * e^{b_t}) S                                                  (inter)
 //   S'  = diag(e^{b_last}) S + sum_s (k_s * e^{b_last - b_s})^T v_s          (state)
-// which is the token recurrence S_t = diag(alpha_t) S_{t-1} + k_t^T v_t,
-// o_t = q_t S_t regrouped.  The intra term uses the factorised operands
-// q~ = q e^{b}, k~ = k e^{-b} (one bf16 MFMA product per tile); when a chunk's
-// cumulative gate leaves [-2^6, 2^6] in log2 units that factorisation could
-// overflow, so such a chunk computes the intra weights pairwise on the VALU
-// instead (exact exponent differences), which keeps any finite log-gate <= 0
-// accurate.  Every other product is already bounded (e^{b} <= 1 and
-// e^{b_last - b_s} <= 1 for non-positive gates).
+// which regroups the token recurrence S_t = diag(alpha_t) S_{t-1} + k_t^T v_t,
+// o_t = q_t S_t.  The intra weights use the factorised operands q~ = q e^{b},
+// k~ = k e^{-b} (one bf16 MFMA product per tile).  When a chunk's gates are
+// large enough for that factorisation to overflow, the chunk computes the
+// intra weights pairwise on the VALU instead (exact exponent differences), so
+// any finite log-gate <= 0 stays accurate.  Every other factor is bounded by 1
+// for non-positive gates.
+//
+// Sequence segments.  To give the GPU enough independent work, each
+// (batch, head) scan is split into G segments of whole chunks, one workgroup
+// each.  A non-final segment first streams its k, v and gates once to form its
+// state aggregate A_g (its own contribution, from a zero state) and the
+// product of its gates Gam_g, and publishes them.  It then obtains the state
+// entering it by a decoupled look-back: walk back to the nearest segment j
+// that has published its inclusive state P_j (or to the start, s0), then fold
+// forward S = fma(Gam_m, S, A_m) for m = j+1 .. g-1.  The fold always replays
+// the serial recurrence P_m = Gam_m * P_{m-1} + A_m element by element, so the
+// result is bitwise independent of which segments had finished: the output is
+// deterministic.  The segment publishes P_g and then runs the full chunk loop
+// from that state, writing o.  The second read of k, v and the gates mostly
+// hits the L2 / Infinity Cache.
 //
 // gfx950 mapping
-//   * one workgroup per (batch, head); NW = max(DP/16, 4) waves; wave w owns
-//     the value columns [16w, 16w+16) of the state and of the output, so the
-//     fp32 state lives in that wave's MFMA accumulators for the whole scan;
-//   * the scan permutation is applied in the loads: scan position p reads
-//     canonical token scan_to_canon(p), whole 16-byte channel groups per lane,
-//     so no transposed or flipped copy of the inputs is ever written;
-//   * v_mfma_f32_16x16x32_bf16 with fp32 accumulation, the only MFMA shape
-//     used: key channels are zero-padded to a multiple of 32 and an odd
-//     16-token tile count pads its last token block with zeros;
-//     operands staged in LDS in the two orders the products need
-//     (token-major q~, k~; channel-major k^, v);
-//   * the next chunk's loads are issued before this chunk's MFMA work.
+//   * NW = DP/16 waves; wave w owns value columns [16w, 16w+16): the fp32
+//     state of those columns stays in the wave's MFMA accumulators;
+//   * the scan permutation is applied in the loads (scan position p reads
+//     canonical token scan_to_canon(p)); no permuted copy is ever written;
+//   * all LDS tiles are token-major rows written with 16-byte stores; the
+//     products that contract over tokens (V^T P^T and k^T v) fetch their
+//     operands with ds_read_b64_tr_b16, whose transpose puts tokens along K;
+//   * v_mfma_f32_16x16x32_bf16 with fp32 accumulation is the only MFMA shape:
+//     channels are zero-padded to a multiple of 32, an odd 16-token tile count
+//     pads its last token block with zeros;
+//   * barriers fence LDS only, so the next chunk's global loads stay in flight
+//     across the whole chunk;
+//   * workgroups take tickets in launch order and are laid out XCD-major, so
+//     the segments of one scan run on one XCD and share its L2.
 //
-// Operand layout facts used (CDNA3/CDNA4 MFMA 16x16xK): lane l supplies row
-// (A) / column (B) l % 16 and the K slice of group l / 16; the accumulator
-// holds rows 4*(l/16) + e, column l % 16.  The K order inside one MFMA is
-// free as long as A and B agree, which lets accumulators be reused directly
-// as the next product's operands (P^T -> B of the P V product, S -> A of the
-// S^T q~^T product) without a trip through LDS.
+// MFMA 16x16xK operand layout used: lane l supplies row (A) / column (B)
+// l % 16 and K slice l / 16; the accumulator holds rows 4*(l/16) + e, column
+// l % 16.  The K order inside one MFMA is free as long as A and B agree, which
+// lets accumulators feed the next product directly (P^T -> B of V^T P^T,
+// S -> A of S^T q~^T) without a trip through LDS.
 #include "dig_internal.h"
 
 namespace dig {
@@ -44,9 +58,14 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kFastRange = 64.0f;   // |cumulative log2 gate| bound of the factorised path
+// Sum of |log2 gate| over one quarter of a chunk above which the chunk takes
+// the pairwise path: keeps |b| <= 64 on the factorised path, so q~, k~ and
+// their products stay far inside the fp32/bf16 range.
+constexpr float kPartRange = 16.0f;
 
 __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -57,7 +76,37 @@ __device__ __forceinline__ uint2 pack4(f32x4_t x) {
 }
 __device__ __forceinline__ uint4 cat(uint2 lo, uint2 hi) { return make_uint4(lo.x, lo.y, hi.x, hi.y); }
 __device__ __forceinline__ uint2 lds2(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+// Global memory accesses through address-space-1 pointers, so they compile to
+// global_load/global_store (vmcnt only) rather than FLAT instructions, which
+// would also count in lgkmcnt and be waited on by every LDS barrier.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 gload16(const uint16_t *p) {
+  const u32x4_t v = *(__attribute__((address_space(1))) const u32x4_t *)(size_t)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void gstore8(uint16_t *p, uint2 v) {
+  *(__attribute__((address_space(1))) u32x2_t *)(size_t)p = u32x2_t{v.x, v.y};
+}
 __device__ __forceinline__ uint4 lds4(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane j
+// receives element (j % 4) of the 8-byte read addressed by lane 4e + j/4,
+// e = 0..3.  If lane s of the group addresses row t0 + s/4, column
+// c0 + 4*(s%4) of a token-major tile, lane j receives column c0 + j of rows
+// t0 .. t0+3.
+__device__ __forceinline__ uint2 lds_tr(const uint16_t *p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16_t *)(__attribute__((address_space(3))) char *)(size_t)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its
+// global loads, so prefetches stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 struct Params {
   const uint16_t *q, *k, *v, *g;
@@ -66,60 +115,89 @@ struct Params {
   float *s_final;
   int64_t qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
   int B, T, H, dk, dv, gh, gw, dir, nchunks, units;
+  int seg_chunks, nseg, per_xcd;   // chunks per segment, segments per scan, scans per XCD
+  int blk_floats;                  // floats of one published state block
+  int *ticket;                     // launch-order ticket counter (reset by the last taker)
+  unsigned *flags;                 // [units][nseg]: epoch*4 + {1 aggregate, 2 inclusive}
+  float *gam;                      // [units][nseg][DP] product of the segment's gates
+  float *agg;                      // [units][nseg][blk_floats] aggregate state
+  float *inc;                      // [units][nseg][blk_floats] inclusive state
+  unsigned epoch;
 };
 
 template <int DP>
 struct Shape {
-  static constexpr int NW = DP / 16 > 4 ? DP / 16 : 4;   // waves per workgroup
+  static constexpr int NW = DP / 16 > 2 ? DP / 16 : 2;   // waves per workgroup
   static constexpr int NT = NW * kWave;
+  static constexpr int NPART = NT / DP;                   // scan parts per channel (4)
 };
 
 template <int DP, int M>
 struct Lds {
-  static constexpr int QS = DP + 8;   // token-major row stride (elements)
-  static constexpr int TS = M + 8;    // channel-major row stride (elements)
-  static constexpr int oQt = 0;                       // q~  [M][QS] bf16
-  static constexpr int oKt = oQt + M * QS * 2;        // k~  [M][QS] bf16 (raw k on the pairwise path)
-  static constexpr int oKh = oKt + M * QS * 2;        // k^  [DP][TS] bf16 (channel-major)
-  static constexpr int oVT = oKh + DP * TS * 2;       // v   [DP][TS] bf16 (channel-major)
-  static constexpr int oP = oVT + DP * TS * 2;        // P   [M][TS] bf16 (pairwise path)
-  static constexpr int oB = oP + M * TS * 2;          // b   [M][DP] fp32 (log2 units)
-  static constexpr int oGam = oB + M * DP * 4;        // e^{b_last} [DP] fp32
-  static constexpr int oFlag = oGam + DP * 4;
-  static constexpr int bytes = oFlag + 16;
+  static constexpr int QS = DP + 16;    // token-major row stride (elements): spreads LDS banks
+  static constexpr int PS = M + 8;      // row stride of the pairwise weight tile
+  static constexpr int TILE = M * QS * 2;
+  static constexpr int KTILE = (M * PS > M * QS ? M * PS : M * QS) * 2;
+  static constexpr int oQ = 0;                         // q~ (raw q on the pairwise path)
+  static constexpr int oK = oQ + TILE;                 // k~ (raw k, then P, on the pairwise path)
+  static constexpr int oKh = oK + KTILE;               // k^ = k e^{b_last - b}
+  static constexpr int oV = oKh + TILE;                // v
+  static constexpr int oB = oV + TILE;                 // gates -> scan partials [M][DP] fp32
+  static constexpr int oTot = oB + M * DP * 4;         // part totals [NPART][DP] fp32
+  static constexpr int oGam = oTot + Shape<DP>::NPART * DP * 4;   // e^{b_last} [DP]
+  static constexpr int oMisc = oGam + DP * 4;          // flag, ticket, look-back result
+  static constexpr int bytes = oMisc + 64;
 };
 
 template <int DP, int M>
 __global__ void __launch_bounds__(Shape<DP>::NT)
 gla_fwd_bf16_kernel(Params P) {
   constexpr int NT = Shape<DP>::NT;
+  constexpr int NPART = Shape<DP>::NPART;
+  constexpr int TPP = M / NPART;             // tokens per scan part
   constexpr int CG = DP / 8;                 // 16-byte channel groups per token row
   constexpr int ITEMS = M * CG;
   constexpr int R = (ITEMS + NT - 1) / NT;   // 16-byte items per thread per tensor
   constexpr int MT = M / 16;                 // token tiles per chunk
   constexpr int DT = DP / 16;                // channel tiles
-  constexpr int K32 = DP / 32;               // 32-wide channel blocks (DP is a multiple of 32)
-  static_assert(DP % 32 == 0, "key channels are padded to a multiple of 32");
-  constexpr int QS = Lds<DP, M>::QS, TS = Lds<DP, M>::TS;
+  constexpr int K32 = DP / 32;               // 32-wide channel blocks
+  constexpr int JP = (MT + 1) / 2;           // 32-token K blocks
+  constexpr int QS = Lds<DP, M>::QS, PS = Lds<DP, M>::PS;
+  static_assert(DP % 32 == 0 && NT == NPART * DP && M % NPART == 0, "shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t *sQt = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oQt);
-  uint16_t *sKt = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oKt);
+  uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oQ);
+  uint16_t *sK = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oK);
   uint16_t *sKh = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oKh);
-  uint16_t *sVT = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oVT);
-  uint16_t *sP = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oP);
+  uint16_t *sV = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oV);
   float *sB = reinterpret_cast<float *>(smem + Lds<DP, M>::oB);
+  float *sTot = reinterpret_cast<float *>(smem + Lds<DP, M>::oTot);
   float *sGam = reinterpret_cast<float *>(smem + Lds<DP, M>::oGam);
-  int *sFlag = reinterpret_cast<int *>(smem + Lds<DP, M>::oFlag);
+  int *sMisc = reinterpret_cast<int *>(smem + Lds<DP, M>::oMisc);   // [0] pairwise [1] ticket [2] look-back
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  const int unit = xcd_linear_block(blockIdx.x, gridDim.x);
+  // ---- work assignment: tickets in launch order, XCD-major layout; segment
+  // g of a scan always holds a larger ticket than segment g-1 of it.
+  if (tid == 0) {
+    const int t = __hip_atomic_fetch_add(P.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == (int)gridDim.x - 1) __hip_atomic_store(P.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sMisc[1] = t;
+  }
+  __syncthreads();
+  const int lid = sMisc[1];
+  const int xcd = lid & 7, kslot = lid >> 3;
+  const int unit = xcd * P.per_xcd + kslot / P.nseg;
+  const int seg = kslot % P.nseg;
   if (unit >= P.units) return;
+  const int c_begin = seg * P.seg_chunks;
+  if (c_begin >= P.nchunks) return;
+  const int c_end = min(c_begin + P.seg_chunks, P.nchunks);
+  const bool last_seg = (c_end == P.nchunks);
+
   const int b = unit / P.H, h = unit - b * P.H;
   const int T = P.T, dk = P.dk, dv = P.dv;
-
   const uint16_t *qb = P.q + b * P.qk_sb + h * P.qk_sh;
   const uint16_t *kb = P.k + b * P.qk_sb + h * P.qk_sh;
   const uint16_t *gb = P.g + b * P.qk_sb + h * P.qk_sh;
@@ -128,20 +206,12 @@ gla_fwd_bf16_kernel(Params P) {
 
   const int n0 = 16 * wave;                 // this wave's value columns
   const bool has_cols = (n0 < dv);
+  const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;   // tiles present in a state block
+  const int64_t slot0 = (int64_t)unit * P.nseg;
 
-  // fp32 state, accumulator layout: S[r][e] = S[16r + 4*g4 + e][n0 + l16]
-  f32x4_t S[DT];
-#pragma unroll
-  for (int r = 0; r < DT; ++r) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ch = 16 * r + 4 * g4 + e, n = n0 + l16;
-      S[r][e] = (P.s0 && ch < dk && n < dv) ? P.s0[((int64_t)unit * dk + ch) * dv + n] : 0.f;
-    }
-  }
-
+  // ---- loads: item idx -> (token tl, 16-byte channel group cg)
   uint4 rq[R], rk[R], rg[R], rv[R];
-  auto load_chunk = [&](int c) {
+  auto load_chunk = [&](int c, bool with_q) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = tid + r * NT;
@@ -151,58 +221,273 @@ gla_fwd_bf16_kernel(Params P) {
       const int64_t n = tok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
       const uint4 z = make_uint4(0, 0, 0, 0);
       const bool kin = tok && (8 * cg < dk), vin = tok && (8 * cg < dv);
-      rq[r] = kin ? *reinterpret_cast<const uint4 *>(qb + n * P.qk_st + 8 * cg) : z;
-      rk[r] = kin ? *reinterpret_cast<const uint4 *>(kb + n * P.qk_st + 8 * cg) : z;
-      rg[r] = kin ? *reinterpret_cast<const uint4 *>(gb + n * P.qk_st + 8 * cg) : z;
-      rv[r] = vin ? *reinterpret_cast<const uint4 *>(vb + n * P.v_st + 8 * cg) : z;
+      if (with_q) rq[r] = kin ? gload16(qb + n * P.qk_st + 8 * cg) : z;
+      rk[r] = kin ? gload16(kb + n * P.qk_st + 8 * cg) : z;
+      rg[r] = kin ? gload16(gb + n * P.qk_st + 8 * cg) : z;
+      rv[r] = vin ? gload16(vb + n * P.v_st + 8 * cg) : z;
     }
   };
 
-  load_chunk(0);
-
-  for (int c = 0; c < P.nchunks; ++c) {
-    // ---- stage 1: gates (log2 units, fp32) token-major; v channel-major
+  // Stage 1: gates (fp32, log2 units) and v to LDS.
+  auto stage1 = [&]() {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = tid + r * NT;
       if (idx < ITEMS) {
         const int tl = idx / CG, cg = idx - tl * CG;
-        const uint32_t gw4[4] = {rg[r].x, rg[r].y, rg[r].z, rg[r].w};
         float4 lo, hi;
-        lo.x = bf16lo(gw4[0]) * kLog2e; lo.y = bf16hi(gw4[0]) * kLog2e;
-        lo.z = bf16lo(gw4[1]) * kLog2e; lo.w = bf16hi(gw4[1]) * kLog2e;
-        hi.x = bf16lo(gw4[2]) * kLog2e; hi.y = bf16hi(gw4[2]) * kLog2e;
-        hi.z = bf16lo(gw4[3]) * kLog2e; hi.w = bf16hi(gw4[3]) * kLog2e;
+        lo.x = bf16lo(rg[r].x) * kLog2e; lo.y = bf16hi(rg[r].x) * kLog2e;
+        lo.z = bf16lo(rg[r].y) * kLog2e; lo.w = bf16hi(rg[r].y) * kLog2e;
+        hi.x = bf16lo(rg[r].z) * kLog2e; hi.y = bf16hi(rg[r].z) * kLog2e;
+        hi.z = bf16lo(rg[r].w) * kLog2e; hi.w = bf16hi(rg[r].w) * kLog2e;
         float4 *dst = reinterpret_cast<float4 *>(sB + tl * DP + 8 * cg);
         dst[0] = lo;
         dst[1] = hi;
-        const uint32_t vw[4] = {rv[r].x, rv[r].y, rv[r].z, rv[r].w};
+        *reinterpret_cast<uint4 *>(sV + tl * QS + 8 * cg) = rv[r];
+      }
+    }
+    if (tid == 0) sMisc[0] = 0;
+  };
+
+  // Stage 2: per-channel inclusive scan of the gates, NPART token parts in parallel.
+  auto stage2 = [&]() {
+    const int ch = tid % DP, part = tid / DP;
+    float run = 0.f, mag = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sVT[(8 * cg + 2 * e) * TS + tl] = (uint16_t)(vw[e] & 0xffffu);
-          sVT[(8 * cg + 2 * e + 1) * TS + tl] = (uint16_t)(vw[e] >> 16);
+    for (int t = part * TPP; t < (part + 1) * TPP; ++t) {
+      const float x = sB[t * DP + ch];
+      run += x;
+      mag += fabsf(x);
+      sB[t * DP + ch] = run;
+    }
+    sTot[part * DP + ch] = run;
+    if (!(mag <= kPartRange)) sMisc[0] = 1;   // also catches NaN
+  };
+
+  // Cumulative gate (log2) of item (tl, cg) and the chunk total, for 8 channels.
+  auto item_gates = [&](int tl, int cg, float *bt, float *bl) {
+    const int part = tl / TPP;
+    const float4 p0 = *reinterpret_cast<const float4 *>(sB + tl * DP + 8 * cg);
+    const float4 p1 = *reinterpret_cast<const float4 *>(sB + tl * DP + 8 * cg + 4);
+    float off[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tot[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int pp = 0; pp < NPART; ++pp) {
+      const float4 t0 = *reinterpret_cast<const float4 *>(sTot + pp * DP + 8 * cg);
+      const float4 t1 = *reinterpret_cast<const float4 *>(sTot + pp * DP + 8 * cg + 4);
+      const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (pp < part) off[e] += tv[e];
+        tot[e] += tv[e];
+      }
+    }
+    const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bt[e] = pv[e] + off[e];
+      bl[e] = tot[e];
+    }
+  };
+
+  // e^{b_last} per channel, summed in the same order as item_gates' total.
+  auto stage3_gamma = [&]() {
+    if (tid < DP) {
+      float tot = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < NPART; ++pp) tot += sTot[pp * DP + tid];
+      sGam[tid] = exp2f(tot);
+    }
+  };
+
+  // k^ = k e^{b_last - b} -> sKh (token-major)
+  auto write_khat = [&](int r, int tl, int cg, const float *bt, const float *bl) {
+    const uint32_t kw[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+    uint32_t oh[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      oh[e] = pack_bf16x2(bf16lo(kw[e]) * exp2f(bl[2 * e] - bt[2 * e]),
+                          bf16hi(kw[e]) * exp2f(bl[2 * e + 1] - bt[2 * e + 1]));
+    *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+  };
+
+  // v fragments with tokens along K: K block jp holds tokens 32jp + 4*g4 + e
+  // (slots 0..3) and 32jp + 16 + 4*g4 + e (slots 4..7); this wave's columns.
+  auto v_frags = [&](uint4 *vf) {
+    const int rowoff = l16 >> 2, coloff = n0 + 4 * (l16 & 3);
+#pragma unroll
+    for (int jp = 0; jp < JP; ++jp) {
+      const uint2 lo = lds_tr(sV + (32 * jp + 4 * g4 + rowoff) * QS + coloff);
+      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(sV + (32 * jp + 16 + 4 * g4 + rowoff) * QS + coloff)
+                                         : make_uint2(0, 0);
+      vf[jp] = cat(lo, hi);
+    }
+  };
+
+  // S = diag(e^{b_last}) S + k^^T v for this wave's columns; optionally
+  // accumulates the product of the gates in gprod (same row layout as S).
+  auto state_update = [&](f32x4_t *S, const uint4 *vf, f32x4_t *gprod) {
+    const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
+#pragma unroll
+    for (int r = 0; r < DT; ++r) {
+      const float4 gm = *reinterpret_cast<const float4 *>(sGam + 16 * r + 4 * g4);
+      S[r][0] *= gm.x; S[r][1] *= gm.y; S[r][2] *= gm.z; S[r][3] *= gm.w;
+      if (gprod) { gprod[r][0] *= gm.x; gprod[r][1] *= gm.y; gprod[r][2] *= gm.z; gprod[r][3] *= gm.w; }
+#pragma unroll
+      for (int jp = 0; jp < JP; ++jp) {
+        const uint2 lo = lds_tr(sKh + (32 * jp + 4 * g4 + rowoff) * QS + 16 * r + coloff);
+        const uint2 hi = (2 * jp + 1 < MT)
+                             ? lds_tr(sKh + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * r + coloff)
+                             : make_uint2(0, 0);
+        S[r] = mfma32(cat(lo, hi), vf[jp], S[r]);
+      }
+    }
+  };
+
+  // Initial state s0 for this wave's tiles (0 when absent).
+  auto load_s0 = [&](f32x4_t *S) {
+#pragma unroll
+    for (int r = 0; r < DT; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ch = 16 * r + 4 * g4 + e, n = n0 + l16;
+        S[r][e] = (P.s0 && ch < dk && n < dv) ? P.s0[((int64_t)unit * dk + ch) * dv + n] : 0.f;
+      }
+  };
+  auto blk_at = [&](int r) { return ((r * NWv + wave) * 64 + lane) * 4; };
+
+  f32x4_t S[DT];
+#pragma unroll
+  for (int r = 0; r < DT; ++r) S[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t gp[DT];   // product of this segment's gates (rows of S)
+#pragma unroll
+  for (int r = 0; r < DT; ++r) gp[r] = f32x4_t{1.f, 1.f, 1.f, 1.f};
+
+  // ======================= pass 1: segment aggregate =========================
+  if (!last_seg) {
+    load_chunk(c_begin, false);
+    for (int c = c_begin; c < c_end; ++c) {
+      stage1();
+      lds_barrier();
+      stage2();
+      lds_barrier();
+      stage3_gamma();
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int idx = tid + r * NT;
+        if (idx < ITEMS) {
+          const int tl = idx / CG, cg = idx - tl * CG;
+          float bt[8], bl[8];
+          item_gates(tl, cg, bt, bl);
+          write_khat(r, tl, cg, bt, bl);
+        }
+      }
+      if (c + 1 < c_end) load_chunk(c + 1, false);
+      lds_barrier();
+      if (has_cols) {
+        uint4 vf[JP];
+        v_frags(vf);
+        state_update(S, vf, gp);
+      }
+      lds_barrier();
+    }
+    if (has_cols) {
+      float *blk = P.agg + (slot0 + seg) * P.blk_floats;
+#pragma unroll
+      for (int r = 0; r < DT; ++r)
+        if (r < DTr) *reinterpret_cast<float4 *>(blk + blk_at(r)) = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+      if (wave == 0 && l16 == 0) {
+#pragma unroll
+        for (int r = 0; r < DT; ++r)
+          *reinterpret_cast<float4 *>(P.gam + (slot0 + seg) * DP + 16 * r + 4 * g4) =
+              make_float4(gp[r][0], gp[r][1], gp[r][2], gp[r][3]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ================== look-back: state entering the segment ==================
+  f32x4_t Sin[DT];
+  if (seg == 0) {
+    load_s0(Sin);
+  } else {
+    if (tid == 0) {
+      int j = seg - 1;
+      while (j >= 0) {
+        unsigned f;
+        while (((f = __hip_atomic_load(P.flags + slot0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 2) !=
+               P.epoch)
+          __builtin_amdgcn_s_sleep(2);
+        if ((f & 3u) == 2u) break;
+        --j;
+      }
+      sMisc[2] = j;
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int jstar = sMisc[2];
+    if (jstar >= 0) {
+      const float *blk = P.inc + (slot0 + jstar) * P.blk_floats;
+#pragma unroll
+      for (int r = 0; r < DT; ++r) {
+        const float4 x = (has_cols && r < DTr) ? *reinterpret_cast<const float4 *>(blk + blk_at(r))
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        Sin[r] = f32x4_t{x.x, x.y, x.z, x.w};
+      }
+    } else {
+      load_s0(Sin);
+    }
+    if (has_cols) {
+      for (int m = jstar + 1; m < seg; ++m) {
+        const float *blk = P.agg + (slot0 + m) * P.blk_floats;
+        const float *gm_ = P.gam + (slot0 + m) * DP;
+#pragma unroll
+        for (int r = 0; r < DT; ++r) {
+          if (r < DTr) {
+            const float4 a = *reinterpret_cast<const float4 *>(blk + blk_at(r));
+            const float4 gm = *reinterpret_cast<const float4 *>(gm_ + 16 * r + 4 * g4);
+            Sin[r][0] = fmaf(gm.x, Sin[r][0], a.x);
+            Sin[r][1] = fmaf(gm.y, Sin[r][1], a.y);
+            Sin[r][2] = fmaf(gm.z, Sin[r][2], a.z);
+            Sin[r][3] = fmaf(gm.w, Sin[r][3], a.w);
+          }
         }
       }
     }
-    if (tid == 0) *sFlag = 0;
-    __syncthreads();
-
-    // ---- stage 2: inclusive cumulative gate per key channel
-    if (tid < DP) {
-      float run = 0.f, amax = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < M; ++t) {
-        run += sB[t * DP + tid];
-        sB[t * DP + tid] = run;
-        amax = fmaxf(amax, fabsf(run));
-      }
-      sGam[tid] = exp2f(run);
-      if (!(amax <= kFastRange)) *sFlag = 1;   // also catches NaN
+  }
+  if (!last_seg) {
+    // inclusive state P_g = Gam_g * S_in + A_g
+    if (has_cols) {
+      float *blk = P.inc + (slot0 + seg) * P.blk_floats;
+#pragma unroll
+      for (int r = 0; r < DT; ++r)
+        if (r < DTr)
+          *reinterpret_cast<float4 *>(blk + blk_at(r)) =
+              make_float4(fmaf(gp[r][0], Sin[r][0], S[r][0]), fmaf(gp[r][1], Sin[r][1], S[r][1]),
+                          fmaf(gp[r][2], Sin[r][2], S[r][2]), fmaf(gp[r][3], Sin[r][3], S[r][3]));
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
-    const bool pairwise = (*sFlag != 0);
+    if (tid == 0)
+      __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int r = 0; r < DT; ++r) S[r] = Sin[r];
 
-    // ---- stage 3: scaled operands
+  // ========================= pass 2: outputs ==================================
+  // Drain this wave's outstanding global loads (the state loads above) so the
+  // loop below never waits on anything but its own prefetches.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  load_chunk(c_begin, true);
+  for (int c = c_begin; c < c_end; ++c) {
+    stage1();
+    lds_barrier();
+    stage2();
+    lds_barrier();
+    const bool pairwise = (sMisc[0] != 0);
+    stage3_gamma();
     if (pairwise) {
       // raw q, k for the exact pairwise intra weights
 #pragma unroll
@@ -210,152 +495,193 @@ gla_fwd_bf16_kernel(Params P) {
         const int idx = tid + r * NT;
         if (idx < ITEMS) {
           const int tl = idx / CG, cg = idx - tl * CG;
-          *reinterpret_cast<uint4 *>(sQt + tl * QS + 8 * cg) = rq[r];
-          *reinterpret_cast<uint4 *>(sKt + tl * QS + 8 * cg) = rk[r];
+          *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = rq[r];
+          *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = rk[r];
         }
       }
-      __syncthreads();
-      for (int pr = tid; pr < M * M; pr += NT) {
+      lds_barrier();
+      constexpr int NPAIR = (M * M + NT - 1) / NT;
+      float pw[NPAIR];
+#pragma unroll
+      for (int x = 0; x < NPAIR; ++x) {
+        const int pr = tid + x * NT;
         const int t = pr / M, s = pr - t * M;
         float acc = 0.f;
-        if (s <= t) {
-          for (int i = 0; i < dk; i += 2) {
-            const uint32_t qw = *reinterpret_cast<const uint32_t *>(sQt + t * QS + i);
-            const uint32_t kw = *reinterpret_cast<const uint32_t *>(sKt + s * QS + i);
-            acc += bf16lo(qw) * bf16lo(kw) * exp2f(sB[t * DP + i] - sB[s * DP + i]);
-            acc += bf16hi(qw) * bf16hi(kw) * exp2f(sB[t * DP + i + 1] - sB[s * DP + i + 1]);
+        if (pr < M * M && s <= t) {
+          const int pt_ = t / TPP, ps_ = s / TPP;
+          for (int i = 0; i < dk; ++i) {
+            float bti = sB[t * DP + i], bsi = sB[s * DP + i];
+            for (int pp = 0; pp < NPART; ++pp) {
+              const float tv = sTot[pp * DP + i];
+              if (pp < pt_) bti += tv;
+              if (pp < ps_) bsi += tv;
+            }
+            const float qv = __uint_as_float((uint32_t)sQ[t * QS + i] << 16);
+            const float kv = __uint_as_float((uint32_t)sK[s * QS + i] << 16);
+            acc += qv * kv * exp2f(bti - bsi);
           }
         }
-        sP[t * TS + s] = (uint16_t)f2bf(acc);
+        pw[x] = acc;
       }
-      __syncthreads();
+      lds_barrier();
+#pragma unroll
+      for (int x = 0; x < NPAIR; ++x) {
+        const int pr = tid + x * NT;
+        if (pr < M * M) {
+          const int t = pr / M, s = pr - t * M;
+          sK[t * PS + s] = (uint16_t)f2bf(pw[x]);
+        }
+      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = tid + r * NT;
       if (idx < ITEMS) {
         const int tl = idx / CG, cg = idx - tl * CG;
-        const float *bt = sB + tl * DP + 8 * cg;
-        const float *bl = sB + (M - 1) * DP + 8 * cg;
+        float bt[8], bl[8];
+        item_gates(tl, cg, bt, bl);
         const uint32_t qw[4] = {rq[r].x, rq[r].y, rq[r].z, rq[r].w};
         const uint32_t kw[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
         uint32_t oq[4], ok[4];
-        float kh[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float b0 = bt[2 * e], b1 = bt[2 * e + 1];
-          const float q0 = bf16lo(qw[e]), q1 = bf16hi(qw[e]);
-          const float k0 = bf16lo(kw[e]), k1 = bf16hi(kw[e]);
-          oq[e] = pack_bf16x2(q0 * exp2f(b0), q1 * exp2f(b1));
-          ok[e] = pack_bf16x2(k0 * exp2f(-b0), k1 * exp2f(-b1));
-          kh[2 * e] = k0 * exp2f(bl[2 * e] - b0);
-          kh[2 * e + 1] = k1 * exp2f(bl[2 * e + 1] - b1);
+          oq[e] = pack_bf16x2(bf16lo(qw[e]) * exp2f(bt[2 * e]), bf16hi(qw[e]) * exp2f(bt[2 * e + 1]));
+          ok[e] = pack_bf16x2(bf16lo(kw[e]) * exp2f(-bt[2 * e]), bf16hi(kw[e]) * exp2f(-bt[2 * e + 1]));
         }
-        *reinterpret_cast<uint4 *>(sQt + tl * QS + 8 * cg) = make_uint4(oq[0], oq[1], oq[2], oq[3]);
-        if (!pairwise)
-          *reinterpret_cast<uint4 *>(sKt + tl * QS + 8 * cg) = make_uint4(ok[0], ok[1], ok[2], ok[3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sKh[(8 * cg + e) * TS + tl] = (uint16_t)f2bf(kh[e]);
+        *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = make_uint4(oq[0], oq[1], oq[2], oq[3]);
+        if (!pairwise) *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = make_uint4(ok[0], ok[1], ok[2], ok[3]);
+        write_khat(r, tl, cg, bt, bl);
       }
     }
-    if (c + 1 < P.nchunks) load_chunk(c + 1);
-    __syncthreads();
+    if (c + 1 < c_end) load_chunk(c + 1, true);
+    lds_barrier();
 
-    // ---- stage 4: MFMA products of this wave's 16 value columns
     if (has_cols) {
-      // v fragments, k = token pairs (16j0 + 4g4 + e, 16j1 + 4g4 + e)
-      uint4 vf[(MT + 1) / 2];
-#pragma unroll
-      for (int jp = 0; jp < MT / 2; ++jp)
-        vf[jp] = cat(lds2(sVT + (n0 + l16) * TS + 32 * jp + 4 * g4),
-                     lds2(sVT + (n0 + l16) * TS + 32 * jp + 16 + 4 * g4));
-      if (MT & 1)   // odd tile count (16-token chunks): zero upper half of the last K block
-        vf[MT / 2] = cat(lds2(sVT + (n0 + l16) * TS + 16 * (MT - 1) + 4 * g4), make_uint2(0, 0));
-
-      // S^T as the A operand of the inter-chunk product (bf16)
-      uint4 sa[K32];
-#pragma unroll
-      for (int kb = 0; kb < K32; ++kb) sa[kb] = cat(pack4(S[2 * kb]), pack4(S[2 * kb + 1]));
+      uint4 vf[JP];
+      v_frags(vf);
 
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const uint16_t *qrow = sQt + (16 * i + l16) * QS;
+        const uint16_t *qrow = sQ + (16 * i + l16) * QS;
         f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-        // intra-chunk weights P^T[s][t] for the s-tiles j <= i
-        uint2 pt[MT];
-        if (!pairwise) {
-          uint4 qn[K32];
-#pragma unroll
-          for (int kb = 0; kb < K32; ++kb) qn[kb] = lds4(qrow + 32 * kb + 8 * g4);
-#pragma unroll
-          for (int j = 0; j <= i; ++j) {
-            const uint16_t *krow = sKt + (16 * j + l16) * QS;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < K32; ++kb) acc = mfma32(lds4(krow + 32 * kb + 8 * g4), qn[kb], acc);
-            if (j == i) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (4 * g4 + e > l16) acc[e] = 0.f;   // causal: s > t
-            }
-            pt[j] = pack4(acc);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j <= i; ++j) pt[j] = lds2(sP + (16 * i + l16) * TS + 16 * j + 4 * g4);
-        }
-        // O^T += V^T P^T over the s-tiles j <= i
-#pragma unroll
-        for (int jp = 0; jp < MT / 2; ++jp) {
-          const int j0 = 2 * jp, j1 = 2 * jp + 1;
-          if (j0 <= i) {
-            const uint2 hi = (j1 <= i) ? pt[j1] : make_uint2(0, 0);
-            O = mfma32(vf[jp], cat(pt[j0], hi), O);
-          }
-        }
-        if ((MT & 1) && i == MT - 1) O = mfma32(vf[MT / 2], cat(pt[MT - 1], make_uint2(0, 0)), O);
-        // O^T += S^T q~^T
+        // O^T += S^T q~^T  (S^T straight from the accumulators, K = channels)
 #pragma unroll
         for (int kb = 0; kb < K32; ++kb)
-          O = mfma32(sa[kb], cat(lds2(qrow + 32 * kb + 4 * g4), lds2(qrow + 32 * kb + 16 + 4 * g4)), O);
-        // store o[t][n0 + 4g4 .. +4], t = c*M + 16i + l16 (scan position)
+          O = mfma32(cat(pack4(S[2 * kb]), pack4(S[2 * kb + 1])),
+                     cat(lds2(qrow + 32 * kb + 4 * g4), lds2(qrow + 32 * kb + 16 + 4 * g4)), O);
+        // O^T += V^T P^T: P^T tiles (j, i), j <= i, produced two at a time
+#pragma unroll
+        for (int jp = 0; jp < JP; ++jp) {
+          const int j0 = 2 * jp, j1 = 2 * jp + 1;
+          if (j0 <= i) {
+            uint2 pt0, pt1 = make_uint2(0, 0);
+            if (!pairwise) {
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj) {
+                const int j = j0 + jj;
+                if (j <= i) {
+                  const uint16_t *krow = sK + (16 * j + l16) * QS;
+                  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                  for (int kb = 0; kb < K32; ++kb)
+                    acc = mfma32(lds4(krow + 32 * kb + 8 * g4), lds4(qrow + 32 * kb + 8 * g4), acc);
+                  if (j == i) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                      if (4 * g4 + e > l16) acc[e] = 0.f;   // causal: s > t
+                  }
+                  if (jj == 0) pt0 = pack4(acc); else pt1 = pack4(acc);
+                }
+              }
+            } else {
+              pt0 = lds2(sK + (16 * i + l16) * PS + 16 * j0 + 4 * g4);
+              if (j1 <= i) pt1 = lds2(sK + (16 * i + l16) * PS + 16 * j1 + 4 * g4);
+            }
+            O = mfma32(vf[jp], cat(pt0, pt1), O);
+          }
+        }
         const int p = c * M + 16 * i + l16;
         const int n = n0 + 4 * g4;
-        if (p < T && n < dv)
-          *reinterpret_cast<uint2 *>(ob + (int64_t)p * P.o_st + n) = pack4(O);
+        if (p < T && n < dv) gstore8(ob + (int64_t)p * P.o_st + n, pack4(O));
       }
-
-      // S = diag(e^{b_last}) S + k^T v
-#pragma unroll
-      for (int r = 0; r < DT; ++r) {
-        const float4 gm = *reinterpret_cast<const float4 *>(sGam + 16 * r + 4 * g4);
-        S[r][0] *= gm.x; S[r][1] *= gm.y; S[r][2] *= gm.z; S[r][3] *= gm.w;
-        const uint16_t *krow = sKh + (16 * r + l16) * TS;
-#pragma unroll
-        for (int jp = 0; jp < MT / 2; ++jp)
-          S[r] = mfma32(cat(lds2(krow + 32 * jp + 4 * g4), lds2(krow + 32 * jp + 16 + 4 * g4)), vf[jp], S[r]);
-        if (MT & 1)
-          S[r] = mfma32(cat(lds2(krow + 16 * (MT - 1) + 4 * g4), make_uint2(0, 0)), vf[MT / 2], S[r]);
-      }
+      state_update(S, vf, nullptr);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
-  if (P.s_final && has_cols) {
+  if (last_seg && P.s_final && has_cols) {
 #pragma unroll
-    for (int r = 0; r < DT; ++r) {
+    for (int r = 0; r < DT; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ch = 16 * r + 4 * g4 + e, n = n0 + l16;
         if (ch < dk && n < dv) P.s_final[((int64_t)unit * dk + ch) * dv + n] = S[r][e];
       }
-    }
   }
 }
 
+// ------------------------------ host side -----------------------------------
+
+int pad32(int d) { return ((d + 31) / 32) * 32; }
+
+int lds_bytes(int DP, int M) {
+  switch (DP * 1000 + M) {
+#define DIG_LDS_CASE(D, MM) case D * 1000 + MM: return Lds<D, MM>::bytes;
+    DIG_LDS_CASE(32, 16) DIG_LDS_CASE(32, 32) DIG_LDS_CASE(32, 64)
+    DIG_LDS_CASE(64, 16) DIG_LDS_CASE(64, 32) DIG_LDS_CASE(64, 64)
+    DIG_LDS_CASE(96, 16) DIG_LDS_CASE(96, 32) DIG_LDS_CASE(96, 64)
+    DIG_LDS_CASE(128, 16) DIG_LDS_CASE(128, 32) DIG_LDS_CASE(128, 64)
+#undef DIG_LDS_CASE
+    default: return 160 * 1024;
+  }
+}
+
+struct Plan {
+  int DP, M, nchunks, units, nseg, seg_chunks, per_xcd, grid, blk_floats;
+  size_t off_flags, off_gam, off_agg, off_inc, bytes;
+};
+
+// Segmentation: enough workgroups for about two rounds of the workgroups that
+// fit on the chip at once (LDS-limited), but segments of at least 512 tokens
+// so that the published states stay small next to the streamed inputs.
+Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
+  Plan pl;
+  pl.DP = pad32(dk > dv ? dk : dv);
+  pl.M = M;
+  pl.nchunks = (T + M - 1) / M;
+  pl.units = B * H;
+  int per_cu = (160 * 1024) / lds_bytes(pl.DP, M);
+  if (per_cu < 1) per_cu = 1;
+  const long want = (long)num_cu * per_cu * 2;
+  long nseg = (want + pl.units - 1) / pl.units;
+  const int min_chunks = (512 + M - 1) / M;
+  long max_seg = pl.nchunks / min_chunks;
+  if (max_seg < 1) max_seg = 1;
+  if (nseg > max_seg) nseg = max_seg;
+  if (nseg < 1) nseg = 1;
+  pl.seg_chunks = (int)((pl.nchunks + nseg - 1) / nseg);
+  pl.nseg = (pl.nchunks + pl.seg_chunks - 1) / pl.seg_chunks;
+  pl.per_xcd = (pl.units + 7) / 8;
+  pl.grid = 8 * pl.per_xcd * pl.nseg;
+  const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;
+  pl.blk_floats = DTr * NWv * 64 * 4;
+  const size_t slots = (size_t)pl.units * pl.nseg;
+  auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
+  size_t off = 256;   // the ticket counter lives at offset 0
+  pl.off_flags = off;
+  off += up(slots * 4);
+  pl.off_gam = off;
+  off += up(slots * pl.DP * 4);
+  pl.off_agg = off;
+  off += up(slots * pl.blk_floats * 4);
+  pl.off_inc = off;
+  off += up(slots * pl.blk_floats * 4);
+  pl.bytes = off;
+  return pl;
+}
+
 template <int DP, int M>
-hipError_t launch(const Params &p, hipStream_t s) {
-  const int grid = ((p.units + 7) / 8) * 8;
+hipError_t launch(const Params &p, int grid, hipStream_t s) {
   const size_t lds = Lds<DP, M>::bytes;
   auto *fn = gla_fwd_bf16_kernel<DP, M>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -366,11 +692,11 @@ hipError_t launch(const Params &p, hipStream_t s) {
 }
 
 template <int DP>
-hipError_t launch_m(const Params &p, int M, hipStream_t s) {
+hipError_t launch_m(const Params &p, int M, int grid, hipStream_t s) {
   switch (M) {
-    case 16: return launch<DP, 16>(p, s);
-    case 32: return launch<DP, 32>(p, s);
-    case 64: return launch<DP, 64>(p, s);
+    case 16: return launch<DP, 16>(p, grid, s);
+    case 32: return launch<DP, 32>(p, grid, s);
+    case 64: return launch<DP, 64>(p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -378,10 +704,13 @@ hipError_t launch_m(const Params &p, int M, hipStream_t s) {
 }  // namespace
 }  // namespace dig
 
-size_t dig_gla_bf16_workspace(int, int, int, int, int, int, int) { return 0; }
+size_t dig_gla_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
+  return dig::make_plan(B, T, H, dk, dv, chunk, num_cu).bytes;
+}
 
 hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   using namespace dig;
+  const Plan pl = make_plan(a.B, a.T, a.H, a.dk, a.dv, a.chunk, a.num_cu);
   Params p;
   p.q = static_cast<const uint16_t *>(a.q);
   p.k = static_cast<const uint16_t *>(a.k);
@@ -395,16 +724,24 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   p.o_sb = a.o_sb; p.o_st = a.o_st; p.o_sh = a.o_sh;
   p.B = a.B; p.T = a.T; p.H = a.H; p.dk = a.dk; p.dv = a.dv;
   p.gh = a.gh; p.gw = a.gw; p.dir = a.dir;
-  const int M = a.chunk;
-  p.nchunks = (a.T + M - 1) / M;
-  p.units = a.B * a.H;
-  const int d = a.dk > a.dv ? a.dk : a.dv;
-  const int DP = ((d + 31) / 32) * 32;
-  switch (DP) {
-    case 32: return launch_m<32>(p, M, s);
-    case 64: return launch_m<64>(p, M, s);
-    case 96: return launch_m<96>(p, M, s);
-    case 128: return launch_m<128>(p, M, s);
+  p.nchunks = pl.nchunks;
+  p.units = pl.units;
+  p.seg_chunks = pl.seg_chunks;
+  p.nseg = pl.nseg;
+  p.per_xcd = pl.per_xcd;
+  p.blk_floats = pl.blk_floats;
+  char *ws = static_cast<char *>(a.workspace);
+  p.ticket = reinterpret_cast<int *>(ws);
+  p.flags = reinterpret_cast<unsigned *>(ws + pl.off_flags);
+  p.gam = reinterpret_cast<float *>(ws + pl.off_gam);
+  p.agg = reinterpret_cast<float *>(ws + pl.off_agg);
+  p.inc = reinterpret_cast<float *>(ws + pl.off_inc);
+  p.epoch = a.epoch;
+  switch (pl.DP) {
+    case 32: return launch_m<32>(p, a.chunk, pl.grid, s);
+    case 64: return launch_m<64>(p, a.chunk, pl.grid, s);
+    case 96: return launch_m<96>(p, a.chunk, pl.grid, s);
+    case 128: return launch_m<128>(p, a.chunk, pl.grid, s);
     default: return hipErrorInvalidValue;
   }
 }
