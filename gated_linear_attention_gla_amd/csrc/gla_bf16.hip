@@ -62,10 +62,10 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
-// Sum of |log2 gate| over one quarter of a chunk above which the chunk takes
-// the pairwise path: keeps |b| <= 64 on the factorised path, so q~, k~ and
-// their products stay far inside the fp32/bf16 range.
-constexpr float kPartRange = 16.0f;
+// Largest |cumulative log2 gate| inside a chunk for the factorised path; a
+// chunk beyond it takes the pairwise path.  2^64 keeps q~, k~ and their
+// products far inside the fp32/bf16 range.
+constexpr float kFastRange = 64.0f;
 
 __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -100,6 +100,30 @@ __device__ __forceinline__ uint2 lds_tr(const uint16_t *p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// 2^x on the transcendental unit (v_exp_f32); results below 2^-126 flush to 0.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Device-coherent (agent-scope, sc1) accesses for the state hand-off between
+// workgroups: written through to the coherence point and read from it, so no
+// L2 writeback/invalidate fence is needed.
+__device__ __forceinline__ void st_coherent(float *p, float4 v) {
+  __hip_atomic_store(p + 0, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_coherent(const float *p) {
+  float4 v;
+  v.x = __hip_atomic_load(p + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.y = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.z = __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.w = __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+// Wait until all of this wave's vector-memory operations (loads and stores)
+// have completed.
+__device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its
 // global loads, so prefetches stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -129,23 +153,24 @@ template <int DP>
 struct Shape {
   static constexpr int NW = DP / 16 > 2 ? DP / 16 : 2;   // waves per workgroup
   static constexpr int NT = NW * kWave;
-  static constexpr int NPART = NT / DP;                   // scan parts per channel (4)
 };
 
 template <int DP, int M>
 struct Lds {
-  static constexpr int QS = DP + 16;    // token-major row stride (elements): spreads LDS banks
-  static constexpr int PS = M + 8;      // row stride of the pairwise weight tile
+  static constexpr int QS = DP + 16;    // token-major bf16 row stride (elements): spreads LDS banks
+  static constexpr int BS = DP + 4;     // fp32 row stride of the cumulative gates
+  static constexpr int MT = M / 16;
+  static constexpr int NPT = MT * (MT + 1) / 2;        // causal 16x16 tiles of P^T
   static constexpr int TILE = M * QS * 2;
-  static constexpr int KTILE = (M * PS > M * QS ? M * PS : M * QS) * 2;
   static constexpr int oQ = 0;                         // q~ (raw q on the pairwise path)
-  static constexpr int oK = oQ + TILE;                 // k~ (raw k, then P, on the pairwise path)
-  static constexpr int oKh = oK + KTILE;               // k^ = k e^{b_last - b}
+  static constexpr int oK = oQ + TILE;                 // k~ (raw k on the pairwise path)
+  static constexpr int oKh = oK + TILE;                // raw gates, then k^ = k e^{b_last - b}
   static constexpr int oV = oKh + TILE;                // v
-  static constexpr int oB = oV + TILE;                 // gates -> scan partials [M][DP] fp32
-  static constexpr int oTot = oB + M * DP * 4;         // part totals [NPART][DP] fp32
-  static constexpr int oGam = oTot + Shape<DP>::NPART * DP * 4;   // e^{b_last} [DP]
-  static constexpr int oMisc = oGam + DP * 4;          // flag, ticket, look-back result
+  static constexpr int oB = oV + TILE;                 // cumulative gates [M][BS] fp32 (log2)
+  static constexpr int oBl = oB + M * BS * 4;          // chunk total b_last [DP] fp32 (log2)
+  static constexpr int oGam = oBl + DP * 4;            // e^{b_last} [DP]
+  static constexpr int oPT = oGam + DP * 4;            // P^T tiles in MFMA fragment order, 512 B each
+  static constexpr int oMisc = oPT + NPT * 512;        // flag, ticket, look-back result
   static constexpr int bytes = oMisc + 64;
 };
 
@@ -153,8 +178,7 @@ template <int DP, int M>
 __global__ void __launch_bounds__(Shape<DP>::NT)
 gla_fwd_bf16_kernel(Params P) {
   constexpr int NT = Shape<DP>::NT;
-  constexpr int NPART = Shape<DP>::NPART;
-  constexpr int TPP = M / NPART;             // tokens per scan part
+  constexpr int NW = Shape<DP>::NW;
   constexpr int CG = DP / 8;                 // 16-byte channel groups per token row
   constexpr int ITEMS = M * CG;
   constexpr int R = (ITEMS + NT - 1) / NT;   // 16-byte items per thread per tensor
@@ -162,21 +186,24 @@ gla_fwd_bf16_kernel(Params P) {
   constexpr int DT = DP / 16;                // channel tiles
   constexpr int K32 = DP / 32;               // 32-wide channel blocks
   constexpr int JP = (MT + 1) / 2;           // 32-token K blocks
-  constexpr int QS = Lds<DP, M>::QS, PS = Lds<DP, M>::PS;
-  static_assert(DP % 32 == 0 && NT == NPART * DP && M % NPART == 0, "shape");
+  constexpr int QS = Lds<DP, M>::QS, BS = Lds<DP, M>::BS, NPT = Lds<DP, M>::NPT;
+  static_assert(DP % 32 == 0 && NW == DT, "one wave per 16-channel tile");
 
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oQ);
   uint16_t *sK = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oK);
   uint16_t *sKh = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oKh);
+  uint16_t *sG = sKh;   // raw gates live in the k^ tile until the scan has read them
   uint16_t *sV = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oV);
   float *sB = reinterpret_cast<float *>(smem + Lds<DP, M>::oB);
-  float *sTot = reinterpret_cast<float *>(smem + Lds<DP, M>::oTot);
+  float *sBl = reinterpret_cast<float *>(smem + Lds<DP, M>::oBl);
   float *sGam = reinterpret_cast<float *>(smem + Lds<DP, M>::oGam);
+  uint16_t *sPT = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oPT);
   int *sMisc = reinterpret_cast<int *>(smem + Lds<DP, M>::oMisc);   // [0] pairwise [1] ticket [2] look-back
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
+  const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);   // transpose-read addressing
 
   // ---- work assignment: tickets in launch order, XCD-major layout; segment
   // g of a scan always holds a larger ticket than segment g-1 of it.
@@ -204,7 +231,7 @@ gla_fwd_bf16_kernel(Params P) {
   const uint16_t *vb = P.v + b * P.v_sb + h * P.v_sh;
   uint16_t *ob = P.o + b * P.o_sb + h * P.o_sh;
 
-  const int n0 = 16 * wave;                 // this wave's value columns
+  const int n0 = 16 * wave;                 // this wave's value columns / gate channels
   const bool has_cols = (n0 < dv);
   const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;   // tiles present in a state block
   const int64_t slot0 = (int64_t)unit * P.nseg;
@@ -228,96 +255,91 @@ gla_fwd_bf16_kernel(Params P) {
     }
   };
 
-  // Stage 1: gates (fp32, log2 units) and v to LDS.
+  // Stage 1: raw gates and v to LDS.
   auto stage1 = [&]() {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = tid + r * NT;
       if (idx < ITEMS) {
         const int tl = idx / CG, cg = idx - tl * CG;
-        float4 lo, hi;
-        lo.x = bf16lo(rg[r].x) * kLog2e; lo.y = bf16hi(rg[r].x) * kLog2e;
-        lo.z = bf16lo(rg[r].y) * kLog2e; lo.w = bf16hi(rg[r].y) * kLog2e;
-        hi.x = bf16lo(rg[r].z) * kLog2e; hi.y = bf16hi(rg[r].z) * kLog2e;
-        hi.z = bf16lo(rg[r].w) * kLog2e; hi.w = bf16hi(rg[r].w) * kLog2e;
-        float4 *dst = reinterpret_cast<float4 *>(sB + tl * DP + 8 * cg);
-        dst[0] = lo;
-        dst[1] = hi;
+        *reinterpret_cast<uint4 *>(sG + tl * QS + 8 * cg) = rg[r];
         *reinterpret_cast<uint4 *>(sV + tl * QS + 8 * cg) = rv[r];
       }
     }
     if (tid == 0) sMisc[0] = 0;
   };
 
-  // Stage 2: per-channel inclusive scan of the gates, NPART token parts in parallel.
+  // Stage 2: inclusive cumulative gates as an MFMA product, b = L G with L the
+  // lower-triangular ones matrix (bf16 gates and 1.0 are exact, fp32 sums),
+  // then scaled to log2 units.  Wave w owns gate channels [16w, 16w+16).
+  // Also writes the chunk total b_last, e^{b_last}, and flags the chunk for
+  // the pairwise path when any |b| exceeds the factorisable range.
   auto stage2 = [&]() {
-    const int ch = tid % DP, part = tid / DP;
-    float run = 0.f, mag = 0.f;
+    uint4 gf[JP];
 #pragma unroll
-    for (int t = part * TPP; t < (part + 1) * TPP; ++t) {
-      const float x = sB[t * DP + ch];
-      run += x;
-      mag += fabsf(x);
-      sB[t * DP + ch] = run;
+    for (int jp = 0; jp < JP; ++jp) {
+      const uint2 lo = lds_tr(sG + (32 * jp + 4 * g4 + rowoff) * QS + n0 + coloff);
+      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(sG + (32 * jp + 16 + 4 * g4 + rowoff) * QS + n0 + coloff)
+                                         : make_uint2(0, 0);
+      gf[jp] = cat(lo, hi);
     }
-    sTot[part * DP + ch] = run;
-    if (!(mag <= kPartRange)) sMisc[0] = 1;   // also catches NaN
-  };
-
-  // Cumulative gate (log2) of item (tl, cg) and the chunk total, for 8 channels.
-  auto item_gates = [&](int tl, int cg, float *bt, float *bl) {
-    const int part = tl / TPP;
-    const float4 p0 = *reinterpret_cast<const float4 *>(sB + tl * DP + 8 * cg);
-    const float4 p1 = *reinterpret_cast<const float4 *>(sB + tl * DP + 8 * cg + 4);
-    float off[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tot[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float mag = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < NPART; ++pp) {
-      const float4 t0 = *reinterpret_cast<const float4 *>(sTot + pp * DP + 8 * cg);
-      const float4 t1 = *reinterpret_cast<const float4 *>(sTot + pp * DP + 8 * cg + 4);
-      const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    for (int i = 0; i < MT; ++i) {
+      const int t = 16 * i + l16;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (pp < part) off[e] += tv[e];
-        tot[e] += tv[e];
+      for (int jp = 0; jp < JP; ++jp) {
+        if (32 * jp <= 16 * i + 15) {
+          // L fragment: row t, K slots = tokens s0_ + {0..3} and s0_ + 16 + {0..3}; 1.0 where s <= t
+          const int s0_ = 32 * jp + 4 * g4;
+          const uint32_t w0 = (s0_ + 0 <= t ? 0x3F80u : 0u) | (s0_ + 1 <= t ? 0x3F800000u : 0u);
+          const uint32_t w1 = (s0_ + 2 <= t ? 0x3F80u : 0u) | (s0_ + 3 <= t ? 0x3F800000u : 0u);
+          const uint32_t w2 = (s0_ + 16 <= t ? 0x3F80u : 0u) | (s0_ + 17 <= t ? 0x3F800000u : 0u);
+          const uint32_t w3 = (s0_ + 18 <= t ? 0x3F80u : 0u) | (s0_ + 19 <= t ? 0x3F800000u : 0u);
+          acc = mfma32(make_uint4(w0, w1, w2, w3), gf[jp], acc);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float bv = acc[e] * kLog2e;
+        sB[(16 * i + 4 * g4 + e) * BS + n0 + l16] = bv;
+        mag = fmaxf(mag, fabsf(bv));
+        if (i == MT - 1 && e == 3 && g4 == 3) {
+          sBl[n0 + l16] = bv;
+          sGam[n0 + l16] = fexp2(bv);
+        }
       }
     }
-    const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bt[e] = pv[e] + off[e];
-      bl[e] = tot[e];
-    }
+    if (!(mag <= kFastRange)) sMisc[0] = 1;   // also catches NaN
   };
 
-  // e^{b_last} per channel, summed in the same order as item_gates' total.
-  auto stage3_gamma = [&]() {
-    if (tid < DP) {
-      float tot = 0.f;
-#pragma unroll
-      for (int pp = 0; pp < NPART; ++pp) tot += sTot[pp * DP + tid];
-      sGam[tid] = exp2f(tot);
-    }
+  // 8 consecutive fp32 values from LDS.
+  auto lds8f = [&](const float *p, float *out) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b2 = *reinterpret_cast<const float4 *>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b2.x; out[5] = b2.y; out[6] = b2.z; out[7] = b2.w;
   };
 
-  // k^ = k e^{b_last - b} -> sKh (token-major)
-  auto write_khat = [&](int r, int tl, int cg, const float *bt, const float *bl) {
+  // k^ = k e^{b_last - b} for item r (exact exponent difference)
+  auto khat_direct = [&](int r, const float *bt, const float *bl) {
     const uint32_t kw[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
-    uint32_t oh[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      oh[e] = pack_bf16x2(bf16lo(kw[e]) * exp2f(bl[2 * e] - bt[2 * e]),
-                          bf16hi(kw[e]) * exp2f(bl[2 * e + 1] - bt[2 * e + 1]));
-    *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+    uint4 oh;
+    oh.x = pack_bf16x2(bf16lo(kw[0]) * fexp2(bl[0] - bt[0]), bf16hi(kw[0]) * fexp2(bl[1] - bt[1]));
+    oh.y = pack_bf16x2(bf16lo(kw[1]) * fexp2(bl[2] - bt[2]), bf16hi(kw[1]) * fexp2(bl[3] - bt[3]));
+    oh.z = pack_bf16x2(bf16lo(kw[2]) * fexp2(bl[4] - bt[4]), bf16hi(kw[2]) * fexp2(bl[5] - bt[5]));
+    oh.w = pack_bf16x2(bf16lo(kw[3]) * fexp2(bl[6] - bt[6]), bf16hi(kw[3]) * fexp2(bl[7] - bt[7]));
+    return oh;
   };
 
   // v fragments with tokens along K: K block jp holds tokens 32jp + 4*g4 + e
   // (slots 0..3) and 32jp + 16 + 4*g4 + e (slots 4..7); this wave's columns.
   auto v_frags = [&](uint4 *vf) {
-    const int rowoff = l16 >> 2, coloff = n0 + 4 * (l16 & 3);
 #pragma unroll
     for (int jp = 0; jp < JP; ++jp) {
-      const uint2 lo = lds_tr(sV + (32 * jp + 4 * g4 + rowoff) * QS + coloff);
-      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(sV + (32 * jp + 16 + 4 * g4 + rowoff) * QS + coloff)
+      const uint2 lo = lds_tr(sV + (32 * jp + 4 * g4 + rowoff) * QS + n0 + coloff);
+      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(sV + (32 * jp + 16 + 4 * g4 + rowoff) * QS + n0 + coloff)
                                          : make_uint2(0, 0);
       vf[jp] = cat(lo, hi);
     }
@@ -326,7 +348,6 @@ gla_fwd_bf16_kernel(Params P) {
   // S = diag(e^{b_last}) S + k^^T v for this wave's columns; optionally
   // accumulates the product of the gates in gprod (same row layout as S).
   auto state_update = [&](f32x4_t *S, const uint4 *vf, f32x4_t *gprod) {
-    const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
 #pragma unroll
     for (int r = 0; r < DT; ++r) {
       const float4 gm = *reinterpret_cast<const float4 *>(sGam + 16 * r + 4 * g4);
@@ -370,15 +391,15 @@ gla_fwd_bf16_kernel(Params P) {
       lds_barrier();
       stage2();
       lds_barrier();
-      stage3_gamma();
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int idx = tid + r * NT;
         if (idx < ITEMS) {
           const int tl = idx / CG, cg = idx - tl * CG;
           float bt[8], bl[8];
-          item_gates(tl, cg, bt, bl);
-          write_khat(r, tl, cg, bt, bl);
+          lds8f(sB + tl * BS + 8 * cg, bt);
+          lds8f(sBl + 8 * cg, bl);
+          *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = khat_direct(r, bt, bl);
         }
       }
       if (c + 1 < c_end) load_chunk(c + 1, false);
@@ -394,15 +415,14 @@ gla_fwd_bf16_kernel(Params P) {
       float *blk = P.agg + (slot0 + seg) * P.blk_floats;
 #pragma unroll
       for (int r = 0; r < DT; ++r)
-        if (r < DTr) *reinterpret_cast<float4 *>(blk + blk_at(r)) = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+        if (r < DTr) st_coherent(blk + blk_at(r), make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
       if (wave == 0 && l16 == 0) {
 #pragma unroll
         for (int r = 0; r < DT; ++r)
-          *reinterpret_cast<float4 *>(P.gam + (slot0 + seg) * DP + 16 * r + 4 * g4) =
-              make_float4(gp[r][0], gp[r][1], gp[r][2], gp[r][3]);
+          st_coherent(P.gam + (slot0 + seg) * DP + 16 * r + 4 * g4, make_float4(gp[r][0], gp[r][1], gp[r][2], gp[r][3]));
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    drain_vmem();
     __syncthreads();
     if (tid == 0)
       __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -426,14 +446,12 @@ gla_fwd_bf16_kernel(Params P) {
       sMisc[2] = j;
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int jstar = sMisc[2];
     if (jstar >= 0) {
       const float *blk = P.inc + (slot0 + jstar) * P.blk_floats;
 #pragma unroll
       for (int r = 0; r < DT; ++r) {
-        const float4 x = (has_cols && r < DTr) ? *reinterpret_cast<const float4 *>(blk + blk_at(r))
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 x = (has_cols && r < DTr) ? ld_coherent(blk + blk_at(r)) : make_float4(0.f, 0.f, 0.f, 0.f);
         Sin[r] = f32x4_t{x.x, x.y, x.z, x.w};
       }
     } else {
@@ -446,8 +464,8 @@ gla_fwd_bf16_kernel(Params P) {
 #pragma unroll
         for (int r = 0; r < DT; ++r) {
           if (r < DTr) {
-            const float4 a = *reinterpret_cast<const float4 *>(blk + blk_at(r));
-            const float4 gm = *reinterpret_cast<const float4 *>(gm_ + 16 * r + 4 * g4);
+            const float4 a = ld_coherent(blk + blk_at(r));
+            const float4 gm = ld_coherent(gm_ + 16 * r + 4 * g4);
             Sin[r][0] = fmaf(gm.x, Sin[r][0], a.x);
             Sin[r][1] = fmaf(gm.y, Sin[r][1], a.y);
             Sin[r][2] = fmaf(gm.z, Sin[r][2], a.z);
@@ -464,11 +482,11 @@ gla_fwd_bf16_kernel(Params P) {
 #pragma unroll
       for (int r = 0; r < DT; ++r)
         if (r < DTr)
-          *reinterpret_cast<float4 *>(blk + blk_at(r)) =
-              make_float4(fmaf(gp[r][0], Sin[r][0], S[r][0]), fmaf(gp[r][1], Sin[r][1], S[r][1]),
-                          fmaf(gp[r][2], Sin[r][2], S[r][2]), fmaf(gp[r][3], Sin[r][3], S[r][3]));
+          st_coherent(blk + blk_at(r),
+                      make_float4(fmaf(gp[r][0], Sin[r][0], S[r][0]), fmaf(gp[r][1], Sin[r][1], S[r][1]),
+                                  fmaf(gp[r][2], Sin[r][2], S[r][2]), fmaf(gp[r][3], Sin[r][3], S[r][3])));
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    drain_vmem();
     __syncthreads();
     if (tid == 0)
       __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -479,7 +497,7 @@ gla_fwd_bf16_kernel(Params P) {
   // ========================= pass 2: outputs ==================================
   // Drain this wave's outstanding global loads (the state loads above) so the
   // loop below never waits on anything but its own prefetches.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  drain_vmem();
   load_chunk(c_begin, true);
   for (int c = c_begin; c < c_end; ++c) {
     stage1();
@@ -487,116 +505,138 @@ gla_fwd_bf16_kernel(Params P) {
     stage2();
     lds_barrier();
     const bool pairwise = (sMisc[0] != 0);
-    stage3_gamma();
-    if (pairwise) {
-      // raw q, k for the exact pairwise intra weights
+    if (!pairwise) {
+      // q~ = q e^{b}, k~ = k e^{-b}, k^ = k~ e^{b_last}   (|b| <= 64: no overflow)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int idx = tid + r * NT;
         if (idx < ITEMS) {
           const int tl = idx / CG, cg = idx - tl * CG;
+          float bt[8], gm[8];
+          lds8f(sB + tl * BS + 8 * cg, bt);
+          lds8f(sGam + 8 * cg, gm);
+          const uint32_t qw[4] = {rq[r].x, rq[r].y, rq[r].z, rq[r].w};
+          const uint32_t kw[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+          uint32_t oq[4], ok[4], oh[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            oq[e] = pack_bf16x2(bf16lo(qw[e]) * fexp2(bt[2 * e]), bf16hi(qw[e]) * fexp2(bt[2 * e + 1]));
+            const float k0 = bf16lo(kw[e]) * fexp2(-bt[2 * e]), k1 = bf16hi(kw[e]) * fexp2(-bt[2 * e + 1]);
+            ok[e] = pack_bf16x2(k0, k1);
+            oh[e] = pack_bf16x2(k0 * gm[2 * e], k1 * gm[2 * e + 1]);
+          }
+          *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = make_uint4(oq[0], oq[1], oq[2], oq[3]);
+          *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = make_uint4(ok[0], ok[1], ok[2], ok[3]);
+          *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+        }
+      }
+      if (c + 1 < c_end) load_chunk(c + 1, true);
+      lds_barrier();
+      // P^T tiles (j, i), j <= i, each computed once, spread over the waves
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int j = 0; j <= i; ++j) {
+          const int ti = i * (i + 1) / 2 + j;
+          if (ti % NW == wave) {
+            const uint16_t *krow = sK + (16 * j + l16) * QS;
+            const uint16_t *qrow = sQ + (16 * i + l16) * QS;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb2 = 0; kb2 < K32; ++kb2) acc = mfma32(lds4(krow + 32 * kb2 + 8 * g4), lds4(qrow + 32 * kb2 + 8 * g4), acc);
+            if (j == i) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (4 * g4 + e > l16) acc[e] = 0.f;   // causal: s > t
+            }
+            *reinterpret_cast<uint2 *>(sPT + ti * 256 + lane * 4) = pack4(acc);
+          }
+        }
+      }
+    } else {
+      // exact pairwise intra weights: raw q, k to LDS, k^ directly
+      uint4 qsave[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int idx = tid + r * NT;
+        if (idx < ITEMS) {
+          const int tl = idx / CG, cg = idx - tl * CG;
+          float bt[8], bl[8];
+          lds8f(sB + tl * BS + 8 * cg, bt);
+          lds8f(sBl + 8 * cg, bl);
+          const uint32_t qw[4] = {rq[r].x, rq[r].y, rq[r].z, rq[r].w};
+          qsave[r].x = pack_bf16x2(bf16lo(qw[0]) * fexp2(bt[0]), bf16hi(qw[0]) * fexp2(bt[1]));
+          qsave[r].y = pack_bf16x2(bf16lo(qw[1]) * fexp2(bt[2]), bf16hi(qw[1]) * fexp2(bt[3]));
+          qsave[r].z = pack_bf16x2(bf16lo(qw[2]) * fexp2(bt[4]), bf16hi(qw[2]) * fexp2(bt[5]));
+          qsave[r].w = pack_bf16x2(bf16lo(qw[3]) * fexp2(bt[6]), bf16hi(qw[3]) * fexp2(bt[7]));
           *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = rq[r];
           *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = rk[r];
+          *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = khat_direct(r, bt, bl);
         }
       }
       lds_barrier();
-      constexpr int NPAIR = (M * M + NT - 1) / NT;
-      float pw[NPAIR];
+      // P^T fragment slots: tile ti = (j, i), lane l, element e  <->  t = 16i + l%16,
+      // s = 16j + 4(l/16) + e;  value sum_c q_tc k_sc 2^(b_tc - b_sc) for s <= t, else 0
+      constexpr int NSLOT = NPT * 256;
+      constexpr int NS = (NSLOT + NT - 1) / NT;
+      float pw[NS];
 #pragma unroll
-      for (int x = 0; x < NPAIR; ++x) {
-        const int pr = tid + x * NT;
-        const int t = pr / M, s = pr - t * M;
+      for (int x = 0; x < NS; ++x) {
+        const int sl = tid + x * NT;
         float acc = 0.f;
-        if (pr < M * M && s <= t) {
-          const int pt_ = t / TPP, ps_ = s / TPP;
-          for (int i = 0; i < dk; ++i) {
-            float bti = sB[t * DP + i], bsi = sB[s * DP + i];
-            for (int pp = 0; pp < NPART; ++pp) {
-              const float tv = sTot[pp * DP + i];
-              if (pp < pt_) bti += tv;
-              if (pp < ps_) bsi += tv;
+        if (sl < NSLOT) {
+          const int ti = sl >> 8, ln = (sl >> 2) & 63, e = sl & 3;
+          int i = 0;
+          while ((i + 1) * (i + 2) / 2 <= ti) ++i;
+          const int j = ti - i * (i + 1) / 2;
+          const int t = 16 * i + (ln & 15), s_ = 16 * j + 4 * (ln >> 4) + e;
+          if (s_ <= t) {
+            for (int ch = 0; ch < dk; ++ch) {
+              const float qv = __uint_as_float((uint32_t)sQ[t * QS + ch] << 16);
+              const float kv = __uint_as_float((uint32_t)sK[s_ * QS + ch] << 16);
+              acc += qv * kv * fexp2(sB[t * BS + ch] - sB[s_ * BS + ch]);
             }
-            const float qv = __uint_as_float((uint32_t)sQ[t * QS + i] << 16);
-            const float kv = __uint_as_float((uint32_t)sK[s * QS + i] << 16);
-            acc += qv * kv * exp2f(bti - bsi);
           }
         }
         pw[x] = acc;
       }
+      if (c + 1 < c_end) load_chunk(c + 1, true);
       lds_barrier();
 #pragma unroll
-      for (int x = 0; x < NPAIR; ++x) {
-        const int pr = tid + x * NT;
-        if (pr < M * M) {
-          const int t = pr / M, s = pr - t * M;
-          sK[t * PS + s] = (uint16_t)f2bf(pw[x]);
+      for (int x = 0; x < NS; ++x) {
+        const int sl = tid + x * NT;
+        if (sl < NSLOT) sPT[sl] = (uint16_t)f2bf(pw[x]);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int idx = tid + r * NT;
+        if (idx < ITEMS) {
+          const int tl = idx / CG, cg = idx - tl * CG;
+          *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = qsave[r];
         }
       }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int idx = tid + r * NT;
-      if (idx < ITEMS) {
-        const int tl = idx / CG, cg = idx - tl * CG;
-        float bt[8], bl[8];
-        item_gates(tl, cg, bt, bl);
-        const uint32_t qw[4] = {rq[r].x, rq[r].y, rq[r].z, rq[r].w};
-        const uint32_t kw[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
-        uint32_t oq[4], ok[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          oq[e] = pack_bf16x2(bf16lo(qw[e]) * exp2f(bt[2 * e]), bf16hi(qw[e]) * exp2f(bt[2 * e + 1]));
-          ok[e] = pack_bf16x2(bf16lo(kw[e]) * exp2f(-bt[2 * e]), bf16hi(kw[e]) * exp2f(-bt[2 * e + 1]));
-        }
-        *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = make_uint4(oq[0], oq[1], oq[2], oq[3]);
-        if (!pairwise) *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = make_uint4(ok[0], ok[1], ok[2], ok[3]);
-        write_khat(r, tl, cg, bt, bl);
-      }
-    }
-    if (c + 1 < c_end) load_chunk(c + 1, true);
     lds_barrier();
 
     if (has_cols) {
       uint4 vf[JP];
       v_frags(vf);
-
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const uint16_t *qrow = sQ + (16 * i + l16) * QS;
         f32x4_t O = {0.f, 0.f, 0.f, 0.f};
         // O^T += S^T q~^T  (S^T straight from the accumulators, K = channels)
 #pragma unroll
-        for (int kb = 0; kb < K32; ++kb)
-          O = mfma32(cat(pack4(S[2 * kb]), pack4(S[2 * kb + 1])),
-                     cat(lds2(qrow + 32 * kb + 4 * g4), lds2(qrow + 32 * kb + 16 + 4 * g4)), O);
-        // O^T += V^T P^T: P^T tiles (j, i), j <= i, produced two at a time
+        for (int kb2 = 0; kb2 < K32; ++kb2)
+          O = mfma32(cat(pack4(S[2 * kb2]), pack4(S[2 * kb2 + 1])),
+                     cat(lds2(qrow + 32 * kb2 + 4 * g4), lds2(qrow + 32 * kb2 + 16 + 4 * g4)), O);
+        // O^T += V^T P^T over the s-tiles j <= i
 #pragma unroll
         for (int jp = 0; jp < JP; ++jp) {
           const int j0 = 2 * jp, j1 = 2 * jp + 1;
           if (j0 <= i) {
-            uint2 pt0, pt1 = make_uint2(0, 0);
-            if (!pairwise) {
-#pragma unroll
-              for (int jj = 0; jj < 2; ++jj) {
-                const int j = j0 + jj;
-                if (j <= i) {
-                  const uint16_t *krow = sK + (16 * j + l16) * QS;
-                  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                  for (int kb = 0; kb < K32; ++kb)
-                    acc = mfma32(lds4(krow + 32 * kb + 8 * g4), lds4(qrow + 32 * kb + 8 * g4), acc);
-                  if (j == i) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                      if (4 * g4 + e > l16) acc[e] = 0.f;   // causal: s > t
-                  }
-                  if (jj == 0) pt0 = pack4(acc); else pt1 = pack4(acc);
-                }
-              }
-            } else {
-              pt0 = lds2(sK + (16 * i + l16) * PS + 16 * j0 + 4 * g4);
-              if (j1 <= i) pt1 = lds2(sK + (16 * i + l16) * PS + 16 * j1 + 4 * g4);
-            }
+            const uint2 pt0 = lds2(sPT + (i * (i + 1) / 2 + j0) * 256 + lane * 4);
+            const uint2 pt1 = (j1 <= i) ? lds2(sPT + (i * (i + 1) / 2 + j1) * 256 + lane * 4) : make_uint2(0, 0);
             O = mfma32(vf[jp], cat(pt0, pt1), O);
           }
         }
