@@ -117,6 +117,10 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, 
       if ((qk_sb | qk_st | qk_sh | v_sb | v_st | v_sh) % 8)
         return fail(DIG_EINVAL, "gla_fwd: bf16 input strides must be multiples of 8 elements");
       if ((o_sb | o_st | o_sh) % 4) return fail(DIG_EINVAL, "gla_fwd: bf16 output strides must be multiples of 4");
+      // the kernel addresses one (batch, head) slice with 32-bit byte offsets
+      if (((int64_t)(T - 1) * qk_st + dk) * 2 >= ((int64_t)1 << 31) ||
+          ((int64_t)(T - 1) * v_st + dv) * 2 >= ((int64_t)1 << 31))
+        return fail(DIG_EINVAL, "gla_fwd: one (batch, head) slice of q/k/log_alpha or v spans 2 GiB or more");
     } else {
       if (dig_gla_f32_lds_bytes(dk, dv, M) > 160 * 1024)
         return fail(DIG_EINVAL, "gla_fwd: fp32 path LDS need exceeds 160 KiB for dk=%d dv=%d chunk=%d", dk, dv, M);

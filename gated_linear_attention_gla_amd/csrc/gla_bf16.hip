@@ -88,6 +88,18 @@ __device__ __forceinline__ uint4 gload16(const uint16_t *p) {
 __device__ __forceinline__ void gstore8(uint16_t *p, uint2 v) {
   *(__attribute__((address_space(1))) u32x2_t *)(size_t)p = u32x2_t{v.x, v.y};
 }
+// Raw buffer loads: 48-bit base (one (batch, head) slice, wave-uniform) plus
+// a 32-bit byte offset per lane.  Offsets at or beyond num_records return
+// zeros, which serves both the ragged tail and the channel padding without
+// predication.  Word 3 = untyped 32-bit data format (CDNA).
+constexpr unsigned kOOB = 0x80000000u;   // an offset past every valid span
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint4 lds4(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane j
 // receives element (j % 4) of the 8-byte read addressed by lane 4e + j/4,
@@ -140,6 +152,9 @@ struct Params {
   int64_t qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
   int B, T, H, dk, dv, gh, gw, dir, nchunks, units;
   int seg_chunks, nseg, per_xcd;   // chunks per segment, segments per scan, scans per XCD
+  int cgr;                         // 16-byte channel groups holding data: ceil(max(dk, dv) / 8)
+  unsigned cg_magic;               // ceil(2^31 / cgr): idx / cgr == umulhi(2 idx, cg_magic) for idx < 2^20
+  unsigned qk_span, v_span;        // bytes addressable in one (batch, head) slice of q/k/g and of v
   int blk_floats;                  // floats of one published state block
   int *ticket;                     // launch-order ticket counter (reset by the last taker)
   unsigned *flags;                 // [units][nseg]: epoch*4 + {1 aggregate, 2 inclusive}
@@ -157,37 +172,49 @@ struct Shape {
 
 template <int DP, int M>
 struct Lds {
-  static constexpr int QS = DP + 16;    // token-major bf16 row stride (elements): spreads LDS banks
-  static constexpr int BS = DP + 4;     // fp32 row stride of the cumulative gates
+  static constexpr int QS = DP + 16;    // token-major bf16 row stride (elements): conflict-free transpose reads
+  static constexpr int HS = DP / 2 + 4; // fp32 row stride of one plane of the cumulative gates
   static constexpr int MT = M / 16;
+  static constexpr int JP = (MT + 1) / 2;
   static constexpr int NPT = MT * (MT + 1) / 2;        // causal 16x16 tiles of P^T
   static constexpr int TILE = M * QS * 2;
   static constexpr int oQ = 0;                         // q~ (raw q on the pairwise path)
   static constexpr int oK = oQ + TILE;                 // k~ (raw k on the pairwise path)
   static constexpr int oKh = oK + TILE;                // raw gates, then k^ = k e^{b_last - b}
   static constexpr int oV = oKh + TILE;                // v
-  static constexpr int oB = oV + TILE;                 // cumulative gates [M][BS] fp32 (log2)
-  static constexpr int oBl = oB + M * BS * 4;          // chunk total b_last [DP] fp32 (log2)
+  static constexpr int oB = oV + TILE;                 // cumulative gates, 2 planes [2][M][HS] fp32 (log2)
+  static constexpr int oPT = oB;                       // P^T tiles (MFMA fragment order, 512 B each),
+                                                       // in the gate buffer once it is dead
+  static constexpr int oBl = oB + 2 * M * HS * 4;      // chunk total b_last [DP] fp32 (log2)
   static constexpr int oGam = oBl + DP * 4;            // e^{b_last} [DP]
-  static constexpr int oPT = oGam + DP * 4;            // P^T tiles in MFMA fragment order, 512 B each
-  static constexpr int oMisc = oPT + NPT * 512;        // flag, ticket, look-back result
+  static constexpr int oL = oGam + DP * 4;             // lower-triangular ones, MFMA fragments [MT][JP][64] x 16 B
+  static constexpr int oTok = oL + MT * JP * 1024;     // byte offsets of the next chunk's tokens [2][M]
+  static constexpr int oMisc = oTok + 2 * M * 4;       // flag, ticket, look-back result
   static constexpr int bytes = oMisc + 64;
+  static_assert(NPT * 512 <= 2 * M * HS * 4, "P^T tiles fit in the gate buffer");
+};
+
+// Occupancy target (waves per SIMD): chunks of <= 32 tokens fit three waves
+// per SIMD; 64-token chunks need the larger register budget of two.
+template <int M>
+struct Occ {
+  static constexpr int waves_per_simd = M <= 32 ? 3 : 2;
 };
 
 template <int DP, int M>
-__global__ void __launch_bounds__(Shape<DP>::NT)
+__global__ void __launch_bounds__(Shape<DP>::NT) __attribute__((amdgpu_waves_per_eu(Occ<M>::waves_per_simd)))
 gla_fwd_bf16_kernel(Params P) {
   constexpr int NT = Shape<DP>::NT;
   constexpr int NW = Shape<DP>::NW;
-  constexpr int CG = DP / 8;                 // 16-byte channel groups per token row
-  constexpr int ITEMS = M * CG;
-  constexpr int R = (ITEMS + NT - 1) / NT;   // 16-byte items per thread per tensor
   constexpr int MT = M / 16;                 // token tiles per chunk
   constexpr int DT = DP / 16;                // channel tiles
   constexpr int K32 = DP / 32;               // 32-wide channel blocks
   constexpr int JP = (MT + 1) / 2;           // 32-token K blocks
-  constexpr int QS = Lds<DP, M>::QS, BS = Lds<DP, M>::BS, NPT = Lds<DP, M>::NPT;
+  constexpr int R = (M * (DP / 8) + NT - 1) / NT;   // max 16-byte items per thread per tensor
+  constexpr int QS = Lds<DP, M>::QS, HS = Lds<DP, M>::HS, NPT = Lds<DP, M>::NPT;
   static_assert(DP % 32 == 0 && NW == DT, "one wave per 16-channel tile");
+  const int CG = P.cgr;                      // 16-byte channel groups carrying data (the rest stay 0)
+  const int ITEMS = M * CG;
 
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oQ);
@@ -199,6 +226,8 @@ gla_fwd_bf16_kernel(Params P) {
   float *sBl = reinterpret_cast<float *>(smem + Lds<DP, M>::oBl);
   float *sGam = reinterpret_cast<float *>(smem + Lds<DP, M>::oGam);
   uint16_t *sPT = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oPT);
+  uint4 *sL = reinterpret_cast<uint4 *>(smem + Lds<DP, M>::oL);
+  unsigned *sTok = reinterpret_cast<unsigned *>(smem + Lds<DP, M>::oTok);   // [0..M) q/k/g, [M..2M) v
   int *sMisc = reinterpret_cast<int *>(smem + Lds<DP, M>::oMisc);   // [0] pairwise [1] ticket [2] look-back
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -225,10 +254,10 @@ gla_fwd_bf16_kernel(Params P) {
 
   const int b = unit / P.H, h = unit - b * P.H;
   const int T = P.T, dk = P.dk, dv = P.dv;
-  const uint16_t *qb = P.q + b * P.qk_sb + h * P.qk_sh;
-  const uint16_t *kb = P.k + b * P.qk_sb + h * P.qk_sh;
-  const uint16_t *gb = P.g + b * P.qk_sb + h * P.qk_sh;
-  const uint16_t *vb = P.v + b * P.v_sb + h * P.v_sh;
+  const __amdgpu_buffer_rsrc_t rq_ = make_rsrc(P.q + b * P.qk_sb + h * P.qk_sh, P.qk_span);
+  const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(P.k + b * P.qk_sb + h * P.qk_sh, P.qk_span);
+  const __amdgpu_buffer_rsrc_t rg_ = make_rsrc(P.g + b * P.qk_sb + h * P.qk_sh, P.qk_span);
+  const __amdgpu_buffer_rsrc_t rv_ = make_rsrc(P.v + b * P.v_sb + h * P.v_sh, P.v_span);
   uint16_t *ob = P.o + b * P.o_sb + h * P.o_sh;
 
   const int n0 = 16 * wave;                 // this wave's value columns / gate channels
@@ -236,44 +265,86 @@ gla_fwd_bf16_kernel(Params P) {
   const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;   // tiles present in a state block
   const int64_t slot0 = (int64_t)unit * P.nseg;
 
-  // ---- loads: item idx -> (token tl, 16-byte channel group cg)
-  uint4 rq[R], rk[R], rg[R], rv[R];
-  auto load_chunk = [&](int c, bool with_q) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int idx = tid + r * NT;
-      const int tl = idx / CG, cg = idx - tl * CG;
-      const int p = c * M + tl;
-      const bool tok = (idx < ITEMS) && (p < T);
-      const int64_t n = tok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
+  // ---- one-time set-up: zero channel padding, lower-triangular fragments
+  if (CG < DP / 8) {
+    const int PADG = DP / 8 - CG;
+    for (int x = tid; x < M * PADG; x += NT) {
+      const int tl = x / PADG, cg = CG + (x - tl * PADG);
       const uint4 z = make_uint4(0, 0, 0, 0);
-      const bool kin = tok && (8 * cg < dk), vin = tok && (8 * cg < dv);
-      if (with_q) rq[r] = kin ? gload16(qb + n * P.qk_st + 8 * cg) : z;
-      rk[r] = kin ? gload16(kb + n * P.qk_st + 8 * cg) : z;
-      rg[r] = kin ? gload16(gb + n * P.qk_st + 8 * cg) : z;
-      rv[r] = vin ? gload16(vb + n * P.v_st + 8 * cg) : z;
+      *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = z;
+      *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = z;
+      *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = z;
+      *reinterpret_cast<uint4 *>(sV + tl * QS + 8 * cg) = z;
+    }
+  }
+  // L^T fragment (B operand) of the scan: column t = 16i + l16, K slots =
+  // tokens 32jp + 4g4 + {0..3} and 32jp + 16 + 4g4 + {0..3}; 1.0 where s <= t.
+  for (int f = wave; f < MT * JP; f += NW) {
+    const int i = f / JP, jp = f - i * JP;
+    const int t = 16 * i + l16, s0_ = 32 * jp + 4 * g4;
+    uint4 w;
+    w.x = (s0_ + 0 <= t ? 0x3F80u : 0u) | (s0_ + 1 <= t ? 0x3F800000u : 0u);
+    w.y = (s0_ + 2 <= t ? 0x3F80u : 0u) | (s0_ + 3 <= t ? 0x3F800000u : 0u);
+    w.z = (s0_ + 16 <= t ? 0x3F80u : 0u) | (s0_ + 17 <= t ? 0x3F800000u : 0u);
+    w.w = (s0_ + 18 <= t ? 0x3F80u : 0u) | (s0_ + 19 <= t ? 0x3F800000u : 0u);
+    sL[f * 64 + lane] = w;
+  }
+
+  // ---- token offsets of chunk c (scan order -> canonical token), kOOB past the end
+  auto fill_tok = [&](int c) {
+    if (tid < M) {
+      const int p = c * M + tid;
+      unsigned oqk = kOOB, ov = kOOB;
+      if (p < T) {
+        const unsigned n = (unsigned)scan_to_canon(P.dir, P.gh, P.gw, T, p);
+        oqk = n * (unsigned)P.qk_st * 2u;
+        ov = n * (unsigned)P.v_st * 2u;
+      }
+      sTok[tid] = oqk;
+      sTok[M + tid] = ov;
     }
   };
 
-  // Stage 1: raw gates and v to LDS.
-  auto stage1 = [&]() {
+  // ---- loads: item idx -> (token tl, 16-byte channel group cg), from the token table
+  uint4 rq[R], rk[R], rg[R], rv[R];
+  auto load_chunk = [&](bool with_q) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = tid + r * NT;
+      if (r * NT < ITEMS) {   // wave-uniform for all but one wave
+        const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
+        const bool ok = idx < ITEMS;
+        const unsigned ok_qk = ok && (8 * cg < dk) ? sTok[tl] + 16u * cg : kOOB;
+        const unsigned ok_v = ok && (8 * cg < dv) ? sTok[M + tl] + 16u * cg : kOOB;
+        if (with_q) rq[r] = bload16(rq_, ok_qk);
+        rk[r] = bload16(rk_, ok_qk);
+        rg[r] = bload16(rg_, ok_qk);
+        rv[r] = bload16(rv_, ok_v);
+      }
+    }
+  };
+
+  // Stage 1: raw gates and v to LDS; token table of the next chunk.
+  auto stage1 = [&](int c_next) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = tid + r * NT;
       if (idx < ITEMS) {
-        const int tl = idx / CG, cg = idx - tl * CG;
+        const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
         *reinterpret_cast<uint4 *>(sG + tl * QS + 8 * cg) = rg[r];
         *reinterpret_cast<uint4 *>(sV + tl * QS + 8 * cg) = rv[r];
       }
     }
+    if (c_next >= 0) fill_tok(c_next);
     if (tid == 0) sMisc[0] = 0;
   };
 
-  // Stage 2: inclusive cumulative gates as an MFMA product, b = L G with L the
-  // lower-triangular ones matrix (bf16 gates and 1.0 are exact, fp32 sums),
-  // then scaled to log2 units.  Wave w owns gate channels [16w, 16w+16).
-  // Also writes the chunk total b_last, e^{b_last}, and flags the chunk for
-  // the pairwise path when any |b| exceeds the factorisable range.
+  // Stage 2: inclusive cumulative gates as an MFMA product, b^T = G^T L^T
+  // (bf16 gates and 1.0 are exact; fp32 sums), scaled to log2 units.  Wave w
+  // owns gate channels [16w, 16w+16); lane (l16, g4) receives token 16i + l16,
+  // channels 16w + 4g4 .. +3, stored as one float4 in plane (g4 & 1) of sB.
+  // Also writes b_last and e^{b_last}, and flags the chunk for the pairwise
+  // path when any |b| exceeds the factorisable range.
   auto stage2 = [&]() {
     uint4 gf[JP];
 #pragma unroll
@@ -284,36 +355,33 @@ gla_fwd_bf16_kernel(Params P) {
       gf[jp] = cat(lo, hi);
     }
     float mag = 0.f;
+    const int ch0 = n0 + 4 * g4;
+    float *plane = sB + (g4 & 1) * (M * HS) + (ch0 >> 3) * 4;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      const int t = 16 * i + l16;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jp = 0; jp < JP; ++jp) {
-        if (32 * jp <= 16 * i + 15) {
-          // L fragment: row t, K slots = tokens s0_ + {0..3} and s0_ + 16 + {0..3}; 1.0 where s <= t
-          const int s0_ = 32 * jp + 4 * g4;
-          const uint32_t w0 = (s0_ + 0 <= t ? 0x3F80u : 0u) | (s0_ + 1 <= t ? 0x3F800000u : 0u);
-          const uint32_t w1 = (s0_ + 2 <= t ? 0x3F80u : 0u) | (s0_ + 3 <= t ? 0x3F800000u : 0u);
-          const uint32_t w2 = (s0_ + 16 <= t ? 0x3F80u : 0u) | (s0_ + 17 <= t ? 0x3F800000u : 0u);
-          const uint32_t w3 = (s0_ + 18 <= t ? 0x3F80u : 0u) | (s0_ + 19 <= t ? 0x3F800000u : 0u);
-          acc = mfma32(make_uint4(w0, w1, w2, w3), gf[jp], acc);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float bv = acc[e] * kLog2e;
-        sB[(16 * i + 4 * g4 + e) * BS + n0 + l16] = bv;
-        mag = fmaxf(mag, fabsf(bv));
-        if (i == MT - 1 && e == 3 && g4 == 3) {
-          sBl[n0 + l16] = bv;
-          sGam[n0 + l16] = fexp2(bv);
-        }
+      for (int jp = 0; jp < JP; ++jp)
+        if (32 * jp <= 16 * i + 15) acc = mfma32(gf[jp], sL[(i * JP + jp) * 64 + lane], acc);
+      const float4 bv = make_float4(acc[0] * kLog2e, acc[1] * kLog2e, acc[2] * kLog2e, acc[3] * kLog2e);
+      *reinterpret_cast<float4 *>(plane + (16 * i + l16) * HS) = bv;
+      mag = fmaxf(mag, fmaxf(fmaxf(fabsf(bv.x), fabsf(bv.y)), fmaxf(fabsf(bv.z), fabsf(bv.w))));
+      if (i == MT - 1 && l16 == 15) {
+        *reinterpret_cast<float4 *>(sBl + ch0) = bv;
+        *reinterpret_cast<float4 *>(sGam + ch0) = make_float4(fexp2(bv.x), fexp2(bv.y), fexp2(bv.z), fexp2(bv.w));
       }
     }
     if (!(mag <= kFastRange)) sMisc[0] = 1;   // also catches NaN
   };
 
+  // cumulative gates of token tl, channels 8cg .. 8cg+7
+  auto item_b = [&](int tl, int cg, float *bt) {
+    const float4 a = *reinterpret_cast<const float4 *>(sB + tl * HS + 4 * cg);
+    const float4 c2 = *reinterpret_cast<const float4 *>(sB + M * HS + tl * HS + 4 * cg);
+    bt[0] = a.x; bt[1] = a.y; bt[2] = a.z; bt[3] = a.w;
+    bt[4] = c2.x; bt[5] = c2.y; bt[6] = c2.z; bt[7] = c2.w;
+  };
+  auto b_at = [&](int t, int ch) { return sB[((ch >> 2) & 1) * (M * HS) + t * HS + (ch >> 3) * 4 + (ch & 3)]; };
   // 8 consecutive fp32 values from LDS.
   auto lds8f = [&](const float *p, float *out) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
@@ -385,9 +453,11 @@ gla_fwd_bf16_kernel(Params P) {
 
   // ======================= pass 1: segment aggregate =========================
   if (!last_seg) {
-    load_chunk(c_begin, false);
+    fill_tok(c_begin);
+    __syncthreads();
+    load_chunk(false);
     for (int c = c_begin; c < c_end; ++c) {
-      stage1();
+      stage1(c + 1 < c_end ? c + 1 : -1);
       lds_barrier();
       stage2();
       lds_barrier();
@@ -395,14 +465,14 @@ gla_fwd_bf16_kernel(Params P) {
       for (int r = 0; r < R; ++r) {
         const int idx = tid + r * NT;
         if (idx < ITEMS) {
-          const int tl = idx / CG, cg = idx - tl * CG;
+          const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
           float bt[8], bl[8];
-          lds8f(sB + tl * BS + 8 * cg, bt);
+          item_b(tl, cg, bt);
           lds8f(sBl + 8 * cg, bl);
           *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = khat_direct(r, bt, bl);
         }
       }
-      if (c + 1 < c_end) load_chunk(c + 1, false);
+      if (c + 1 < c_end) load_chunk(false);
       lds_barrier();
       if (has_cols) {
         uint4 vf[JP];
@@ -498,9 +568,11 @@ gla_fwd_bf16_kernel(Params P) {
   // Drain this wave's outstanding global loads (the state loads above) so the
   // loop below never waits on anything but its own prefetches.
   drain_vmem();
-  load_chunk(c_begin, true);
+  fill_tok(c_begin);
+  __syncthreads();
+  load_chunk(true);
   for (int c = c_begin; c < c_end; ++c) {
-    stage1();
+    stage1(c + 1 < c_end ? c + 1 : -1);
     lds_barrier();
     stage2();
     lds_barrier();
@@ -511,9 +583,9 @@ gla_fwd_bf16_kernel(Params P) {
       for (int r = 0; r < R; ++r) {
         const int idx = tid + r * NT;
         if (idx < ITEMS) {
-          const int tl = idx / CG, cg = idx - tl * CG;
+          const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
           float bt[8], gm[8];
-          lds8f(sB + tl * BS + 8 * cg, bt);
+          item_b(tl, cg, bt);
           lds8f(sGam + 8 * cg, gm);
           const uint32_t qw[4] = {rq[r].x, rq[r].y, rq[r].z, rq[r].w};
           const uint32_t kw[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
@@ -530,7 +602,7 @@ gla_fwd_bf16_kernel(Params P) {
           *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
         }
       }
-      if (c + 1 < c_end) load_chunk(c + 1, true);
+      if (c + 1 < c_end) load_chunk(true);
       lds_barrier();
       // P^T tiles (j, i), j <= i, each computed once, spread over the waves
 #pragma unroll
@@ -543,7 +615,8 @@ gla_fwd_bf16_kernel(Params P) {
             const uint16_t *qrow = sQ + (16 * i + l16) * QS;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb2 = 0; kb2 < K32; ++kb2) acc = mfma32(lds4(krow + 32 * kb2 + 8 * g4), lds4(qrow + 32 * kb2 + 8 * g4), acc);
+            for (int kb2 = 0; kb2 < K32; ++kb2)
+              acc = mfma32(lds4(krow + 32 * kb2 + 8 * g4), lds4(qrow + 32 * kb2 + 8 * g4), acc);
             if (j == i) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
@@ -560,9 +633,9 @@ gla_fwd_bf16_kernel(Params P) {
       for (int r = 0; r < R; ++r) {
         const int idx = tid + r * NT;
         if (idx < ITEMS) {
-          const int tl = idx / CG, cg = idx - tl * CG;
+          const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
           float bt[8], bl[8];
-          lds8f(sB + tl * BS + 8 * cg, bt);
+          item_b(tl, cg, bt);
           lds8f(sBl + 8 * cg, bl);
           const uint32_t qw[4] = {rq[r].x, rq[r].y, rq[r].z, rq[r].w};
           qsave[r].x = pack_bf16x2(bf16lo(qw[0]) * fexp2(bt[0]), bf16hi(qw[0]) * fexp2(bt[1]));
@@ -594,13 +667,13 @@ gla_fwd_bf16_kernel(Params P) {
             for (int ch = 0; ch < dk; ++ch) {
               const float qv = __uint_as_float((uint32_t)sQ[t * QS + ch] << 16);
               const float kv = __uint_as_float((uint32_t)sK[s_ * QS + ch] << 16);
-              acc += qv * kv * fexp2(sB[t * BS + ch] - sB[s_ * BS + ch]);
+              acc += qv * kv * fexp2(b_at(t, ch) - b_at(s_, ch));
             }
           }
         }
         pw[x] = acc;
       }
-      if (c + 1 < c_end) load_chunk(c + 1, true);
+      if (c + 1 < c_end) load_chunk(true);
       lds_barrier();
 #pragma unroll
       for (int x = 0; x < NS; ++x) {
@@ -611,7 +684,7 @@ gla_fwd_bf16_kernel(Params P) {
       for (int r = 0; r < R; ++r) {
         const int idx = tid + r * NT;
         if (idx < ITEMS) {
-          const int tl = idx / CG, cg = idx - tl * CG;
+          const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
           *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = qsave[r];
         }
       }
@@ -621,15 +694,17 @@ gla_fwd_bf16_kernel(Params P) {
     if (has_cols) {
       uint4 vf[JP];
       v_frags(vf);
+      uint4 sa[K32];   // S^T (bf16) as the A operand, K = channels
+#pragma unroll
+      for (int kb2 = 0; kb2 < K32; ++kb2) sa[kb2] = cat(pack4(S[2 * kb2]), pack4(S[2 * kb2 + 1]));
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const uint16_t *qrow = sQ + (16 * i + l16) * QS;
         f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-        // O^T += S^T q~^T  (S^T straight from the accumulators, K = channels)
+        // O^T += S^T q~^T
 #pragma unroll
         for (int kb2 = 0; kb2 < K32; ++kb2)
-          O = mfma32(cat(pack4(S[2 * kb2]), pack4(S[2 * kb2 + 1])),
-                     cat(lds2(qrow + 32 * kb2 + 4 * g4), lds2(qrow + 32 * kb2 + 16 + 4 * g4)), O);
+          O = mfma32(sa[kb2], cat(lds2(qrow + 32 * kb2 + 4 * g4), lds2(qrow + 32 * kb2 + 16 + 4 * g4)), O);
         // O^T += V^T P^T over the s-tiles j <= i
 #pragma unroll
         for (int jp = 0; jp < JP; ++jp) {
@@ -666,7 +741,9 @@ int pad32(int d) { return ((d + 31) / 32) * 32; }
 
 int lds_bytes(int DP, int M) {
   switch (DP * 1000 + M) {
-#define DIG_LDS_CASE(D, MM) case D * 1000 + MM: return Lds<D, MM>::bytes;
+#define DIG_LDS_CASE(D, MM) \
+  case D * 1000 + MM:       \
+    return Lds<D, MM>::bytes;
     DIG_LDS_CASE(32, 16) DIG_LDS_CASE(32, 32) DIG_LDS_CASE(32, 64)
     DIG_LDS_CASE(64, 16) DIG_LDS_CASE(64, 32) DIG_LDS_CASE(64, 64)
     DIG_LDS_CASE(96, 16) DIG_LDS_CASE(96, 32) DIG_LDS_CASE(96, 64)
@@ -690,9 +767,16 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   pl.M = M;
   pl.nchunks = (T + M - 1) / M;
   pl.units = B * H;
+  // workgroups resident per CU: LDS (160 KiB) and the register budget
+  // (waves per SIMD, 4 SIMDs) both bound it
   int per_cu = (160 * 1024) / lds_bytes(pl.DP, M);
+  const int nw = pl.DP / 16 > 2 ? pl.DP / 16 : 2;
+  const int reg_cap = 4 * (M <= 32 ? Occ<32>::waves_per_simd : Occ<64>::waves_per_simd) / nw;
+  if (per_cu > reg_cap) per_cu = reg_cap;
   if (per_cu < 1) per_cu = 1;
-  const long want = (long)num_cu * per_cu * 2;
+  // one wave of resident workgroups: every segment but the last of a scan
+  // reads its chunks twice, so more segments than that cost more than they hide
+  const long want = (long)num_cu * per_cu;
   long nseg = (want + pl.units - 1) / pl.units;
   const int min_chunks = (512 + M - 1) / M;
   long max_seg = pl.nchunks / min_chunks;
@@ -770,6 +854,10 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   p.nseg = pl.nseg;
   p.per_xcd = pl.per_xcd;
   p.blk_floats = pl.blk_floats;
+  p.cgr = ((a.dk > a.dv ? a.dk : a.dv) + 7) / 8;
+  p.cg_magic = (unsigned)((0x80000000ull + p.cgr - 1) / p.cgr);
+  p.qk_span = (unsigned)(((int64_t)(a.T - 1) * a.qk_st + a.dk) * 2);
+  p.v_span = (unsigned)(((int64_t)(a.T - 1) * a.v_st + a.dv) * 2);
   char *ws = static_cast<char *>(a.workspace);
   p.ticket = reinterpret_cast<int *>(ws);
   p.flags = reinterpret_cast<unsigned *>(ws + pl.off_flags);

@@ -97,7 +97,9 @@ extern "C" {
  *   B, T, H, dk, dv  sizes; T = gh*gw; 1 <= dk, dv <= 128.  The bf16 path
  *                    needs dk and dv multiples of 8, 16-byte aligned q/k/v/
  *                    log_alpha/o pointers and strides that are multiples of 8
- *                    elements; the fp32 path takes any layout.
+ *                    elements (o: 4), and one (batch, head) slice of q/k/
+ *                    log_alpha or of v must span less than 2 GiB; the fp32
+ *                    path takes any layout.
  *   gh, gw, dir      the token grid and the scan direction.
  *   chunk            tokens per chunk: 0 = automatic (64 for bf16, 16 for
  *                    fp32); else 16, 32 or 64 (bf16) or 16, 32 (fp32).  The
