@@ -121,6 +121,80 @@ def cpu_baseline(cfg, x_cpu, budget_s: float = 20.0):
     }
 
 
+COPY_PROBE_BYTES = 256 << 20   # the plain copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
+
+
+def traffic_probe(cfg_key: str, chunk: int) -> int:
+    """Launch sequence for the two rocprofv3 PMC passes: three plain device copies of
+    COPY_PROBE_BYTES (read + write of known size), then three gla_fwd launches of the workload."""
+    import torch
+
+    from gated_linear_attention_gla_amd import binding as dg
+    from gated_linear_attention_gla_amd import inputs as gen
+
+    dev = torch.device("cuda:0")
+    cfg = gen.CONFIGS[cfg_key]
+    src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    x = gen.make_inputs(cfg.key, set_index=0, device=dev)
+    if cfg.adaln:
+        m = dg.adaln_modulate(x["x_qkv"], x["ada_scale"], x["ada_shift"], 1e-6, x["ada_out_scale"])
+        q, k, v = (m[j].view(cfg.B, cfg.T, cfg.H, cfg.d) for j in range(3))
+    else:
+        q, k, v = x["q"], x["k"], x["v"]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for i in range(3):
+        dg.gla_fwd(q, k, v, x["log_alpha"], (cfg.gh, cfg.gw), cfg.direction(i), chunk=chunk)
+    torch.cuda.synchronize()
+    log(f"[bench] traffic probe done: {cfg.key}, 3 copies of {COPY_PROBE_BYTES} B, 3 gla_fwd launches")
+    return 0
+
+
+def write_traffic(cfg_key: str, fetch_dir: str, write_dir: str, command: str) -> int:
+    """Turn the counter CSVs of the two PMC passes over --traffic-probe into the per-launch HBM
+    traffic record read by traffic_record().  Each counter is scaled by bytes / counter of the copy."""
+    import csv
+    import glob
+    import statistics
+
+    from gated_linear_attention_gla_amd import inputs as gen
+
+    cfg = gen.CONFIGS[cfg_key]
+
+    def per_dispatch(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        gla = [float(r["Counter_Value"]) * 1024 for r in rows if "gla_fwd_bf16_kernel" in r["Kernel_Name"]]
+        # torch's same-dtype device copy is the runtime's blit kernel
+        cp = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if len(gla) < 1 or len(cp) < 1:
+            raise SystemExit(f"write_traffic: no gla/copy dispatches with {counter} under {d}")
+        return statistics.median(gla), statistics.median(cp), len(gla), len(cp)
+
+    gf, cf, ng, nc = per_dispatch(fetch_dir, "FETCH_SIZE")
+    gw, cw, _, _ = per_dispatch(write_dir, "WRITE_SIZE")
+    kf, kw = COPY_PROBE_BYTES / cf, COPY_PROBE_BYTES / cw
+    total = gf * kf + gw * kw
+    src = os.path.join(ROOT, "gated_linear_attention_gla_amd", "csrc", "gla_bf16.hip")
+    rec = {"kernel": "gla_fwd_bf16_kernel", "workload": cfg_key,
+           "kernel_src_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "bytes_per_launch": total, "fetch_bytes_raw": gf, "write_bytes_raw": gw,
+           "copy_scale_fetch": kf, "copy_scale_write": kw, "copy_bytes": COPY_PROBE_BYTES,
+           "alg_bytes_per_launch": gla_alg_bytes(cfg), "gla_dispatches": ng, "copy_dispatches": nc,
+           "command": command}
+    out = os.path.join(ROOT, "profiles", f"gla_fwd_{cfg_key.lower()}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    log(f"[bench] {out}: {total / 1e6:.1f} MB per launch "
+        f"(alg {gla_alg_bytes(cfg) / 1e6:.1f} MB; copy scale fetch {kf:.3f}, write {kw:.3f})")
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,11 +204,18 @@ def main(argv=None) -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 512 MB)")
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = the workload's, 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only the launches the PMC passes count: 3 plain copies, 3 gla_fwd")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
+                    help="(no GPU) build the traffic record from the two PMC passes' output folders")
     a = ap.parse_args(argv)
+
+    if a.write_traffic:
+        return write_traffic(a.config, *a.write_traffic)
 
     if a.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {a.gpus} is not supported "
-              "(head/batch sharding needs no communication; see the design notes)", file=sys.stderr)
+              "(the path shards by whole (batch, head) units with no communication; run one process per GPU)", file=sys.stderr)
         return 2
 
     import torch
@@ -146,6 +227,8 @@ def main(argv=None) -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     dg.lib()
+    if a.traffic_probe:
+        return traffic_probe(a.config, a.chunk)
     dev = torch.device("cuda:0")
     cfg = gen.CONFIGS[a.config]
     B, T, H, d, C = cfg.B, cfg.T, cfg.H, cfg.d, cfg.C
