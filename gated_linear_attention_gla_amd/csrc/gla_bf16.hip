@@ -290,12 +290,14 @@ gla_fwd_bf16_kernel(Params P) {
     sL[f * 64 + lane] = w;
   }
 
-  // ---- token offsets of chunk c (scan order -> canonical token), kOOB past the end
+  // ---- token offsets of chunk c (scan order -> canonical token), kOOB past the
+  // end of the sequence and for the chunk after the segment (its loads then
+  // return zeros without touching memory)
   auto fill_tok = [&](int c) {
     if (tid < M) {
       const int p = c * M + tid;
       unsigned oqk = kOOB, ov = kOOB;
-      if (p < T) {
+      if (c < c_end && p < T) {
         const unsigned n = (unsigned)scan_to_canon(P.dir, P.gh, P.gw, T, p);
         oqk = n * (unsigned)P.qk_st * 2u;
         ov = n * (unsigned)P.v_st * 2u;
@@ -308,19 +310,21 @@ gla_fwd_bf16_kernel(Params P) {
   // ---- loads: item idx -> (token tl, 16-byte channel group cg), from the token table
   uint4 rq[R], rk[R], rg[R], rv[R];
   auto load_chunk = [&](bool with_q) {
+    // Unconditional: a load under a branch would make the loop-carried
+    // registers merge with their old values, which forces the prefetch to be
+    // waited for right away.
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = tid + r * NT;
-      if (r * NT < ITEMS) {   // wave-uniform for all but one wave
-        const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
-        const bool ok = idx < ITEMS;
-        const unsigned ok_qk = ok && (8 * cg < dk) ? sTok[tl] + 16u * cg : kOOB;
-        const unsigned ok_v = ok && (8 * cg < dv) ? sTok[M + tl] + 16u * cg : kOOB;
-        if (with_q) rq[r] = bload16(rq_, ok_qk);
-        rk[r] = bload16(rk_, ok_qk);
-        rg[r] = bload16(rg_, ok_qk);
-        rv[r] = bload16(rv_, ok_v);
-      }
+      const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
+      const bool ok = idx < ITEMS;
+      const unsigned tq = sTok[ok ? tl : 0], tv = sTok[M + (ok ? tl : 0)];
+      const unsigned ok_qk = ok && (8 * cg < dk) ? tq + 16u * cg : kOOB;
+      const unsigned ok_v = ok && (8 * cg < dv) ? tv + 16u * cg : kOOB;
+      if (with_q) rq[r] = bload16(rq_, ok_qk);
+      rk[r] = bload16(rk_, ok_qk);
+      rg[r] = bload16(rg_, ok_qk);
+      rv[r] = bload16(rv_, ok_v);
     }
   };
 
@@ -335,7 +339,7 @@ gla_fwd_bf16_kernel(Params P) {
         *reinterpret_cast<uint4 *>(sV + tl * QS + 8 * cg) = rv[r];
       }
     }
-    if (c_next >= 0) fill_tok(c_next);
+    fill_tok(c_next);
     if (tid == 0) sMisc[0] = 0;
   };
 
@@ -457,7 +461,7 @@ gla_fwd_bf16_kernel(Params P) {
     __syncthreads();
     load_chunk(false);
     for (int c = c_begin; c < c_end; ++c) {
-      stage1(c + 1 < c_end ? c + 1 : -1);
+      stage1(c + 1);
       lds_barrier();
       stage2();
       lds_barrier();
@@ -472,7 +476,7 @@ gla_fwd_bf16_kernel(Params P) {
           *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = khat_direct(r, bt, bl);
         }
       }
-      if (c + 1 < c_end) load_chunk(false);
+      load_chunk(false);
       lds_barrier();
       if (has_cols) {
         uint4 vf[JP];
@@ -572,7 +576,7 @@ gla_fwd_bf16_kernel(Params P) {
   __syncthreads();
   load_chunk(true);
   for (int c = c_begin; c < c_end; ++c) {
-    stage1(c + 1 < c_end ? c + 1 : -1);
+    stage1(c + 1);
     lds_barrier();
     stage2();
     lds_barrier();
@@ -602,7 +606,7 @@ gla_fwd_bf16_kernel(Params P) {
           *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
         }
       }
-      if (c + 1 < c_end) load_chunk(true);
+      load_chunk(true);
       lds_barrier();
       // P^T tiles (j, i), j <= i, each computed once, spread over the waves
 #pragma unroll
@@ -673,7 +677,7 @@ gla_fwd_bf16_kernel(Params P) {
         }
         pw[x] = acc;
       }
-      if (c + 1 < c_end) load_chunk(true);
+      load_chunk(true);
       lds_barrier();
 #pragma unroll
       for (int x = 0; x < NS; ++x) {
