@@ -170,6 +170,9 @@ int srem_dwconv(const void *x_scan, int dtype, int B, int T, int C, int64_t x_sb
     if ((x_sb | x_st | y_sb | y_st) % vec || x_sb < 0 || x_st < C || y_sb < 0 || y_st < C)
       return fail(DIG_EINVAL, "srem_dwconv: strides must be multiples of %d and token strides >= C", vec);
     if (x_scan == y) return fail(DIG_EINVAL, "srem_dwconv: in-place is not allowed");
+    // the kernel addresses one batch slice of x with 32-bit byte offsets
+    if (((int64_t)(T - 1) * x_st + C) * (dtype == DIG_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
+      return fail(DIG_EINVAL, "srem_dwconv: one batch slice of x spans 2 GiB or more");
     DevInfo di;
     int rc = current_device(di);
     if (rc) return rc;

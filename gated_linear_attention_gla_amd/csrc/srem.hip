@@ -9,114 +9,168 @@
 // result is stored straight to the canonical token order (the arrange-back of
 // the ZigMa notes, 关键设计 / 异构逐层扫描), so no remapped copy is written.
 //
-// Work split: a thread owns one 16-byte channel group (8 bf16 / 4 fp32) of one
-// frame column and a run of frame rows; its 9 x VEC fp32 weights sit in
-// registers and a 3x3 window slides down the column, so every input row is
-// fetched once per walker (three columns wide).  Workgroups are ordered so
-// that each XCD sweeps neighbouring columns, whose shared cells hit its L2.
+// Work split: a thread owns 4 channels of one frame column and a run of frame
+// rows; its 9 x 4 fp32 weights sit in registers and a ring of rows slides
+// down the column with three rows of loads in flight.  Workgroups are ordered so that each XCD sweeps
+// neighbouring columns, whose shared cells hit its L2.
 #include "dig_internal.h"
 
 namespace dig {
 namespace {
 
-template <int VEC>
-struct Vec;
+// A walker's cell: 4 channels of one token, as NW 32-bit words of PW
+// channels each (bf16: 2 words of 2, fp32: 4 words of 1).
+template <int NW>
+struct CellT;
 template <>
-struct Vec<8> {   // bf16
-  static __device__ __forceinline__ void load(const void *p, float *f) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { f[2 * e] = bf16lo(w[e]); f[2 * e + 1] = bf16hi(w[e]); }
-  }
-  static __device__ __forceinline__ void store(void *p, const float *f) {
-    *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                               pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
-  }
-  static constexpr int esize = 2;
-};
+struct CellT<2> { typedef uint2 type; };
 template <>
-struct Vec<4> {   // fp32
-  static __device__ __forceinline__ void load(const void *p, float *f) {
-    const float4 u = *reinterpret_cast<const float4 *>(p);
-    f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
-  }
-  static __device__ __forceinline__ void store(void *p, const float *f) {
-    *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
-  }
-  static constexpr int esize = 4;
-};
+struct CellT<4> { typedef uint4 type; };
+
+__device__ __forceinline__ uint32_t word(const uint2 &u, int j) { return j == 0 ? u.x : u.y; }
+__device__ __forceinline__ uint32_t word(const uint4 &u, int j) {
+  return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
+}
+__device__ __forceinline__ void unpack_word(uint32_t w, float *f, int pw) {
+  if (pw == 2) { f[0] = bf16lo(w); f[1] = bf16hi(w); } else { f[0] = __uint_as_float(w); }
+}
 
 constexpr int kNT = 256;
+constexpr unsigned kOOB = 0x80000000u;   // an offset past every valid span: loads return 0
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int VEC>
+__device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, unsigned off, uint2 &d) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  d = make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, unsigned off, uint4 &d) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  d = make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void gstore(unsigned char *p, const uint32_t *w, uint2 *) {
+  *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+}
+__device__ __forceinline__ void gstore(unsigned char *p, const uint32_t *w, uint4 *) {
+  *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// A walker owns (batch, frame column c, 4-channel group, run of frame rows
+// [r0, r1)).  It keeps three frame rows x three columns of cells in registers
+// as fp32 (rows t-1, t, t+1 feed output row t) while rows t+2 .. t+4 are in
+// flight, so each step waits for a load issued three steps earlier.  Cells
+// outside the frame (zero padding) and rows past r1 come from out-of-range
+// buffer offsets, which read as zero without touching memory.
+template <int NW, int PW>
 __global__ void __launch_bounds__(kNT)
 srem_dwconv_kernel(const unsigned char *x, int64_t x_sb, int64_t x_st, const float *w,
                    unsigned char *y, int64_t y_sb, int64_t y_st, int B, int T, int C,
-                   int gh, int gw, int dir, int rows_per_walker, int nseg) {
-  // A walker owns (batch, frame column c, channel group, run of frame rows)
-  // and slides a 3x3 register window down its column: each step loads the
-  // three new cells of the next row and stores one output token.
-  constexpr int ES = Vec<VEC>::esize;
-  const int CV = C / VEC;
+                   int gh, int gw, int dir, int rows_per_walker, int nseg, unsigned span) {
+  typedef typename CellT<NW>::type cell_t;
+  constexpr int CH = NW * PW;        // channels per walker (4)
+  constexpr int ES = 4 / PW;         // bytes per element
+  const int CV = C / CH;
   int R, Q;
   scan_frame(dir, gh, gw, R, Q);
-  const int64_t id = (int64_t)xcd_linear_block(blockIdx.x, gridDim.x) * kNT + threadIdx.x;
-  const int64_t total = (int64_t)B * Q * CV * nseg;
+  // batch from the grid's y dimension: the buffer descriptor stays wave-uniform
+  const int bb = blockIdx.y;
+  const int id = xcd_linear_block(blockIdx.x, gridDim.x) * kNT + threadIdx.x;
+  const int total = Q * CV * nseg;
   if (id >= total) return;
-  const int cv = (int)(id % CV);
-  int64_t rest = id / CV;
-  const int c = (int)(rest % Q);
-  rest /= Q;
-  const int seg = (int)(rest % nseg);
-  const int bb = (int)(rest / nseg);
+  const int cv = id % CV;
+  const int rest = id / CV;
+  const int c = rest % Q;
+  const int seg = rest / Q;
   const int r0 = seg * rows_per_walker;
   const int r1 = r0 + rows_per_walker < R ? r0 + rows_per_walker : R;
   if (r0 >= r1) return;
-  const int ch0 = cv * VEC;
+  const int ch0 = cv * CH;
 
-  float wr[9][VEC];
+  float wr[9][CH];
 #pragma unroll
   for (int tap = 0; tap < 9; ++tap)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) wr[tap][e] = w[(ch0 + e) * 9 + tap];
+    for (int e = 0; e < CH; ++e) wr[tap][e] = w[(ch0 + e) * 9 + tap];
 
-  const unsigned char *xb = x + (bb * x_sb + (int64_t)ch0) * ES;
-  auto load_row = [&](int r, float (*dst)[VEC]) {
-#pragma unroll
-    for (int e2 = 0; e2 < 3; ++e2) {
-      const int cc = c + e2 - 1;
-      if (r >= 0 && r < R && cc >= 0 && cc < Q) {
-        Vec<VEC>::load(xb + (int64_t)(r * Q + cc) * x_st * ES, dst[e2]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) dst[e2][e] = 0.f;
-      }
-    }
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char *>(x + bb * x_sb * ES), (short)0, (int)span, 0x00020000);
+  const unsigned colB = (unsigned)(x_st * ES), rowB = colB * (unsigned)Q, chB = (unsigned)(ch0 * ES);
+  const unsigned oL = c > 0 ? chB + (unsigned)(c - 1) * colB : kOOB;
+  const unsigned oC = chB + (unsigned)c * colB;
+  const unsigned oR = c + 1 < Q ? chB + (unsigned)(c + 1) * colB : kOOB;
+  auto load_row = [&](int r, cell_t *dst) {
+    const bool ok = r >= 0 && r <= r1 && r < R;
+    const unsigned base = ok ? (unsigned)r * rowB : 0u;
+    bload(rx, ok && oL != kOOB ? base + oL : kOOB, dst[0]);
+    bload(rx, ok ? base + oC : kOOB, dst[1]);
+    bload(rx, ok && oR != kOOB ? base + oR : kOOB, dst[2]);
   };
-  float top[3][VEC], mid[3][VEC], bot[3][VEC];
-  load_row(r0 - 1, top);
-  load_row(r0, mid);
-  for (int r = r0; r < r1; ++r) {
-    load_row(r + 1, bot);
-    float acc[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float a = 0.f;
-#pragma unroll
-      for (int e2 = 0; e2 < 3; ++e2) {
-        a = fmaf(wr[0 * 3 + e2][e], top[e2][e], a);
-        a = fmaf(wr[1 * 3 + e2][e], mid[e2][e], a);
-        a = fmaf(wr[2 * 3 + e2][e], bot[e2][e], a);
-      }
-      acc[e] = a;
-    }
-    const int n = scan_to_canon(dir, gh, gw, T, r * Q + c);
-    Vec<VEC>::store(y + (bb * y_sb + (int64_t)n * y_st + ch0) * ES, acc);
+
+  // canonical token of frame cell (t, c) is affine in t for every direction
+  const int n0 = scan_to_canon(dir, gh, gw, T, r0 * Q + c);
+  const int dn = dir == 0 ? Q : dir == 1 ? -Q : dir == 2 ? 1 : -1;
+  unsigned char *yb = y + (bb * y_sb + (int64_t)ch0) * ES;
+
+  // Two rings indexed by the local row u = t - r0 (mod 3): raw cells of the
+  // rows in flight (u+1 .. u+3) and fp32 cells of the window rows (u-1 .. u+1).
+  // Each cell is unpacked once, when its row enters the window.
+  cell_t raw[3][3];
+  float win[3][3][CH];
+  auto unpack_row = [&](const cell_t *src, float (*dst)[CH]) {
 #pragma unroll
     for (int e2 = 0; e2 < 3; ++e2)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) { top[e2][e] = mid[e2][e]; mid[e2][e] = bot[e2][e]; }
+      for (int j = 0; j < NW; ++j) {
+        float v[2];
+        unpack_word(word(src[e2], j), v, PW);
+#pragma unroll
+        for (int e = 0; e < PW; ++e) dst[e2][PW * j + e] = v[e];
+      }
+  };
+  load_row(r0 - 1, raw[2]);
+  load_row(r0, raw[0]);
+  unpack_row(raw[2], win[2]);
+  unpack_row(raw[0], win[0]);
+  load_row(r0 + 1, raw[1]);
+  load_row(r0 + 2, raw[2]);
+  load_row(r0 + 3, raw[0]);
+
+  // step for local row u with k = u mod 3: window slots (k+2)%3, k, (k+1)%3
+  auto step = [&](int u, int k) {
+    const int kd = (k + 1) % 3, ku = (k + 2) % 3;
+    unpack_row(raw[kd], win[kd]);   // row u+1 enters the window
+    load_row(r0 + u + 4, raw[kd]);  // its raw slot takes row u+4
+    uint32_t out[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      float acc[2];
+#pragma unroll
+      for (int e = 0; e < PW; ++e) {
+        const int ch = PW * j + e;
+        float a = 0.f;
+#pragma unroll
+        for (int e2 = 0; e2 < 3; ++e2) {
+          a = fmaf(wr[0 * 3 + e2][ch], win[ku][e2][ch], a);
+          a = fmaf(wr[1 * 3 + e2][ch], win[k][e2][ch], a);
+          a = fmaf(wr[2 * 3 + e2][ch], win[kd][e2][ch], a);
+        }
+        acc[e] = a;
+      }
+      out[j] = PW == 2 ? pack_bf16x2(acc[0], acc[PW - 1]) : __float_as_uint(acc[0]);
+    }
+    const int64_t n = n0 + (int64_t)u * dn;
+    gstore(yb + n * y_st * ES, out, (cell_t *)nullptr);
+  };
+
+  // three steps per trip: every ring slot is fixed at compile time
+  const int nrows = r1 - r0;
+  for (int u = 0;; u += 3) {
+    step(u, 0);
+    if (u + 1 >= nrows) break;
+    step(u + 1, 1);
+    if (u + 2 >= nrows) break;
+    step(u + 2, 2);
+    if (u + 3 >= nrows) break;
   }
 }
 
@@ -148,28 +202,28 @@ hipError_t dig_launch_dwconv(const void *x, int dtype, int B, int T, int C, int6
                              const float *w, int gh, int gw, int dir, void *y, int64_t y_sb,
                              int64_t y_st, int num_cu, hipStream_t s) {
   using namespace dig;
-  const int VEC = dtype == 1 ? 8 : 4;
-  const int CV = C / VEC;
+  const int CV = C / 4;   // 4 channels per walker
   int R, Q;
   scan_frame(dir, gh, gw, R, Q);
-  // rows per walker: enough walkers for ~8 workgroups per CU, at least 4 rows
+  // rows per walker: about two resident waves of walkers, at least 8 rows each
   const int64_t cols = (int64_t)B * Q * CV;
-  const int64_t want_threads = (int64_t)num_cu * 8 * kNT;
+  const int64_t want_threads = (int64_t)num_cu * 4 * 8 * 64;
   int64_t nseg = (want_threads + cols - 1) / cols;
-  if (nseg > (R + 3) / 4) nseg = (R + 3) / 4;
+  if (nseg > (R + 7) / 8) nseg = (R + 7) / 8;
   if (nseg < 1) nseg = 1;
   const int rows = (int)((R + nseg - 1) / nseg);
   nseg = (R + rows - 1) / rows;
-  const int64_t total = cols * nseg;
-  const int64_t grid = ((total + kNT - 1) / kNT + 7) / 8 * 8;
+  const int64_t per_batch = (int64_t)Q * CV * nseg;
+  const int64_t grid = ((per_batch + kNT - 1) / kNT + 7) / 8 * 8;
+  const unsigned span = (unsigned)(((int64_t)(T - 1) * x_st + C) * (dtype == 1 ? 2 : 4));
   if (dtype == 1)
-    hipLaunchKernelGGL(srem_dwconv_kernel<8>, dim3(grid), dim3(kNT), 0, s,
+    hipLaunchKernelGGL((srem_dwconv_kernel<2, 2>), dim3(grid, B), dim3(kNT), 0, s,
                        static_cast<const unsigned char *>(x), x_sb, x_st, w,
-                       static_cast<unsigned char *>(y), y_sb, y_st, B, T, C, gh, gw, dir, rows, (int)nseg);
+                       static_cast<unsigned char *>(y), y_sb, y_st, B, T, C, gh, gw, dir, rows, (int)nseg, span);
   else
-    hipLaunchKernelGGL(srem_dwconv_kernel<4>, dim3(grid), dim3(kNT), 0, s,
+    hipLaunchKernelGGL((srem_dwconv_kernel<4, 1>), dim3(grid, B), dim3(kNT), 0, s,
                        static_cast<const unsigned char *>(x), x_sb, x_st, w,
-                       static_cast<unsigned char *>(y), y_sb, y_st, B, T, C, gh, gw, dir, rows, (int)nseg);
+                       static_cast<unsigned char *>(y), y_sb, y_st, B, T, C, gh, gw, dir, rows, (int)nseg, span);
   return hipGetLastError();
 }
 

@@ -151,7 +151,8 @@ size_t gla_fwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, in
  * Accumulation is fp32; y has the dtype of x.  With the identity kernel
  * (centre tap 1) y is exactly the canonical reordering of x.
  * Constraints: C >= 1; bf16 needs C % 8 == 0 and 16-byte aligned pointers and
- * strides; fp32 needs C % 4 == 0 and 16-byte alignment.  y must not overlap x.
+ * strides; fp32 needs C % 4 == 0 and 16-byte alignment; one batch slice of x
+ * ((T-1)*x_st + C elements) must span less than 2 GiB.  y must not overlap x.
  */
 int srem_dwconv(const void *x_scan, int dtype, int B, int T, int C,
                 int64_t x_sb, int64_t x_st,
