@@ -58,9 +58,10 @@ int current_device(DevInfo &out) {
 
 std::atomic<uint32_t> g_epoch{1};
 
-int auto_chunk(int dtype, int chunk) {
+int auto_chunk(int dtype, int chunk, int dk, int dv) {
   if (chunk != 0) return chunk;
-  return dtype == DIG_BF16 ? 64 : 16;
+  if (dtype != DIG_BF16) return 16;
+  return (dk > 96 || dv > 96) ? 32 : 64;
 }
 
 int check_gla_sizes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
@@ -69,10 +70,12 @@ int check_gla_sizes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
   if (dk <= 0 || dv <= 0 || dk > 128 || dv > 128)
     return fail(DIG_EINVAL, "gla_fwd: dk and dv must be in [1, 128] (got %d, %d)", dk, dv);
   if ((int64_t)B * H > (int64_t)1 << 30) return fail(DIG_EINVAL, "gla_fwd: B*H too large");
-  const int M = auto_chunk(dtype, chunk);
+  const int M = auto_chunk(dtype, chunk, dk, dv);
   if (dtype == DIG_BF16) {
     if (dk % 8 || dv % 8) return fail(DIG_EINVAL, "gla_fwd: bf16 path needs dk, dv multiples of 8");
     if (M != 16 && M != 32 && M != 64) return fail(DIG_EINVAL, "gla_fwd: bf16 chunk must be 0, 16, 32 or 64");
+    if (M == 64 && (dk > 96 || dv > 96))
+      return fail(DIG_EINVAL, "gla_fwd: bf16 chunk 64 needs dk, dv <= 96 (use 0, 16 or 32)");
   } else {
     if (M != 16 && M != 32) return fail(DIG_EINVAL, "gla_fwd: fp32 chunk must be 0, 16 or 32");
   }
@@ -92,7 +95,7 @@ size_t gla_fwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, in
   if (dtype == DIG_F32) return 0;
   DevInfo di;
   const int num_cu = (current_device(di) == DIG_OK) ? di.num_cu : 256;
-  return dig_gla_bf16_workspace(B, T, H, dk, dv, auto_chunk(dtype, chunk), num_cu);
+  return dig_gla_bf16_workspace(B, T, H, dk, dv, auto_chunk(dtype, chunk, dk, dv), num_cu);
 }
 
 int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
@@ -110,7 +113,7 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, 
     if (qk_sb < 0 || qk_st < 0 || qk_sh < 0 || v_sb < 0 || v_st < 0 || v_sh < 0 || o_sb < 0 || o_st < 0 || o_sh < 0)
       return fail(DIG_EINVAL, "gla_fwd: negative stride");
     if (o == q || o == k || o == v || o == log_alpha) return fail(DIG_EINVAL, "gla_fwd: o aliases an input");
-    const int M = auto_chunk(dtype, chunk);
+    const int M = auto_chunk(dtype, chunk, dk, dv);
     if (dtype == DIG_BF16) {
       if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(o))
         return fail(DIG_EINVAL, "gla_fwd: bf16 path needs 16-byte aligned q, k, v, log_alpha, o");
@@ -119,8 +122,9 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, 
       if ((o_sb | o_st | o_sh) % 4) return fail(DIG_EINVAL, "gla_fwd: bf16 output strides must be multiples of 4");
       // the kernel addresses one (batch, head) slice with 32-bit byte offsets
       if (((int64_t)(T - 1) * qk_st + dk) * 2 >= ((int64_t)1 << 31) ||
-          ((int64_t)(T - 1) * v_st + dv) * 2 >= ((int64_t)1 << 31))
-        return fail(DIG_EINVAL, "gla_fwd: one (batch, head) slice of q/k/log_alpha or v spans 2 GiB or more");
+          ((int64_t)(T - 1) * v_st + dv) * 2 >= ((int64_t)1 << 31) ||
+          ((int64_t)(T - 1) * o_st + dv) * 2 >= ((int64_t)1 << 31))
+        return fail(DIG_EINVAL, "gla_fwd: one (batch, head) slice of q/k/log_alpha, v or o spans 2 GiB or more");
     } else {
       if (dig_gla_f32_lds_bytes(dk, dv, M) > 160 * 1024)
         return fail(DIG_EINVAL, "gla_fwd: fp32 path LDS need exceeds 160 KiB for dk=%d dv=%d chunk=%d", dk, dv, M);

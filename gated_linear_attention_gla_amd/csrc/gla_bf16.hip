@@ -14,7 +14,8 @@
 // large enough for that factorisation to overflow, the chunk computes the
 // intra weights pairwise on the VALU instead (exact exponent differences), so
 // any finite log-gate <= 0 stays accurate.  Every other factor is bounded by 1
-// for non-positive gates.
+// for non-positive gates.  The choice is made per chunk from M * max|log-gate|,
+// a bound on every |b| in the chunk.
 //
 // Sequence segments.  To give the GPU enough independent work, each
 // (batch, head) scan is split into G segments of whole chunks, one workgroup
@@ -31,13 +32,19 @@
 // hits the L2 / Infinity Cache.
 //
 // gfx950 mapping
-//   * NW = DP/16 waves; wave w owns value columns [16w, 16w+16): the fp32
-//     state of those columns stays in the wave's MFMA accumulators;
+//   * a workgroup has DT = DP/16 consumer waves and DT producer waves.  A
+//     consumer owns 16 value columns: the fp32 state of those columns stays in
+//     its MFMA accumulators; it writes o and updates the state.  A producer
+//     owns 16 key channels: it loads the next chunk, scans its gates and forms
+//     q~, k~, k^; the producers together build the causal P^T tiles.  The
+//     producers work one chunk ahead on the other half of double-buffered LDS
+//     tiles, so the two roles overlap (three barriers per chunk);
 //   * the scan permutation is applied in the loads (scan position p reads
 //     canonical token scan_to_canon(p)); no permuted copy is ever written;
 //   * all LDS tiles are token-major rows written with 16-byte stores; the
-//     products that contract over tokens (V^T P^T and k^T v) fetch their
-//     operands with ds_read_b64_tr_b16, whose transpose puts tokens along K;
+//     products that contract over tokens (V^T P^T, k^T v and the gate scan)
+//     fetch their operands with ds_read_b64_tr_b16, whose transpose puts
+//     tokens along K;
 //   * v_mfma_f32_16x16x32_bf16 with fp32 accumulation is the only MFMA shape:
 //     channels are zero-padded to a multiple of 32, an odd 16-token tile count
 //     pads its last token block with zeros;
@@ -85,9 +92,6 @@ __device__ __forceinline__ uint4 gload16(const uint16_t *p) {
   const u32x4_t v = *(__attribute__((address_space(1))) const u32x4_t *)(size_t)p;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ void gstore8(uint16_t *p, uint2 v) {
-  *(__attribute__((address_space(1))) u32x2_t *)(size_t)p = u32x2_t{v.x, v.y};
-}
 // Raw buffer loads: 48-bit base (one (batch, head) slice, wave-uniform) plus
 // a 32-bit byte offset per lane.  Offsets at or beyond num_records return
 // zeros, which serves both the ragged tail and the channel padding without
@@ -99,6 +103,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, un
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, unsigned off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Raw buffer store of 8 bytes; out-of-range offsets are dropped, so stores
+// need no branch (which would split the surrounding MFMA code into blocks).
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, unsigned off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, (int)off, 0, 0);
 }
 __device__ __forceinline__ uint4 lds4(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane j
@@ -154,7 +163,7 @@ struct Params {
   int seg_chunks, nseg, per_xcd;   // chunks per segment, segments per scan, scans per XCD
   int cgr;                         // 16-byte channel groups holding data: ceil(max(dk, dv) / 8)
   unsigned cg_magic;               // ceil(2^31 / cgr): idx / cgr == umulhi(2 idx, cg_magic) for idx < 2^20
-  unsigned qk_span, v_span;        // bytes addressable in one (batch, head) slice of q/k/g and of v
+  unsigned qk_span, v_span, o_span;   // bytes addressable in one (batch, head) slice of q/k/g, v, o
   int blk_floats;                  // floats of one published state block
   int *ticket;                     // launch-order ticket counter (reset by the last taker)
   unsigned *flags;                 // [units][nseg]: epoch*4 + {1 aggregate, 2 inclusive}
@@ -164,75 +173,80 @@ struct Params {
   unsigned epoch;
 };
 
+// Workgroup: DT = DP/16 consumer waves, one per 16 value columns (they hold
+// the fp32 state of those columns and write o), and DT producer waves, one per
+// 16 key channels (they stage the next chunk: loads, gate scan, q~/k~/k^,
+// P^T tiles).  Producers run one chunk ahead of the consumers on the other
+// half of double-buffered LDS tiles, so the two halves of the work overlap.
 template <int DP>
 struct Shape {
-  static constexpr int NW = DP / 16 > 2 ? DP / 16 : 2;   // waves per workgroup
+  static constexpr int DT = DP / 16;
+  static constexpr int NW = 2 * DT;        // waves per workgroup
   static constexpr int NT = NW * kWave;
+  static constexpr int NTP = DT * kWave;   // producer threads
 };
 
 template <int DP, int M>
 struct Lds {
-  static constexpr int QS = DP + 16;    // token-major bf16 row stride (elements): conflict-free transpose reads
-  static constexpr int HS = DP / 2 + 4; // fp32 row stride of one plane of the cumulative gates
+  // Token-major bf16 row stride (elements).  Row-parallel reads (16 lanes on
+  // 16 rows, 8 or 16 bytes each) are bank-conflict free when the stride is
+  // 4 * odd dwords; the transposing reads (4 rows x 32 bytes) need the four
+  // rows on disjoint 8-bank groups.  DP + 8 satisfies both for 64 and 96
+  // channels, DP + 24 for 32 and 128.
+  static constexpr int QS = (DP == 64 || DP == 96) ? DP + 8 : DP + 24;
   static constexpr int MT = M / 16;
-  static constexpr int JP = (MT + 1) / 2;
   static constexpr int NPT = MT * (MT + 1) / 2;        // causal 16x16 tiles of P^T
   static constexpr int TILE = M * QS * 2;
-  static constexpr int oQ = 0;                         // q~ (raw q on the pairwise path)
-  static constexpr int oK = oQ + TILE;                 // k~ (raw k on the pairwise path)
-  static constexpr int oKh = oK + TILE;                // raw gates, then k^ = k e^{b_last - b}
-  static constexpr int oV = oKh + TILE;                // v
-  static constexpr int oB = oV + TILE;                 // cumulative gates, 2 planes [2][M][HS] fp32 (log2)
-  static constexpr int oPT = oB;                       // P^T tiles (MFMA fragment order, 512 B each),
-                                                       // in the gate buffer once it is dead
-  static constexpr int oBl = oB + 2 * M * HS * 4;      // chunk total b_last [DP] fp32 (log2)
-  static constexpr int oGam = oBl + DP * 4;            // e^{b_last} [DP]
-  static constexpr int oL = oGam + DP * 4;             // lower-triangular ones, MFMA fragments [MT][JP][64] x 16 B
-  static constexpr int oTok = oL + MT * JP * 1024;     // byte offsets of the next chunk's tokens [2][M]
-  static constexpr int oMisc = oTok + 2 * M * 4;       // flag, ticket, look-back result
+  // per buffer (chunk parity): q -> q~, k -> k~, gates -> k^, v
+  static constexpr int BUF = 4 * TILE;
+  static constexpr int oBuf = 0;                       // [2][4][M][QS] bf16
+  static constexpr int oPT = 2 * BUF;                  // [2][NPT][256] bf16 P^T tiles (MFMA fragment order)
+  static constexpr int oB32 = oPT + 2 * NPT * 512;     // [M][DP] fp32 cumulative gates (pairwise chunks only)
+  static constexpr int oGam = oB32 + M * DP * 4;       // [2][DP] e^{b_last}
+  static constexpr int oTok = oGam + 2 * DP * 4;       // [2][2][M] token byte offsets (chunk parity; q/k/g, v)
+  static constexpr int oVote = oTok + 4 * M * 4;       // [2][16] per producer wave: chunk needs the pairwise path
+  static constexpr int oMisc = oVote + 2 * 16 * 4;     // ticket, look-back result
   static constexpr int bytes = oMisc + 64;
-  static_assert(NPT * 512 <= 2 * M * HS * 4, "P^T tiles fit in the gate buffer");
 };
 
-// Occupancy target (waves per SIMD): chunks of <= 32 tokens fit three waves
-// per SIMD; 64-token chunks need the larger register budget of two.
-template <int M>
+// Register budget: the whole workgroup on one CU, 2*DT waves over 4 SIMDs.
+template <int DP>
 struct Occ {
-  static constexpr int waves_per_simd = M <= 32 ? 3 : 2;
+  static constexpr int waves_per_simd = (2 * (DP / 16) + 3) / 4 < 2 ? 2 : (2 * (DP / 16) + 3) / 4;
 };
 
 template <int DP, int M>
-__global__ void __launch_bounds__(Shape<DP>::NT) __attribute__((amdgpu_waves_per_eu(Occ<M>::waves_per_simd)))
+__global__ void __launch_bounds__(Shape<DP>::NT) __attribute__((amdgpu_waves_per_eu(Occ<DP>::waves_per_simd)))
 gla_fwd_bf16_kernel(Params P) {
-  constexpr int NT = Shape<DP>::NT;
-  constexpr int NW = Shape<DP>::NW;
+  constexpr int NT = Shape<DP>::NT, NTP = Shape<DP>::NTP;
+  constexpr int DT = DP / 16;                // channel tiles = consumer waves = producer waves
   constexpr int MT = M / 16;                 // token tiles per chunk
-  constexpr int DT = DP / 16;                // channel tiles
   constexpr int K32 = DP / 32;               // 32-wide channel blocks
   constexpr int JP = (MT + 1) / 2;           // 32-token K blocks
-  constexpr int R = (M * (DP / 8) + NT - 1) / NT;   // max 16-byte items per thread per tensor
-  constexpr int QS = Lds<DP, M>::QS, HS = Lds<DP, M>::HS, NPT = Lds<DP, M>::NPT;
-  static_assert(DP % 32 == 0 && NW == DT, "one wave per 16-channel tile");
+  constexpr int R = (M * (DP / 8) + NTP - 1) / NTP;   // max 16-byte items per producer thread per tensor
+  constexpr int QS = Lds<DP, M>::QS, NPT = Lds<DP, M>::NPT, TILE = Lds<DP, M>::TILE;
+  static_assert(DP % 32 == 0 && DT <= 16, "channel tiling");
+  static_assert(Lds<DP, M>::bytes <= 160 * 1024, "LDS plan exceeds 160 KiB");
   const int CG = P.cgr;                      // 16-byte channel groups carrying data (the rest stay 0)
   const int ITEMS = M * CG;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oQ);
-  uint16_t *sK = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oK);
-  uint16_t *sKh = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oKh);
-  uint16_t *sG = sKh;   // raw gates live in the k^ tile until the scan has read them
-  uint16_t *sV = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oV);
-  float *sB = reinterpret_cast<float *>(smem + Lds<DP, M>::oB);
-  float *sBl = reinterpret_cast<float *>(smem + Lds<DP, M>::oBl);
-  float *sGam = reinterpret_cast<float *>(smem + Lds<DP, M>::oGam);
-  uint16_t *sPT = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oPT);
-  uint4 *sL = reinterpret_cast<uint4 *>(smem + Lds<DP, M>::oL);
-  unsigned *sTok = reinterpret_cast<unsigned *>(smem + Lds<DP, M>::oTok);   // [0..M) q/k/g, [M..2M) v
-  int *sMisc = reinterpret_cast<int *>(smem + Lds<DP, M>::oMisc);   // [0] pairwise [1] ticket [2] look-back
+  auto tile = [&](int par, int which) {      // which: 0 q, 1 k, 2 gates / k^, 3 v
+    return reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oBuf + par * Lds<DP, M>::BUF + which * TILE);
+  };
+  auto ptile = [&](int par) { return reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oPT + par * NPT * 512); };
+  float *sB32 = reinterpret_cast<float *>(smem + Lds<DP, M>::oB32);
+  auto gam = [&](int par) { return reinterpret_cast<float *>(smem + Lds<DP, M>::oGam) + par * DP; };
+  unsigned *sTok = reinterpret_cast<unsigned *>(smem + Lds<DP, M>::oTok);
+  int *sVote = reinterpret_cast<int *>(smem + Lds<DP, M>::oVote);
+  int *sMisc = reinterpret_cast<int *>(smem + Lds<DP, M>::oMisc);   // [1] ticket [2] look-back
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);   // transpose-read addressing
+  const bool producer = wave >= DT;
+  const int pw = wave - DT;                  // producer wave index (channel tile)
+  const int ptid = tid - NTP;                // producer thread index
 
   // ---- work assignment: tickets in launch order, XCD-major layout; segment
   // g of a scan always holds a larger ticket than segment g-1 of it.
@@ -258,67 +272,70 @@ gla_fwd_bf16_kernel(Params P) {
   const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(P.k + b * P.qk_sb + h * P.qk_sh, P.qk_span);
   const __amdgpu_buffer_rsrc_t rg_ = make_rsrc(P.g + b * P.qk_sb + h * P.qk_sh, P.qk_span);
   const __amdgpu_buffer_rsrc_t rv_ = make_rsrc(P.v + b * P.v_sb + h * P.v_sh, P.v_span);
-  uint16_t *ob = P.o + b * P.o_sb + h * P.o_sh;
+  const __amdgpu_buffer_rsrc_t ro_ = make_rsrc(P.o + b * P.o_sb + h * P.o_sh, P.o_span);
 
-  const int n0 = 16 * wave;                 // this wave's value columns / gate channels
-  const bool has_cols = (n0 < dv);
+  const int n0 = 16 * (producer ? pw : wave);   // consumer: value columns; producer: key channels
+  const bool has_cols = !producer && (n0 < dv), has_rows = producer && (n0 < dk);
   const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;   // tiles present in a state block
   const int64_t slot0 = (int64_t)unit * P.nseg;
+  const int acol = n0 + 4 * g4;             // accumulator-layout channel of this lane (4 channels)
 
-  // ---- one-time set-up: zero channel padding, lower-triangular fragments
+  // ---- one-time set-up: e^{b_last} = 1 for channel tiles no wave scans
+  // (beyond dk), zero the channel padding of every tile of both buffers
+  for (int x = tid; x < 2 * DP; x += NT) gam(0)[x] = 1.f;
   if (CG < DP / 8) {
     const int PADG = DP / 8 - CG;
-    for (int x = tid; x < M * PADG; x += NT) {
-      const int tl = x / PADG, cg = CG + (x - tl * PADG);
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = z;
-      *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = z;
-      *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = z;
-      *reinterpret_cast<uint4 *>(sV + tl * QS + 8 * cg) = z;
+    for (int x = tid; x < 8 * M * PADG; x += NT) {
+      const int tb = x / (M * PADG), r2 = x - tb * (M * PADG);
+      const int tl = r2 / PADG, cg = CG + (r2 - tl * PADG);
+      *reinterpret_cast<uint4 *>(tile(tb >> 2, tb & 3) + tl * QS + 8 * cg) = make_uint4(0, 0, 0, 0);
     }
   }
-  // L^T fragment (B operand) of the scan: column t = 16i + l16, K slots =
-  // tokens 32jp + 4g4 + {0..3} and 32jp + 16 + 4g4 + {0..3}; 1.0 where s <= t.
-  for (int f = wave; f < MT * JP; f += NW) {
-    const int i = f / JP, jp = f - i * JP;
-    const int t = 16 * i + l16, s0_ = 32 * jp + 4 * g4;
+  // Lower-triangular ones as the B operand of the gate scan, b^T = G^T L^T:
+  // column t = d + l16, K slots s = 4*g4 + {0..3} and 16 + 4*g4 + {0..3}
+  // (relative to the K block); 1.0 where s <= t.  Only d = 0 and d = 16
+  // occur partially, every other (tile, K block) is all ones or skipped.
+  auto lfrag = [&](int d) {
+    const int t = d + l16, s0_ = 4 * g4;
     uint4 w;
     w.x = (s0_ + 0 <= t ? 0x3F80u : 0u) | (s0_ + 1 <= t ? 0x3F800000u : 0u);
     w.y = (s0_ + 2 <= t ? 0x3F80u : 0u) | (s0_ + 3 <= t ? 0x3F800000u : 0u);
     w.z = (s0_ + 16 <= t ? 0x3F80u : 0u) | (s0_ + 17 <= t ? 0x3F800000u : 0u);
     w.w = (s0_ + 18 <= t ? 0x3F80u : 0u) | (s0_ + 19 <= t ? 0x3F800000u : 0u);
-    sL[f * 64 + lane] = w;
-  }
+    return w;
+  };
+  const uint4 ONES = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
-  // ---- token offsets of chunk c (scan order -> canonical token), kOOB past the
-  // end of the sequence and for the chunk after the segment (its loads then
-  // return zeros without touching memory)
-  auto fill_tok = [&](int c) {
-    if (tid < M) {
-      const int p = c * M + tid;
+  // ================================ producers =================================
+  // token offsets of chunk x (scan order -> canonical token) into parity
+  // buffer x & 1; kOOB past the end of the sequence and for chunks after the
+  // segment (their loads then return zeros without touching memory)
+  auto fill_tok = [&](int x) {
+    if (ptid >= 0 && ptid < M) {
+      const int p = x * M + ptid;
       unsigned oqk = kOOB, ov = kOOB;
-      if (c < c_end && p < T) {
+      if (x < c_end && p < T) {
         const unsigned n = (unsigned)scan_to_canon(P.dir, P.gh, P.gw, T, p);
         oqk = n * (unsigned)P.qk_st * 2u;
         ov = n * (unsigned)P.v_st * 2u;
       }
-      sTok[tid] = oqk;
-      sTok[M + tid] = ov;
+      unsigned *tb = sTok + (x & 1) * 2 * M;
+      tb[ptid] = oqk;
+      tb[M + ptid] = ov;
     }
   };
-
-  // ---- loads: item idx -> (token tl, 16-byte channel group cg), from the token table
+  // Loads of chunk x: item idx -> (token tl, 16-byte channel group cg).
+  // Unconditional: a load under a branch would make the loop-carried
+  // registers merge with their old values and force an early wait.
   uint4 rq[R], rk[R], rg[R], rv[R];
-  auto load_chunk = [&](bool with_q) {
-    // Unconditional: a load under a branch would make the loop-carried
-    // registers merge with their old values, which forces the prefetch to be
-    // waited for right away.
+  auto load_chunk = [&](int x, bool with_q) {
+    const unsigned *tb = sTok + (x & 1) * 2 * M;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int idx = tid + r * NT;
+      const int idx = ptid + r * NTP;
       const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
       const bool ok = idx < ITEMS;
-      const unsigned tq = sTok[ok ? tl : 0], tv = sTok[M + (ok ? tl : 0)];
+      const unsigned tq = tb[ok ? tl : 0], tv = tb[M + (ok ? tl : 0)];
       const unsigned ok_qk = ok && (8 * cg < dk) ? tq + 16u * cg : kOOB;
       const unsigned ok_v = ok && (8 * cg < dv) ? tv + 16u * cg : kOOB;
       if (with_q) rq[r] = bload16(rq_, ok_qk);
@@ -327,115 +344,259 @@ gla_fwd_bf16_kernel(Params P) {
       rv[r] = bload16(rv_, ok_v);
     }
   };
-
-  // Stage 1: raw gates and v to LDS; token table of the next chunk.
-  auto stage1 = [&](int c_next) {
+  // P1(x): the loaded chunk x to its tiles, then the loads of chunk x+1 and
+  // the token table of chunk x+2.  with_q: also a vote per wave on whether
+  // M * max|log-gate| * log2(e) can exceed kFastRange (then the chunk takes
+  // the pairwise path; the bound covers every |b| in the chunk).
+  const float bound_scale = (float)M * kLog2e;
+  auto produce1 = [&](int x, bool with_q) {
+    const int par = x & 1;
+    uint16_t *tq = tile(par, 0), *tk = tile(par, 1), *tg = tile(par, 2), *tv = tile(par, 3);
+    unsigned gmax = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int idx = tid + r * NT;
+      const int idx = ptid + r * NTP;
       if (idx < ITEMS) {
         const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
-        *reinterpret_cast<uint4 *>(sG + tl * QS + 8 * cg) = rg[r];
-        *reinterpret_cast<uint4 *>(sV + tl * QS + 8 * cg) = rv[r];
+        const int off = tl * QS + 8 * cg;
+        if (with_q) *reinterpret_cast<uint4 *>(tq + off) = rq[r];
+        *reinterpret_cast<uint4 *>(tk + off) = rk[r];
+        *reinterpret_cast<uint4 *>(tg + off) = rg[r];
+        *reinterpret_cast<uint4 *>(tv + off) = rv[r];
+        if (with_q) {
+          const uint32_t gw_[4] = {rg[r].x, rg[r].y, rg[r].z, rg[r].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            gmax = max(gmax, max(gw_[e] & 0x7fffu, (gw_[e] >> 16) & 0x7fffu));   // |bf16| bits
+        }
       }
     }
-    fill_tok(c_next);
-    if (tid == 0) sMisc[0] = 0;
+    if (with_q) {
+      const bool bad = !(__uint_as_float(gmax << 16) * bound_scale <= kFastRange);   // NaN / inf too
+      const bool any_bad = __any(bad);
+      if (lane == 0) sVote[par * 16 + pw] = any_bad ? 1 : 0;
+    }
+    load_chunk(x + 1, with_q);
+    fill_tok(x + 2);
   };
-
-  // Stage 2: inclusive cumulative gates as an MFMA product, b^T = G^T L^T
-  // (bf16 gates and 1.0 are exact; fp32 sums), scaled to log2 units.  Wave w
-  // owns gate channels [16w, 16w+16); lane (l16, g4) receives token 16i + l16,
-  // channels 16w + 4g4 .. +3, stored as one float4 in plane (g4 & 1) of sB.
-  // Also writes b_last and e^{b_last}, and flags the chunk for the pairwise
-  // path when any |b| exceeds the factorisable range.
-  auto stage2 = [&]() {
+  auto chunk_pairwise = [&](int x) {
+    int v = 0;
+#pragma unroll
+    for (int w = 0; w < DT; ++w) v |= sVote[(x & 1) * 16 + w];
+    return v != 0;
+  };
+  // Inclusive cumulative gates of this producer wave's 16 channels as an MFMA
+  // product, b^T = G^T L^T (bf16 gates and 1.0 are exact; fp32 sums), log2
+  // units.  bt[i] of lane (l16, g4): token 16i + l16, channels acol .. acol+3.
+  auto scan = [&](const uint16_t *tg, f32x4_t *bt) {
+    const uint4 L0 = lfrag(0), L1 = lfrag(16);
     uint4 gf[JP];
 #pragma unroll
     for (int jp = 0; jp < JP; ++jp) {
-      const uint2 lo = lds_tr(sG + (32 * jp + 4 * g4 + rowoff) * QS + n0 + coloff);
-      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(sG + (32 * jp + 16 + 4 * g4 + rowoff) * QS + n0 + coloff)
+      const uint2 lo = lds_tr(tg + (32 * jp + 4 * g4 + rowoff) * QS + n0 + coloff);
+      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(tg + (32 * jp + 16 + 4 * g4 + rowoff) * QS + n0 + coloff)
                                          : make_uint2(0, 0);
       gf[jp] = cat(lo, hi);
     }
-    float mag = 0.f;
-    const int ch0 = n0 + 4 * g4;
-    float *plane = sB + (g4 & 1) * (M * HS) + (ch0 >> 3) * 4;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jp = 0; jp < JP; ++jp)
-        if (32 * jp <= 16 * i + 15) acc = mfma32(gf[jp], sL[(i * JP + jp) * 64 + lane], acc);
-      const float4 bv = make_float4(acc[0] * kLog2e, acc[1] * kLog2e, acc[2] * kLog2e, acc[3] * kLog2e);
-      *reinterpret_cast<float4 *>(plane + (16 * i + l16) * HS) = bv;
-      mag = fmaxf(mag, fmaxf(fmaxf(fabsf(bv.x), fabsf(bv.y)), fmaxf(fabsf(bv.z), fabsf(bv.w))));
-      if (i == MT - 1 && l16 == 15) {
-        *reinterpret_cast<float4 *>(sBl + ch0) = bv;
-        *reinterpret_cast<float4 *>(sGam + ch0) = make_float4(fexp2(bv.x), fexp2(bv.y), fexp2(bv.z), fexp2(bv.w));
+      for (int jp = 0; jp < JP; ++jp) {
+        const int d = 16 * i - 32 * jp;
+        if (d >= 0) acc = mfma32(gf[jp], d >= 32 ? ONES : (d == 16 ? L1 : L0), acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bt[i][e] = acc[e] * kLog2e;
+    }
+  };
+  // b_last of this lane's 4 channels (held by lane l16 = 15 of the last tile);
+  // e^{b_last} goes to LDS for the consumers' state update.
+  auto chunk_total = [&](const f32x4_t *bt, float *gmo, float *bl, int par) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bl[e] = __shfl(bt[MT - 1][e], 15 + 16 * g4);
+      gmo[e] = fexp2(bl[e]);
+    }
+    if (l16 == 0) *reinterpret_cast<float4 *>(gam(par) + acol) = make_float4(gmo[0], gmo[1], gmo[2], gmo[3]);
+  };
+  // k^ = k e^{b_last - b} (exact exponent difference) into the gate tile
+  auto khat_direct = [&](const uint16_t *tk, uint16_t *tg, const f32x4_t *bt, const float *bl) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int off = (16 * i + l16) * QS + acol;
+      const uint2 kw = lds2(tk + off);
+      *reinterpret_cast<uint2 *>(tg + off) =
+          make_uint2(pack_bf16x2(bf16lo(kw.x) * fexp2(bl[0] - bt[i][0]), bf16hi(kw.x) * fexp2(bl[1] - bt[i][1])),
+                     pack_bf16x2(bf16lo(kw.y) * fexp2(bl[2] - bt[i][2]), bf16hi(kw.y) * fexp2(bl[3] - bt[i][3])));
+    }
+  };
+  // q~ = q e^{b} in place
+  auto qtilde = [&](uint16_t *tq, const f32x4_t *bt) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int off = (16 * i + l16) * QS + acol;
+      const uint2 qw = lds2(tq + off);
+      *reinterpret_cast<uint2 *>(tq + off) =
+          make_uint2(pack_bf16x2(bf16lo(qw.x) * fexp2(bt[i][0]), bf16hi(qw.x) * fexp2(bt[i][1])),
+                     pack_bf16x2(bf16lo(qw.y) * fexp2(bt[i][2]), bf16hi(qw.y) * fexp2(bt[i][3])));
+    }
+  };
+  // P2(x): per producer wave, its 16 channels: b, e^{b_last}; fast chunks:
+  // q~ = q e^{b}, k~ = k e^{-b}, k^ = k~ e^{b_last} in place (|b| <= 64: no
+  // overflow); pairwise chunks: b to LDS (fp32) and k^ directly.  bt stays in
+  // registers for P3 of a pairwise chunk.
+  f32x4_t bt[MT];
+  auto produce2 = [&](int x, bool pairwise) {
+    const int par = x & 1;
+    uint16_t *tq = tile(par, 0), *tk = tile(par, 1), *tg = tile(par, 2);
+    float gmo[4], bl[4];
+    scan(tg, bt);
+    chunk_total(bt, gmo, bl, par);
+    if (!pairwise) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int off = (16 * i + l16) * QS + acol;
+        const uint2 qw = lds2(tq + off), kw = lds2(tk + off);
+        const uint32_t qa[2] = {qw.x, qw.y}, ka[2] = {kw.x, kw.y};
+        uint32_t oq[2], ok[2], oh[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          oq[e] = pack_bf16x2(bf16lo(qa[e]) * fexp2(bt[i][2 * e]), bf16hi(qa[e]) * fexp2(bt[i][2 * e + 1]));
+          const float k0 = bf16lo(ka[e]) * fexp2(-bt[i][2 * e]), k1 = bf16hi(ka[e]) * fexp2(-bt[i][2 * e + 1]);
+          ok[e] = pack_bf16x2(k0, k1);
+          oh[e] = pack_bf16x2(k0 * gmo[2 * e], k1 * gmo[2 * e + 1]);
+        }
+        *reinterpret_cast<uint2 *>(tq + off) = make_uint2(oq[0], oq[1]);
+        *reinterpret_cast<uint2 *>(tk + off) = make_uint2(ok[0], ok[1]);
+        *reinterpret_cast<uint2 *>(tg + off) = make_uint2(oh[0], oh[1]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        *reinterpret_cast<float4 *>(sB32 + (16 * i + l16) * DP + acol) =
+            make_float4(bt[i][0], bt[i][1], bt[i][2], bt[i][3]);
+      khat_direct(tk, tg, bt, bl);
+    }
+  };
+  // P3(x), fast chunks: causal P^T tiles (j, i), j <= i, from q~ and k~,
+  // spread over the producer waves.
+  auto produce3_fast = [&](int x) {
+    const int par = x & 1;
+    const uint16_t *tq = tile(par, 0), *tk = tile(par, 1);
+    uint16_t *pt = ptile(par);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+      for (int j = 0; j <= i; ++j) {
+        const int ti = i * (i + 1) / 2 + j;
+        if (ti % DT == pw) {
+          const uint16_t *krow = tk + (16 * j + l16) * QS;
+          const uint16_t *qrow = tq + (16 * i + l16) * QS;
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb2 = 0; kb2 < K32; ++kb2)
+            acc = mfma32(lds4(krow + 32 * kb2 + 8 * g4), lds4(qrow + 32 * kb2 + 8 * g4), acc);
+          if (j == i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * g4 + e > l16) acc[e] = 0.f;   // causal: s > t
+          }
+          *reinterpret_cast<uint2 *>(pt + ti * 256 + lane * 4) = pack4(acc);
+        }
       }
     }
-    if (!(mag <= kFastRange)) sMisc[0] = 1;   // also catches NaN
+  };
+  // P3(x), pairwise chunks: P^T slot (tile ti = (j, i), lane l, element e) is
+  // t = 16i + l%16, s = 16j + 4(l/16) + e; value sum_c q_tc k_sc 2^(b_tc - b_sc)
+  // over all key channels for s <= t, else 0.  Slots spread over the producers.
+  auto produce3_pairwise = [&](int x) {
+    const int par = x & 1;
+    const uint16_t *tq = tile(par, 0), *tk = tile(par, 1);
+    uint16_t *pt = ptile(par);
+    for (int sl = ptid; sl < NPT * 256; sl += NTP) {
+      const int ti = sl >> 8, ln = (sl >> 2) & 63, e = sl & 3;
+      int i = 0;
+      while ((i + 1) * (i + 2) / 2 <= ti) ++i;
+      const int j = ti - i * (i + 1) / 2;
+      const int t = 16 * i + (ln & 15), s_ = 16 * j + 4 * (ln >> 4) + e;
+      float acc = 0.f;
+      if (s_ <= t) {
+        for (int ch = 0; ch < dk; ++ch) {
+          const float qv = __uint_as_float((uint32_t)tq[t * QS + ch] << 16);
+          const float kv = __uint_as_float((uint32_t)tk[s_ * QS + ch] << 16);
+          acc += qv * kv * fexp2(sB32[t * DP + ch] - sB32[s_ * DP + ch]);
+        }
+      }
+      pt[sl] = (uint16_t)f2bf(acc);
+    }
   };
 
-  // cumulative gates of token tl, channels 8cg .. 8cg+7
-  auto item_b = [&](int tl, int cg, float *bt) {
-    const float4 a = *reinterpret_cast<const float4 *>(sB + tl * HS + 4 * cg);
-    const float4 c2 = *reinterpret_cast<const float4 *>(sB + M * HS + tl * HS + 4 * cg);
-    bt[0] = a.x; bt[1] = a.y; bt[2] = a.z; bt[3] = a.w;
-    bt[4] = c2.x; bt[5] = c2.y; bt[6] = c2.z; bt[7] = c2.w;
-  };
-  auto b_at = [&](int t, int ch) { return sB[((ch >> 2) & 1) * (M * HS) + t * HS + (ch >> 3) * 4 + (ch & 3)]; };
-  // 8 consecutive fp32 values from LDS.
-  auto lds8f = [&](const float *p, float *out) {
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    const float4 b2 = *reinterpret_cast<const float4 *>(p + 4);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b2.x; out[5] = b2.y; out[6] = b2.z; out[7] = b2.w;
-  };
-
-  // k^ = k e^{b_last - b} for item r (exact exponent difference)
-  auto khat_direct = [&](int r, const float *bt, const float *bl) {
-    const uint32_t kw[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
-    uint4 oh;
-    oh.x = pack_bf16x2(bf16lo(kw[0]) * fexp2(bl[0] - bt[0]), bf16hi(kw[0]) * fexp2(bl[1] - bt[1]));
-    oh.y = pack_bf16x2(bf16lo(kw[1]) * fexp2(bl[2] - bt[2]), bf16hi(kw[1]) * fexp2(bl[3] - bt[3]));
-    oh.z = pack_bf16x2(bf16lo(kw[2]) * fexp2(bl[4] - bt[4]), bf16hi(kw[2]) * fexp2(bl[5] - bt[5]));
-    oh.w = pack_bf16x2(bf16lo(kw[3]) * fexp2(bl[6] - bt[6]), bf16hi(kw[3]) * fexp2(bl[7] - bt[7]));
-    return oh;
-  };
-
+  // ================================ consumers =================================
   // v fragments with tokens along K: K block jp holds tokens 32jp + 4*g4 + e
   // (slots 0..3) and 32jp + 16 + 4*g4 + e (slots 4..7); this wave's columns.
-  auto v_frags = [&](uint4 *vf) {
+  auto v_frags = [&](const uint16_t *tv, uint4 *vf) {
 #pragma unroll
     for (int jp = 0; jp < JP; ++jp) {
-      const uint2 lo = lds_tr(sV + (32 * jp + 4 * g4 + rowoff) * QS + n0 + coloff);
-      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(sV + (32 * jp + 16 + 4 * g4 + rowoff) * QS + n0 + coloff)
+      const uint2 lo = lds_tr(tv + (32 * jp + 4 * g4 + rowoff) * QS + n0 + coloff);
+      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(tv + (32 * jp + 16 + 4 * g4 + rowoff) * QS + n0 + coloff)
                                          : make_uint2(0, 0);
       vf[jp] = cat(lo, hi);
     }
   };
-
-  // S = diag(e^{b_last}) S + k^^T v for this wave's columns; optionally
-  // accumulates the product of the gates in gprod (same row layout as S).
-  auto state_update = [&](f32x4_t *S, const uint4 *vf, f32x4_t *gprod) {
+  // S = diag(e^{b_last}) S + k^^T v for this wave's columns (k^ in the gate
+  // tile); optionally accumulates the product of the gates in gprod.
+  auto state_update = [&](int par, f32x4_t *S, f32x4_t *gprod) {
+    const uint16_t *th = tile(par, 2);
+    uint4 vf[JP];
+    v_frags(tile(par, 3), vf);
+    const float *gm_ = gam(par);
 #pragma unroll
     for (int r = 0; r < DT; ++r) {
-      const float4 gm = *reinterpret_cast<const float4 *>(sGam + 16 * r + 4 * g4);
+      const float4 gm = *reinterpret_cast<const float4 *>(gm_ + 16 * r + 4 * g4);
       S[r][0] *= gm.x; S[r][1] *= gm.y; S[r][2] *= gm.z; S[r][3] *= gm.w;
       if (gprod) { gprod[r][0] *= gm.x; gprod[r][1] *= gm.y; gprod[r][2] *= gm.z; gprod[r][3] *= gm.w; }
 #pragma unroll
       for (int jp = 0; jp < JP; ++jp) {
-        const uint2 lo = lds_tr(sKh + (32 * jp + 4 * g4 + rowoff) * QS + 16 * r + coloff);
+        const uint2 lo = lds_tr(th + (32 * jp + 4 * g4 + rowoff) * QS + 16 * r + coloff);
         const uint2 hi = (2 * jp + 1 < MT)
-                             ? lds_tr(sKh + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * r + coloff)
+                             ? lds_tr(th + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * r + coloff)
                              : make_uint2(0, 0);
         S[r] = mfma32(cat(lo, hi), vf[jp], S[r]);
       }
     }
   };
-
+  // o of chunk c for this wave's columns: O^T = S^T q~^T + V^T P^T (S: the
+  // state entering the chunk), stored 8 bytes per lane.
+  auto outputs = [&](int c, const f32x4_t *S) {
+    const int par = c & 1;
+    const uint16_t *tq = tile(par, 0), *pt = ptile(par);
+    uint4 vf[JP];
+    v_frags(tile(par, 3), vf);
+    uint4 sa[K32];   // S^T (bf16) as the A operand, K = channels
+#pragma unroll
+    for (int kb2 = 0; kb2 < K32; ++kb2) sa[kb2] = cat(pack4(S[2 * kb2]), pack4(S[2 * kb2 + 1]));
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const uint16_t *qrow = tq + (16 * i + l16) * QS;
+      f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb2 = 0; kb2 < K32; ++kb2)
+        O = mfma32(sa[kb2], cat(lds2(qrow + 32 * kb2 + 4 * g4), lds2(qrow + 32 * kb2 + 16 + 4 * g4)), O);
+#pragma unroll
+      for (int jp = 0; jp < JP; ++jp) {
+        const int j0 = 2 * jp, j1 = 2 * jp + 1;
+        if (j0 <= i) {
+          const uint2 pt0 = lds2(pt + (i * (i + 1) / 2 + j0) * 256 + lane * 4);
+          const uint2 pt1 = (j1 <= i) ? lds2(pt + (i * (i + 1) / 2 + j1) * 256 + lane * 4) : make_uint2(0, 0);
+          O = mfma32(vf[jp], cat(pt0, pt1), O);
+        }
+      }
+      const int p = c * M + 16 * i + l16;
+      const int n = n0 + 4 * g4;
+      bstore8(ro_, (p < T && n < dv) ? ((unsigned)p * (unsigned)P.o_st + (unsigned)n) * 2u : kOOB, pack4(O));
+    }
+  };
   // Initial state s0 for this wave's tiles (0 when absent).
   auto load_s0 = [&](f32x4_t *S) {
 #pragma unroll
@@ -443,7 +604,7 @@ gla_fwd_bf16_kernel(Params P) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ch = 16 * r + 4 * g4 + e, n = n0 + l16;
-        S[r][e] = (P.s0 && ch < dk && n < dv) ? P.s0[((int64_t)unit * dk + ch) * dv + n] : 0.f;
+        S[r][e] = (has_cols && P.s0 && ch < dk && n < dv) ? P.s0[((int64_t)unit * dk + ch) * dv + n] : 0.f;
       }
   };
   auto blk_at = [&](int r) { return ((r * NWv + wave) * 64 + lane) * 4; };
@@ -456,32 +617,36 @@ gla_fwd_bf16_kernel(Params P) {
   for (int r = 0; r < DT; ++r) gp[r] = f32x4_t{1.f, 1.f, 1.f, 1.f};
 
   // ======================= pass 1: segment aggregate =========================
+  // producers stage chunk c+1 (k, v, gates -> k^, e^{b_last}) while the
+  // consumers fold chunk c into the aggregate.
   if (!last_seg) {
     fill_tok(c_begin);
+    fill_tok(c_begin + 1);
     __syncthreads();
-    load_chunk(false);
+    if (producer) load_chunk(c_begin, false);
+    lds_barrier();
+    if (producer) produce1(c_begin, false);
+    lds_barrier();
+    if (has_rows) {
+      float gmo[4], bl[4];
+      scan(tile(c_begin & 1, 2), bt);
+      chunk_total(bt, gmo, bl, c_begin & 1);
+      khat_direct(tile(c_begin & 1, 1), tile(c_begin & 1, 2), bt, bl);
+    }
+    lds_barrier();
     for (int c = c_begin; c < c_end; ++c) {
-      stage1(c + 1);
-      lds_barrier();
-      stage2();
-      lds_barrier();
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int idx = tid + r * NT;
-        if (idx < ITEMS) {
-          const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
-          float bt[8], bl[8];
-          item_b(tl, cg, bt);
-          lds8f(sBl + 8 * cg, bl);
-          *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = khat_direct(r, bt, bl);
-        }
+      const int x = c + 1;
+      if (producer) {
+        if (x < c_end) produce1(x, false);
+      } else if (has_cols) {
+        state_update(c & 1, S, gp);
       }
-      load_chunk(false);
       lds_barrier();
-      if (has_cols) {
-        uint4 vf[JP];
-        v_frags(vf);
-        state_update(S, vf, gp);
+      if (has_rows && x < c_end) {
+        float gmo[4], bl[4];
+        scan(tile(x & 1, 2), bt);
+        chunk_total(bt, gmo, bl, x & 1);
+        khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
       }
       lds_barrier();
     }
@@ -525,8 +690,8 @@ gla_fwd_bf16_kernel(Params P) {
       const float *blk = P.inc + (slot0 + jstar) * P.blk_floats;
 #pragma unroll
       for (int r = 0; r < DT; ++r) {
-        const float4 x = (has_cols && r < DTr) ? ld_coherent(blk + blk_at(r)) : make_float4(0.f, 0.f, 0.f, 0.f);
-        Sin[r] = f32x4_t{x.x, x.y, x.z, x.w};
+        const float4 xx = (has_cols && r < DTr) ? ld_coherent(blk + blk_at(r)) : make_float4(0.f, 0.f, 0.f, 0.f);
+        Sin[r] = f32x4_t{xx.x, xx.y, xx.z, xx.w};
       }
     } else {
       load_s0(Sin);
@@ -569,163 +734,53 @@ gla_fwd_bf16_kernel(Params P) {
   for (int r = 0; r < DT; ++r) S[r] = Sin[r];
 
   // ========================= pass 2: outputs ==================================
-  // Drain this wave's outstanding global loads (the state loads above) so the
-  // loop below never waits on anything but its own prefetches.
+  // Three barrier intervals per chunk c: producers P1/P2/P3 of chunk c+1,
+  // consumers the outputs of chunk c, then its state update.  A pairwise
+  // chunk c+1 adds one interval (its q~ may be written only after every
+  // producer has read its raw q).
   drain_vmem();
   fill_tok(c_begin);
+  fill_tok(c_begin + 1);
   __syncthreads();
-  load_chunk(true);
+  if (producer) load_chunk(c_begin, true);
+  lds_barrier();
+  if (producer) produce1(c_begin, true);
+  lds_barrier();
+  bool pw_next = chunk_pairwise(c_begin);
+  if (has_rows) produce2(c_begin, pw_next);
+  lds_barrier();
+  if (producer) {
+    if (!pw_next) produce3_fast(c_begin); else produce3_pairwise(c_begin);
+  }
+  lds_barrier();
+  if (pw_next) {
+    if (has_rows) qtilde(tile(c_begin & 1, 0), bt);
+    lds_barrier();
+  }
   for (int c = c_begin; c < c_end; ++c) {
-    stage1(c + 1);
-    lds_barrier();
-    stage2();
-    lds_barrier();
-    const bool pairwise = (sMisc[0] != 0);
-    if (!pairwise) {
-      // q~ = q e^{b}, k~ = k e^{-b}, k^ = k~ e^{b_last}   (|b| <= 64: no overflow)
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int idx = tid + r * NT;
-        if (idx < ITEMS) {
-          const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
-          float bt[8], gm[8];
-          item_b(tl, cg, bt);
-          lds8f(sGam + 8 * cg, gm);
-          const uint32_t qw[4] = {rq[r].x, rq[r].y, rq[r].z, rq[r].w};
-          const uint32_t kw[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
-          uint32_t oq[4], ok[4], oh[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            oq[e] = pack_bf16x2(bf16lo(qw[e]) * fexp2(bt[2 * e]), bf16hi(qw[e]) * fexp2(bt[2 * e + 1]));
-            const float k0 = bf16lo(kw[e]) * fexp2(-bt[2 * e]), k1 = bf16hi(kw[e]) * fexp2(-bt[2 * e + 1]);
-            ok[e] = pack_bf16x2(k0, k1);
-            oh[e] = pack_bf16x2(k0 * gm[2 * e], k1 * gm[2 * e + 1]);
-          }
-          *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = make_uint4(oq[0], oq[1], oq[2], oq[3]);
-          *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = make_uint4(ok[0], ok[1], ok[2], ok[3]);
-          *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
-        }
-      }
-      load_chunk(true);
-      lds_barrier();
-      // P^T tiles (j, i), j <= i, each computed once, spread over the waves
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-#pragma unroll
-        for (int j = 0; j <= i; ++j) {
-          const int ti = i * (i + 1) / 2 + j;
-          if (ti % NW == wave) {
-            const uint16_t *krow = sK + (16 * j + l16) * QS;
-            const uint16_t *qrow = sQ + (16 * i + l16) * QS;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb2 = 0; kb2 < K32; ++kb2)
-              acc = mfma32(lds4(krow + 32 * kb2 + 8 * g4), lds4(qrow + 32 * kb2 + 8 * g4), acc);
-            if (j == i) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (4 * g4 + e > l16) acc[e] = 0.f;   // causal: s > t
-            }
-            *reinterpret_cast<uint2 *>(sPT + ti * 256 + lane * 4) = pack4(acc);
-          }
-        }
-      }
-    } else {
-      // exact pairwise intra weights: raw q, k to LDS, k^ directly
-      uint4 qsave[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int idx = tid + r * NT;
-        if (idx < ITEMS) {
-          const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
-          float bt[8], bl[8];
-          item_b(tl, cg, bt);
-          lds8f(sBl + 8 * cg, bl);
-          const uint32_t qw[4] = {rq[r].x, rq[r].y, rq[r].z, rq[r].w};
-          qsave[r].x = pack_bf16x2(bf16lo(qw[0]) * fexp2(bt[0]), bf16hi(qw[0]) * fexp2(bt[1]));
-          qsave[r].y = pack_bf16x2(bf16lo(qw[1]) * fexp2(bt[2]), bf16hi(qw[1]) * fexp2(bt[3]));
-          qsave[r].z = pack_bf16x2(bf16lo(qw[2]) * fexp2(bt[4]), bf16hi(qw[2]) * fexp2(bt[5]));
-          qsave[r].w = pack_bf16x2(bf16lo(qw[3]) * fexp2(bt[6]), bf16hi(qw[3]) * fexp2(bt[7]));
-          *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = rq[r];
-          *reinterpret_cast<uint4 *>(sK + tl * QS + 8 * cg) = rk[r];
-          *reinterpret_cast<uint4 *>(sKh + tl * QS + 8 * cg) = khat_direct(r, bt, bl);
-        }
-      }
-      lds_barrier();
-      // P^T fragment slots: tile ti = (j, i), lane l, element e  <->  t = 16i + l%16,
-      // s = 16j + 4(l/16) + e;  value sum_c q_tc k_sc 2^(b_tc - b_sc) for s <= t, else 0
-      constexpr int NSLOT = NPT * 256;
-      constexpr int NS = (NSLOT + NT - 1) / NT;
-      float pw[NS];
-#pragma unroll
-      for (int x = 0; x < NS; ++x) {
-        const int sl = tid + x * NT;
-        float acc = 0.f;
-        if (sl < NSLOT) {
-          const int ti = sl >> 8, ln = (sl >> 2) & 63, e = sl & 3;
-          int i = 0;
-          while ((i + 1) * (i + 2) / 2 <= ti) ++i;
-          const int j = ti - i * (i + 1) / 2;
-          const int t = 16 * i + (ln & 15), s_ = 16 * j + 4 * (ln >> 4) + e;
-          if (s_ <= t) {
-            for (int ch = 0; ch < dk; ++ch) {
-              const float qv = __uint_as_float((uint32_t)sQ[t * QS + ch] << 16);
-              const float kv = __uint_as_float((uint32_t)sK[s_ * QS + ch] << 16);
-              acc += qv * kv * fexp2(b_at(t, ch) - b_at(s_, ch));
-            }
-          }
-        }
-        pw[x] = acc;
-      }
-      load_chunk(true);
-      lds_barrier();
-#pragma unroll
-      for (int x = 0; x < NS; ++x) {
-        const int sl = tid + x * NT;
-        if (sl < NSLOT) sPT[sl] = (uint16_t)f2bf(pw[x]);
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int idx = tid + r * NT;
-        if (idx < ITEMS) {
-          const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
-          *reinterpret_cast<uint4 *>(sQ + tl * QS + 8 * cg) = qsave[r];
-        }
-      }
+    const int x = c + 1;
+    const bool live = x < c_end;
+    // interval 1: producers stage chunk x; consumers write o of chunk c
+    if (producer) {
+      if (live) produce1(x, true);
+    } else if (has_cols) {
+      outputs(c, S);
     }
     lds_barrier();
-
-    if (has_cols) {
-      uint4 vf[JP];
-      v_frags(vf);
-      uint4 sa[K32];   // S^T (bf16) as the A operand, K = channels
-#pragma unroll
-      for (int kb2 = 0; kb2 < K32; ++kb2) sa[kb2] = cat(pack4(S[2 * kb2]), pack4(S[2 * kb2 + 1]));
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const uint16_t *qrow = sQ + (16 * i + l16) * QS;
-        f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-        // O^T += S^T q~^T
-#pragma unroll
-        for (int kb2 = 0; kb2 < K32; ++kb2)
-          O = mfma32(sa[kb2], cat(lds2(qrow + 32 * kb2 + 4 * g4), lds2(qrow + 32 * kb2 + 16 + 4 * g4)), O);
-        // O^T += V^T P^T over the s-tiles j <= i
-#pragma unroll
-        for (int jp = 0; jp < JP; ++jp) {
-          const int j0 = 2 * jp, j1 = 2 * jp + 1;
-          if (j0 <= i) {
-            const uint2 pt0 = lds2(sPT + (i * (i + 1) / 2 + j0) * 256 + lane * 4);
-            const uint2 pt1 = (j1 <= i) ? lds2(sPT + (i * (i + 1) / 2 + j1) * 256 + lane * 4) : make_uint2(0, 0);
-            O = mfma32(vf[jp], cat(pt0, pt1), O);
-          }
-        }
-        const int p = c * M + 16 * i + l16;
-        const int n = n0 + 4 * g4;
-        if (p < T && n < dv) gstore8(ob + (int64_t)p * P.o_st + n, pack4(O));
-      }
-      state_update(S, vf, nullptr);
+    pw_next = live && chunk_pairwise(x);
+    // interval 2: producers transform chunk x; consumers update the state
+    if (has_rows && live) produce2(x, pw_next);
+    if (has_cols) state_update(c & 1, S, nullptr);
+    lds_barrier();
+    // interval 3: producers build the P^T tiles of chunk x
+    if (producer && live) {
+      if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
     }
     lds_barrier();
+    if (pw_next) {
+      if (has_rows) qtilde(tile(x & 1, 0), bt);
+      lds_barrier();
+    }
   }
 
   if (last_seg && P.s_final && has_cols) {
@@ -762,9 +817,9 @@ struct Plan {
   size_t off_flags, off_gam, off_agg, off_inc, bytes;
 };
 
-// Segmentation: enough workgroups for about two rounds of the workgroups that
-// fit on the chip at once (LDS-limited), but segments of at least 512 tokens
-// so that the published states stay small next to the streamed inputs.
+// Segmentation: as many workgroups as fit on the chip at once (LDS and
+// registers), but segments of at least 512 tokens so that the published
+// states stay small next to the streamed inputs.
 Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   Plan pl;
   pl.DP = pad32(dk > dv ? dk : dv);
@@ -774,14 +829,16 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   // workgroups resident per CU: LDS (160 KiB) and the register budget
   // (waves per SIMD, 4 SIMDs) both bound it
   int per_cu = (160 * 1024) / lds_bytes(pl.DP, M);
-  const int nw = pl.DP / 16 > 2 ? pl.DP / 16 : 2;
-  const int reg_cap = 4 * (M <= 32 ? Occ<32>::waves_per_simd : Occ<64>::waves_per_simd) / nw;
+  const int nw = 2 * (pl.DP / 16);
+  const int wps = (nw + 3) / 4 < 2 ? 2 : (nw + 3) / 4;   // as Occ<DP>
+  const int reg_cap = 4 * wps / nw;
   if (per_cu > reg_cap) per_cu = reg_cap;
   if (per_cu < 1) per_cu = 1;
-  // one wave of resident workgroups: every segment but the last of a scan
-  // reads its chunks twice, so more segments than that cost more than they hide
+  // at most one wave of resident workgroups: a workgroup beyond it waits for
+  // a whole one to finish, and every segment but the last of a scan reads
+  // its chunks twice, so more segments cost more than they hide
   const long want = (long)num_cu * per_cu;
-  long nseg = (want + pl.units - 1) / pl.units;
+  long nseg = want / pl.units;
   const int min_chunks = (512 + M - 1) / M;
   long max_seg = pl.nchunks / min_chunks;
   if (max_seg < 1) max_seg = 1;
@@ -824,7 +881,9 @@ hipError_t launch_m(const Params &p, int M, int grid, hipStream_t s) {
   switch (M) {
     case 16: return launch<DP, 16>(p, grid, s);
     case 32: return launch<DP, 32>(p, grid, s);
-    case 64: return launch<DP, 64>(p, grid, s);
+    case 64:
+      if constexpr (DP <= 96) return launch<DP, 64>(p, grid, s);   // 128 channels: LDS holds 32-token chunks
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -862,6 +921,7 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   p.cg_magic = (unsigned)((0x80000000ull + p.cgr - 1) / p.cgr);
   p.qk_span = (unsigned)(((int64_t)(a.T - 1) * a.qk_st + a.dk) * 2);
   p.v_span = (unsigned)(((int64_t)(a.T - 1) * a.v_st + a.dv) * 2);
+  p.o_span = (unsigned)(((int64_t)(a.T - 1) * a.o_st + a.dv) * 2);
   char *ws = static_cast<char *>(a.workspace);
   p.ticket = reinterpret_cast<int *>(ws);
   p.flags = reinterpret_cast<unsigned *>(ws + pl.off_flags);

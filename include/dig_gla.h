@@ -98,12 +98,13 @@ extern "C" {
  *                    needs dk and dv multiples of 8, 16-byte aligned q/k/v/
  *                    log_alpha/o pointers and strides that are multiples of 8
  *                    elements (o: 4), and one (batch, head) slice of q/k/
- *                    log_alpha or of v must span less than 2 GiB; the fp32
+ *                    log_alpha, v or o must span less than 2 GiB; the fp32
  *                    path takes any layout.
  *   gh, gw, dir      the token grid and the scan direction.
- *   chunk            tokens per chunk: 0 = automatic (64 for bf16, 16 for
- *                    fp32); else 16, 32 or 64 (bf16) or 16, 32 (fp32).  The
- *                    chunk size changes rounding only, never the result.
+ *   chunk            tokens per chunk: 0 = automatic (bf16: 64, or 32 when
+ *                    dk or dv exceeds 96; fp32: 16); else 16, 32 or 64
+ *                    (bf16; 64 only for dk, dv <= 96) or 16, 32 (fp32).
+ *                    The chunk size changes rounding only, never the result.
  *   s0               nullable; [B, H, dk, dv] contiguous fp32 initial state.
  *   o                [B, T, H, dv] written in SCAN order (row p is scan
  *                    position p), strides (o_sb, o_st, o_sh).  Must not

@@ -54,7 +54,7 @@ def _gla(L, **kw):
     dict(q=None), dict(o=None), dict(B=0), dict(T=-1), dict(dk=0), dict(dv=136),
     dict(gh=7), dict(dir=4), dict(dtype=7), dict(chunk=48), dict(dk=12, dv=12),
     dict(q=18), dict(qk=(4096 * 64, 60, 8)), dict(o=16), dict(dtype=0, chunk=64),
-    dict(qk=(-8, 64, 8)),
+    dict(qk=(-8, 64, 8)), dict(dk=128, dv=128, chunk=64),
 ])
 def test_gla_rejects_bad_arguments(L, bad):
     rc = _gla(L, **bad)
@@ -65,6 +65,9 @@ def test_gla_rejects_bad_arguments(L, bad):
 def test_workspace_size_rejects_bad_sizes(L):
     assert L.gla_fwd_workspace_size(1, 1, 64, 8, 12, 12, 0) == ctypes.c_size_t(-1).value
     assert L.gla_fwd_workspace_size(0, 1, 64, 8, 16, 16, 0) == 0
+    # automatic chunk for 128 channels is 32 (64-token chunks are limited to 96 channels)
+    assert L.gla_fwd_workspace_size(1, 1, 64, 8, 128, 128, 0) != ctypes.c_size_t(-1).value
+    assert L.gla_fwd_workspace_size(1, 1, 64, 8, 128, 128, 64) == ctypes.c_size_t(-1).value
 
 
 def _conv(L, **kw):
