@@ -480,7 +480,7 @@ gla_fwd_bf16_kernel(Params P) {
     }
   };
   // P3(x), fast chunks: causal P^T tiles (j, i), j <= i, from q~ and k~,
-  // spread over the producer waves.
+  // spread over all waves (the consumers have nothing else to do then).
   auto produce3_fast = [&](int x) {
     const int par = x & 1;
     const uint16_t *tq = tile(par, 0), *tk = tile(par, 1);
@@ -490,7 +490,7 @@ gla_fwd_bf16_kernel(Params P) {
 #pragma unroll
       for (int j = 0; j <= i; ++j) {
         const int ti = i * (i + 1) / 2 + j;
-        if (ti % DT == pw) {
+        if (ti % (2 * DT) == wave) {
           const uint16_t *krow = tk + (16 * j + l16) * QS;
           const uint16_t *qrow = tq + (16 * i + l16) * QS;
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -509,12 +509,12 @@ gla_fwd_bf16_kernel(Params P) {
   };
   // P3(x), pairwise chunks: P^T slot (tile ti = (j, i), lane l, element e) is
   // t = 16i + l%16, s = 16j + 4(l/16) + e; value sum_c q_tc k_sc 2^(b_tc - b_sc)
-  // over all key channels for s <= t, else 0.  Slots spread over the producers.
+  // over all key channels for s <= t, else 0.  Slots spread over all threads.
   auto produce3_pairwise = [&](int x) {
     const int par = x & 1;
     const uint16_t *tq = tile(par, 0), *tk = tile(par, 1);
     uint16_t *pt = ptile(par);
-    for (int sl = ptid; sl < NPT * 256; sl += NTP) {
+    for (int sl = tid; sl < NPT * 256; sl += NT) {
       const int ti = sl >> 8, ln = (sl >> 2) & 63, e = sl & 3;
       int i = 0;
       while ((i + 1) * (i + 2) / 2 <= ti) ++i;
@@ -734,10 +734,11 @@ gla_fwd_bf16_kernel(Params P) {
   for (int r = 0; r < DT; ++r) S[r] = Sin[r];
 
   // ========================= pass 2: outputs ==================================
-  // Three barrier intervals per chunk c: producers P1/P2/P3 of chunk c+1,
-  // consumers the outputs of chunk c, then its state update.  A pairwise
+  // Three barrier intervals per chunk c: producers P1/P2 of chunk c+1 while
+  // the consumers write o of chunk c, then update its state; all waves build
+  // the P^T tiles of chunk c+1 in the third.  A pairwise
   // chunk c+1 adds one interval (its q~ may be written only after every
-  // producer has read its raw q).
+  // thread has read its raw q).
   drain_vmem();
   fill_tok(c_begin);
   fill_tok(c_begin + 1);
@@ -749,9 +750,7 @@ gla_fwd_bf16_kernel(Params P) {
   bool pw_next = chunk_pairwise(c_begin);
   if (has_rows) produce2(c_begin, pw_next);
   lds_barrier();
-  if (producer) {
-    if (!pw_next) produce3_fast(c_begin); else produce3_pairwise(c_begin);
-  }
+  if (!pw_next) produce3_fast(c_begin); else produce3_pairwise(c_begin);
   lds_barrier();
   if (pw_next) {
     if (has_rows) qtilde(tile(c_begin & 1, 0), bt);
@@ -772,8 +771,8 @@ gla_fwd_bf16_kernel(Params P) {
     if (has_rows && live) produce2(x, pw_next);
     if (has_cols) state_update(c & 1, S, nullptr);
     lds_barrier();
-    // interval 3: producers build the P^T tiles of chunk x
-    if (producer && live) {
+    // interval 3: all waves build the P^T tiles of chunk x
+    if (live) {
       if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
     }
     lds_barrier();
