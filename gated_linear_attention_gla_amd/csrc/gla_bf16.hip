@@ -161,6 +161,7 @@ struct Params {
   int64_t qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
   int B, T, H, dk, dv, gh, gw, dir, nchunks, units;
   int seg_chunks, nseg, per_xcd;   // chunks per segment, segments per scan, scans per XCD
+  int split_L, split_K;            // two-segment split (split_K > 0): see the kernel
   int cgr;                         // 16-byte channel groups holding data: ceil(max(dk, dv) / 8)
   unsigned cg_magic;               // ceil(2^31 / cgr): idx / cgr == umulhi(2 idx, cg_magic) for idx < 2^20
   unsigned qk_span, v_span, o_span;   // bytes addressable in one (batch, head) slice of q/k/g, v, o
@@ -261,10 +262,29 @@ gla_fwd_bf16_kernel(Params P) {
   const int unit = xcd * P.per_xcd + kslot / P.nseg;
   const int seg = kslot % P.nseg;
   if (unit >= P.units) return;
-  const int c_begin = seg * P.seg_chunks;
-  if (c_begin >= P.nchunks) return;
-  const int c_end = min(c_begin + P.seg_chunks, P.nchunks);
-  const bool last_seg = (c_end == P.nchunks);
+  // Chunk ranges.  Uniform segments: segment g aggregates and then outputs
+  // its own chunks.  Two-segment split (split_K > 0): segment 0 outputs
+  // chunks [0, L+K) straight from s0 and publishes the state entering chunk L
+  // on the way; segment 1 meanwhile aggregates chunks [L, L+K), folds that
+  // onto the published state and outputs [L+K, N), so neither waits idle.
+  int out_begin, out_end, agg_begin = 0, agg_end = 0, publish_at = -1;
+  bool do_pass1;
+  if (P.split_K > 0) {
+    if (seg == 0) {
+      out_begin = 0; out_end = P.split_L + P.split_K; do_pass1 = false; publish_at = P.split_L;
+    } else {
+      agg_begin = P.split_L; agg_end = P.split_L + P.split_K;
+      out_begin = agg_end; out_end = P.nchunks; do_pass1 = true;
+    }
+  } else {
+    out_begin = seg * P.seg_chunks;
+    if (out_begin >= P.nchunks) return;
+    out_end = min(out_begin + P.seg_chunks, P.nchunks);
+    do_pass1 = out_end < P.nchunks;
+    agg_begin = out_begin; agg_end = out_end;
+  }
+  const bool last_seg = (out_end == P.nchunks);
+  int c_begin = agg_begin, c_end = agg_end;   // the range of the pass being run
 
   const int b = unit / P.H, h = unit - b * P.H;
   const int T = P.T, dk = P.dk, dv = P.dv;
@@ -619,7 +639,7 @@ gla_fwd_bf16_kernel(Params P) {
   // ======================= pass 1: segment aggregate =========================
   // producers stage chunk c+1 (k, v, gates -> k^, e^{b_last}) while the
   // consumers fold chunk c into the aggregate.
-  if (!last_seg) {
+  if (do_pass1) {
     fill_tok(c_begin);
     fill_tok(c_begin + 1);
     __syncthreads();
@@ -650,7 +670,7 @@ gla_fwd_bf16_kernel(Params P) {
       }
       lds_barrier();
     }
-    if (has_cols) {
+    if (has_cols && P.split_K == 0) {
       float *blk = P.agg + (slot0 + seg) * P.blk_floats;
 #pragma unroll
       for (int r = 0; r < DT; ++r)
@@ -663,7 +683,7 @@ gla_fwd_bf16_kernel(Params P) {
     }
     drain_vmem();
     __syncthreads();
-    if (tid == 0)
+    if (tid == 0 && P.split_K == 0)
       __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -714,7 +734,7 @@ gla_fwd_bf16_kernel(Params P) {
       }
     }
   }
-  if (!last_seg) {
+  if (do_pass1 && P.split_K == 0) {
     // inclusive state P_g = Gam_g * S_in + A_g
     if (has_cols) {
       float *blk = P.inc + (slot0 + seg) * P.blk_floats;
@@ -730,8 +750,16 @@ gla_fwd_bf16_kernel(Params P) {
     if (tid == 0)
       __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (P.split_K > 0 && do_pass1) {
+    // split segment 1: the state entering its outputs is Gam * S(L) + A
 #pragma unroll
-  for (int r = 0; r < DT; ++r) S[r] = Sin[r];
+    for (int r = 0; r < DT; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[r][e] = fmaf(gp[r][e], Sin[r][e], S[r][e]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < DT; ++r) S[r] = Sin[r];
+  }
 
   // ========================= pass 2: outputs ==================================
   // Three barrier intervals per chunk c: producers P1/P2 of chunk c+1 while
@@ -740,6 +768,8 @@ gla_fwd_bf16_kernel(Params P) {
   // chunk c+1 adds one interval (its q~ may be written only after every
   // thread has read its raw q).
   drain_vmem();
+  c_begin = out_begin;
+  c_end = out_end;
   fill_tok(c_begin);
   fill_tok(c_begin + 1);
   __syncthreads();
@@ -769,13 +799,24 @@ gla_fwd_bf16_kernel(Params P) {
     pw_next = live && chunk_pairwise(x);
     // interval 2: producers transform chunk x; consumers update the state
     if (has_rows && live) produce2(x, pw_next);
-    if (has_cols) state_update(c & 1, S, nullptr);
+    if (has_cols) {
+      state_update(c & 1, S, nullptr);
+      if (c + 1 == publish_at) {   // split segment 0: the state entering chunk L
+        float *blk = P.inc + slot0 * P.blk_floats;
+#pragma unroll
+        for (int r = 0; r < DT; ++r)
+          if (r < DTr) st_coherent(blk + blk_at(r), make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
+        drain_vmem();
+      }
+    }
     lds_barrier();
     // interval 3: all waves build the P^T tiles of chunk x
     if (live) {
       if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
     }
     lds_barrier();
+    if (c + 1 == publish_at && tid == 0)
+      __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (pw_next) {
       if (has_rows) qtilde(tile(x & 1, 0), bt);
       lds_barrier();
@@ -811,8 +852,13 @@ int lds_bytes(int DP, int M) {
   }
 }
 
+// aggregate chunks of segment 1 in the two-segment split, as a fraction of
+// the scan (measured best at 64-token chunks; an aggregate chunk costs about
+// 0.45 of an output chunk)
+constexpr float kSplitFrac = 0.44f;
+
 struct Plan {
-  int DP, M, nchunks, units, nseg, seg_chunks, per_xcd, grid, blk_floats;
+  int DP, M, nchunks, units, nseg, seg_chunks, per_xcd, grid, blk_floats, split_L, split_K;
   size_t off_flags, off_gam, off_agg, off_inc, bytes;
 };
 
@@ -845,6 +891,14 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   if (nseg < 1) nseg = 1;
   pl.seg_chunks = (int)((pl.nchunks + nseg - 1) / nseg);
   pl.nseg = (pl.nchunks + pl.seg_chunks - 1) / pl.seg_chunks;
+  // Two segments: pipelined split.  With p1, p2 the times of an aggregate and
+  // an output chunk, segment 1 aggregates K chunks while segment 0 outputs L,
+  // then each outputs N - L - K: balanced at K = N p2 / (2 p2 + p1), L = N - 2K.
+  pl.split_L = pl.split_K = 0;
+  if (pl.nseg == 2) {
+    const int K = (int)(pl.nchunks * kSplitFrac + 0.5f), L = pl.nchunks - 2 * K;
+    if (K >= 1 && L >= 1) { pl.split_K = K; pl.split_L = L; }
+  }
   pl.per_xcd = (pl.units + 7) / 8;
   pl.grid = 8 * pl.per_xcd * pl.nseg;
   const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;
@@ -913,6 +967,8 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   p.nchunks = pl.nchunks;
   p.units = pl.units;
   p.seg_chunks = pl.seg_chunks;
+  p.split_L = pl.split_L;
+  p.split_K = pl.split_K;
   p.nseg = pl.nseg;
   p.per_xcd = pl.per_xcd;
   p.blk_floats = pl.blk_floats;
