@@ -273,6 +273,21 @@ def main(argv=None) -> int:
             ev.append((e0, e1))
         dg.srem_dwconv(bf["o"].view(B, T, C), x["w"], grid, direction, out=bf["y"])
 
+    # device-copy probe: what a plain read+write stream reaches on this GPU
+    # (256 MiB read + 256 MiB written, runtime blit kernel, best of 5)
+    csrc = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    copy_ms = []
+    for _ in range(6):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        cdst.copy_(csrc)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms.append(c0.elapsed_time(c1))
+    copy_gbs = 2 * COPY_PROBE_BYTES / (min(copy_ms[1:]) * 1e-3) / 1e9
+    del csrc, cdst
+
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -301,7 +316,8 @@ def main(argv=None) -> int:
     achieved = abytes / (gla_avg_ms * 1e-3) / 1e9
     traffic = traffic_record(cfg.key)
     log(f"[bench] step {ms_step * 1e3:.1f} us, gla_fwd avg {gla_avg_ms * 1e3:.1f} us "
-        f"(p10 {gla_sorted[len(gla_sorted) // 10] * 1e3:.1f}, p90 {gla_sorted[(9 * len(gla_sorted)) // 10] * 1e3:.1f}), "
+        f"(median {gla_sorted[len(gla_sorted) // 2] * 1e3:.1f}, p10 {gla_sorted[len(gla_sorted) // 10] * 1e3:.1f}, "
+        f"p90 {gla_sorted[(9 * len(gla_sorted)) // 10] * 1e3:.1f}), copy probe {copy_gbs:.0f} GB/s, "
         f"{achieved:.0f} GB/s, wall {wall:.3f} s")
 
     cpu = None
@@ -331,9 +347,11 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gla_fwd_bf16_kernel", "alg_bytes_per_launch": abytes,
-                     "avg_launch_us": gla_avg_ms * 1e3},
+                     "avg_launch_us": gla_avg_ms * 1e3,
+                     "copy_probe_gbs": copy_gbs, "frac_of_copy_probe": achieved / copy_gbs},
         "gla_fwd": {"tokens_per_s": tokens / (gla_avg_ms * 1e-3), "tflops_alg": aflops / (gla_avg_ms * 1e-3) / 1e12,
                     "mfma_frac": aflops / (gla_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "median_us": gla_sorted[len(gla_sorted) // 2] * 1e3,
                     "p10_us": gla_sorted[len(gla_sorted) // 10] * 1e3,
                     "p90_us": gla_sorted[(9 * len(gla_sorted)) // 10] * 1e3},
         "cpu_baseline": cpu,

@@ -194,6 +194,27 @@ def _sampled(orc, key, directions, units):
             assert_state_close(sf[b:b + 1, h:h + 1], rs, TOL_BF16, f"{key} s[{d}] unit {(b, h)}")
 
 
+@pytest.mark.parametrize("shape", [
+    (6, 16, 32, 32, 64, 64),    # 96 scans: two segments, the pipelined split (64-token chunks)
+    (6, 16, 32, 32, 64, 32),    # the same with 32-token chunks
+    (1, 8, 64, 64, 64, 64),     # 8 scans: eight segments, decoupled look-back
+], ids=lambda s: "x".join(map(str, s)))
+def test_bf16_segmented_scans_with_s0(orc, shape):
+    """Scans split over several workgroups (two-segment split and look-back
+    chains) against the oracle, with an initial state."""
+    B, H, gh, gw, d, chunk = shape
+    T = gh * gw
+    x = gen.gla_inputs(B, T, H, d, d, seed=33 + B, qkv_scale=1 / 8)
+    s0 = torch.randn(B, H, d, d, generator=torch.Generator().manual_seed(5)) * 0.5
+    units = [(0, 0), (B // 2, H // 2), (B - 1, H - 1)] if B * H > 8 else [(0, h) for h in range(H)]
+    for direction in ("l2r", "b2t"):
+        o, sf = run_gla(x, (gh, gw), direction, chunk=chunk, s0=s0)
+        for (b, h), (ro, rs) in zip(units, oracle_gla(orc, x, (gh, gw), direction, s0=s0.double().numpy(),
+                                                        units=units)):
+            assert_o_close(o[b:b + 1, :, h:h + 1], ro, TOL_BF16, f"o[{direction}] unit {(b, h)}")
+            assert_state_close(sf[b:b + 1, h:h + 1], rs, TOL_BF16, f"s[{direction}] unit {(b, h)}")
+
+
 def test_c2_full_size_sampled(orc):
     _sampled(orc, "C2", DIRS, [(0, 0), (3, 7), (7, 15)])
 
