@@ -164,6 +164,7 @@ struct Params {
   int split_L, split_K;            // two-segment split (split_K > 0): see the kernel
   int cgr;                         // 16-byte channel groups holding data: ceil(max(dk, dv) / 8)
   unsigned cg_magic;               // ceil(2^31 / cgr): idx / cgr == umulhi(2 idx, cg_magic) for idx < 2^20
+  unsigned gh_magic;               // ceil(2^31 / gh): scan-order decode by a scalar multiply (fill_tok)
   unsigned qk_span, v_span, o_span;   // bytes addressable in one (batch, head) slice of q/k/g, v, o
   int blk_floats;                  // floats of one published state block
   int *ticket;                     // launch-order ticket counter (reset by the last taker)
@@ -242,7 +243,8 @@ gla_fwd_bf16_kernel(Params P) {
   int *sVote = reinterpret_cast<int *>(smem + Lds<DP, M>::oVote);
   int *sMisc = reinterpret_cast<int *>(smem + Lds<DP, M>::oMisc);   // [1] ticket [2] look-back
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: from a scalar register, role branches are scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
   const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);   // transpose-read addressing
   const bool producer = wave >= DT;
@@ -335,7 +337,16 @@ gla_fwd_bf16_kernel(Params P) {
       const int p = x * M + ptid;
       unsigned oqk = kOOB, ov = kOOB;
       if (x < c_end && p < T) {
-        const unsigned n = (unsigned)scan_to_canon(P.dir, P.gh, P.gw, T, p);
+        // scan position -> canonical token (the four orders of scan_to_canon),
+        // the quotient by gh from a magic multiplier held in scalar registers
+        const unsigned s_ = (P.dir & 1) ? (unsigned)(T - 1 - p) : (unsigned)p;
+        unsigned n = s_;
+        if (P.dir >= 2) {
+          unsigned col = __umulhi(2u * s_, P.gh_magic);   // floor(s/gh) or one more
+          int row = (int)(s_ - col * (unsigned)P.gh);
+          if (row < 0) { --col; row += P.gh; }
+          n = (unsigned)row * (unsigned)P.gw + col;
+        }
         oqk = n * (unsigned)P.qk_st * 2u;
         ov = n * (unsigned)P.v_st * 2u;
       }
@@ -378,11 +389,11 @@ gla_fwd_bf16_kernel(Params P) {
       const int idx = ptid + r * NTP;
       if (idx < ITEMS) {
         const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
-        const int off = tl * QS + 8 * cg;
-        if (with_q) *reinterpret_cast<uint4 *>(tq + off) = rq[r];
-        *reinterpret_cast<uint4 *>(tk + off) = rk[r];
-        *reinterpret_cast<uint4 *>(tg + off) = rg[r];
-        *reinterpret_cast<uint4 *>(tv + off) = rv[r];
+        const unsigned off = (unsigned)(tl * QS + 8 * cg) * 2u;   // bytes, 32-bit LDS offset
+        if (with_q) *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tq) + off) = rq[r];
+        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tk) + off) = rk[r];
+        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tg) + off) = rg[r];
+        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tv) + off) = rv[r];
         if (with_q) {
           const uint32_t gw_[4] = {rg[r].x, rg[r].y, rg[r].z, rg[r].w};
 #pragma unroll
@@ -654,21 +665,31 @@ gla_fwd_bf16_kernel(Params P) {
       khat_direct(tile(c_begin & 1, 1), tile(c_begin & 1, 2), bt, bl);
     }
     lds_barrier();
-    for (int c = c_begin; c < c_end; ++c) {
-      const int x = c + 1;
-      if (producer) {
+    // One loop per role with the same barriers: the registers each role
+    // carries through its loop (in-flight loads; state) are not held by the
+    // other role's code.
+    if (producer) {
+      for (int c = c_begin; c < c_end; ++c) {
+        const int x = c + 1;
         if (x < c_end) produce1(x, false);
-      } else if (has_cols) {
-        state_update(c & 1, S, gp);
+        lds_barrier();
+        if (has_rows && x < c_end) {
+          float gmo[4], bl[4];
+          scan(tile(x & 1, 2), bt);
+          chunk_total(bt, gmo, bl, x & 1);
+          khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
+        }
+        lds_barrier();
       }
-      lds_barrier();
-      if (has_rows && x < c_end) {
-        float gmo[4], bl[4];
-        scan(tile(x & 1, 2), bt);
-        chunk_total(bt, gmo, bl, x & 1);
-        khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
+      // producers hold no state: its carried value ends here
+#pragma unroll
+      for (int r = 0; r < DT; ++r) { S[r] = f32x4_t{0.f, 0.f, 0.f, 0.f}; gp[r] = f32x4_t{1.f, 1.f, 1.f, 1.f}; }
+    } else {
+      for (int c = c_begin; c < c_end; ++c) {
+        if (has_cols) state_update(c & 1, S, gp);
+        lds_barrier();
+        lds_barrier();
       }
-      lds_barrier();
     }
     if (has_cols && P.split_K == 0) {
       float *blk = P.agg + (slot0 + seg) * P.blk_floats;
@@ -786,51 +807,66 @@ gla_fwd_bf16_kernel(Params P) {
     if (has_rows) qtilde(tile(c_begin & 1, 0), bt);
     lds_barrier();
   }
-  for (int c = c_begin; c < c_end; ++c) {
-    const int x = c + 1;
-    const bool live = x < c_end;
-    // interval 1: producers stage chunk x; consumers write o of chunk c
-    if (producer) {
+  if (producer) {
+    for (int c = c_begin; c < c_end; ++c) {
+      const int x = c + 1;
+      const bool live = x < c_end;
+      // interval 1: stage chunk x (the consumers write o of chunk c)
       if (live) produce1(x, true);
-    } else if (has_cols) {
-      outputs(c, S);
-    }
-    lds_barrier();
-    pw_next = live && chunk_pairwise(x);
-    // interval 2: producers transform chunk x; consumers update the state
-    if (has_rows && live) produce2(x, pw_next);
-    if (has_cols) {
-      state_update(c & 1, S, nullptr);
-      if (c + 1 == publish_at) {   // split segment 0: the state entering chunk L
-        float *blk = P.inc + slot0 * P.blk_floats;
-#pragma unroll
-        for (int r = 0; r < DT; ++r)
-          if (r < DTr) st_coherent(blk + blk_at(r), make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
-        drain_vmem();
-      }
-    }
-    lds_barrier();
-    // interval 3: all waves build the P^T tiles of chunk x
-    if (live) {
-      if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
-    }
-    lds_barrier();
-    if (c + 1 == publish_at && tid == 0)
-      __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (pw_next) {
-      if (has_rows) qtilde(tile(x & 1, 0), bt);
       lds_barrier();
-    }
-  }
-
-  if (last_seg && P.s_final && has_cols) {
-#pragma unroll
-    for (int r = 0; r < DT; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ch = 16 * r + 4 * g4 + e, n = n0 + l16;
-        if (ch < dk && n < dv) P.s_final[((int64_t)unit * dk + ch) * dv + n] = S[r][e];
+      pw_next = live && chunk_pairwise(x);
+      // interval 2: transform chunk x (the consumers update the state)
+      if (has_rows && live) produce2(x, pw_next);
+      lds_barrier();
+      // interval 3: all waves build the P^T tiles of chunk x
+      if (live) {
+        if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
       }
+      lds_barrier();
+      if (pw_next) {
+        if (has_rows) qtilde(tile(x & 1, 0), bt);
+        lds_barrier();
+      }
+    }
+  } else {
+    for (int c = c_begin; c < c_end; ++c) {
+      const int x = c + 1;
+      const bool live = x < c_end;
+      // interval 1: o of chunk c
+      if (has_cols) outputs(c, S);
+      lds_barrier();
+      pw_next = live && chunk_pairwise(x);
+      // interval 2: the state after chunk c
+      if (has_cols) {
+        state_update(c & 1, S, nullptr);
+        if (c + 1 == publish_at) {   // split segment 0: the state entering chunk L
+          float *blk = P.inc + slot0 * P.blk_floats;
+#pragma unroll
+          for (int r = 0; r < DT; ++r)
+            if (r < DTr) st_coherent(blk + blk_at(r), make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
+          drain_vmem();
+        }
+      }
+      lds_barrier();
+      // interval 3: P^T tiles of chunk x
+      if (live) {
+        if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
+      }
+      lds_barrier();
+      if (c + 1 == publish_at && tid == 0)
+        __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (pw_next) lds_barrier();
+    }
+
+    if (last_seg && P.s_final && has_cols) {
+#pragma unroll
+      for (int r = 0; r < DT; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ch = 16 * r + 4 * g4 + e, n = n0 + l16;
+          if (ch < dk && n < dv) P.s_final[((int64_t)unit * dk + ch) * dv + n] = S[r][e];
+        }
+    }
   }
 }
 
@@ -974,6 +1010,9 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   p.blk_floats = pl.blk_floats;
   p.cgr = ((a.dk > a.dv ? a.dk : a.dv) + 7) / 8;
   p.cg_magic = (unsigned)((0x80000000ull + p.cgr - 1) / p.cgr);
+  // umulhi(2s, ceil(2^31/gh)) = floor(s/gh + s*e/(gh*2^31)) with e < gh, so it
+  // exceeds floor(s/gh) by at most one for every s < 2^31: one correction
+  p.gh_magic = (unsigned)((0x80000000ull + (unsigned)a.gh - 1) / (unsigned)a.gh);
   p.qk_span = (unsigned)(((int64_t)(a.T - 1) * a.qk_st + a.dk) * 2);
   p.v_span = (unsigned)(((int64_t)(a.T - 1) * a.v_st + a.dv) * 2);
   p.o_span = (unsigned)(((int64_t)(a.T - 1) * a.o_st + a.dv) * 2);
