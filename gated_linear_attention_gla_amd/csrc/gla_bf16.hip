@@ -109,6 +109,9 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, unsigned off)
 __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, unsigned off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, unsigned off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)off, 0, 0);
+}
 __device__ __forceinline__ uint4 lds4(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane j
 // receives element (j % 4) of the 8-byte read addressed by lane 4e + j/4,
@@ -207,7 +210,8 @@ struct Lds {
   static constexpr int oGam = oB32 + M * DP * 4;       // [2][DP] e^{b_last}
   static constexpr int oTok = oGam + 2 * DP * 4;       // [2][2][M] token byte offsets (chunk parity; q/k/g, v)
   static constexpr int oVote = oTok + 4 * M * 4;       // [2][16] per producer wave: chunk needs the pairwise path
-  static constexpr int oMisc = oVote + 2 * 16 * 4;     // ticket, look-back result
+  static constexpr int oStg = oVote + 2 * 16 * 4;      // [M][QS] bf16 o of the chunk being written
+  static constexpr int oMisc = oStg + TILE;            // ticket, look-back result
   static constexpr int bytes = oMisc + 64;
 };
 
@@ -599,6 +603,7 @@ gla_fwd_bf16_kernel(Params P) {
   };
   // o of chunk c for this wave's columns: O^T = S^T q~^T + V^T P^T (S: the
   // state entering the chunk), stored 8 bytes per lane.
+  uint16_t *stg = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oStg);
   auto outputs = [&](int c, const f32x4_t *S) {
     const int par = c & 1;
     const uint16_t *tq = tile(par, 0), *pt = ptile(par);
@@ -623,9 +628,21 @@ gla_fwd_bf16_kernel(Params P) {
           O = mfma32(vf[jp], cat(pt0, pt1), O);
         }
       }
-      const int p = c * M + 16 * i + l16;
-      const int n = n0 + 4 * g4;
-      bstore8(ro_, (p < T && n < dv) ? ((unsigned)p * (unsigned)P.o_st + (unsigned)n) * 2u : kOOB, pack4(O));
+      *reinterpret_cast<uint2 *>(stg + (16 * i + l16) * QS + n0 + 4 * g4) = pack4(O);
+    }
+  };
+  // o of chunk c from the staging tile to memory: whole token rows, 16 bytes
+  // per lane (a 64-lane store covers a few complete rows instead of 16-column
+  // slices of many)
+  auto store_stage = [&](int c) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = tid + r * NTP;
+      const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
+      const int p = c * M + tl;
+      const bool ok = idx < ITEMS && 8 * cg < dv && p < T;
+      const uint4 w = *reinterpret_cast<const uint4 *>(stg + (ok ? tl * QS + 8 * cg : 0));
+      bstore16(ro_, ok ? ((unsigned)p * (unsigned)P.o_st + 8u * cg) * 2u : kOOB, w);
     }
   };
   // Initial state s0 for this wave's tiles (0 when absent).
@@ -836,7 +853,8 @@ gla_fwd_bf16_kernel(Params P) {
       if (has_cols) outputs(c, S);
       lds_barrier();
       pw_next = live && chunk_pairwise(x);
-      // interval 2: the state after chunk c
+      // interval 2: o of chunk c to memory, the state after chunk c
+      store_stage(c);
       if (has_cols) {
         state_update(c & 1, S, nullptr);
         if (c + 1 == publish_at) {   // split segment 0: the state entering chunk L
