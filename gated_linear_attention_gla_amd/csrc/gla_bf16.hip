@@ -78,6 +78,12 @@ __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+// A 16-wide K block on the 32-wide instruction, upper half zero.  (Kept on
+// one MFMA shape: a 16x16x16 result feeding a 16x16x32 accumulator in
+// another register was issued without the wait states it needs.)
+__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
+  return mfma32(make_uint4(a.x, a.y, 0u, 0u), make_uint4(b.x, b.y, 0u, 0u), c);
+}
 __device__ __forceinline__ uint2 pack4(f32x4_t x) {
   return make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
 }
@@ -197,7 +203,7 @@ struct Lds {
   // 16 rows, 8 or 16 bytes each) are bank-conflict free when the stride is
   // 4 * odd dwords; the transposing reads (4 rows x 32 bytes) need the four
   // rows on disjoint 8-bank groups.  DP + 8 satisfies both for 64 and 96
-  // channels, DP + 24 for 32 and 128.
+  // channels, DP + 24 for 32, 80 and 128.
   static constexpr int QS = (DP == 64 || DP == 96) ? DP + 8 : DP + 24;
   static constexpr int MT = M / 16;
   static constexpr int NPT = MT * (MT + 1) / 2;        // causal 16x16 tiles of P^T
@@ -228,10 +234,11 @@ gla_fwd_bf16_kernel(Params P) {
   constexpr int DT = DP / 16;                // channel tiles = consumer waves = producer waves
   constexpr int MT = M / 16;                 // token tiles per chunk
   constexpr int K32 = DP / 32;               // 32-wide channel blocks
+  constexpr bool KH = (DP % 32) != 0;        // and a 16-wide one after them (80 channels)
   constexpr int JP = (MT + 1) / 2;           // 32-token K blocks
   constexpr int R = (M * (DP / 8) + NTP - 1) / NTP;   // max 16-byte items per producer thread per tensor
   constexpr int QS = Lds<DP, M>::QS, NPT = Lds<DP, M>::NPT, TILE = Lds<DP, M>::TILE;
-  static_assert(DP % 32 == 0 && DT <= 16, "channel tiling");
+  static_assert(DP % 16 == 0 && DT <= 16, "channel tiling");
   static_assert(Lds<DP, M>::bytes <= 160 * 1024, "LDS plan exceeds 160 KiB");
   const int CG = P.cgr;                      // 16-byte channel groups carrying data (the rest stay 0)
   const int ITEMS = M * CG;
@@ -532,6 +539,7 @@ gla_fwd_bf16_kernel(Params P) {
 #pragma unroll
           for (int kb2 = 0; kb2 < K32; ++kb2)
             acc = mfma32(lds4(krow + 32 * kb2 + 8 * g4), lds4(qrow + 32 * kb2 + 8 * g4), acc);
+          if (KH) acc = mfma16(lds2(krow + 32 * K32 + 4 * g4), lds2(qrow + 32 * K32 + 4 * g4), acc);
           if (j == i) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -619,6 +627,7 @@ gla_fwd_bf16_kernel(Params P) {
 #pragma unroll
       for (int kb2 = 0; kb2 < K32; ++kb2)
         O = mfma32(sa[kb2], cat(lds2(qrow + 32 * kb2 + 4 * g4), lds2(qrow + 32 * kb2 + 16 + 4 * g4)), O);
+      if (KH) O = mfma16(pack4(S[2 * K32]), lds2(qrow + 32 * K32 + 4 * g4), O);
 #pragma unroll
       for (int jp = 0; jp < JP; ++jp) {
         const int j0 = 2 * jp, j1 = 2 * jp + 1;
@@ -890,7 +899,8 @@ gla_fwd_bf16_kernel(Params P) {
 
 // ------------------------------ host side -----------------------------------
 
-int pad32(int d) { return ((d + 31) / 32) * 32; }
+// channel padding of a tile: 32, 64, 80, 96 or 128
+int pad_dp(int d) { return d <= 64 ? ((d + 31) / 32) * 32 : d <= 80 ? 80 : d <= 96 ? 96 : 128; }
 
 int lds_bytes(int DP, int M) {
   switch (DP * 1000 + M) {
@@ -899,6 +909,7 @@ int lds_bytes(int DP, int M) {
     return Lds<D, MM>::bytes;
     DIG_LDS_CASE(32, 16) DIG_LDS_CASE(32, 32) DIG_LDS_CASE(32, 64)
     DIG_LDS_CASE(64, 16) DIG_LDS_CASE(64, 32) DIG_LDS_CASE(64, 64)
+    DIG_LDS_CASE(80, 16) DIG_LDS_CASE(80, 32) DIG_LDS_CASE(80, 64)
     DIG_LDS_CASE(96, 16) DIG_LDS_CASE(96, 32) DIG_LDS_CASE(96, 64)
     DIG_LDS_CASE(128, 16) DIG_LDS_CASE(128, 32) DIG_LDS_CASE(128, 64)
 #undef DIG_LDS_CASE
@@ -909,7 +920,7 @@ int lds_bytes(int DP, int M) {
 // aggregate chunks of segment 1 in the two-segment split, as a fraction of
 // the scan (measured best at 64-token chunks; an aggregate chunk costs about
 // 0.45 of an output chunk)
-constexpr float kSplitFrac = 0.44f;
+constexpr float kSplitFrac = 0.40f;
 
 struct Plan {
   int DP, M, nchunks, units, nseg, seg_chunks, per_xcd, grid, blk_floats, split_L, split_K;
@@ -921,7 +932,7 @@ struct Plan {
 // states stay small next to the streamed inputs.
 Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   Plan pl;
-  pl.DP = pad32(dk > dv ? dk : dv);
+  pl.DP = pad_dp(dk > dv ? dk : dv);
   pl.M = M;
   pl.nchunks = (T + M - 1) / M;
   pl.units = B * H;
@@ -1044,6 +1055,7 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   switch (pl.DP) {
     case 32: return launch_m<32>(p, a.chunk, pl.grid, s);
     case 64: return launch_m<64>(p, a.chunk, pl.grid, s);
+    case 80: return launch_m<80>(p, a.chunk, pl.grid, s);
     case 96: return launch_m<96>(p, a.chunk, pl.grid, s);
     case 128: return launch_m<128>(p, a.chunk, pl.grid, s);
     default: return hipErrorInvalidValue;

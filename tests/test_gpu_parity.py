@@ -89,6 +89,8 @@ BF16_SHAPES = [
     (2, 2, 8, 12, 16, 16, 16),
     (1, 3, 12, 11, 128, 128, 32),   # maximum head dim
     (2, 2, 7, 9, 48, 80, 64),       # dk != dv
+    (1, 2, 11, 7, 80, 80, 32),      # 80-channel tiles, no padding
+    (1, 2, 5, 9, 72, 72, 16),       # 80-channel tiles, 16-token chunks
     (1, 2, 1, 1, 8, 8, 64),         # a single token
     (3, 1, 16, 16, 32, 32, 0),      # automatic chunk
 ]
@@ -198,6 +200,7 @@ def _sampled(orc, key, directions, units):
     (6, 16, 32, 32, 64, 64),    # 96 scans: two segments, the pipelined split (64-token chunks)
     (6, 16, 32, 32, 64, 32),    # the same with 32-token chunks
     (1, 8, 64, 64, 64, 64),     # 8 scans: eight segments, decoupled look-back
+    (1, 8, 64, 64, 72, 64),     # the same with the DiG-XL head dim (80-channel tiles)
 ], ids=lambda s: "x".join(map(str, s)))
 def test_bf16_segmented_scans_with_s0(orc, shape):
     """Scans split over several workgroups (two-segment split and look-back
