@@ -205,10 +205,12 @@ hipError_t dig_launch_dwconv(const void *x, int dtype, int B, int T, int C, int6
   const int CV = C / 4;   // 4 channels per walker
   int R, Q;
   scan_frame(dir, gh, gw, R, Q);
-  // rows per walker: about two resident waves of walkers, at least 8 rows each
+  // rows per walker: about 18 walker waves per CU (measured best: fewer
+  // leave memory latency exposed, more split the columns into short runs
+  // whose halo rows and start-up cost more than they hide), at least 8 rows
   const int64_t cols = (int64_t)B * Q * CV;
-  const int64_t want_threads = (int64_t)num_cu * 4 * 8 * 64;
-  int64_t nseg = (want_threads + cols - 1) / cols;
+  const int64_t want_threads = (int64_t)num_cu * 18 * 64;
+  int64_t nseg = (want_threads + cols / 2) / cols;
   if (nseg > (R + 7) / 8) nseg = (R + 7) / 8;
   if (nseg < 1) nseg = 1;
   const int rows = (int)((R + nseg - 1) / nseg);
