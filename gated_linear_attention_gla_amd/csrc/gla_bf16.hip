@@ -485,8 +485,9 @@ gla_fwd_bf16_kernel(Params P) {
     }
   };
   // P2(x): per producer wave, its 16 channels: b, e^{b_last}; fast chunks:
-  // q~ = q e^{b}, k~ = k e^{-b}, k^ = k~ e^{b_last} in place (|b| <= 64: no
-  // overflow); pairwise chunks: b to LDS (fp32) and k^ directly.  bt stays in
+  // q~ = q e^{b}, k~ = k e^{-b} in place (|b| <= 64: no overflow; the state
+  // update applies e^{b_last} after its product); pairwise chunks: b to LDS
+  // (fp32) and k^ = k e^{b_last - b} directly.  bt stays in
   // registers for P3 of a pairwise chunk.
   f32x4_t bt[MT];
   auto produce2 = [&](int x, bool pairwise) {
@@ -501,17 +502,14 @@ gla_fwd_bf16_kernel(Params P) {
         const int off = (16 * i + l16) * QS + acol;
         const uint2 qw = lds2(tq + off), kw = lds2(tk + off);
         const uint32_t qa[2] = {qw.x, qw.y}, ka[2] = {kw.x, kw.y};
-        uint32_t oq[2], ok[2], oh[2];
+        uint32_t oq[2], ok[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           oq[e] = pack_bf16x2(bf16lo(qa[e]) * fexp2(bt[i][2 * e]), bf16hi(qa[e]) * fexp2(bt[i][2 * e + 1]));
-          const float k0 = bf16lo(ka[e]) * fexp2(-bt[i][2 * e]), k1 = bf16hi(ka[e]) * fexp2(-bt[i][2 * e + 1]);
-          ok[e] = pack_bf16x2(k0, k1);
-          oh[e] = pack_bf16x2(k0 * gmo[2 * e], k1 * gmo[2 * e + 1]);
+          ok[e] = pack_bf16x2(bf16lo(ka[e]) * fexp2(-bt[i][2 * e]), bf16hi(ka[e]) * fexp2(-bt[i][2 * e + 1]));
         }
         *reinterpret_cast<uint2 *>(tq + off) = make_uint2(oq[0], oq[1]);
         *reinterpret_cast<uint2 *>(tk + off) = make_uint2(ok[0], ok[1]);
-        *reinterpret_cast<uint2 *>(tg + off) = make_uint2(oh[0], oh[1]);
       }
     } else {
 #pragma unroll
@@ -587,17 +585,23 @@ gla_fwd_bf16_kernel(Params P) {
       vf[jp] = cat(lo, hi);
     }
   };
-  // S = diag(e^{b_last}) S + k^^T v for this wave's columns (k^ in the gate
-  // tile); optionally accumulates the product of the gates in gprod.
-  auto state_update = [&](int par, f32x4_t *S, f32x4_t *gprod) {
-    const uint16_t *th = tile(par, 2);
+  // The state after a chunk for this wave's columns: fast chunks
+  // S = diag(e^{b_last}) (S + k~^T v) (k~ = k e^{-b} in tile 1: the same
+  // product as k^^T v, scaled once per row afterwards); pairwise chunks and
+  // segment aggregates S = diag(e^{b_last}) S + k^^T v (k^ in tile 2), which
+  // optionally also accumulates the product of the gates in gprod.
+  auto state_update = [&](int par, f32x4_t *S, f32x4_t *gprod, bool fast) {
+    const uint16_t *th = tile(par, fast ? 1 : 2);
     uint4 vf[JP];
     v_frags(tile(par, 3), vf);
     const float *gm_ = gam(par);
+    // one code path for both forms: the row scale goes before or after the product
 #pragma unroll
     for (int r = 0; r < DT; ++r) {
       const float4 gm = *reinterpret_cast<const float4 *>(gm_ + 16 * r + 4 * g4);
-      S[r][0] *= gm.x; S[r][1] *= gm.y; S[r][2] *= gm.z; S[r][3] *= gm.w;
+      const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[r][e] *= fast ? 1.f : gv[e];
       if (gprod) { gprod[r][0] *= gm.x; gprod[r][1] *= gm.y; gprod[r][2] *= gm.z; gprod[r][3] *= gm.w; }
 #pragma unroll
       for (int jp = 0; jp < JP; ++jp) {
@@ -607,6 +611,8 @@ gla_fwd_bf16_kernel(Params P) {
                              : make_uint2(0, 0);
         S[r] = mfma32(cat(lo, hi), vf[jp], S[r]);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[r][e] *= fast ? gv[e] : 1.f;
     }
   };
   // o of chunk c for this wave's columns: O^T = S^T q~^T + V^T P^T (S: the
@@ -666,6 +672,91 @@ gla_fwd_bf16_kernel(Params P) {
   };
   auto blk_at = [&](int r) { return ((r * NWv + wave) * 64 + lane) * 4; };
 
+  // The two roles run separate copies of the whole schedule with the same
+  // sequence of barriers (marked B in the comments: both sides must pass
+  // the same ones in the same order), so the registers one role carries (the
+  // producers' in-flight loads and gate sums, the consumers' state) are never
+  // allocated in the other role's code.
+  if (producer) {
+    // ===================== pass 1: segment aggregate ==========================
+    // stage chunk c+1 (k, v, gates -> k^, e^{b_last}) while the consumers
+    // fold chunk c into the aggregate
+    if (do_pass1) {
+      fill_tok(c_begin);
+      fill_tok(c_begin + 1);
+      __syncthreads();                                          // B a
+      load_chunk(c_begin, false);
+      lds_barrier();                                            // B 1
+      produce1(c_begin, false);
+      lds_barrier();                                            // B 2
+      if (has_rows) {
+        float gmo[4], bl[4];
+        scan(tile(c_begin & 1, 2), bt);
+        chunk_total(bt, gmo, bl, c_begin & 1);
+        khat_direct(tile(c_begin & 1, 1), tile(c_begin & 1, 2), bt, bl);
+      }
+      lds_barrier();                                            // B 3
+      for (int c = c_begin; c < c_end; ++c) {
+        const int x = c + 1;
+        if (x < c_end) produce1(x, false);
+        lds_barrier();                                          // B loop 1
+        if (has_rows && x < c_end) {
+          float gmo[4], bl[4];
+          scan(tile(x & 1, 2), bt);
+          chunk_total(bt, gmo, bl, x & 1);
+          khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
+        }
+        lds_barrier();                                          // B loop 2
+      }
+      drain_vmem();
+      __syncthreads();                                          // B e
+    }
+    // ================ look-back (the consumers' work) ========================
+    if (seg != 0) __syncthreads();                              // B l
+    if (do_pass1 && P.split_K == 0) __syncthreads();            // B p
+    // ======================= pass 2: outputs ==================================
+    c_begin = out_begin;
+    c_end = out_end;
+    fill_tok(c_begin);
+    fill_tok(c_begin + 1);
+    __syncthreads();                                            // B s
+    load_chunk(c_begin, true);
+    lds_barrier();                                              // B t
+    produce1(c_begin, true);
+    lds_barrier();                                              // B u
+    bool pw_next = chunk_pairwise(c_begin);
+    if (has_rows) produce2(c_begin, pw_next);
+    lds_barrier();                                              // B v
+    if (!pw_next) produce3_fast(c_begin); else produce3_pairwise(c_begin);
+    lds_barrier();                                              // B w
+    if (pw_next) {
+      if (has_rows) qtilde(tile(c_begin & 1, 0), bt);
+      lds_barrier();                                            // B x
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+      const int x = c + 1;
+      const bool live = x < c_end;
+      // interval 1: stage chunk x (the consumers write o of chunk c)
+      if (live) produce1(x, true);
+      lds_barrier();                                            // B loop 1
+      pw_next = live && chunk_pairwise(x);
+      // interval 2: transform chunk x (the consumers update the state)
+      if (has_rows && live) produce2(x, pw_next);
+      lds_barrier();                                            // B loop 2
+      // interval 3: all waves build the P^T tiles of chunk x
+      if (live) {
+        if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
+      }
+      lds_barrier();                                            // B loop 3
+      if (pw_next) {
+        if (has_rows) qtilde(tile(x & 1, 0), bt);
+        lds_barrier();                                          // B loop 4
+      }
+    }
+    return;
+  }
+
+  // ================================ consumers =================================
   f32x4_t S[DT];
 #pragma unroll
   for (int r = 0; r < DT; ++r) S[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -674,48 +765,15 @@ gla_fwd_bf16_kernel(Params P) {
   for (int r = 0; r < DT; ++r) gp[r] = f32x4_t{1.f, 1.f, 1.f, 1.f};
 
   // ======================= pass 1: segment aggregate =========================
-  // producers stage chunk c+1 (k, v, gates -> k^, e^{b_last}) while the
-  // consumers fold chunk c into the aggregate.
   if (do_pass1) {
-    fill_tok(c_begin);
-    fill_tok(c_begin + 1);
-    __syncthreads();
-    if (producer) load_chunk(c_begin, false);
-    lds_barrier();
-    if (producer) produce1(c_begin, false);
-    lds_barrier();
-    if (has_rows) {
-      float gmo[4], bl[4];
-      scan(tile(c_begin & 1, 2), bt);
-      chunk_total(bt, gmo, bl, c_begin & 1);
-      khat_direct(tile(c_begin & 1, 1), tile(c_begin & 1, 2), bt, bl);
-    }
-    lds_barrier();
-    // One loop per role with the same barriers: the registers each role
-    // carries through its loop (in-flight loads; state) are not held by the
-    // other role's code.
-    if (producer) {
-      for (int c = c_begin; c < c_end; ++c) {
-        const int x = c + 1;
-        if (x < c_end) produce1(x, false);
-        lds_barrier();
-        if (has_rows && x < c_end) {
-          float gmo[4], bl[4];
-          scan(tile(x & 1, 2), bt);
-          chunk_total(bt, gmo, bl, x & 1);
-          khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
-        }
-        lds_barrier();
-      }
-      // producers hold no state: its carried value ends here
-#pragma unroll
-      for (int r = 0; r < DT; ++r) { S[r] = f32x4_t{0.f, 0.f, 0.f, 0.f}; gp[r] = f32x4_t{1.f, 1.f, 1.f, 1.f}; }
-    } else {
-      for (int c = c_begin; c < c_end; ++c) {
-        if (has_cols) state_update(c & 1, S, gp);
-        lds_barrier();
-        lds_barrier();
-      }
+    __syncthreads();                                            // B a
+    lds_barrier();                                              // B 1
+    lds_barrier();                                              // B 2
+    lds_barrier();                                              // B 3
+    for (int c = c_begin; c < c_end; ++c) {
+      if (has_cols) state_update(c & 1, S, gp, false);
+      lds_barrier();                                            // B loop 1
+      lds_barrier();                                            // B loop 2
     }
     if (has_cols && P.split_K == 0) {
       float *blk = P.agg + (slot0 + seg) * P.blk_floats;
@@ -729,7 +787,7 @@ gla_fwd_bf16_kernel(Params P) {
       }
     }
     drain_vmem();
-    __syncthreads();
+    __syncthreads();                                            // B e
     if (tid == 0 && P.split_K == 0)
       __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -751,7 +809,7 @@ gla_fwd_bf16_kernel(Params P) {
       }
       sMisc[2] = j;
     }
-    __syncthreads();
+    __syncthreads();                                            // B l
     const int jstar = sMisc[2];
     if (jstar >= 0) {
       const float *blk = P.inc + (slot0 + jstar) * P.blk_floats;
@@ -793,7 +851,7 @@ gla_fwd_bf16_kernel(Params P) {
                                   fmaf(gp[r][2], Sin[r][2], S[r][2]), fmaf(gp[r][3], Sin[r][3], S[r][3])));
     }
     drain_vmem();
-    __syncthreads();
+    __syncthreads();                                            // B p
     if (tid == 0)
       __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -809,91 +867,62 @@ gla_fwd_bf16_kernel(Params P) {
   }
 
   // ========================= pass 2: outputs ==================================
-  // Three barrier intervals per chunk c: producers P1/P2 of chunk c+1 while
-  // the consumers write o of chunk c, then update its state; all waves build
-  // the P^T tiles of chunk c+1 in the third.  A pairwise
+  // Three barrier intervals per chunk c: the producers stage and transform
+  // chunk c+1 while the consumers write o of chunk c, then update its state;
+  // all waves build the P^T tiles of chunk c+1 in the third.  A pairwise
   // chunk c+1 adds one interval (its q~ may be written only after every
   // thread has read its raw q).
   drain_vmem();
   c_begin = out_begin;
   c_end = out_end;
-  fill_tok(c_begin);
-  fill_tok(c_begin + 1);
-  __syncthreads();
-  if (producer) load_chunk(c_begin, true);
-  lds_barrier();
-  if (producer) produce1(c_begin, true);
-  lds_barrier();
+  __syncthreads();                                              // B s
+  lds_barrier();                                                // B t
+  lds_barrier();                                                // B u
   bool pw_next = chunk_pairwise(c_begin);
-  if (has_rows) produce2(c_begin, pw_next);
-  lds_barrier();
+  lds_barrier();                                                // B v
   if (!pw_next) produce3_fast(c_begin); else produce3_pairwise(c_begin);
-  lds_barrier();
-  if (pw_next) {
-    if (has_rows) qtilde(tile(c_begin & 1, 0), bt);
-    lds_barrier();
+  lds_barrier();                                                // B w
+  if (pw_next) lds_barrier();                                   // B x
+  bool pw_c = pw_next;   // chunk c took the pairwise path
+  for (int c = c_begin; c < c_end; ++c) {
+    const int x = c + 1;
+    const bool live = x < c_end;
+    // interval 1: o of chunk c
+    if (has_cols) outputs(c, S);
+    lds_barrier();                                              // B loop 1
+    pw_next = live && chunk_pairwise(x);
+    // interval 2: o of chunk c to memory, the state after chunk c
+    store_stage(c);
+    if (has_cols) {
+      state_update(c & 1, S, nullptr, !pw_c);
+      if (c + 1 == publish_at) {   // split segment 0: the state entering chunk L
+        float *blk = P.inc + slot0 * P.blk_floats;
+#pragma unroll
+        for (int r = 0; r < DT; ++r)
+          if (r < DTr) st_coherent(blk + blk_at(r), make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
+        drain_vmem();
+      }
+    }
+    lds_barrier();                                              // B loop 2
+    // interval 3: P^T tiles of chunk x
+    if (live) {
+      if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
+    }
+    lds_barrier();                                              // B loop 3
+    if (c + 1 == publish_at && tid == 0)
+      __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (pw_next) lds_barrier();                                 // B loop 4
+    pw_c = pw_next;
   }
-  if (producer) {
-    for (int c = c_begin; c < c_end; ++c) {
-      const int x = c + 1;
-      const bool live = x < c_end;
-      // interval 1: stage chunk x (the consumers write o of chunk c)
-      if (live) produce1(x, true);
-      lds_barrier();
-      pw_next = live && chunk_pairwise(x);
-      // interval 2: transform chunk x (the consumers update the state)
-      if (has_rows && live) produce2(x, pw_next);
-      lds_barrier();
-      // interval 3: all waves build the P^T tiles of chunk x
-      if (live) {
-        if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
-      }
-      lds_barrier();
-      if (pw_next) {
-        if (has_rows) qtilde(tile(x & 1, 0), bt);
-        lds_barrier();
-      }
-    }
-  } else {
-    for (int c = c_begin; c < c_end; ++c) {
-      const int x = c + 1;
-      const bool live = x < c_end;
-      // interval 1: o of chunk c
-      if (has_cols) outputs(c, S);
-      lds_barrier();
-      pw_next = live && chunk_pairwise(x);
-      // interval 2: o of chunk c to memory, the state after chunk c
-      store_stage(c);
-      if (has_cols) {
-        state_update(c & 1, S, nullptr);
-        if (c + 1 == publish_at) {   // split segment 0: the state entering chunk L
-          float *blk = P.inc + slot0 * P.blk_floats;
-#pragma unroll
-          for (int r = 0; r < DT; ++r)
-            if (r < DTr) st_coherent(blk + blk_at(r), make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
-          drain_vmem();
-        }
-      }
-      lds_barrier();
-      // interval 3: P^T tiles of chunk x
-      if (live) {
-        if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
-      }
-      lds_barrier();
-      if (c + 1 == publish_at && tid == 0)
-        __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (pw_next) lds_barrier();
-    }
 
-    if (last_seg && P.s_final && has_cols) {
+  if (last_seg && P.s_final && has_cols) {
 #pragma unroll
-      for (int r = 0; r < DT; ++r)
+    for (int r = 0; r < DT; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ch = 16 * r + 4 * g4 + e, n = n0 + l16;
-          if (ch < dk && n < dv) P.s_final[((int64_t)unit * dk + ch) * dv + n] = S[r][e];
-        }
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int ch = 16 * r + 4 * g4 + e, n = n0 + l16;
+        if (ch < dk && n < dv) P.s_final[((int64_t)unit * dk + ch) * dv + n] = S[r][e];
+      }
   }
 }
 
