@@ -214,8 +214,8 @@ struct Lds {
   static constexpr int oPT = 2 * BUF;                  // [2][NPT][256] bf16 P^T tiles (MFMA fragment order)
   static constexpr int oB32 = oPT + 2 * NPT * 512;     // [M][DP] fp32 cumulative gates (pairwise chunks only)
   static constexpr int oGam = oB32 + M * DP * 4;       // [2][DP] e^{b_last}
-  static constexpr int oTok = oGam + 2 * DP * 4;       // [2][2][M] token byte offsets (chunk parity; q/k/g, v)
-  static constexpr int oVote = oTok + 4 * M * 4;       // [2][16] per producer wave: chunk needs the pairwise path
+  static constexpr int oTok = oGam + 2 * DP * 4;       // [4][2][M] token byte offsets (chunk mod 4; q/k/g, v)
+  static constexpr int oVote = oTok + 8 * M * 4;       // [2][16] per producer wave: chunk needs the pairwise path
   static constexpr int oStg = oVote + 2 * 16 * 4;      // [M][QS] bf16 o of the chunk being written
   static constexpr int oMisc = oStg + TILE;            // ticket, look-back result
   static constexpr int bytes = oMisc + 64;
@@ -361,17 +361,20 @@ gla_fwd_bf16_kernel(Params P) {
         oqk = n * (unsigned)P.qk_st * 2u;
         ov = n * (unsigned)P.v_st * 2u;
       }
-      unsigned *tb = sTok + (x & 1) * 2 * M;
+      unsigned *tb = sTok + (x & 3) * 2 * M;
       tb[ptid] = oqk;
       tb[M + ptid] = ov;
     }
   };
   // Loads of chunk x: item idx -> (token tl, 16-byte channel group cg).
   // Unconditional: a load under a branch would make the loop-carried
-  // registers merge with their old values and force an early wait.
-  uint4 rq[R], rk[R], rg[R], rv[R];
-  auto load_chunk = [&](int x, bool with_q) {
-    const unsigned *tb = sTok + (x & 1) * 2 * M;
+  // registers merge with their old values and force an early wait.  Two
+  // register sets alternate by chunk, so a chunk's loads are issued two
+  // chunks before its data is stored to LDS.
+  struct LoadSet { uint4 q[R], k[R], g[R], v[R]; };
+  LoadSet lsA, lsB;
+  auto load_chunk = [&](int x, bool with_q, LoadSet &ls) {
+    const unsigned *tb = sTok + (x & 3) * 2 * M;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = ptid + r * NTP;
@@ -380,18 +383,19 @@ gla_fwd_bf16_kernel(Params P) {
       const unsigned tq = tb[ok ? tl : 0], tv = tb[M + (ok ? tl : 0)];
       const unsigned ok_qk = ok && (8 * cg < dk) ? tq + 16u * cg : kOOB;
       const unsigned ok_v = ok && (8 * cg < dv) ? tv + 16u * cg : kOOB;
-      if (with_q) rq[r] = bload16(rq_, ok_qk);
-      rk[r] = bload16(rk_, ok_qk);
-      rg[r] = bload16(rg_, ok_qk);
-      rv[r] = bload16(rv_, ok_v);
+      if (with_q) ls.q[r] = bload16(rq_, ok_qk);
+      ls.k[r] = bload16(rk_, ok_qk);
+      ls.g[r] = bload16(rg_, ok_qk);
+      ls.v[r] = bload16(rv_, ok_v);
     }
   };
-  // P1(x): the loaded chunk x to its tiles, then the loads of chunk x+1 and
-  // the token table of chunk x+2.  with_q: also a vote per wave on whether
-  // M * max|log-gate| * log2(e) can exceed kFastRange (then the chunk takes
-  // the pairwise path; the bound covers every |b| in the chunk).
+  // P1(x): the loaded chunk x (register set ls) to its tiles, then the loads
+  // of chunk x+2 into the same set and the token table of chunk x+3.
+  // with_q: also a vote per wave on whether M * max|log-gate| * log2(e) can
+  // exceed kFastRange (then the chunk takes the pairwise path; the bound
+  // covers every |b| in the chunk).
   const float bound_scale = (float)M * kLog2e;
-  auto produce1 = [&](int x, bool with_q) {
+  auto produce1 = [&](int x, bool with_q, LoadSet &ls) {
     const int par = x & 1;
     uint16_t *tq = tile(par, 0), *tk = tile(par, 1), *tg = tile(par, 2), *tv = tile(par, 3);
     unsigned gmax = 0;
@@ -401,12 +405,12 @@ gla_fwd_bf16_kernel(Params P) {
       if (idx < ITEMS) {
         const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
         const unsigned off = (unsigned)(tl * QS + 8 * cg) * 2u;   // bytes, 32-bit LDS offset
-        if (with_q) *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tq) + off) = rq[r];
-        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tk) + off) = rk[r];
-        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tg) + off) = rg[r];
-        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tv) + off) = rv[r];
+        if (with_q) *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tq) + off) = ls.q[r];
+        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tk) + off) = ls.k[r];
+        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tg) + off) = ls.g[r];
+        *reinterpret_cast<uint4 *>(reinterpret_cast<unsigned char *>(tv) + off) = ls.v[r];
         if (with_q) {
-          const uint32_t gw_[4] = {rg[r].x, rg[r].y, rg[r].z, rg[r].w};
+          const uint32_t gw_[4] = {ls.g[r].x, ls.g[r].y, ls.g[r].z, ls.g[r].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             gmax = max(gmax, max(gw_[e] & 0x7fffu, (gw_[e] >> 16) & 0x7fffu));   // |bf16| bits
@@ -418,8 +422,8 @@ gla_fwd_bf16_kernel(Params P) {
       const bool any_bad = __any(bad);
       if (lane == 0) sVote[par * 16 + pw] = any_bad ? 1 : 0;
     }
-    load_chunk(x + 1, with_q);
-    fill_tok(x + 2);
+    load_chunk(x + 2, with_q, ls);
+    fill_tok(x + 3);
   };
   auto chunk_pairwise = [&](int x) {
     int v = 0;
@@ -684,10 +688,12 @@ gla_fwd_bf16_kernel(Params P) {
     if (do_pass1) {
       fill_tok(c_begin);
       fill_tok(c_begin + 1);
+      fill_tok(c_begin + 2);
       __syncthreads();                                          // B a
-      load_chunk(c_begin, false);
+      load_chunk(c_begin, false, lsA);
+      load_chunk(c_begin + 1, false, lsB);
       lds_barrier();                                            // B 1
-      produce1(c_begin, false);
+      produce1(c_begin, false, lsA);
       lds_barrier();                                            // B 2
       if (has_rows) {
         float gmo[4], bl[4];
@@ -696,9 +702,14 @@ gla_fwd_bf16_kernel(Params P) {
         khat_direct(tile(c_begin & 1, 1), tile(c_begin & 1, 2), bt, bl);
       }
       lds_barrier();                                            // B 3
-      for (int c = c_begin; c < c_end; ++c) {
+      // chunk c: stage chunk x = c+1 from register set (x - c_begin) & 1
+      auto agg_step = [&](int c, LoadSet &ls) {
         const int x = c + 1;
-        if (x < c_end) produce1(x, false);
+        // unconditional (past the segment the token table reads zeros and
+        // the stores land in a buffer nobody reads): a skipped load would
+        // make the compiler's count of outstanding loads, and its waits,
+        // conservative for every chunk
+        produce1(x, false, ls);
         lds_barrier();                                          // B loop 1
         if (has_rows && x < c_end) {
           float gmo[4], bl[4];
@@ -707,6 +718,14 @@ gla_fwd_bf16_kernel(Params P) {
           khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
         }
         lds_barrier();                                          // B loop 2
+      };
+      // Steps in pairs (register sets B, A); an odd count ends with a step
+      // past the segment that only stages zeros, matched by the consumers.
+      // (A conditional second step would leave the compiler unsure which
+      // set was loaded last, and it would wait for both.)
+      for (int c = c_begin; c < c_end; c += 2) {
+        agg_step(c, lsB);
+        agg_step(c + 1, lsA);
       }
       drain_vmem();
       __syncthreads();                                          // B e
@@ -719,10 +738,12 @@ gla_fwd_bf16_kernel(Params P) {
     c_end = out_end;
     fill_tok(c_begin);
     fill_tok(c_begin + 1);
+    fill_tok(c_begin + 2);
     __syncthreads();                                            // B s
-    load_chunk(c_begin, true);
+    load_chunk(c_begin, true, lsA);
+    load_chunk(c_begin + 1, true, lsB);
     lds_barrier();                                              // B t
-    produce1(c_begin, true);
+    produce1(c_begin, true, lsA);
     lds_barrier();                                              // B u
     bool pw_next = chunk_pairwise(c_begin);
     if (has_rows) produce2(c_begin, pw_next);
@@ -733,25 +754,30 @@ gla_fwd_bf16_kernel(Params P) {
       if (has_rows) qtilde(tile(c_begin & 1, 0), bt);
       lds_barrier();                                            // B x
     }
-    for (int c = c_begin; c < c_end; ++c) {
+    // chunk c: stage and transform chunk x = c+1 from register set (x - c_begin) & 1
+    auto out_step = [&](int c, LoadSet &ls) {
       const int x = c + 1;
       const bool live = x < c_end;
       // interval 1: stage chunk x (the consumers write o of chunk c)
-      if (live) produce1(x, true);
+      produce1(x, true, ls);   // unconditional, as in the aggregate pass
       lds_barrier();                                            // B loop 1
-      pw_next = live && chunk_pairwise(x);
+      const bool pwx = live && chunk_pairwise(x);
       // interval 2: transform chunk x (the consumers update the state)
-      if (has_rows && live) produce2(x, pw_next);
+      if (has_rows && live) produce2(x, pwx);
       lds_barrier();                                            // B loop 2
       // interval 3: all waves build the P^T tiles of chunk x
       if (live) {
-        if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
+        if (!pwx) produce3_fast(x); else produce3_pairwise(x);
       }
       lds_barrier();                                            // B loop 3
-      if (pw_next) {
+      if (pwx) {
         if (has_rows) qtilde(tile(x & 1, 0), bt);
         lds_barrier();                                          // B loop 4
       }
+    };
+    for (int c = c_begin; c < c_end; c += 2) {   // in pairs, as in the aggregate pass
+      out_step(c, lsB);
+      out_step(c + 1, lsA);
     }
     return;
   }
@@ -772,6 +798,10 @@ gla_fwd_bf16_kernel(Params P) {
     lds_barrier();                                              // B 3
     for (int c = c_begin; c < c_end; ++c) {
       if (has_cols) state_update(c & 1, S, gp, false);
+      lds_barrier();                                            // B loop 1
+      lds_barrier();                                            // B loop 2
+    }
+    if ((c_end - c_begin) & 1) {   // the producers' step past the segment
       lds_barrier();                                            // B loop 1
       lds_barrier();                                            // B loop 2
     }
@@ -913,6 +943,11 @@ gla_fwd_bf16_kernel(Params P) {
       __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (pw_next) lds_barrier();                                 // B loop 4
     pw_c = pw_next;
+  }
+  if ((c_end - c_begin) & 1) {   // the producers' step past the segment
+    lds_barrier();                                              // B loop 1
+    lds_barrier();                                              // B loop 2
+    lds_barrier();                                              // B loop 3
   }
 
   if (last_seg && P.s_final && has_cols) {
