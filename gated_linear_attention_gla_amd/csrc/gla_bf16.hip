@@ -236,7 +236,8 @@ gla_fwd_bf16_kernel(Params P) {
   constexpr int K32 = DP / 32;               // 32-wide channel blocks
   constexpr bool KH = (DP % 32) != 0;        // and a 16-wide one after them (80 channels)
   constexpr int JP = (MT + 1) / 2;           // 32-token K blocks
-  constexpr int R = (M * (DP / 8) + NTP - 1) / NTP;   // max 16-byte items per producer thread per tensor
+  constexpr int R = (M * (DP / 8) + NTP - 1) / NTP;
+  constexpr int RA = (R + 1) / 2;   // load rounds issued right after the staging stores   // max 16-byte items per producer thread per tensor
   constexpr int QS = Lds<DP, M>::QS, NPT = Lds<DP, M>::NPT, TILE = Lds<DP, M>::TILE;
   static_assert(DP % 16 == 0 && DT <= 16, "channel tiling");
   static_assert(Lds<DP, M>::bytes <= 160 * 1024, "LDS plan exceeds 160 KiB");
@@ -373,10 +374,10 @@ gla_fwd_bf16_kernel(Params P) {
   // chunks before its data is stored to LDS.
   struct LoadSet { uint4 q[R], k[R], g[R], v[R]; };
   LoadSet lsA, lsB;
-  auto load_chunk = [&](int x, bool with_q, LoadSet &ls) {
+  auto load_chunk = [&](int x, bool with_q, LoadSet &ls, int r_lo, int r_hi) {
     const unsigned *tb = sTok + (x & 3) * 2 * M;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = r_lo; r < r_hi; ++r) {
       const int idx = ptid + r * NTP;
       const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
       const bool ok = idx < ITEMS;
@@ -422,7 +423,12 @@ gla_fwd_bf16_kernel(Params P) {
       const bool any_bad = __any(bad);
       if (lane == 0) sVote[par * 16 + pw] = any_bad ? 1 : 0;
     }
-    load_chunk(x + 2, with_q, ls);
+    load_chunk(x + 2, with_q, ls, 0, RA);   // the rest after the P^T tiles (late_loads)
+  };
+  // The remaining loads of chunk x+2 and the token table of chunk x+3, issued
+  // in the last interval of the step, where the memory pipeline is idle.
+  auto late_loads = [&](int x, bool with_q, LoadSet &ls) {
+    load_chunk(x + 2, with_q, ls, RA, R);
     fill_tok(x + 3);
   };
   auto chunk_pairwise = [&](int x) {
@@ -690,10 +696,11 @@ gla_fwd_bf16_kernel(Params P) {
       fill_tok(c_begin + 1);
       fill_tok(c_begin + 2);
       __syncthreads();                                          // B a
-      load_chunk(c_begin, false, lsA);
-      load_chunk(c_begin + 1, false, lsB);
+      load_chunk(c_begin, false, lsA, 0, R);
+      load_chunk(c_begin + 1, false, lsB, 0, R);
       lds_barrier();                                            // B 1
       produce1(c_begin, false, lsA);
+      late_loads(c_begin, false, lsA);
       lds_barrier();                                            // B 2
       if (has_rows) {
         float gmo[4], bl[4];
@@ -717,6 +724,7 @@ gla_fwd_bf16_kernel(Params P) {
           chunk_total(bt, gmo, bl, x & 1);
           khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
         }
+        late_loads(x, false, ls);
         lds_barrier();                                          // B loop 2
       };
       // Steps in pairs (register sets B, A); an odd count ends with a step
@@ -740,10 +748,11 @@ gla_fwd_bf16_kernel(Params P) {
     fill_tok(c_begin + 1);
     fill_tok(c_begin + 2);
     __syncthreads();                                            // B s
-    load_chunk(c_begin, true, lsA);
-    load_chunk(c_begin + 1, true, lsB);
+    load_chunk(c_begin, true, lsA, 0, R);
+    load_chunk(c_begin + 1, true, lsB, 0, R);
     lds_barrier();                                              // B t
     produce1(c_begin, true, lsA);
+    late_loads(c_begin, true, lsA);
     lds_barrier();                                              // B u
     bool pw_next = chunk_pairwise(c_begin);
     if (has_rows) produce2(c_begin, pw_next);
@@ -769,6 +778,7 @@ gla_fwd_bf16_kernel(Params P) {
       if (live) {
         if (!pwx) produce3_fast(x); else produce3_pairwise(x);
       }
+      late_loads(x, true, ls);
       lds_barrier();                                            // B loop 3
       if (pwx) {
         if (has_rows) qtilde(tile(x & 1, 0), bt);
