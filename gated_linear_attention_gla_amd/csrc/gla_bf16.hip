@@ -237,7 +237,10 @@ gla_fwd_bf16_kernel(Params P) {
   constexpr bool KH = (DP % 32) != 0;        // and a 16-wide one after them (80 channels)
   constexpr int JP = (MT + 1) / 2;           // 32-token K blocks
   constexpr int R = (M * (DP / 8) + NTP - 1) / NTP;
-  constexpr int RA = (R + 1) / 2;   // load rounds issued right after the staging stores   // max 16-byte items per producer thread per tensor
+  // load split points (see mid_loads): with 64-token chunks half after the
+  // staging stores, half after the transform (measured best of the three-way
+  // splits at C2); shorter chunks issue them all at once
+  constexpr int JA = M >= 64 ? 2 * R : 4 * R, JB = 4 * R;   // max 16-byte items per producer thread per tensor
   constexpr int QS = Lds<DP, M>::QS, NPT = Lds<DP, M>::NPT, TILE = Lds<DP, M>::TILE;
   static_assert(DP % 16 == 0 && DT <= 16, "channel tiling");
   static_assert(Lds<DP, M>::bytes <= 160 * 1024, "LDS plan exceeds 160 KiB");
@@ -374,20 +377,24 @@ gla_fwd_bf16_kernel(Params P) {
   // chunks before its data is stored to LDS.
   struct LoadSet { uint4 q[R], k[R], g[R], v[R]; };
   LoadSet lsA, lsB;
-  auto load_chunk = [&](int x, bool with_q, LoadSet &ls, int r_lo, int r_hi) {
+  // Load j of a chunk (j = 4 r + tensor, tensors q, k, g, v; q skipped
+  // without with_q), for j in [j_lo, j_hi).
+  auto load_chunk = [&](int x, bool with_q, LoadSet &ls, int j_lo, int j_hi) {
     const unsigned *tb = sTok + (x & 3) * 2 * M;
 #pragma unroll
-    for (int r = r_lo; r < r_hi; ++r) {
+    for (int r = 0; r < R; ++r) {
+      if (4 * r + 4 <= j_lo || 4 * r >= j_hi) continue;
       const int idx = ptid + r * NTP;
       const int tl = (int)__umulhi(2u * (unsigned)idx, P.cg_magic), cg = idx - tl * CG;
       const bool ok = idx < ITEMS;
       const unsigned tq = tb[ok ? tl : 0], tv = tb[M + (ok ? tl : 0)];
       const unsigned ok_qk = ok && (8 * cg < dk) ? tq + 16u * cg : kOOB;
       const unsigned ok_v = ok && (8 * cg < dv) ? tv + 16u * cg : kOOB;
-      if (with_q) ls.q[r] = bload16(rq_, ok_qk);
-      ls.k[r] = bload16(rk_, ok_qk);
-      ls.g[r] = bload16(rg_, ok_qk);
-      ls.v[r] = bload16(rv_, ok_v);
+      auto in = [&](int t) { return 4 * r + t >= j_lo && 4 * r + t < j_hi; };
+      if (with_q && in(0)) ls.q[r] = bload16(rq_, ok_qk);
+      if (in(1)) ls.k[r] = bload16(rk_, ok_qk);
+      if (in(2)) ls.g[r] = bload16(rg_, ok_qk);
+      if (in(3)) ls.v[r] = bload16(rv_, ok_v);
     }
   };
   // P1(x): the loaded chunk x (register set ls) to its tiles, then the loads
@@ -423,12 +430,15 @@ gla_fwd_bf16_kernel(Params P) {
       const bool any_bad = __any(bad);
       if (lane == 0) sVote[par * 16 + pw] = any_bad ? 1 : 0;
     }
-    load_chunk(x + 2, with_q, ls, 0, RA);   // the rest after the P^T tiles (late_loads)
+    load_chunk(x + 2, with_q, ls, 0, JA);   // the rest in later intervals
   };
-  // The remaining loads of chunk x+2 and the token table of chunk x+3, issued
-  // in the last interval of the step, where the memory pipeline is idle.
+  // The loads of chunk x+2 are spread over the intervals of the step (the
+  // producers' vector-memory issue otherwise stalls the first interval):
+  // loads [0, JA) after the staging stores, [JA, JB) after the transform,
+  // the rest and the token table of chunk x+3 after the P^T tiles.
+  auto mid_loads = [&](int x, bool with_q, LoadSet &ls) { load_chunk(x + 2, with_q, ls, JA, JB); };
   auto late_loads = [&](int x, bool with_q, LoadSet &ls) {
-    load_chunk(x + 2, with_q, ls, RA, R);
+    load_chunk(x + 2, with_q, ls, JB, 4 * R);
     fill_tok(x + 3);
   };
   auto chunk_pairwise = [&](int x) {
@@ -696,10 +706,11 @@ gla_fwd_bf16_kernel(Params P) {
       fill_tok(c_begin + 1);
       fill_tok(c_begin + 2);
       __syncthreads();                                          // B a
-      load_chunk(c_begin, false, lsA, 0, R);
-      load_chunk(c_begin + 1, false, lsB, 0, R);
+      load_chunk(c_begin, false, lsA, 0, 4 * R);
+      load_chunk(c_begin + 1, false, lsB, 0, 4 * R);
       lds_barrier();                                            // B 1
       produce1(c_begin, false, lsA);
+      mid_loads(c_begin, false, lsA);
       late_loads(c_begin, false, lsA);
       lds_barrier();                                            // B 2
       if (has_rows) {
@@ -724,6 +735,7 @@ gla_fwd_bf16_kernel(Params P) {
           chunk_total(bt, gmo, bl, x & 1);
           khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
         }
+        mid_loads(x, false, ls);
         late_loads(x, false, ls);
         lds_barrier();                                          // B loop 2
       };
@@ -748,10 +760,11 @@ gla_fwd_bf16_kernel(Params P) {
     fill_tok(c_begin + 1);
     fill_tok(c_begin + 2);
     __syncthreads();                                            // B s
-    load_chunk(c_begin, true, lsA, 0, R);
-    load_chunk(c_begin + 1, true, lsB, 0, R);
+    load_chunk(c_begin, true, lsA, 0, 4 * R);
+    load_chunk(c_begin + 1, true, lsB, 0, 4 * R);
     lds_barrier();                                              // B t
     produce1(c_begin, true, lsA);
+    mid_loads(c_begin, true, lsA);
     late_loads(c_begin, true, lsA);
     lds_barrier();                                              // B u
     bool pw_next = chunk_pairwise(c_begin);
@@ -773,6 +786,7 @@ gla_fwd_bf16_kernel(Params P) {
       const bool pwx = live && chunk_pairwise(x);
       // interval 2: transform chunk x (the consumers update the state)
       if (has_rows && live) produce2(x, pwx);
+      mid_loads(x, true, ls);
       lds_barrier();                                            // B loop 2
       // interval 3: all waves build the P^T tiles of chunk x
       if (live) {
