@@ -28,15 +28,19 @@
 // the serial recurrence P_m = Gam_m * P_{m-1} + A_m element by element, so the
 // result is bitwise independent of which segments had finished: the output is
 // deterministic.  The segment publishes P_g and then runs the full chunk loop
-// from that state, writing o.  The second read of k, v and the gates mostly
-// hits the L2 / Infinity Cache.
+// from that state, writing o.  With two segments the scan is split in a
+// pipelined way instead (see the kernel): segment 1 aggregates a stretch that
+// segment 0 is still writing and starts from the state segment 0 publishes
+// at its start.
 //
 // gfx950 mapping
-//   * a workgroup has DT = DP/16 consumer waves and DT producer waves.  A
+//   * a workgroup has DT = DP/16 consumer waves and DT producer waves, each
+//     role running its own copy of the schedule with the same barriers.  A
 //     consumer owns 16 value columns: the fp32 state of those columns stays in
-//     its MFMA accumulators; it writes o and updates the state.  A producer
-//     owns 16 key channels: it loads the next chunk, scans its gates and forms
-//     q~, k~, k^; the producers together build the causal P^T tiles.  The
+//     its MFMA accumulators; it writes o (staged in LDS, stored as whole
+//     rows) and updates the state.  A producer owns 16 key channels: it
+//     stages a chunk loaded two chunks earlier, scans its gates and forms q~,
+//     k~ (k^ for pairwise chunks); all waves build the causal P^T tiles.  The
 //     producers work one chunk ahead on the other half of double-buffered LDS
 //     tiles, so the two roles overlap (three barriers per chunk);
 //   * the scan permutation is applied in the loads (scan position p reads
@@ -46,12 +50,13 @@
 //     fetch their operands with ds_read_b64_tr_b16, whose transpose puts
 //     tokens along K;
 //   * v_mfma_f32_16x16x32_bf16 with fp32 accumulation is the only MFMA shape:
-//     channels are zero-padded to a multiple of 32, an odd 16-token tile count
-//     pads its last token block with zeros;
+//     channels are zero-padded to 32, 64, 80, 96 or 128 (a 16-channel tail
+//     block and an odd 16-token tile count run with a zero upper half);
 //   * barriers fence LDS only, so the next chunk's global loads stay in flight
 //     across the whole chunk;
-//   * workgroups take tickets in launch order and are laid out XCD-major, so
-//     the segments of one scan run on one XCD and share its L2.
+//   * workgroups take tickets per XCD in start order; an XCD holds a
+//     contiguous range of scans (the heads of a batch element, whose rows
+//     share cache lines, and all segments of each), so they share its L2.
 //
 // MFMA 16x16xK operand layout used: lane l supplies row (A) / column (B)
 // l % 16 and K slice l / 16; the accumulator holds rows 4*(l/16) + e, column
@@ -176,7 +181,7 @@ struct Params {
   unsigned gh_magic;               // ceil(2^31 / gh): scan-order decode by a scalar multiply (fill_tok)
   unsigned qk_span, v_span, o_span;   // bytes addressable in one (batch, head) slice of q/k/g, v, o
   int blk_floats;                  // floats of one published state block
-  int *ticket;                     // launch-order ticket counter (reset by the last taker)
+  int *ticket;                     // [8] launch-order ticket counters, one per XCD (reset by the last taker)
   unsigned *flags;                 // [units][nseg]: epoch*4 + {1 aggregate, 2 inclusive}
   float *gam;                      // [units][nseg][DP] product of the segment's gates
   float *agg;                      // [units][nseg][blk_floats] aggregate state
@@ -266,12 +271,18 @@ gla_fwd_bf16_kernel(Params P) {
   const int pw = wave - DT;                  // producer wave index (channel tile)
   const int ptid = tid - NTP;                // producer thread index
 
-  // ---- work assignment: tickets in launch order, XCD-major layout; segment
-  // g of a scan always holds a larger ticket than segment g-1 of it.
+  // ---- work assignment.  Workgroups are dealt round-robin to the 8 XCDs
+  // (workgroup i runs on XCD i % 8), and all segments of the scans of one
+  // XCD's slot range stay on that XCD: the heads of a batch element, whose
+  // 144-byte rows share 128-byte lines, then meet in one L2.  Within an XCD,
+  // tickets taken in start order assign the work, so segment g of a scan
+  // always holds a larger ticket than segment g-1 of it and only ever waits
+  // for a workgroup that started before it.
   if (tid == 0) {
-    const int t = __hip_atomic_fetch_add(P.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == (int)gridDim.x - 1) __hip_atomic_store(P.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sMisc[1] = t;
+    const int g = blockIdx.x & 7, gsize = (int)gridDim.x >> 3;
+    const int t = __hip_atomic_fetch_add(P.ticket + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == gsize - 1) __hip_atomic_store(P.ticket + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sMisc[1] = (t << 3) | g;
   }
   __syncthreads();
   const int lid = sMisc[1];
@@ -1058,7 +1069,7 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   pl.blk_floats = DTr * NWv * 64 * 4;
   const size_t slots = (size_t)pl.units * pl.nseg;
   auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
-  size_t off = 256;   // the ticket counter lives at offset 0
+  size_t off = 256;   // the 8 ticket counters live at offset 0
   pl.off_flags = off;
   off += up(slots * 4);
   pl.off_gam = off;
