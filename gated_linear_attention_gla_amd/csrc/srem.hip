@@ -9,10 +9,13 @@
 // result is stored straight to the canonical token order (the arrange-back of
 // the ZigMa notes, 关键设计 / 异构逐层扫描), so no remapped copy is written.
 //
-// Work split: a thread owns 4 channels of one frame column and a run of frame
-// rows; its 9 x 4 fp32 weights sit in registers and a ring of rows slides
-// down the column with three rows of loads in flight.  Workgroups are ordered so that each XCD sweeps
-// neighbouring columns, whose shared cells hit its L2.
+// Work split: a thread owns 4 channels of NC adjacent frame columns and a run
+// of frame rows; its 9 x 4 fp32 weights sit in registers and a ring of rows
+// slides down the columns with three rows of loads in flight.  A row costs
+// NC + 2 loads for NC outputs, so wider walkers issue fewer loads per output
+// (the kernel is bound by the texture units' address issue, not by HBM).
+// Workgroups are ordered so that each XCD sweeps neighbouring columns, whose
+// shared cells hit its L2.
 #include "dig_internal.h"
 
 namespace dig {
@@ -55,13 +58,14 @@ __device__ __forceinline__ void gstore(unsigned char *p, const uint32_t *w, uint
   *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// A walker owns (batch, frame column c, 4-channel group, run of frame rows
-// [r0, r1)).  It keeps three frame rows x three columns of cells in registers
-// as fp32 (rows t-1, t, t+1 feed output row t) while rows t+2 .. t+4 are in
-// flight, so each step waits for a load issued three steps earlier.  Cells
-// outside the frame (zero padding) and rows past r1 come from out-of-range
-// buffer offsets, which read as zero without touching memory.
-template <int NW, int PW>
+// A walker owns (batch, frame columns [c, c + NC), 4-channel group, run of
+// frame rows [r0, r1)).  It keeps three frame rows x (NC + 2) columns of cells
+// in registers as fp32 (rows t-1, t, t+1 feed output row t) while rows
+// t+2 .. t+4 are in flight, so each step waits for a load issued three steps
+// earlier.  Cells outside the frame (zero padding), columns past Q and rows
+// past r1 come from out-of-range buffer offsets, which read as zero without
+// touching memory.
+template <int NW, int PW, int NC>
 __global__ void __launch_bounds__(kNT)
 srem_dwconv_kernel(const unsigned char *x, int64_t x_sb, int64_t x_st, const float *w,
                    unsigned char *y, int64_t y_sb, int64_t y_st, int B, int T, int C,
@@ -69,18 +73,20 @@ srem_dwconv_kernel(const unsigned char *x, int64_t x_sb, int64_t x_st, const flo
   typedef typename CellT<NW>::type cell_t;
   constexpr int CH = NW * PW;        // channels per walker (4)
   constexpr int ES = 4 / PW;         // bytes per element
+  constexpr int NCC = NC + 2;        // cells per row: the columns and one neighbour each side
   const int CV = C / CH;
   int R, Q;
   scan_frame(dir, gh, gw, R, Q);
+  const int QP = (Q + NC - 1) / NC;  // column groups
   // batch from the grid's y dimension: the buffer descriptor stays wave-uniform
   const int bb = blockIdx.y;
   const int id = xcd_linear_block(blockIdx.x, gridDim.x) * kNT + threadIdx.x;
-  const int total = Q * CV * nseg;
+  const int total = QP * CV * nseg;
   if (id >= total) return;
   const int cv = id % CV;
   const int rest = id / CV;
-  const int c = rest % Q;
-  const int seg = rest / Q;
+  const int c = (rest % QP) * NC;
+  const int seg = rest / QP;
   const int r0 = seg * rows_per_walker;
   const int r1 = r0 + rows_per_walker < R ? r0 + rows_per_walker : R;
   if (r0 >= r1) return;
@@ -95,30 +101,34 @@ srem_dwconv_kernel(const unsigned char *x, int64_t x_sb, int64_t x_st, const flo
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<unsigned char *>(x + bb * x_sb * ES), (short)0, (int)span, 0x00020000);
   const unsigned colB = (unsigned)(x_st * ES), rowB = colB * (unsigned)Q, chB = (unsigned)(ch0 * ES);
-  const unsigned oL = c > 0 ? chB + (unsigned)(c - 1) * colB : kOOB;
-  const unsigned oC = chB + (unsigned)c * colB;
-  const unsigned oR = c + 1 < Q ? chB + (unsigned)(c + 1) * colB : kOOB;
+  unsigned oc[NCC];                  // byte offset of each cell column in a row
+#pragma unroll
+  for (int j = 0; j < NCC; ++j) {
+    const int cc = c - 1 + j;
+    oc[j] = cc >= 0 && cc < Q ? chB + (unsigned)cc * colB : kOOB;
+  }
   auto load_row = [&](int r, cell_t *dst) {
     const bool ok = r >= 0 && r <= r1 && r < R;
     const unsigned base = ok ? (unsigned)r * rowB : 0u;
-    bload(rx, ok && oL != kOOB ? base + oL : kOOB, dst[0]);
-    bload(rx, ok ? base + oC : kOOB, dst[1]);
-    bload(rx, ok && oR != kOOB ? base + oR : kOOB, dst[2]);
+#pragma unroll
+    for (int j = 0; j < NCC; ++j) bload(rx, ok && oc[j] != kOOB ? base + oc[j] : kOOB, dst[j]);
   };
 
-  // canonical token of frame cell (t, c) is affine in t for every direction
-  const int n0 = scan_to_canon(dir, gh, gw, T, r0 * Q + c);
+  // canonical token of frame cell (t, c + o) is affine in t for every direction
+  int n0[NC];
+#pragma unroll
+  for (int o = 0; o < NC; ++o) n0[o] = scan_to_canon(dir, gh, gw, T, r0 * Q + (c + o < Q ? c + o : c));
   const int dn = dir == 0 ? Q : dir == 1 ? -Q : dir == 2 ? 1 : -1;
   unsigned char *yb = y + (bb * y_sb + (int64_t)ch0) * ES;
 
   // Two rings indexed by the local row u = t - r0 (mod 3): raw cells of the
   // rows in flight (u+1 .. u+3) and fp32 cells of the window rows (u-1 .. u+1).
   // Each cell is unpacked once, when its row enters the window.
-  cell_t raw[3][3];
-  float win[3][3][CH];
+  cell_t raw[3][NCC];
+  float win[3][NCC][CH];
   auto unpack_row = [&](const cell_t *src, float (*dst)[CH]) {
 #pragma unroll
-    for (int e2 = 0; e2 < 3; ++e2)
+    for (int e2 = 0; e2 < NCC; ++e2)
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
         float v[2];
@@ -140,26 +150,31 @@ srem_dwconv_kernel(const unsigned char *x, int64_t x_sb, int64_t x_st, const flo
     const int kd = (k + 1) % 3, ku = (k + 2) % 3;
     unpack_row(raw[kd], win[kd]);   // row u+1 enters the window
     load_row(r0 + u + 4, raw[kd]);  // its raw slot takes row u+4
-    uint32_t out[NW];
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      float acc[2];
+    for (int o = 0; o < NC; ++o) {
+      uint32_t out[NW];
 #pragma unroll
-      for (int e = 0; e < PW; ++e) {
-        const int ch = PW * j + e;
-        float a = 0.f;
+      for (int j = 0; j < NW; ++j) {
+        float acc[2];
 #pragma unroll
-        for (int e2 = 0; e2 < 3; ++e2) {
-          a = fmaf(wr[0 * 3 + e2][ch], win[ku][e2][ch], a);
-          a = fmaf(wr[1 * 3 + e2][ch], win[k][e2][ch], a);
-          a = fmaf(wr[2 * 3 + e2][ch], win[kd][e2][ch], a);
+        for (int e = 0; e < PW; ++e) {
+          const int ch = PW * j + e;
+          float a = 0.f;
+#pragma unroll
+          for (int e2 = 0; e2 < 3; ++e2) {
+            a = fmaf(wr[0 * 3 + e2][ch], win[ku][o + e2][ch], a);
+            a = fmaf(wr[1 * 3 + e2][ch], win[k][o + e2][ch], a);
+            a = fmaf(wr[2 * 3 + e2][ch], win[kd][o + e2][ch], a);
+          }
+          acc[e] = a;
         }
-        acc[e] = a;
+        out[j] = PW == 2 ? pack_bf16x2(acc[0], acc[PW - 1]) : __float_as_uint(acc[0]);
       }
-      out[j] = PW == 2 ? pack_bf16x2(acc[0], acc[PW - 1]) : __float_as_uint(acc[0]);
+      if (c + o < Q) {
+        const int64_t n = n0[o] + (int64_t)u * dn;
+        gstore(yb + n * y_st * ES, out, (cell_t *)nullptr);
+      }
     }
-    const int64_t n = n0 + (int64_t)u * dn;
-    gstore(yb + n * y_st * ES, out, (cell_t *)nullptr);
   };
 
   // three steps per trip: every ring slot is fixed at compile time
@@ -172,6 +187,42 @@ srem_dwconv_kernel(const unsigned char *x, int64_t x_sb, int64_t x_st, const flo
     step(u + 2, 2);
     if (u + 3 >= nrows) break;
   }
+}
+
+// Launch with walkers of NC columns.  The runs of rows are as short as keeps
+// every workgroup resident at once (one round over the CUs, at the occupancy
+// the kernel's registers allow) and at least 8 rows long: a second, partial
+// round leaves most CUs idle while it drains, and shorter runs only add halo
+// rows.
+template <int NW, int PW, int NC>
+hipError_t launch_walkers(const void *x, int B, int T, int C, int64_t x_sb, int64_t x_st,
+                          const float *w, int gh, int gw, int dir, void *y, int64_t y_sb,
+                          int64_t y_st, int num_cu, hipStream_t s) {
+  constexpr int CH = NW * PW, ES = 4 / PW;
+  static int per_cu = 0;   // resident workgroups per CU; the same on every gfx950
+  if (per_cu == 0) {
+    int nb = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, srem_dwconv_kernel<NW, PW, NC>, kNT, 0);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+  }
+  int R, Q;
+  scan_frame(dir, gh, gw, R, Q);
+  const int64_t walkers = (int64_t)((Q + NC - 1) / NC) * (C / CH);   // per batch and run
+  auto grid_x = [&](int64_t n) { return ((walkers * n + kNT - 1) / kNT + 7) / 8 * 8; };
+  const int64_t cap = (int64_t)per_cu * num_cu;
+  const int64_t nmax = (R + 7) / 8;
+  int64_t nseg = 1;
+  while (nseg < nmax && B * grid_x(nseg + 1) <= cap) ++nseg;
+  const int rows = (int)((R + nseg - 1) / nseg);
+  nseg = (R + rows - 1) / rows;
+  const unsigned span = (unsigned)(((int64_t)(T - 1) * x_st + C) * ES);
+  hipLaunchKernelGGL((srem_dwconv_kernel<NW, PW, NC>), dim3(grid_x(nseg), B), dim3(kNT), 0, s,
+                     static_cast<const unsigned char *>(x), x_sb, x_st, w,
+                     static_cast<unsigned char *>(y), y_sb, y_st, B, T, C, gh, gw, dir, rows,
+                     (int)nseg, span);
+  return hipGetLastError();
 }
 
 template <int ES>
@@ -202,31 +253,15 @@ hipError_t dig_launch_dwconv(const void *x, int dtype, int B, int T, int C, int6
                              const float *w, int gh, int gw, int dir, void *y, int64_t y_sb,
                              int64_t y_st, int num_cu, hipStream_t s) {
   using namespace dig;
-  const int CV = C / 4;   // 4 channels per walker
   int R, Q;
   scan_frame(dir, gh, gw, R, Q);
-  // rows per walker: about 18 walker waves per CU (measured best: fewer
-  // leave memory latency exposed, more split the columns into short runs
-  // whose halo rows and start-up cost more than they hide), at least 8 rows
-  const int64_t cols = (int64_t)B * Q * CV;
-  const int64_t want_threads = (int64_t)num_cu * 18 * 64;
-  int64_t nseg = (want_threads + cols / 2) / cols;
-  if (nseg > (R + 7) / 8) nseg = (R + 7) / 8;
-  if (nseg < 1) nseg = 1;
-  const int rows = (int)((R + nseg - 1) / nseg);
-  nseg = (R + rows - 1) / rows;
-  const int64_t per_batch = (int64_t)Q * CV * nseg;
-  const int64_t grid = ((per_batch + kNT - 1) / kNT + 7) / 8 * 8;
-  const unsigned span = (unsigned)(((int64_t)(T - 1) * x_st + C) * (dtype == 1 ? 2 : 4));
-  if (dtype == 1)
-    hipLaunchKernelGGL((srem_dwconv_kernel<2, 2>), dim3(grid, B), dim3(kNT), 0, s,
-                       static_cast<const unsigned char *>(x), x_sb, x_st, w,
-                       static_cast<unsigned char *>(y), y_sb, y_st, B, T, C, gh, gw, dir, rows, (int)nseg, span);
-  else
-    hipLaunchKernelGGL((srem_dwconv_kernel<4, 1>), dim3(grid, B), dim3(kNT), 0, s,
-                       static_cast<const unsigned char *>(x), x_sb, x_st, w,
-                       static_cast<unsigned char *>(y), y_sb, y_st, B, T, C, gh, gw, dir, rows, (int)nseg, span);
-  return hipGetLastError();
+  if (dtype != 1)
+    return launch_walkers<4, 1, 1>(x, B, T, C, x_sb, x_st, w, gh, gw, dir, y, y_sb, y_st, num_cu, s);
+  // bf16: four columns per walker on wide frames; narrow ones keep two so
+  // that there are still enough walkers to cover the CUs
+  if (Q >= 32)
+    return launch_walkers<2, 2, 4>(x, B, T, C, x_sb, x_st, w, gh, gw, dir, y, y_sb, y_st, num_cu, s);
+  return launch_walkers<2, 2, 2>(x, B, T, C, x_sb, x_st, w, gh, gw, dir, y, y_sb, y_st, num_cu, s);
 }
 
 hipError_t dig_launch_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw, int from,

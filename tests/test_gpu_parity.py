@@ -252,6 +252,26 @@ def test_dwconv_vs_oracle(orc, direction, dtype):
     assert_conv_close(y, ref, 1e-2 if dtype == "bf16" else 1e-5)
 
 
+@pytest.mark.parametrize("direction", DIRS)
+def test_dwconv_wide_frame_vs_oracle(orc, direction):
+    """Frames of 37 x 45: at least 32 columns in every scan frame (the
+    four-column walkers), a ragged last column group (37 and 45 are 1 mod 4)
+    and several runs of rows with a ragged last run."""
+    gh, gw, C = 37, 45, 64
+    g = torch.Generator().manual_seed(14)
+    x = torch.randn(2, gh * gw, C, generator=g).to(torch.bfloat16)
+    w = gen.conv_weight(C, 0.3, g)
+    y = dg.srem_dwconv(dev(x), dev(w), (gh, gw), direction).cpu()
+    ref = orc.srem_dwconv(x, w, (gh, gw), direction)
+    assert_conv_close(y, ref, 1e-2)
+    # one tap at a time is a shifted copy: exact at every column-group edge
+    for tap in ((0, 0), (2, 2)):
+        w1 = torch.zeros(C, 3, 3)
+        w1[:, tap[0], tap[1]] = 1.0
+        y1 = dg.srem_dwconv(dev(x), dev(w1), (gh, gw), direction).cpu()
+        assert np.array_equal(to_np(y1), orc.srem_dwconv(x, w1, (gh, gw), direction)), tap
+
+
 @pytest.mark.parametrize("tap", [(0, 0), (0, 1), (1, 2), (2, 2)])
 def test_dwconv_one_hot_tap_exact(orc, tap):
     gh, gw, C = 6, 10, 16
