@@ -21,13 +21,14 @@
 // (batch, head) scan is split into G segments of whole chunks, one workgroup
 // each.  A non-final segment first streams its k, v and gates once to form its
 // state aggregate A_g (its own contribution, from a zero state) and the
-// product of its gates Gam_g, and publishes them.  It then obtains the state
-// entering it by a decoupled look-back: walk back to the nearest segment j
-// that has published its inclusive state P_j (or to the start, s0), then fold
-// forward S = fma(Gam_m, S, A_m) for m = j+1 .. g-1.  The fold always replays
-// the serial recurrence P_m = Gam_m * P_{m-1} + A_m element by element, so the
-// result is bitwise independent of which segments had finished: the output is
-// deterministic.  The segment publishes P_g and then runs the full chunk loop
+// product of its gates Gam_g, and publishes them.  It then waits for the
+// aggregates of all earlier segments (they are computed concurrently, so
+// they arrive together) and folds them forward from s0:
+// S = fma(Gam_m, S, A_m) for m = 0 .. g-1, the serial recurrence
+// P_m = Gam_m * P_{m-1} + A_m element by element in a fixed order, so the
+// output does not depend on timing.  The loads of several aggregates are
+// issued before they are folded, so the fold costs a few memory round trips
+// rather than one per segment.  The segment then runs the full chunk loop
 // from that state, writing o.  With two segments the scan is split in a
 // pipelined way instead (see the kernel): segment 1 aggregates a stretch that
 // segment 0 is still writing and starts from the state segment 0 publishes
@@ -155,6 +156,18 @@ __device__ __forceinline__ float4 ld_coherent(const float *p) {
   v.w = __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return v;
 }
+// The same accesses 16 bytes at a time through a buffer descriptor
+// (cache-policy bit sc1, as the agent-scope atomics above use).
+constexpr int kCohPolicy = 16;
+__device__ __forceinline__ float4 bload_coh(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  const f32x4_t v = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCohPolicy));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void bstore_coh(__amdgpu_buffer_rsrc_t r, unsigned off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                                 __float_as_uint(v.w)},
+                                         r, (int)off, 0, kCohPolicy);
+}
 // Wait until all of this wave's vector-memory operations (loads and stores)
 // have completed.
 __device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -182,10 +195,11 @@ struct Params {
   unsigned qk_span, v_span, o_span;   // bytes addressable in one (batch, head) slice of q/k/g, v, o
   int blk_floats;                  // floats of one published state block
   int *ticket;                     // [8] launch-order ticket counters, one per XCD (reset by the last taker)
-  unsigned *flags;                 // [units][nseg]: epoch*4 + {1 aggregate, 2 inclusive}
+  unsigned *flags;                 // [units][nseg]: epoch*4 + {1 aggregate, 2 split hand-off}
   float *gam;                      // [units][nseg][DP] product of the segment's gates
   float *agg;                      // [units][nseg][blk_floats] aggregate state
-  float *inc;                      // [units][nseg][blk_floats] inclusive state
+  float *inc;                      // [units][nseg][blk_floats]: slot 0 holds the state a
+                                   // two-segment split hands over at chunk L
   unsigned epoch;
 };
 
@@ -326,6 +340,9 @@ gla_fwd_bf16_kernel(Params P) {
   const bool has_cols = !producer && (n0 < dv), has_rows = producer && (n0 < dk);
   const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;   // tiles present in a state block
   const int64_t slot0 = (int64_t)unit * P.nseg;
+  // this scan's published segment aggregates and gate products
+  const __amdgpu_buffer_rsrc_t ragg_ = make_rsrc(P.agg + slot0 * P.blk_floats, (unsigned)(P.nseg * P.blk_floats * 4));
+  const __amdgpu_buffer_rsrc_t rgam_ = make_rsrc(P.gam + slot0 * DP, (unsigned)(P.nseg * DP * 4));
   const int acol = n0 + 4 * g4;             // accumulator-layout channel of this lane (4 channels)
 
   // ---- one-time set-up: e^{b_last} = 1 for channel tiles no wave scans
@@ -762,17 +779,18 @@ gla_fwd_bf16_kernel(Params P) {
       __syncthreads();                                          // B e
     }
     // ================ look-back (the consumers' work) ========================
-    if (seg != 0) __syncthreads();                              // B l
-    if (do_pass1 && P.split_K == 0) __syncthreads();            // B p
-    // ======================= pass 2: outputs ==================================
+    // the first two output chunks' loads are issued before it
     c_begin = out_begin;
     c_end = out_end;
     fill_tok(c_begin);
     fill_tok(c_begin + 1);
     fill_tok(c_begin + 2);
-    __syncthreads();                                            // B s
+    __syncthreads();                                            // B r
     load_chunk(c_begin, true, lsA, 0, 4 * R);
     load_chunk(c_begin + 1, true, lsB, 0, 4 * R);
+    if (seg != 0) __syncthreads();                              // B l
+    // ======================= pass 2: outputs ==================================
+    __syncthreads();                                            // B s
     lds_barrier();                                              // B t
     produce1(c_begin, true, lsA);
     mid_loads(c_begin, true, lsA);
@@ -841,14 +859,14 @@ gla_fwd_bf16_kernel(Params P) {
       lds_barrier();                                            // B loop 2
     }
     if (has_cols && P.split_K == 0) {
-      float *blk = P.agg + (slot0 + seg) * P.blk_floats;
+      const unsigned mb = (unsigned)(seg * P.blk_floats) * 4u;
 #pragma unroll
       for (int r = 0; r < DT; ++r)
-        if (r < DTr) st_coherent(blk + blk_at(r), make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
+        if (r < DTr) bstore_coh(ragg_, mb + (unsigned)blk_at(r) * 4u, make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
       if (wave == 0 && l16 == 0) {
 #pragma unroll
         for (int r = 0; r < DT; ++r)
-          st_coherent(P.gam + (slot0 + seg) * DP + 16 * r + 4 * g4, make_float4(gp[r][0], gp[r][1], gp[r][2], gp[r][3]));
+          bstore_coh(rgam_, (unsigned)(seg * DP + 16 * r + 4 * g4) * 4u, make_float4(gp[r][0], gp[r][1], gp[r][2], gp[r][3]));
       }
     }
     drain_vmem();
@@ -858,79 +876,93 @@ gla_fwd_bf16_kernel(Params P) {
   }
 
   // ================== look-back: state entering the segment ==================
-  f32x4_t Sin[DT];
+  // (the producers meanwhile issue the loads of the first two output chunks)
+  // Each branch leaves the state entering the segment's outputs in S.
+  __syncthreads();                                              // B r
   if (seg == 0) {
-    load_s0(Sin);
-  } else {
-    if (tid == 0) {
-      int j = seg - 1;
-      while (j >= 0) {
-        unsigned f;
-        while (((f = __hip_atomic_load(P.flags + slot0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 2) !=
-               P.epoch)
-          __builtin_amdgcn_s_sleep(2);
-        if ((f & 3u) == 2u) break;
-        --j;
-      }
-      sMisc[2] = j;
-    }
+    load_s0(S);
+  } else if (P.split_K > 0) {
+    // split segment 1: the state segment 0 publishes on its way past chunk L
+    if (tid == 0)
+      while ((__hip_atomic_load(P.flags + slot0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 2) != P.epoch)
+        __builtin_amdgcn_s_sleep(2);
     __syncthreads();                                            // B l
-    const int jstar = sMisc[2];
-    if (jstar >= 0) {
-      const float *blk = P.inc + (slot0 + jstar) * P.blk_floats;
+    // S(L) folded with this segment's aggregate of chunks [L, L+K)
+    const float *blk = P.inc + slot0 * P.blk_floats;
 #pragma unroll
-      for (int r = 0; r < DT; ++r) {
-        const float4 xx = (has_cols && r < DTr) ? ld_coherent(blk + blk_at(r)) : make_float4(0.f, 0.f, 0.f, 0.f);
-        Sin[r] = f32x4_t{xx.x, xx.y, xx.z, xx.w};
-      }
-    } else {
-      load_s0(Sin);
+    for (int r = 0; r < DT; ++r) {
+      const float4 xx = (has_cols && r < DTr) ? ld_coherent(blk + blk_at(r)) : make_float4(0.f, 0.f, 0.f, 0.f);
+      S[r][0] = fmaf(gp[r][0], xx.x, S[r][0]);
+      S[r][1] = fmaf(gp[r][1], xx.y, S[r][1]);
+      S[r][2] = fmaf(gp[r][2], xx.z, S[r][2]);
+      S[r][3] = fmaf(gp[r][3], xx.w, S[r][3]);
     }
+  } else {
+    // Every earlier segment's aggregate: the lanes of wave 0 watch one flag
+    // each.  Then S_in = P_{g-1} of the serial recurrence
+    // P_m = Gam_m * P_{m-1} + A_m from P_{-1} = s0, element by element in
+    // segment order, so the result does not depend on timing.  The loads of
+    // kFoldBatch segments are issued before their folds.
+    if (wave == 0)
+      for (int j = lane; j < seg; j += 64)
+        while ((__hip_atomic_load(P.flags + slot0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 2) != P.epoch)
+          __builtin_amdgcn_s_sleep(2);
+    __syncthreads();                                            // B l
+    load_s0(S);
     if (has_cols) {
-      for (int m = jstar + 1; m < seg; ++m) {
-        const float *blk = P.agg + (slot0 + m) * P.blk_floats;
-        const float *gm_ = P.gam + (slot0 + m) * DP;
+      // segments whose aggregates are loaded before they are folded: 8 DT
+      // registers each, as many as fit beside the rest (measured: no spills)
+      constexpr int kFoldBatch = DT <= 4 ? 4 : DT == 5 ? 3 : 1;
+      if constexpr (DT >= 8) {
+        // 128 channels: sixteen waves of 128 registers; one segment at a time
+        for (int m = 0; m < seg; ++m) {
 #pragma unroll
-        for (int r = 0; r < DT; ++r) {
-          if (r < DTr) {
-            const float4 a = ld_coherent(blk + blk_at(r));
-            const float4 gm = ld_coherent(gm_ + 16 * r + 4 * g4);
-            Sin[r][0] = fmaf(gm.x, Sin[r][0], a.x);
-            Sin[r][1] = fmaf(gm.y, Sin[r][1], a.y);
-            Sin[r][2] = fmaf(gm.z, Sin[r][2], a.z);
-            Sin[r][3] = fmaf(gm.w, Sin[r][3], a.w);
+          for (int r = 0; r < DT; ++r) {
+            if (r < DTr) {
+              const float4 av = bload_coh(ragg_, (unsigned)(m * P.blk_floats + blk_at(r)) * 4u);
+              const float4 gv = bload_coh(rgam_, (unsigned)(m * DP + 16 * r + 4 * g4) * 4u);
+              S[r][0] = fmaf(gv.x, S[r][0], av.x);
+              S[r][1] = fmaf(gv.y, S[r][1], av.y);
+              S[r][2] = fmaf(gv.z, S[r][2], av.z);
+              S[r][3] = fmaf(gv.w, S[r][3], av.w);
+            }
+          }
+        }
+      } else {
+        for (int m0 = 0; m0 < seg; m0 += kFoldBatch) {
+          float4 av[kFoldBatch][DT], gv[kFoldBatch][DT];
+#pragma unroll
+          for (int i = 0; i < kFoldBatch; ++i) {
+            const int m = m0 + i < seg ? m0 + i : seg - 1;
+#pragma unroll
+            for (int r = 0; r < DT; ++r) {
+              av[i][r] = bload_coh(ragg_, r < DTr ? (unsigned)(m * P.blk_floats + blk_at(r)) * 4u : kOOB);
+              gv[i][r] = bload_coh(rgam_, r < DTr ? (unsigned)(m * DP + 16 * r + 4 * g4) * 4u : kOOB);
+            }
+          }
+          // (a select, not a branch, past the last segment: a branch would
+          // let the compiler sink each segment's loads behind the previous fold)
+#pragma unroll
+          for (int i = 0; i < kFoldBatch; ++i) {
+            const bool live = m0 + i < seg;
+#pragma unroll
+            for (int r = 0; r < DT; ++r) {
+              if (r < DTr) {
+                const float x0 = fmaf(gv[i][r].x, S[r][0], av[i][r].x);
+                const float x1 = fmaf(gv[i][r].y, S[r][1], av[i][r].y);
+                const float x2 = fmaf(gv[i][r].z, S[r][2], av[i][r].z);
+                const float x3 = fmaf(gv[i][r].w, S[r][3], av[i][r].w);
+                S[r][0] = live ? x0 : S[r][0];
+                S[r][1] = live ? x1 : S[r][1];
+                S[r][2] = live ? x2 : S[r][2];
+                S[r][3] = live ? x3 : S[r][3];
+              }
+            }
           }
         }
       }
     }
   }
-  if (do_pass1 && P.split_K == 0) {
-    // inclusive state P_g = Gam_g * S_in + A_g
-    if (has_cols) {
-      float *blk = P.inc + (slot0 + seg) * P.blk_floats;
-#pragma unroll
-      for (int r = 0; r < DT; ++r)
-        if (r < DTr)
-          st_coherent(blk + blk_at(r),
-                      make_float4(fmaf(gp[r][0], Sin[r][0], S[r][0]), fmaf(gp[r][1], Sin[r][1], S[r][1]),
-                                  fmaf(gp[r][2], Sin[r][2], S[r][2]), fmaf(gp[r][3], Sin[r][3], S[r][3])));
-    }
-    drain_vmem();
-    __syncthreads();                                            // B p
-    if (tid == 0)
-      __hip_atomic_store(P.flags + slot0 + seg, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (P.split_K > 0 && do_pass1) {
-    // split segment 1: the state entering its outputs is Gam * S(L) + A
-#pragma unroll
-    for (int r = 0; r < DT; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[r][e] = fmaf(gp[r][e], Sin[r][e], S[r][e]);
-  } else {
-#pragma unroll
-    for (int r = 0; r < DT; ++r) S[r] = Sin[r];
-  }
-
   // ========================= pass 2: outputs ==================================
   // Three barrier intervals per chunk c: the producers stage and transform
   // chunk c+1 while the consumers write o of chunk c, then update its state;
