@@ -139,25 +139,10 @@ __device__ __forceinline__ uint2 lds_tr(const uint16_t *p) {
 // 2^x on the transcendental unit (v_exp_f32); results below 2^-126 flush to 0.
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Device-coherent (agent-scope, sc1) accesses for the state hand-off between
-// workgroups: written through to the coherence point and read from it, so no
-// L2 writeback/invalidate fence is needed.
-__device__ __forceinline__ void st_coherent(float *p, float4 v) {
-  __hip_atomic_store(p + 0, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(p + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(p + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(p + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float4 ld_coherent(const float *p) {
-  float4 v;
-  v.x = __hip_atomic_load(p + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  v.y = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  v.z = __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  v.w = __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v;
-}
-// The same accesses 16 bytes at a time through a buffer descriptor
-// (cache-policy bit sc1, as the agent-scope atomics above use).
+// Device-coherent 16-byte accesses for the state hand-off between
+// workgroups: cache-policy bit sc1 (what the compiler emits for agent-scope
+// atomics) writes through to the coherence point and reads from it, so no L2
+// writeback/invalidate fence is needed.
 constexpr int kCohPolicy = 16;
 __device__ __forceinline__ float4 bload_coh(__amdgpu_buffer_rsrc_t r, unsigned off) {
   const f32x4_t v = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCohPolicy));
@@ -343,6 +328,7 @@ gla_fwd_bf16_kernel(Params P) {
   // this scan's published segment aggregates and gate products
   const __amdgpu_buffer_rsrc_t ragg_ = make_rsrc(P.agg + slot0 * P.blk_floats, (unsigned)(P.nseg * P.blk_floats * 4));
   const __amdgpu_buffer_rsrc_t rgam_ = make_rsrc(P.gam + slot0 * DP, (unsigned)(P.nseg * DP * 4));
+  const __amdgpu_buffer_rsrc_t rinc_ = make_rsrc(P.inc + slot0 * P.blk_floats, (unsigned)(P.blk_floats * 4));
   const int acol = n0 + 4 * g4;             // accumulator-layout channel of this lane (4 channels)
 
   // ---- one-time set-up: e^{b_last} = 1 for channel tiles no wave scans
@@ -888,10 +874,9 @@ gla_fwd_bf16_kernel(Params P) {
         __builtin_amdgcn_s_sleep(2);
     __syncthreads();                                            // B l
     // S(L) folded with this segment's aggregate of chunks [L, L+K)
-    const float *blk = P.inc + slot0 * P.blk_floats;
 #pragma unroll
     for (int r = 0; r < DT; ++r) {
-      const float4 xx = (has_cols && r < DTr) ? ld_coherent(blk + blk_at(r)) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 xx = bload_coh(rinc_, has_cols && r < DTr ? (unsigned)blk_at(r) * 4u : kOOB);
       S[r][0] = fmaf(gp[r][0], xx.x, S[r][0]);
       S[r][1] = fmaf(gp[r][1], xx.y, S[r][1]);
       S[r][2] = fmaf(gp[r][2], xx.z, S[r][2]);
@@ -988,26 +973,30 @@ gla_fwd_bf16_kernel(Params P) {
     if (has_cols) outputs(c, S);
     lds_barrier();                                              // B loop 1
     pw_next = live && chunk_pairwise(x);
-    // interval 2: o of chunk c to memory, the state after chunk c
-    store_stage(c);
+    // interval 2: o of chunk c to memory, the state after chunk c.  Split
+    // segment 0 publishes the state entering chunk L: its stores go out
+    // before the o stores, so the wait that orders them before the flag
+    // (raised right after the barrier) does not cover the o stores.
+    const bool pub = c + 1 == publish_at;
+    if (!pub) store_stage(c);
     if (has_cols) {
       state_update(c & 1, S, nullptr, !pw_c);
-      if (c + 1 == publish_at) {   // split segment 0: the state entering chunk L
-        float *blk = P.inc + slot0 * P.blk_floats;
+      if (pub) {
 #pragma unroll
         for (int r = 0; r < DT; ++r)
-          if (r < DTr) st_coherent(blk + blk_at(r), make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
+          if (r < DTr) bstore_coh(rinc_, (unsigned)blk_at(r) * 4u, make_float4(S[r][0], S[r][1], S[r][2], S[r][3]));
         drain_vmem();
       }
     }
+    if (pub) store_stage(c);
     lds_barrier();                                              // B loop 2
+    if (pub && tid == 0)
+      __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // interval 3: P^T tiles of chunk x
     if (live) {
       if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
     }
     lds_barrier();                                              // B loop 3
-    if (c + 1 == publish_at && tid == 0)
-      __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (pw_next) lds_barrier();                                 // B loop 4
     pw_c = pw_next;
   }
@@ -1049,9 +1038,10 @@ int lds_bytes(int DP, int M) {
 }
 
 // aggregate chunks of segment 1 in the two-segment split, as a fraction of
-// the scan (measured best at 64-token chunks; an aggregate chunk costs about
-// 0.45 of an output chunk)
-constexpr float kSplitFrac = 0.40f;
+// the scan (measured best at 64-token chunks: an aggregate chunk costs about
+// half an output chunk, and the hand-off of the state at chunk L takes about
+// one output chunk)
+constexpr float kSplitFrac = 0.38f;
 
 struct Plan {
   int DP, M, nchunks, units, nseg, seg_chunks, per_xcd, grid, blk_floats, split_L, split_K;
