@@ -1,6 +1,7 @@
 /*
  * gla_oracle.c -- plain, slow, fp64 CPU oracle for the DiG token mixer:
- * the Gated Linear Attention (GLA) forward scanned in one SREM direction,
+ * the Gated Linear Attention (GLA) forward scanned in one SREM direction and
+ * its reverse-mode derivative,
  * the 3x3 depthwise conv of the SREM block with its direction remap, and
  * the adaLN modulation that feeds the block.
  *
@@ -176,6 +177,140 @@ int oracle_gla_fwd(const double *q, const double *k, const double *v,
             memcpy(s_final + (b * H + h) * dk * dv, S, (size_t)(dk * dv) * sizeof(double));
         free(S);
         free(a);
+    }
+    free(perm);
+    return failed ? -1 : 0;
+}
+
+/*
+ * GLA backward, token by token, per (batch, head): the gradients of
+ *   L = sum_{p,j} do[b,p,h,j] * o[b,p,h,j] + sum_{i,j} ds_final[b,h,i,j] * S_final[i,j]
+ * with respect to q, k, v, log_alpha and s0, for the forward above.
+ *
+ * Layouts as in oracle_gla_fwd; do is in SCAN order like o, ds_final is
+ * [B, H, dk, dv] (NULL means zero); dq, dk_out, dlog_alpha are [B, T, H, dk]
+ * and dv_out [B, T, H, dv] in canonical token order; ds0 (nullable) is
+ * [B, H, dk, dv].
+ *
+ * Reading: the pages train the model with this operator but print no
+ * backward; this is the plain reverse-mode derivative of the recurrence.
+ * With S_p the state after scan position p (n its canonical token, a its
+ * gate exp(log_alpha)) and G_p = dL/dS_p,
+ *   G_{T-1} = ds_final + q^T do_{T-1},  G_p = q_n^T do_p + diag(a_{p+1}) G_{p+1}
+ *   dq_n[i]        = sum_j S_p[i,j] do_p[j]
+ *   dk_n[i]        = sum_j G_p[i,j] v_n[j]
+ *   dv_n[j]        = sum_i k_n[i] G_p[i,j]
+ *   dlog_alpha_n[i] = a_n[i] * sum_j G_p[i,j] S_{p-1}[i,j]
+ *   ds0            = diag(a_0) G_0
+ * The states S_p are those of the forward, recomputed in blocks of about
+ * sqrt(T) positions from states stored at block starts (the same operations
+ * in the same order, so the same values) to keep memory at O(sqrt(T) d^2).
+ */
+int oracle_gla_bwd(const double *q, const double *k, const double *v,
+                   const double *log_alpha, int64_t B, int64_t T, int64_t H,
+                   int64_t dk, int64_t dv, int64_t gh, int64_t gw, int dir,
+                   const double *s0, const double *do_scan, const double *ds_final,
+                   double *dq, double *dk_out, double *dv_out, double *dlog_alpha,
+                   double *ds0, int nthreads)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (gh <= 0 || gw <= 0 || gh * gw != T) return -1;
+    if (dir < OR_L2R || dir > OR_B2T) return -1;
+
+    int64_t *perm = (int64_t *)malloc((size_t)T * sizeof(int64_t));
+    if (!perm) return -1;
+    oracle_scan_perm(dir, gh, gw, perm);
+
+    int64_t K = 1;
+    while (K * K < T) ++K;                 /* block length ~ sqrt(T) */
+    const int64_t nblk = (T + K - 1) / K;
+    const int64_t dd = dk * dv;
+    const int64_t units = B * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t b = u / H, h = u % H;
+        double *start = (double *)malloc((size_t)(nblk * dd) * sizeof(double)); /* state before each block */
+        double *blk = (double *)malloc((size_t)(K * dd) * sizeof(double));      /* states after each position */
+        double *S = (double *)malloc((size_t)dd * sizeof(double));
+        double *G = (double *)malloc((size_t)dd * sizeof(double));
+        double *a = (double *)malloc((size_t)dk * sizeof(double));
+        if (!start || !blk || !S || !G || !a) {
+            failed = 1;
+            free(start); free(blk); free(S); free(G); free(a);
+            continue;
+        }
+#define TOK(arr, n, d) ((arr) + ((b * T + (n)) * H + h) * (d))
+        /* forward: the state entering every block */
+        if (s0)
+            memcpy(S, s0 + (b * H + h) * dd, (size_t)dd * sizeof(double));
+        else
+            memset(S, 0, (size_t)dd * sizeof(double));
+        for (int64_t p = 0; p < T; ++p) {
+            if (p % K == 0) memcpy(start + (p / K) * dd, S, (size_t)dd * sizeof(double));
+            const int64_t n = perm[p];
+            const double *kn = TOK(k, n, dk), *gn = TOK(log_alpha, n, dk), *vn = TOK(v, n, dv);
+            for (int64_t i = 0; i < dk; ++i) a[i] = exp(gn[i]);
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] = a[i] * S[i * dv + j] + kn[i] * vn[j];
+        }
+        /* backward, block by block from the end */
+        if (ds_final)
+            memcpy(G, ds_final + (b * H + h) * dd, (size_t)dd * sizeof(double));
+        else
+            memset(G, 0, (size_t)dd * sizeof(double));
+        for (int64_t c = nblk - 1; c >= 0; --c) {
+            const int64_t p0 = c * K, p1 = (p0 + K < T) ? p0 + K : T;
+            memcpy(S, start + c * dd, (size_t)dd * sizeof(double));
+            for (int64_t p = p0; p < p1; ++p) {      /* recompute S_p, p in the block */
+                const int64_t n = perm[p];
+                const double *kn = TOK(k, n, dk), *gn = TOK(log_alpha, n, dk), *vn = TOK(v, n, dv);
+                for (int64_t i = 0; i < dk; ++i) a[i] = exp(gn[i]);
+                for (int64_t i = 0; i < dk; ++i)
+                    for (int64_t j = 0; j < dv; ++j)
+                        S[i * dv + j] = a[i] * S[i * dv + j] + kn[i] * vn[j];
+                memcpy(blk + (p - p0) * dd, S, (size_t)dd * sizeof(double));
+            }
+            for (int64_t p = p1 - 1; p >= p0; --p) {
+                const int64_t n = perm[p];
+                const double *qn = TOK(q, n, dk), *kn = TOK(k, n, dk), *gn = TOK(log_alpha, n, dk);
+                const double *vn = TOK(v, n, dv);
+                const double *dop = do_scan + ((b * T + p) * H + h) * dv;
+                const double *Sp = blk + (p - p0) * dd;
+                const double *Sprev = (p > p0) ? blk + (p - 1 - p0) * dd : start + c * dd;
+                for (int64_t i = 0; i < dk; ++i)
+                    for (int64_t j = 0; j < dv; ++j) G[i * dv + j] += qn[i] * dop[j];
+                double *dqn = TOK(dq, n, dk), *dkn = TOK(dk_out, n, dk), *dgn = TOK(dlog_alpha, n, dk);
+                double *dvn = TOK(dv_out, n, dv);
+                for (int64_t i = 0; i < dk; ++i) {
+                    double sq = 0.0, sk = 0.0, sg = 0.0;
+                    for (int64_t j = 0; j < dv; ++j) {
+                        sq += Sp[i * dv + j] * dop[j];
+                        sk += G[i * dv + j] * vn[j];
+                        sg += G[i * dv + j] * Sprev[i * dv + j];
+                    }
+                    dqn[i] = sq;
+                    dkn[i] = sk;
+                    dgn[i] = exp(gn[i]) * sg;
+                }
+                for (int64_t j = 0; j < dv; ++j) {
+                    double sv = 0.0;
+                    for (int64_t i = 0; i < dk; ++i) sv += kn[i] * G[i * dv + j];
+                    dvn[j] = sv;
+                }
+                for (int64_t i = 0; i < dk; ++i) {
+                    const double ai = exp(gn[i]);
+                    for (int64_t j = 0; j < dv; ++j) G[i * dv + j] *= ai;
+                }
+            }
+        }
+        if (ds0) memcpy(ds0 + (b * H + h) * dd, G, (size_t)dd * sizeof(double));
+#undef TOK
+        free(start); free(blk); free(S); free(G); free(a);
     }
     free(perm);
     return failed ? -1 : 0;

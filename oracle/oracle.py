@@ -48,6 +48,9 @@ def _load():
             d, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
             lib.oracle_gla_fwd.argtypes = [d, d, d, d, i64, i64, i64, i64, i64, i64, i64, i32, d, d, d, i32]
             lib.oracle_gla_fwd.restype = i32
+            lib.oracle_gla_bwd.argtypes = [d, d, d, d, i64, i64, i64, i64, i64, i64, i64, i32, d, d, d,
+                                           d, d, d, d, d, i32]
+            lib.oracle_gla_bwd.restype = i32
             lib.oracle_srem_dwconv.argtypes = [d, i64, i64, i64, d, i64, i64, i32, d, i32]
             lib.oracle_srem_dwconv.restype = i32
             lib.oracle_remap.argtypes = [d, i64, i64, i64, i64, i32, i32, d]
@@ -113,6 +116,36 @@ def gla_fwd(q, k, v, log_alpha, grid, direction, s0=None, nthreads: int = 0):
     if rc != 0:
         raise ValueError("oracle_gla_fwd rejected its arguments")
     return o, sf
+
+
+def gla_bwd(q, k, v, log_alpha, grid, direction, do_scan, ds_final=None, s0=None, nthreads: int = 0):
+    """Token-by-token fp64 GLA backward (reverse-mode derivative of gla_fwd).
+
+    do_scan [B, T, H, dv] in scan order (the gradient of o), ds_final
+    [B, H, dk, dv] or None.  Returns (dq, dk, dv, dlog_alpha, ds0) with dq, dk,
+    dlog_alpha [B, T, H, dk] and dv [B, T, H, dv] in canonical token order and
+    ds0 [B, H, dk, dv].
+    """
+    q, k, v, g, dO = _f64(q), _f64(k), _f64(v), _f64(log_alpha), _f64(do_scan)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H) or dO.shape != v.shape:
+        raise ValueError("shape mismatch")
+    s0a = None if s0 is None else _f64(s0)
+    dsf = None if ds_final is None else _f64(ds_final)
+    for a in (s0a, dsf):
+        if a is not None and a.shape != (B, H, dk, dv):
+            raise ValueError("state shape")
+    dq, dkk, dg = (np.empty((B, T, H, dk)) for _ in range(3))
+    dvv = np.empty((B, T, H, dv))
+    ds0 = np.empty((B, H, dk, dv))
+    rc = _load().oracle_gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), B, T, H, dk, dv, grid[0], grid[1],
+                                _dir(direction), None if s0a is None else _ptr(s0a), _ptr(dO),
+                                None if dsf is None else _ptr(dsf), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                                _ptr(dg), _ptr(ds0), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gla_bwd rejected its arguments")
+    return dq, dkk, dvv, dg, ds0
 
 
 def srem_dwconv(x_scan, w, grid, direction, nthreads: int = 0):

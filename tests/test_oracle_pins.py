@@ -330,3 +330,124 @@ def test_pins_reject_planted_mistakes(orc):
     assert _relerr(run("correct"), ref[0, :, 0]) < 1e-12
     for bad in ("read_before_write", "gate_after_write"):
         assert _relerr(run(bad), ref[0, :, 0]) > 1e-3
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd_case(seed, gh=2, gw=3, H=2, dk=3, dv=2):
+    r = np.random.default_rng(seed)
+    T = gh * gw
+    x = _rand(1, T, H, dk, dv, seed=seed, gate_div=2.0)
+    x["s0"] = r.standard_normal((1, H, dk, dv))
+    x["do"] = r.standard_normal((1, T, H, dv))
+    x["dsf"] = r.standard_normal((1, H, dk, dv))
+    return x
+
+
+def _loss(orc, x, grid, direction):
+    o, sf = orc.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], grid, direction, s0=x["s0"])
+    return float(np.sum(o * x["do"]) + np.sum(sf * x["dsf"]))
+
+
+@pytest.mark.parametrize("direction", ["l2r", "r2l", "t2b", "b2t"])
+def test_bwd_finite_differences(orc, direction):
+    """Every gradient element against a central difference of
+    L = sum(do * o) + sum(ds_final * S_final) through the forward oracle."""
+    grid = (2, 3)
+    x = _bwd_case(21)
+    dq, dk, dv, dg, ds0 = orc.gla_bwd(x["q"], x["k"], x["v"], x["log_alpha"], grid, direction,
+                                      x["do"], ds_final=x["dsf"], s0=x["s0"])
+    h = 1e-6
+    for name, grad in (("q", dq), ("k", dk), ("v", dv), ("log_alpha", dg), ("s0", ds0)):
+        fd = np.empty_like(grad)
+        for idx in np.ndindex(grad.shape):
+            base = x[name][idx]
+            x[name][idx] = base + h
+            lp = _loss(orc, x, grid, direction)
+            x[name][idx] = base - h
+            lm = _loss(orc, x, grid, direction)
+            x[name][idx] = base
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def _closed_form_loss_torch(q, k, v, la, s0, do, dsf, perm):
+    """The forward as explicit sums over pairs of scan positions (not the
+    recurrence): o_t = sum_{s<=t} sum_i q_ti k_si e^{beta_ti - beta_si} v_s
+    + sum_i q_ti e^{beta_ti} s0_i, beta the inclusive cumulative log-gate in
+    scan order; S_final likewise.  Returns sum(do * o) + sum(dsf * S_final)."""
+    idx = torch.as_tensor(perm)
+    qs, ks, vs, gs = (t[:, idx] for t in (q, k, v, la))
+    beta = torch.cumsum(gs, dim=1)                                  # [B, T, H, dk]
+    T = qs.shape[1]
+    causal = torch.tril(torch.ones(T, T, dtype=torch.bool))[None, :, :, None, None]
+    diff = beta[:, :, None] - beta[:, None, :]                      # [B, t, s, H, dk]
+    w = torch.exp(torch.where(causal, diff, torch.full_like(diff, -1e300)))
+    P = (qs[:, :, None] * ks[:, None, :] * w).sum(-1)               # [B, t, s, H]
+    o = (P[..., None] * vs[:, None, :]).sum(2) + torch.einsum("bthi,bhij->bthj", qs * torch.exp(beta), s0)
+    wl = torch.exp(beta[:, -1:] - beta)                             # [B, s, H, dk]
+    sf = torch.einsum("bshi,bshj->bhij", ks * wl, vs) + torch.exp(beta[:, -1])[..., None] * s0
+    return (o * do).sum() + (sf * dsf).sum()
+
+
+@pytest.mark.parametrize("direction", ["l2r", "b2t"])
+def test_bwd_autograd_of_closed_form(orc, direction):
+    """The oracle's gradients against torch autograd through the explicit
+    pairwise form of the forward (fp64)."""
+    gh, gw = 3, 4
+    x = _bwd_case(22, gh=gh, gw=gw, H=2, dk=4, dv=3)
+    perm = orc.scan_perm(direction, gh, gw)
+    ts = {n: torch.tensor(x[n], dtype=torch.float64, requires_grad=n in ("q", "k", "v", "log_alpha", "s0"))
+          for n in ("q", "k", "v", "log_alpha", "s0", "do", "dsf")}
+    L = _closed_form_loss_torch(ts["q"], ts["k"], ts["v"], ts["log_alpha"], ts["s0"], ts["do"], ts["dsf"], perm)
+    L.backward()
+    got = orc.gla_bwd(x["q"], x["k"], x["v"], x["log_alpha"], (gh, gw), direction, x["do"],
+                      ds_final=x["dsf"], s0=x["s0"])
+    for name, g in zip(("q", "k", "v", "log_alpha", "s0"), got):
+        assert _relerr(g, ts[name].grad.numpy()) < 1e-12, name
+
+
+def test_bwd_without_final_gradient_and_state(orc):
+    """ds_final = None and s0 = None mean zero: same as passing zeros."""
+    x = _bwd_case(23)
+    z_s = np.zeros_like(x["s0"])
+    a = orc.gla_bwd(x["q"], x["k"], x["v"], x["log_alpha"], (2, 3), "r2l", x["do"])
+    b = orc.gla_bwd(x["q"], x["k"], x["v"], x["log_alpha"], (2, 3), "r2l", x["do"], ds_final=z_s, s0=z_s)
+    for u, w in zip(a, b):
+        np.testing.assert_array_equal(u, w)
+
+
+def test_bwd_pins_reject_planted_mistakes(orc):
+    """Plausible slips in a reverse recurrence must fail the autograd pin."""
+    gh, gw = 3, 4
+    x = _bwd_case(24, gh=gh, gw=gw, H=1, dk=3, dv=2)
+    perm = orc.scan_perm("l2r", gh, gw)
+    ts = {n: torch.tensor(x[n], dtype=torch.float64, requires_grad=n in ("q", "k", "v", "log_alpha", "s0"))
+          for n in ("q", "k", "v", "log_alpha", "s0", "do", "dsf")}
+    _closed_form_loss_torch(ts["q"], ts["k"], ts["v"], ts["log_alpha"], ts["s0"], ts["do"], ts["dsf"],
+                            perm).backward()
+    ref_dg, ref_dk = ts["log_alpha"].grad.numpy()[0, :, 0], ts["k"].grad.numpy()[0, :, 0]
+    a = np.exp(x["log_alpha"][0, :, 0])
+
+    def run(variant):
+        S = [x["s0"][0, 0].copy()]
+        for p in range(12):
+            n = perm[p]
+            S.append(a[n][:, None] * S[-1] + np.outer(x["k"][0, n, 0], x["v"][0, n, 0]))
+        G = x["dsf"][0, 0].copy()
+        dg, dk = np.zeros((12, 3)), np.zeros((12, 3))
+        for p in range(11, -1, -1):
+            n = perm[p]
+            G = G + np.outer(x["q"][0, n, 0], x["do"][0, p, 0])
+            prev = S[p + 1] if variant == "gate_grad_uses_new_state" else S[p]
+            dg[n] = a[n] * (G * prev).sum(1)
+            dk[n] = G @ x["v"][0, n, 0]
+            if variant != "no_gate_on_propagation":
+                G = a[n][:, None] * G
+        return dg, dk
+
+    dg, dk = run("correct")
+    assert _relerr(dg, ref_dg) < 1e-12 and _relerr(dk, ref_dk) < 1e-12
+    for bad in ("gate_grad_uses_new_state", "no_gate_on_propagation"):
+        dg, dk = run(bad)
+        assert max(_relerr(dg, ref_dg), _relerr(dk, ref_dk)) > 1e-3, bad
