@@ -43,6 +43,12 @@ def lib() -> ctypes.CDLL:
             L.gla_fwd.restype = i32
             L.gla_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
             L.gla_fwd_workspace_size.restype = sz
+            L.gla_bwd.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
+                                  i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                  p, p, i64, i64, i64, p, p, p, p, p, p, p, sz, p]
+            L.gla_bwd.restype = i32
+            L.gla_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+            L.gla_bwd_workspace_size.restype = sz
             L.srem_dwconv.argtypes = [p, i32, i32, i32, i32, i64, i64, p, i32, i32, i32, p, i64, i64, p]
             L.srem_dwconv.restype = i32
             L.srem_remap.argtypes = [p, i32, i32, i32, i32, i32, i32, i32, i32, p, p]
@@ -90,13 +96,14 @@ def workspace_bytes(dtype_code: int, B: int, T: int, H: int, dk: int, dv: int, c
     return int(n)
 
 
-def get_workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
+def get_workspace(device: torch.device, nbytes: int, key: str = "fwd") -> torch.Tensor | None:
     """A cached, zero-initialised workspace of at least nbytes for `device` and its current
     stream (grown on demand).  Calls in flight at the same time must not share a workspace,
-    so the cache is per stream."""
+    so the cache is per stream; gla_fwd's (which keeps flags across calls) and gla_bwd's
+    are separate buffers."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
+    key = (key, device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -144,6 +151,51 @@ def gla_fwd(q, k, v, log_alpha, grid, direction, chunk: int = 0, s0=None, out=No
                        _ptr(sf), _ptr(workspace), wsb, _stream(dev))
     _check(rc, "gla_fwd")
     return out, sf
+
+
+def gla_bwd(q, k, v, log_alpha, grid, direction, d_o, chunk: int = 0, s0=None, ds_final=None,
+            need_ds0: bool = True, workspace=None):
+    """Gradients of gla_fwd (bf16): d_o [B, T, H, dv] in SCAN order (the
+    gradient of o), ds_final fp32 [B, H, dk, dv] or None (zero).
+
+    Returns (dq, dk, dv, dlog_alpha, ds0): dq, dk bf16 [B, T, H, dk], dv bf16
+    [B, T, H, dv], dlog_alpha fp32 [B, T, H, dk], all canonical token order;
+    ds0 fp32 [B, H, dk, dv] (None when need_ds0 is False).
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or log_alpha.shape != q.shape or tuple(v.shape[:3]) != (B, T, H):
+        raise DigError("gla_bwd: shape mismatch")
+    if tuple(d_o.shape) != (B, T, H, dv):
+        raise DigError("gla_bwd: d_o must be [B, T, H, dv]")
+    for t in (q, k, v, log_alpha, d_o):
+        if t.stride(3) != 1 or t.dtype != torch.bfloat16 or t.device != q.device:
+            raise DigError("gla_bwd: bf16 tensors on one device with a contiguous last dim")
+    if k.stride() != q.stride() or log_alpha.stride() != q.stride():
+        raise DigError("gla_bwd: q, k, log_alpha must share strides")
+    dev = q.device
+    for name, t in (("s0", s0), ("ds_final", ds_final)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (B, H, dk, dv) or not t.is_contiguous()):
+            raise DigError(f"gla_bwd: {name} must be contiguous fp32 [B, H, dk, dv]")
+    dq = torch.empty(B, T, H, dk, dtype=torch.bfloat16, device=dev)
+    dk_ = torch.empty(B, T, H, dk, dtype=torch.bfloat16, device=dev)
+    dv_ = torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=dev)
+    dg = torch.empty(B, T, H, dk, dtype=torch.float32, device=dev)
+    ds0 = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) if need_ds0 else None
+    if workspace is None:
+        n = lib().gla_bwd_workspace_size(DIG_BF16, B, T, H, dk, dv, chunk)
+        if n == ctypes.c_size_t(-1).value:
+            raise DigError("gla_bwd: invalid sizes: " + lib().dig_last_error().decode(errors="replace"))
+        workspace = get_workspace(dev, n, key="bwd")
+    wsb = workspace.numel() * workspace.element_size()
+    rc = lib().gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), DIG_BF16,
+                       q.stride(0), q.stride(1), q.stride(2), v.stride(0), v.stride(1), v.stride(2),
+                       B, T, H, dk, dv, grid[0], grid[1], _dir(direction), chunk, _ptr(s0),
+                       _ptr(d_o), d_o.stride(0), d_o.stride(1), d_o.stride(2), _ptr(ds_final),
+                       _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(ds0), _ptr(workspace), wsb,
+                       _stream(dev))
+    _check(rc, "gla_bwd")
+    return dq, dk_, dv_, dg, ds0
 
 
 def srem_dwconv(x_scan, w, grid, direction, out=None):

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libdig_gla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gla_bf16.hip", "gla_f32.hip", "srem.hip", "adaln.hip"]
+SOURCES = ["api.cpp", "gla_bf16.hip", "gla_bwd.hip", "gla_f32.hip", "srem.hip", "adaln.hip"]
 HEADERS = ["dig_internal.h", "dig_mfma.h", os.path.join("..", "..", "include", "dig_gla.h")]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-function",

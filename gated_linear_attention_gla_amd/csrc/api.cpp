@@ -84,6 +84,23 @@ int check_gla_sizes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
 
 }  // namespace
 
+namespace {
+int check_bwd_sizes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+  if (dtype != DIG_BF16) return fail(DIG_EINVAL, "gla_bwd: dtype must be DIG_BF16");
+  if (B <= 0 || T <= 0 || H <= 0) return fail(DIG_EINVAL, "gla_bwd: B, T, H must be positive");
+  if (dk < 1 || dk > 128 || dv < 1 || dv > 128)
+    return fail(DIG_EINVAL, "gla_bwd: dk and dv must be in [1, 128] (got %d, %d)", dk, dv);
+  if (dk % 8 || dv % 8) return fail(DIG_EINVAL, "gla_bwd: dk, dv must be multiples of 8");
+  if ((int64_t)B * H > (int64_t)1 << 24) return fail(DIG_EINVAL, "gla_bwd: B*H too large");
+  const int M = dig_gla_bwd_chunk(dk, dv, chunk);
+  if (M != 16 && M != 32 && M != 64) return fail(DIG_EINVAL, "gla_bwd: chunk must be 0, 16, 32 or 64");
+  if (M == 64 && (dk > 80 || dv > 80)) return fail(DIG_EINVAL, "gla_bwd: chunk 64 needs dk, dv <= 80");
+  const int64_t units_chunks = (int64_t)B * H * ((T + M - 1) / M);
+  if (units_chunks >= ((int64_t)1 << 31)) return fail(DIG_EINVAL, "gla_bwd: too many chunks");
+  return DIG_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char *dig_last_error(void) { return g_err.c_str(); }
@@ -155,6 +172,67 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, 
     return DIG_OK;
   } catch (...) {
     return fail(DIG_EHIP, "gla_fwd: unexpected C++ exception");
+  }
+}
+
+
+size_t gla_bwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+  if (check_bwd_sizes(dtype, B, T, H, dk, dv, chunk) != DIG_OK) return (size_t)-1;
+  return dig_gla_bwd_workspace(B, T, H, dk, dv, chunk);
+}
+
+int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+            int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+            int B, int T, int H, int dk, int dv, int gh, int gw, int dir, int chunk,
+            const float *s0, const void *d_o, int64_t do_sb, int64_t do_st, int64_t do_sh,
+            const float *ds_final, void *dq, void *dk_out, void *dv_out, float *dlog_alpha, float *ds0,
+            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    int rc = check_bwd_sizes(dtype, B, T, H, dk, dv, chunk);
+    if (rc) return rc;
+    if (!q || !k || !v || !log_alpha || !d_o || !dq || !dk_out || !dv_out || !dlog_alpha)
+      return fail(DIG_EINVAL, "gla_bwd: q, k, v, log_alpha, d_o, dq, dk, dv and dlog_alpha are required");
+    if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
+      return fail(DIG_EINVAL, "gla_bwd: grid %dx%d does not hold T=%d tokens", gh, gw, T);
+    if (dir < DIG_L2R || dir > DIG_B2T) return fail(DIG_EINVAL, "gla_bwd: dir must be 0..3");
+    if (qk_sb < 0 || qk_st < 0 || qk_sh < 0 || v_sb < 0 || v_st < 0 || v_sh < 0 || do_sb < 0 || do_st < 0 ||
+        do_sh < 0)
+      return fail(DIG_EINVAL, "gla_bwd: negative stride");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(d_o))
+      return fail(DIG_EINVAL, "gla_bwd: q, k, v, log_alpha, d_o must be 16-byte aligned");
+    if ((qk_sb | qk_st | qk_sh | v_sb | v_st | v_sh | do_sb | do_st | do_sh) % 8)
+      return fail(DIG_EINVAL, "gla_bwd: input strides must be multiples of 8 elements");
+    if (((int64_t)(T - 1) * qk_st + dk) * 2 >= ((int64_t)1 << 31) ||
+        ((int64_t)(T - 1) * v_st + dv) * 2 >= ((int64_t)1 << 31) ||
+        ((int64_t)(T - 1) * do_st + dv) * 2 >= ((int64_t)1 << 31))
+      return fail(DIG_EINVAL, "gla_bwd: one (batch, head) slice of an input spans 2 GiB or more");
+    const void *outs[5] = {dq, dk_out, dv_out, dlog_alpha, ds0};
+    const void *ins[5] = {q, k, v, log_alpha, d_o};
+    for (const void *o : outs)
+      for (const void *i : ins)
+        if (o && o == i) return fail(DIG_EINVAL, "gla_bwd: an output aliases an input");
+    DevInfo di;
+    rc = current_device(di);
+    if (rc) return rc;
+    const size_t need = dig_gla_bwd_workspace(B, T, H, dk, dv, chunk);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(DIG_EWORKSPACE, "gla_bwd: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(DIG_EINVAL, "gla_bwd: workspace must be 256-byte aligned");
+    DigGlaBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.dout = d_o;
+    a.qk_sb = qk_sb; a.qk_st = qk_st; a.qk_sh = qk_sh;
+    a.v_sb = v_sb; a.v_st = v_st; a.v_sh = v_sh;
+    a.do_sb = do_sb; a.do_st = do_st; a.do_sh = do_sh;
+    a.s0 = s0; a.ds_final = ds_final;
+    a.dq = dq; a.dk_out = dk_out; a.dv_out = dv_out; a.dlog_alpha = dlog_alpha; a.ds0 = ds0;
+    a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.gh = gh; a.gw = gw; a.dir = dir; a.chunk = chunk;
+    a.workspace = workspace;
+    const hipError_t e = dig_launch_gla_bwd(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "gla_bwd launch");
+    return DIG_OK;
+  } catch (...) {
+    return fail(DIG_EHIP, "gla_bwd: unexpected C++ exception");
   }
 }
 

@@ -87,6 +87,19 @@ struct DigGlaArgs {
 hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s);
 size_t dig_gla_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk, int num_cu);
 hipError_t dig_launch_gla_f32(const DigGlaArgs &a, hipStream_t s);
+
+struct DigGlaBwdArgs {
+  const void *q, *k, *v, *g, *dout;
+  int64_t qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, do_sb, do_st, do_sh;
+  const float *s0, *ds_final;
+  void *dq, *dk_out, *dv_out;
+  float *dlog_alpha, *ds0;
+  int B, T, H, dk, dv, gh, gw, dir, chunk;
+  void *workspace;
+};
+hipError_t dig_launch_gla_bwd(const DigGlaBwdArgs &a, hipStream_t s);
+size_t dig_gla_bwd_workspace(int B, int T, int H, int dk, int dv, int chunk);
+int dig_gla_bwd_chunk(int dk, int dv, int chunk);
 size_t dig_gla_f32_lds_bytes(int dk, int dv, int chunk);
 
 hipError_t dig_launch_dwconv(const void *x, int dtype, int B, int T, int C, int64_t x_sb, int64_t x_st,

@@ -5,6 +5,7 @@
  * The library computes the token mixer of a DiG block on one GPU:
  *   gla_fwd       chunk-wise Gated Linear Attention forward, scanned in one
  *                 of four SREM directions, output in scan order + final state;
+ *   gla_bwd       its gradients (training);
  *   srem_dwconv   3x3 depthwise conv in the scan frame, stored back to the
  *                 canonical token order (the fused direction remap);
  *   srem_remap    the exact permutation between two scan orders;
@@ -137,6 +138,57 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
  * ticket counter).  Returns 0 when no workspace is needed; (size_t)-1 for
  * invalid sizes. */
 size_t gla_fwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+
+/*
+ * gla_bwd -- gradients of gla_fwd (bf16 path) for training.
+ *
+ * With L a scalar loss, d_o = dL/do ([B, T, H, dv], SCAN order like o) and
+ * ds_final = dL/dS_final, returns dL/dq, dL/dk, dL/dv, dL/dlog_alpha and
+ * dL/ds0 of the forward with the same q, k, v, log_alpha, grid, dir and s0.
+ * (The DiG paper notes train with this operator, 关键设计 / 硬件友好的效率设计;
+ * the gradients are the reverse-mode derivative of the recurrence above:
+ * G_p = q_p^T do_p + diag(alpha_{p+1}) G_{p+1}, dq_p = S_p do_p^T,
+ * dk_p = G_p v_p^T, dv_p = k_p G_p, dlog_alpha_p = alpha_p * rowsum(G_p .
+ * S_{p-1}), ds0 = diag(alpha_0) G_0.)  It runs chunk-wise: a forward and a
+ * reverse scan over the chunk boundaries (states and state gradients, kept
+ * in the workspace as bf16), then every chunk independently on bf16 MFMA
+ * with fp32 accumulation; chunks whose gates are too strong for the
+ * factorised exponentials are evaluated with exact exponent differences.
+ *
+ * Arguments
+ *   q, k, log_alpha, v, strides, B, T, H, dk, dv, gh, gw, dir, s0: as gla_fwd;
+ *                    dtype must be DIG_BF16 (the only path).
+ *   chunk            0 = automatic (64, or 32 when dk or dv exceeds 80); else
+ *                    16, 32 or 64 (64 only for dk, dv <= 80).  Rounding only.
+ *   d_o              bf16 [B, T, H, dv] in SCAN order, strides (do_sb, do_st,
+ *                    do_sh), multiples of 8, 16-byte aligned.
+ *   ds_final         nullable (zero); fp32 [B, H, dk, dv] contiguous.
+ *   dq, dk_out       bf16 [B, T, H, dk] contiguous, CANONICAL token order.
+ *   dv_out           bf16 [B, T, H, dv] contiguous, canonical order.
+ *   dlog_alpha       fp32 [B, T, H, dk] contiguous, canonical order.
+ *   ds0              nullable; fp32 [B, H, dk, dv] contiguous.
+ *   workspace        at least gla_bwd_workspace_size(...) bytes, 256-byte
+ *                    aligned (no zero-filling needed); not shared by two
+ *                    calls in flight at once.
+ * Outputs must not overlap the inputs or each other.  Constraints as for the
+ * bf16 gla_fwd.
+ */
+int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+            int dtype,
+            int64_t qk_sb, int64_t qk_st, int64_t qk_sh,
+            int64_t v_sb, int64_t v_st, int64_t v_sh,
+            int B, int T, int H, int dk, int dv,
+            int gh, int gw, int dir, int chunk,
+            const float *s0,
+            const void *d_o, int64_t do_sb, int64_t do_st, int64_t do_sh,
+            const float *ds_final,
+            void *dq, void *dk_out, void *dv_out, float *dlog_alpha, float *ds0,
+            void *workspace, size_t workspace_bytes,
+            hipStream_t stream);
+
+/* Bytes of workspace gla_bwd needs for these sizes ((size_t)-1 for invalid
+ * sizes or dtypes). */
+size_t gla_bwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk);
 
 /*
  * srem_dwconv -- SREM 3x3 depthwise conv with the direction remap fused in.

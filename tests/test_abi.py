@@ -109,3 +109,32 @@ def test_binding_raises_on_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(binding.DigError):
         binding.lib()
+
+
+def _bwd(L, **kw):
+    a = dict(q=16, k=32, v=48, g=64, dtype=1, qk=(4096 * 8 * 8, 64, 8), vs=(4096 * 8 * 8, 64, 8),
+             B=1, T=64, H=8, dk=8, dv=8, gh=8, gw=8, dir=0, chunk=0, s0=None, do=80,
+             dos=(4096 * 8 * 8, 64, 8), dsf=None, dq=96, dk_=112, dv_=128, dg=144, ds0=None, ws=None, wsb=0)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.gla_bwd(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), a["dtype"], *a["qk"], *a["vs"],
+                     a["B"], a["T"], a["H"], a["dk"], a["dv"], a["gh"], a["gw"], a["dir"], a["chunk"],
+                     p(a["s0"]), p(a["do"]), *a["dos"], p(a["dsf"]), p(a["dq"]), p(a["dk_"]), p(a["dv_"]),
+                     p(a["dg"]), p(a["ds0"]), p(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(q=None), dict(do=None), dict(dq=None), dict(dg=None), dict(dtype=0), dict(B=0), dict(dk=0),
+    dict(dv=136), dict(dk=12, dv=12), dict(gh=7), dict(dir=4), dict(chunk=48), dict(dk=96, dv=96, chunk=64),
+    dict(q=18), dict(do=88), dict(dos=(4096 * 64, 60, 8)), dict(qk=(-8, 64, 8)), dict(dq=16),
+])
+def test_bwd_rejects_bad_arguments(L, bad):
+    rc = _bwd(L, **bad)
+    assert rc == binding.DIG_EINVAL if hasattr(binding, "DIG_EINVAL") else rc == -1, bad
+    assert L.dig_last_error()
+
+
+def test_bwd_workspace_size(L):
+    n = L.gla_bwd_workspace_size(1, 8, 4096, 16, 72, 72, 0)
+    assert n == 3 * 8 * 16 * 64 * 80 * 80 * 2          # three bf16 [units][chunks][80][80] state sets
+    assert L.gla_bwd_workspace_size(0, 8, 4096, 16, 72, 72, 0) == ctypes.c_size_t(-1).value
