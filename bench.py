@@ -48,6 +48,20 @@ def gla_alg_flops(cfg, M=64) -> int:
     return cfg.B * cfg.H * cfg.T * (4 * M * cfg.d + 4 * cfg.d * cfg.d)
 
 
+def bwd_alg_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one gla_bwd call: read q, k, v, log_alpha, do (bf16), write dq, dk,
+    dv (bf16) and dlog_alpha (fp32).  The chunk states the implementation keeps in its workspace
+    are not counted."""
+    return cfg.B * cfg.H * cfg.T * cfg.d * (5 * 2 + 3 * 2 + 4)
+
+
+def bwd_alg_flops(cfg, M=64) -> int:
+    """Chunk-form algorithmic flops per token and head: the two M x M products (dO V^T, Q~K~^T),
+    the three token-contracting products (A K~, A^T Q~, P^T dO) and the state terms (dO S^T,
+    V D^T, K^ D, K^^T V, and the two scans' X^T Y): 2 * (2 M d + 3 M d + 6 d^2)."""
+    return cfg.B * cfg.H * cfg.T * 2 * (5 * M * cfg.d + 6 * cfg.d * cfg.d)
+
+
 def conv_alg_bytes(cfg) -> int:
     el = 2 if cfg.dtype == "bf16" else 4
     return 2 * cfg.B * cfg.T * cfg.C * el + cfg.C * 9 * 4
@@ -119,6 +133,122 @@ def cpu_baseline(cfg, x_cpu, budget_s: float = 20.0):
                   f"({'adaLN + ' if cfg.adaln else ''}GLA fwd + conv, dir {direction}, fp64, "
                   f"{threads} OpenMP threads): {tp:.2f} s, scaled to the whole batch",
     }
+
+
+def cpu_baseline_bwd(cfg, x_cpu, do_cpu, budget_s: float = 20.0):
+    """The fp64 oracle's backward on a bounded sample of (b, h) units, scaled to tokens/s of the
+    whole batch."""
+    from oracle import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    units = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    direction = cfg.direction(0)
+    grid = (cfg.gh, cfg.gw)
+
+    def run(sample):
+        t0 = time.perf_counter()
+        for b in sorted({b for b, _ in sample}):
+            hs = [h for bb, h in sample if bb == b]
+            sl = lambda t: t[b:b + 1][:, :, hs].contiguous()
+            oracle.gla_bwd(sl(x_cpu["q"]), sl(x_cpu["k"]), sl(x_cpu["v"]), sl(x_cpu["log_alpha"]), grid,
+                           direction, sl(do_cpu), nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe = units[:min(len(units), threads)]
+    tp = run(probe)
+    n = len(probe)
+    if tp < budget_s / 4 and n < len(units):
+        want = int(n * (budget_s * 0.6) / max(tp, 1e-3) / threads) * threads
+        want = max(n, min(len(units), want))
+        if want > n:
+            tp = run(units[:want])
+            n = want
+    est_full = tp * len(units) / n
+    return {"value": cfg.B * cfg.T / est_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {len(units)} (batch, head) units of {cfg.key} (GLA backward, dir "
+                      f"{direction}, fp64, {threads} OpenMP threads): {tp:.2f} s, scaled to the whole batch"}
+
+
+def bench_bwd(a, dg, gen, torch) -> int:
+    """gla_bwd on the workload's shape: one step = one backward call (three launches on one
+    stream: forward state scan, reverse state-gradient scan, chunk gradients) over rotating
+    input sets, timed with HIP events on that stream."""
+    dev = torch.device("cuda:0")
+    cfg = gen.CONFIGS[a.config]
+    if cfg.adaln:
+        print("bench.py --bwd: the backward bench runs the GLA-only workloads (C1, C2, C3)", file=sys.stderr)
+        return 2
+    B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.d
+    grid = (cfg.gh, cfg.gw)
+    chunk = a.chunk or cfg.chunk
+    per_set = B * T * H * d * 2 * 5
+    nsets = a.sets or max(1, math.ceil(512e6 / per_set))
+    log(f"[bench] gla_bwd {cfg.key} {cfg.name}: B={B} H={H} T={T} ({cfg.gh}x{cfg.gw}) d={d}; {nsets} input sets")
+    gen_do = torch.Generator(device=dev)
+    sets = []
+    for i in range(nsets):
+        x = gen.make_inputs(cfg.key, set_index=i, device=dev)
+        gen_do.manual_seed(cfg.seed + 4409 * (i + 1))
+        do = torch.randn(B, T, H, d, generator=gen_do, device=dev).to(torch.bfloat16)
+        sets.append((x, do))
+    nbytes = dg.lib().gla_bwd_workspace_size(dg.DIG_BF16, B, T, H, d, d, chunk)
+    ws = dg.get_workspace(dev, nbytes, key="bwd")
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        x, do = sets[i % nsets]
+        dg.gla_bwd(x["q"], x["k"], x["v"], x["log_alpha"], grid, cfg.direction(i), do, chunk=chunk,
+                   need_ds0=False, workspace=ws)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = []
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(a.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(a.warmup + i)
+        e1.record(stream)
+        evs.append((e0, e1))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / a.steps
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    avg = sum(ms) / len(ms)
+    abytes, aflops = bwd_alg_bytes(cfg), bwd_alg_flops(cfg, chunk)
+    achieved = abytes / (avg * 1e-3) / 1e9
+    log(f"[bench] gla_bwd avg {avg * 1e3:.1f} us (median {ms[len(ms) // 2] * 1e3:.1f}), {achieved:.0f} GB/s alg, "
+        f"{aflops / (avg * 1e-3) / 1e12:.1f} TFLOP/s alg")
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle backward on a bounded sample ...")
+        x0, do0 = sets[0]
+        x_cpu = {k_: v_.cpu() for k_, v_ in x0.items() if isinstance(v_, torch.Tensor)}
+        cpu = cpu_baseline_bwd(cfg, x_cpu, do0.cpu())
+        log(f"[bench] cpu oracle bwd: {cpu['value']:.3e} tokens/s on {cpu['cores']} cores")
+    rec = {
+        "metric": "GLA bwd tokens/sec (training backward), DiG-XL/2 shape T=4096 d=72",
+        "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian activations and output gradients of the DiG latent-grid shape)",
+        "config": {"workload": f"{cfg.key} {cfg.name}: GLA backward (chunk {chunk}; dq, dk, dv, dlog_alpha)",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "grid": list(grid),
+                   "directions": list(cfg.dirs), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gla_bwd (gla_bwd_scan x2 + gla_bwd_chunk)", "alg_bytes_per_launch": abytes,
+                     "avg_launch_us": avg * 1e3},
+        "gla_bwd": {"tflops_alg": aflops / (avg * 1e-3) / 1e12,
+                    "mfma_frac": aflops / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "median_us": ms[len(ms) // 2] * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 COPY_PROBE_BYTES = 256 << 20   # the plain copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
@@ -204,6 +334,7 @@ def main(argv=None) -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 512 MB)")
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = the workload's, 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd", action="store_true", help="time gla_bwd (the training backward) instead")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the launches the PMC passes count: 3 plain copies, 3 gla_fwd")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
@@ -229,6 +360,8 @@ def main(argv=None) -> int:
     dg.lib()
     if a.traffic_probe:
         return traffic_probe(a.config, a.chunk)
+    if a.bwd:
+        return bench_bwd(a, dg, gen, torch)
     dev = torch.device("cuda:0")
     cfg = gen.CONFIGS[a.config]
     B, T, H, d, C = cfg.B, cfg.T, cfg.H, cfg.d, cfg.C
