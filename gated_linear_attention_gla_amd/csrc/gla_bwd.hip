@@ -68,6 +68,37 @@ __device__ __forceinline__ uint2 gload8(const uint16_t *p) {
   return make_uint2(v.x, v.y);
 }
 
+// Inclusive sum over the chunk's tokens of a token-major bf16 tile (rows =
+// tokens, columns = channels) for token tile I and channel tile r, on MFMA
+// with a lower-triangular matrix of ones (bf16 values times 1.0 are exact,
+// the sum is fp32).  Result in accumulator layout: rows t = 16 I + 4 (l/16)
+// + e, channel 16 r + l%16.
+template <int MT, int QS>
+__device__ __forceinline__ f32x4_t tile_cumsum(const uint16_t *tg, int I, int r, int l16, int g4) {
+  constexpr int JP = (MT + 1) / 2;
+  const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
+  const int t = 16 * I + l16;   // this lane's row of the ones matrix
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jp = 0; jp < JP; ++jp) {
+    if (32 * jp > 16 * I + 15) break;
+    const bool hi_ok = 2 * jp + 1 < MT;
+    uint32_t w[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int s0 = 32 * jp + 16 * h + 4 * g4;   // K slots 4h .. 4h+3: tokens s0 .. s0+3
+      const uint32_t o0 = (s0 + 0 <= t) ? 0x3f80u : 0u, o1 = (s0 + 1 <= t) ? 0x3f80u : 0u;
+      const uint32_t o2 = (s0 + 2 <= t) ? 0x3f80u : 0u, o3 = (s0 + 3 <= t) ? 0x3f80u : 0u;
+      w[2 * h] = o0 | (o1 << 16);
+      w[2 * h + 1] = o2 | (o3 << 16);
+    }
+    const uint2 lo = lds_tr(tg + (32 * jp + 4 * g4 + rowoff) * QS + 16 * r + coloff);
+    const uint2 hi = hi_ok ? lds_tr(tg + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * r + coloff) : make_uint2(0, 0);
+    acc = mfma32(make_uint4(w[0], w[1], hi_ok ? w[2] : 0u, hi_ok ? w[3] : 0u), cat(lo, hi), acc);
+  }
+  return acc;
+}
+
 // ============================== state scans ==================================
 // One workgroup per (batch, head); wave w holds value columns 16w .. 16w+15 of
 // the dk x dv state in its accumulators (rows 16 r + 4 (l/16) + e, column
@@ -84,7 +115,6 @@ gla_bwd_scan(BwdParams P) {
   uint16_t *tG = tX + M * QS;
   uint16_t *tY = tG + M * QS;
   float *gam = reinterpret_cast<float *>(tY + M * QS);   // [DP] e^{B}
-  int *tok = reinterpret_cast<int *>(gam + DP);           // [M] canonical token, -1 past T
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
   const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
@@ -107,6 +137,27 @@ gla_bwd_scan(BwdParams P) {
       Z[r][e] = (z0 && i < dk && j < dv) ? z0[((int64_t)unit * dk + i) * dv + j] : 0.f;
     }
 
+  // chunk rows go global -> registers (one chunk ahead) -> LDS
+  constexpr int IT = (M * CG + NT - 1) / NT;
+  uint4 px[IT], pg[IT], py[IT];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int kq = 0; kq < IT; ++kq) {
+      const int idx = tid + kq * NT;
+      const int tl = idx / CG, cg = idx - tl * CG;
+      const int p = c * M + tl;
+      const bool ok = idx < M * CG && p < T;
+      const int n = ok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
+      const int64_t yrow = REV ? (int64_t)p : n;
+      const unsigned oxg = (ok && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
+      const unsigned oy = (ok && 8 * cg < dv) ? (unsigned)((yrow * y_st + 8 * cg) * 2) : kOOB;
+      px[kq] = bload16(rx, oxg);
+      pg[kq] = bload16(rg, oxg);
+      py[kq] = bload16(ry, oy);
+    }
+  };
+  fetch(REV ? N - 1 : 0);
+
   for (int it = 0; it < N; ++it) {
     const int c = REV ? N - 1 - it : it;
     // the state for chunk c, bf16, padding included (it is zero)
@@ -119,35 +170,35 @@ gla_bwd_scan(BwdParams P) {
       if (REV) *reinterpret_cast<uint2 *>(P.st_dt + blk + (n0 + l16) * DP + 16 * r + 4 * g4) = pack4(Z[r]);
     }
     // chunk c's rows into LDS (zeros past T and in the channel padding)
-    if (tid < M) {
-      const int p = c * M + tid;
-      tok[tid] = p < T ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < M * CG; idx += NT) {
-      const int tl = idx / CG, cg = idx - tl * CG;
-      const int n = tok[tl];
-      const int64_t yrow = REV ? (int64_t)c * M + tl : n;
-      const unsigned oxg = (n >= 0 && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
-      const unsigned oy = (n >= 0 && 8 * cg < dv) ? (unsigned)((yrow * y_st + 8 * cg) * 2) : kOOB;
-      *reinterpret_cast<uint4 *>(tX + tl * QS + 8 * cg) = bload16(rx, oxg);
-      *reinterpret_cast<uint4 *>(tG + tl * QS + 8 * cg) = bload16(rg, oxg);
-      *reinterpret_cast<uint4 *>(tY + tl * QS + 8 * cg) = bload16(ry, oy);
-    }
-    __syncthreads();
-    // cumulative gates per key channel; X scaled in place by e^{B - b}
-    // (forward) or e^{b} (reverse), both <= 1
-    if (tid < DP) {
-      const int i = tid;
-      float tot = 0.f;
-      for (int t = 0; t < M; ++t) tot += bf_at(tG + t * QS + i);
-      float run = 0.f;
-      for (int t = 0; t < M; ++t) {
-        run += bf_at(tG + t * QS + i);
-        const float f = fexp2((REV ? run : tot - run) * kLog2e);
-        tX[t * QS + i] = to_bf(bf_at(tX + t * QS + i) * f);
+#pragma unroll
+    for (int kq = 0; kq < IT; ++kq) {
+      const int idx = tid + kq * NT;
+      if (idx < M * CG) {
+        const int tl = idx / CG, cg = idx - tl * CG;
+        *reinterpret_cast<uint4 *>(tX + tl * QS + 8 * cg) = px[kq];
+        *reinterpret_cast<uint4 *>(tG + tl * QS + 8 * cg) = pg[kq];
+        *reinterpret_cast<uint4 *>(tY + tl * QS + 8 * cg) = py[kq];
       }
-      gam[i] = fexp2(tot * kLog2e);
+    }
+    __syncthreads();
+    if (it + 1 < N) fetch(REV ? c - 1 : c + 1);
+    // cumulative gates of key-channel tile `wave`; X scaled in place by
+    // e^{B - b} (forward) or e^{b} (reverse), both <= 1
+    {
+      f32x4_t cum[MT];
+#pragma unroll
+      for (int I = 0; I < MT; ++I) cum[I] = tile_cumsum<MT, QS>(tG, I, wave, l16, g4);
+      const float tot = __shfl(cum[MT - 1][3], 48 + l16, 64);   // token M-1: lane group 3, e = 3
+      const int i = n0 + l16;
+#pragma unroll
+      for (int I = 0; I < MT; ++I)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * I + 4 * g4 + e;
+          const float f = fexp2((REV ? cum[I][e] : tot - cum[I][e]) * kLog2e);
+          tX[t * QS + i] = to_bf(bf_at(tX + t * QS + i) * f);
+        }
+      if (g4 == 0) gam[i] = fexp2(tot * kLog2e);
     }
     __syncthreads();
     // Z = diag(e^{B}) Z + X^T Y, K = the chunk's tokens (transposing reads)
@@ -197,7 +248,8 @@ struct BwdLds {
   static constexpr int oA = oB + M * DP * 4;            // [M][SA] bf16 A = dO V^T (causal)
   static constexpr int oP = oA + M * SA * 2;            // [M][SA] bf16 P (causal)
   static constexpr int oR = oP + M * SA * 2;            // [M][DP] fp32 q dq - k dk (extreme: dk sums first)
-  static constexpr int oGam = oR + M * DP * 4;          // [DP] e^{B}
+  static constexpr int oBt = oR + M * DP * 4;           // [DP] B (log2 units)
+  static constexpr int oGam = oBt + DP * 4;             // [DP] e^{B}
   static constexpr int oSuf = oGam + DP * 4;            // [DP/16][DP] rowsum(S_out (.) D), per column tile
   static constexpr int oTok = oSuf + (DP / 16) * DP * 4;   // [M] canonical token, -1 past T
   static constexpr int oFlag = oTok + M * 4;            // bit pattern of max |b|
@@ -225,6 +277,7 @@ gla_bwd_chunk(BwdParams P) {
   float *E1 = reinterpret_cast<float *>(smem + L::oQt);   // extreme chunks only
   float *R = reinterpret_cast<float *>(smem + L::oR);
   float *gam = reinterpret_cast<float *>(smem + L::oGam), *suf = reinterpret_cast<float *>(smem + L::oSuf);
+  float *Bt = reinterpret_cast<float *>(smem + L::oBt);
   int *tok = reinterpret_cast<int *>(smem + L::oTok);
   unsigned *flag = reinterpret_cast<unsigned *>(smem + L::oFlag);
 
@@ -264,25 +317,32 @@ gla_bwd_chunk(BwdParams P) {
   }
   __syncthreads();
 
-  // ---- 2. cumulative gates (log2 units) and the scaled rows
-  if (tid < DP) {
-    const int i = tid;
-    float run = 0.f, mx = 0.f;
-    for (int t = 0; t < M; ++t) {
-      run += bf_at(tKh + t * QS + i) * kLog2e;
-      bL[t * DP + i] = run;
-      mx = fmaxf(mx, fabsf(run));
+  // ---- 2. cumulative gates (log2 units; ones-triangle MFMA over the gate
+  //         tile) and the scaled rows
+  for (int tt = wave; tt < MT * DT; tt += kChunkWaves) {
+    const int I = tt / DT, r = tt - I * DT;
+    const f32x4_t cum = tile_cumsum<MT, QS>(tKh, I, r, l16, g4);
+    const int i = 16 * r + l16;
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float b = cum[e] * kLog2e;
+      bL[(16 * I + 4 * g4 + e) * DP + i] = b;
+      mx = fmaxf(mx, fabsf(b));
     }
-    if (!(mx <= kBwdFastRange)) atomicOr(flag, 1u);   // NaN / inf too
-    gam[i] = fexp2(run);
-    for (int t = 0; t < M; ++t) {
-      const float b = bL[t * DP + i];
-      const float q = bf_at(tQ + t * QS + i), k = bf_at(tK + t * QS + i);
-      tQt[t * QS + i] = to_bf(q * fexp2(b));
-      tKt[t * QS + i] = to_bf(k * fexp2(-b));
-      tKh[t * QS + i] = to_bf(k * fexp2(run - b));
-    }
+    if (I == MT - 1 && g4 == 3) Bt[i] = cum[3] * kLog2e;   // token M-1
+    if (!(mx <= kBwdFastRange)) atomicOr(flag, 1u);          // NaN / inf too
   }
+  __syncthreads();
+  for (int x = tid; x < M * DP; x += NT) {
+    const int t = x / DP, i = x - t * DP;
+    const float b = bL[x], B = Bt[i];
+    const float q = bf_at(tQ + t * QS + i), k = bf_at(tK + t * QS + i);
+    tQt[t * QS + i] = to_bf(q * fexp2(b));
+    tKt[t * QS + i] = to_bf(k * fexp2(-b));
+    tKh[t * QS + i] = to_bf(k * fexp2(B - b));
+  }
+  if (tid < DP) gam[tid] = fexp2(Bt[tid]);
   __syncthreads();
   const bool fast = *flag == 0u;
 
