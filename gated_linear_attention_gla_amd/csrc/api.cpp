@@ -228,6 +228,7 @@ int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha, 
     a.dq = dq; a.dk_out = dk_out; a.dv_out = dv_out; a.dlog_alpha = dlog_alpha; a.ds0 = ds0;
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.gh = gh; a.gw = gw; a.dir = dir; a.chunk = chunk;
     a.workspace = workspace;
+    a.num_cu = di.num_cu;
     const hipError_t e = dig_launch_gla_bwd(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gla_bwd launch");
     return DIG_OK;

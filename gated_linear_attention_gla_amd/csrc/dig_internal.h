@@ -96,6 +96,7 @@ struct DigGlaBwdArgs {
   float *dlog_alpha, *ds0;
   int B, T, H, dk, dv, gh, gw, dir, chunk;
   void *workspace;
+  int num_cu;   // compute units of the device (the chunk kernel's persistent grid)
 };
 hipError_t dig_launch_gla_bwd(const DigGlaBwdArgs &a, hipStream_t s);
 size_t dig_gla_bwd_workspace(int B, int T, int H, int dk, int dv, int chunk);

@@ -26,12 +26,13 @@
 // Three launches:
 //   gla_bwd_scan<.., false>  S_in of every chunk (forward over chunks);
 //   gla_bwd_scan<.., true>   D of every chunk (reverse over chunks), and ds0;
-//   gla_bwd_chunk            every chunk independently: dq, dk, dv, dlog_alpha.
-// The scans use only factors e^{B - b} and e^{b} (<= 1 for gates <= 0).  The
-// chunk kernel factorises e^{b_t - b_s} as e^{b_t} e^{-b_s} when every |b| of
-// the chunk is within 2^64 in log2 units (the forward's bound); other chunks
-// evaluate the decayed intra-chunk sums with exact exponent differences on
-// the vector ALUs.
+//   gla_bwd_chunk            the chunks, independently: dq, dk, dv, dlog_alpha.
+// Both state sets are kept transposed ([value channel j][key channel i],
+// bf16).  The scans use only factors e^{B - b} and e^{b} (<= 1 for gates <=
+// 0).  The chunk kernel factorises e^{b_t - b_s} as e^{b_t} e^{-b_s} when
+// every |b| of the chunk is within 2^64 in log2 units (the forward's bound);
+// other chunks evaluate the decayed intra-chunk sums with exact exponent
+// differences on the vector ALUs.
 #include "dig_mfma.h"
 
 namespace dig {
@@ -47,9 +48,8 @@ struct BwdParams {
   uint16_t *gq, *gk, *gv;   // dq, dk, dv: [B, T, H, dk | dv] contiguous, canonical order
   float *dg;                // [B, T, H, dk] contiguous, canonical order
   float *ds0;               // nullable [B, H, dk, dv]
-  uint16_t *st_s;           // [units][N][DP][DP] bf16: state entering chunk c
-  uint16_t *st_d;           // [units][N][DP][DP] bf16: gradient of the state leaving chunk c
-  uint16_t *st_dt;          // the same, transposed ([j][i])
+  uint16_t *st_s;           // [units][N][DP (j)][DP (i)] bf16: state entering chunk c, transposed
+  uint16_t *st_d;           // the same layout: gradient of the state leaving chunk c
   int B, T, H, dk, dv, gh, gw, dir, nchunks;
   unsigned qk_span, v_span, do_span;   // bytes addressable in one (batch, head) slice
 };
@@ -63,10 +63,10 @@ struct BwdRow {
 
 __device__ __forceinline__ float bf_at(const uint16_t *p) { return __uint_as_float((uint32_t)(*p) << 16); }
 __device__ __forceinline__ uint16_t to_bf(float x) { return (uint16_t)f2bf(x); }
-__device__ __forceinline__ uint2 gload8(const uint16_t *p) {
-  const u32x2_t v = *(__attribute__((address_space(1))) const u32x2_t *)(size_t)p;
-  return make_uint2(v.x, v.y);
+__device__ __forceinline__ float4 unpack4(uint2 u) {
+  return make_float4(bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y));
 }
+__device__ __forceinline__ float elt(const float4 &v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
 // Inclusive sum over the chunk's tokens of a token-major bf16 tile (rows =
 // tokens, columns = channels) for token tile I and channel tile r, on MFMA
@@ -99,27 +99,59 @@ __device__ __forceinline__ f32x4_t tile_cumsum(const uint16_t *tg, int I, int r,
   return acc;
 }
 
-// ============================== state scans ==================================
-// One workgroup per (batch, head); wave w holds value columns 16w .. 16w+15 of
-// the dk x dv state in its accumulators (rows 16 r + 4 (l/16) + e, column
-// 16 w + l%16).  Forward: X = k, Y = v, Z from s0, stores the state entering
-// each chunk.  Reverse: X = q, Y = do (scan order), Z from ds_final, stores
-// the gradient leaving each chunk (and its transpose), then ds0.
-template <int DP, int M, bool REV>
-__global__ void __launch_bounds__(DP / 16 * kWave)
-gla_bwd_scan(BwdParams P) {
-  constexpr int DT = DP / 16, NT = DT * kWave, MT = M / 16, JP = (MT + 1) / 2;
-  constexpr int QS = BwdRow<DP>::QS, CG = DP / 8;
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t *tX = reinterpret_cast<uint16_t *>(smem);
-  uint16_t *tG = tX + M * QS;
-  uint16_t *tY = tG + M * QS;
-  float *gam = reinterpret_cast<float *>(tY + M * QS);   // [DP] e^{B}
+// Token tiles I = 2 jp and 2 jp + 1 of a channel column held in accumulator
+// layout (4 bf16 per lane per tile) as the 32 token K slots of one MFMA
+// operand: slots 8 (l/16) .. +3 are tokens 32 jp + 4 (l/16) + e, slots +4 ..
+// +7 tokens 32 jp + 16 + 4 (l/16) + e -- the order of an lds_tr pair.
+template <int MT>
+__device__ __forceinline__ uint4 kslots(const uint2 (&x)[MT], int jp) {
+  return cat(x[2 * jp], (2 * jp + 1 < MT) ? x[(2 * jp + 1 < MT) ? 2 * jp + 1 : 0] : make_uint2(0, 0));
+}
+// The matching operand read from a token-major tile (rows = tokens), for
+// channels col .. col+15.
+template <int MT>
+__device__ __forceinline__ uint4 tr_pair(const uint16_t *tile, int stride, int jp, int col, int g4, int rowoff,
+                                         int coloff) {
+  const uint2 lo = lds_tr(tile + (32 * jp + 4 * g4 + rowoff) * stride + col + coloff);
+  const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(tile + (32 * jp + 16 + 4 * g4 + rowoff) * stride + col + coloff)
+                                     : make_uint2(0, 0);
+  return cat(lo, hi);
+}
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+// ============================== state scans ==================================
+// One wave per (batch-head unit, key-channel tile r): rows i = 16 r .. 16 r +
+// 15 of the dk x dv state in DT accumulators (rows 16 r + 4 (l/16) + e,
+// columns 16 cc + l%16).  The rows are independent in the recurrence, so the
+// DT waves of a unit never wait for each other; they read the same Y rows
+// (a unit's waves sit on one XCD, so the repeats are L2 hits).  Forward:
+// X = k, Y = v, Z from s0, stores the state entering each chunk.  Reverse:
+// X = q, Y = do (scan order), Z from ds_final, stores the gradient of the
+// state leaving each chunk, then ds0.  The gate cumsum, the scaling of X and
+// X as the MFMA's A operand stay in registers; rows arrive two chunks ahead.
+template <int DP, int M>
+struct ScanLds {
+  static constexpr int QS = BwdRow<DP>::QS;
+  static constexpr int XS = BwdRow<32>::QS;   // [M][XS]: X channels in columns 0..15, gates in 16..31
+  static constexpr int bytes = M * QS * 2 + M * XS * 2;
+};
+
+template <int DP, int M, bool REV>
+__global__ void __launch_bounds__(kWave)
+gla_bwd_scan(BwdParams P) {
+  constexpr int DT = DP / 16, MT = M / 16, JP = (MT + 1) / 2;
+  constexpr int QS = ScanLds<DP, M>::QS, XS = ScanLds<DP, M>::XS, CG = DP / 8;
+  constexpr int ITY = (M * CG + kWave - 1) / kWave, ITX = (2 * M + kWave - 1) / kWave;
+  static_assert(M <= kWave, "one token per lane for the canonical index");
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t *tY = reinterpret_cast<uint16_t *>(smem);
+  uint16_t *tXG = tY + M * QS;
+
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
   const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
-  const int n0 = 16 * wave;
-  const int unit = blockIdx.x, bb = unit / P.H, hh = unit - bb * P.H;
+  const int lb = xcd_linear_block(blockIdx.x, gridDim.x);
+  const int unit = lb / DT, r = lb - unit * DT;
+  if (unit >= P.B * P.H) return;
+  const int bb = unit / P.H, hh = unit - bb * P.H;
   const int T = P.T, dk = P.dk, dv = P.dv, N = P.nchunks;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc((REV ? P.q : P.k) + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(P.g + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
@@ -130,107 +162,115 @@ gla_bwd_scan(BwdParams P) {
   f32x4_t Z[DT];
   const float *z0 = REV ? P.ds_final : P.s0;
 #pragma unroll
-  for (int r = 0; r < DT; ++r)
+  for (int cc = 0; cc < DT; ++cc)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * r + 4 * g4 + e, j = n0 + l16;
-      Z[r][e] = (z0 && i < dk && j < dv) ? z0[((int64_t)unit * dk + i) * dv + j] : 0.f;
+      const int i = 16 * r + 4 * g4 + e, j = 16 * cc + l16;
+      Z[cc][e] = (z0 && i < dk && j < dv) ? z0[((int64_t)unit * dk + i) * dv + j] : 0.f;
     }
 
-  // chunk rows go global -> registers (one chunk ahead) -> LDS
-  constexpr int IT = (M * CG + NT - 1) / NT;
-  uint4 px[IT], pg[IT], py[IT];
-  auto fetch = [&](int c) {
+  struct Rows {
+    uint4 y[ITY], x[ITX], g[ITX];
+  };
+  auto fetch = [&](Rows &f, int c) {
+    const int pl = c * M + (lane < M ? lane : 0);
+    const int nl = (lane < M && pl < T) ? scan_to_canon(P.dir, P.gh, P.gw, T, pl) : -1;
 #pragma unroll
-    for (int kq = 0; kq < IT; ++kq) {
-      const int idx = tid + kq * NT;
+    for (int kq = 0; kq < ITY; ++kq) {
+      const int idx = lane + kq * kWave;
       const int tl = idx / CG, cg = idx - tl * CG;
-      const int p = c * M + tl;
-      const bool ok = idx < M * CG && p < T;
-      const int n = ok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
-      const int64_t yrow = REV ? (int64_t)p : n;
-      const unsigned oxg = (ok && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
-      const unsigned oy = (ok && 8 * cg < dv) ? (unsigned)((yrow * y_st + 8 * cg) * 2) : kOOB;
-      px[kq] = bload16(rx, oxg);
-      pg[kq] = bload16(rg, oxg);
-      py[kq] = bload16(ry, oy);
+      const int n = __shfl(nl, tl < M ? tl : 0, kWave);
+      const bool ok = idx < M * CG && n >= 0 && 8 * cg < dv;
+      const int64_t yrow = REV ? (int64_t)c * M + tl : (int64_t)n;
+      f.y[kq] = bload16(ry, ok ? (unsigned)((yrow * y_st + 8 * cg) * 2) : kOOB);
+    }
+#pragma unroll
+    for (int kq = 0; kq < ITX; ++kq) {
+      const int idx = lane + kq * kWave;
+      const int tl = idx >> 1, ch = 16 * r + 8 * (idx & 1);
+      const int n = __shfl(nl, tl < M ? tl : 0, kWave);
+      const unsigned off = (idx < 2 * M && n >= 0 && ch < dk) ? (unsigned)(((int64_t)n * P.qk_st + ch) * 2) : kOOB;
+      f.x[kq] = bload16(rx, off);
+      f.g[kq] = bload16(rg, off);
     }
   };
-  fetch(REV ? N - 1 : 0);
-
-  for (int it = 0; it < N; ++it) {
-    const int c = REV ? N - 1 - it : it;
-    // the state for chunk c, bf16, padding included (it is zero)
-    const int64_t blk = ((int64_t)unit * N + c) * DP * DP;
-    uint16_t *zs = (REV ? P.st_d : P.st_s) + blk;
+  auto stash = [&](const Rows &f) {
 #pragma unroll
-    for (int r = 0; r < DT; ++r) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) zs[(16 * r + 4 * g4 + e) * DP + n0 + l16] = to_bf(Z[r][e]);
-      if (REV) *reinterpret_cast<uint2 *>(P.st_dt + blk + (n0 + l16) * DP + 16 * r + 4 * g4) = pack4(Z[r]);
+    for (int kq = 0; kq < ITY; ++kq) {
+      const int idx = lane + kq * kWave;
+      const int tl = idx / CG, cg = idx - tl * CG;
+      if (idx < M * CG) *reinterpret_cast<uint4 *>(tY + tl * QS + 8 * cg) = f.y[kq];
     }
-    // chunk c's rows into LDS (zeros past T and in the channel padding)
 #pragma unroll
-    for (int kq = 0; kq < IT; ++kq) {
-      const int idx = tid + kq * NT;
-      if (idx < M * CG) {
-        const int tl = idx / CG, cg = idx - tl * CG;
-        *reinterpret_cast<uint4 *>(tX + tl * QS + 8 * cg) = px[kq];
-        *reinterpret_cast<uint4 *>(tG + tl * QS + 8 * cg) = pg[kq];
-        *reinterpret_cast<uint4 *>(tY + tl * QS + 8 * cg) = py[kq];
+    for (int kq = 0; kq < ITX; ++kq) {
+      const int idx = lane + kq * kWave;
+      const int tl = idx >> 1, h = idx & 1;
+      if (idx < 2 * M) {
+        *reinterpret_cast<uint4 *>(tXG + tl * XS + 8 * h) = f.x[kq];
+        *reinterpret_cast<uint4 *>(tXG + tl * XS + 16 + 8 * h) = f.g[kq];
       }
     }
-    __syncthreads();
-    if (it + 1 < N) fetch(REV ? c - 1 : c + 1);
-    // cumulative gates of key-channel tile `wave`; X scaled in place by
-    // e^{B - b} (forward) or e^{b} (reverse), both <= 1
+  };
+
+  uint16_t *zbase = (REV ? P.st_d : P.st_s) + (int64_t)unit * N * DP * DP;
+  auto step = [&](Rows &f, int it) {
+    const int c = REV ? N - 1 - it : it;
+    // the state for chunk c, transposed ([j][i]), padding included (zero)
+    uint16_t *zt = zbase + (int64_t)c * DP * DP;
+#pragma unroll
+    for (int cc = 0; cc < DT; ++cc)
+      *reinterpret_cast<uint2 *>(zt + (16 * cc + l16) * DP + 16 * r + 4 * g4) = pack4(Z[cc]);
+    stash(f);
+    lds_barrier();
+    if (it + 2 < N) fetch(f, REV ? c - 2 : c + 2);
+    // cumulative gates (accumulator layout: token 16 I + 4 (l/16) + e,
+    // channel 16 r + l%16) and X scaled by e^{B - b} (forward) or e^{b}
+    // (reverse), both <= 1
+    uint2 xh[MT];
+    float tot;
     {
       f32x4_t cum[MT];
 #pragma unroll
-      for (int I = 0; I < MT; ++I) cum[I] = tile_cumsum<MT, QS>(tG, I, wave, l16, g4);
-      const float tot = __shfl(cum[MT - 1][3], 48 + l16, 64);   // token M-1: lane group 3, e = 3
-      const int i = n0 + l16;
+      for (int I = 0; I < MT; ++I) cum[I] = tile_cumsum<MT, XS>(tXG + 16, I, 0, l16, g4);
+      tot = __shfl(cum[MT - 1][3], 48 + l16, kWave);   // token M-1: lane group 3, e = 3
 #pragma unroll
-      for (int I = 0; I < MT; ++I)
+      for (int I = 0; I < MT; ++I) {
+        const float4 xv = unpack4(lds_tr(tXG + (16 * I + 4 * g4 + rowoff) * XS + coloff));
+        f32x4_t sx;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * I + 4 * g4 + e;
-          const float f = fexp2((REV ? cum[I][e] : tot - cum[I][e]) * kLog2e);
-          tX[t * QS + i] = to_bf(bf_at(tX + t * QS + i) * f);
-        }
-      if (g4 == 0) gam[i] = fexp2(tot * kLog2e);
-    }
-    __syncthreads();
-    // Z = diag(e^{B}) Z + X^T Y, K = the chunk's tokens (transposing reads)
-    uint4 yf[JP];
-#pragma unroll
-    for (int jp = 0; jp < JP; ++jp) {
-      const uint2 lo = lds_tr(tY + (32 * jp + 4 * g4 + rowoff) * QS + n0 + coloff);
-      const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(tY + (32 * jp + 16 + 4 * g4 + rowoff) * QS + n0 + coloff)
-                                         : make_uint2(0, 0);
-      yf[jp] = cat(lo, hi);
-    }
-#pragma unroll
-    for (int r = 0; r < DT; ++r) {
-      const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * r + 4 * g4);
-      Z[r][0] *= gm.x; Z[r][1] *= gm.y; Z[r][2] *= gm.z; Z[r][3] *= gm.w;
-#pragma unroll
-      for (int jp = 0; jp < JP; ++jp) {
-        const uint2 lo = lds_tr(tX + (32 * jp + 4 * g4 + rowoff) * QS + 16 * r + coloff);
-        const uint2 hi = (2 * jp + 1 < MT) ? lds_tr(tX + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * r + coloff)
-                                           : make_uint2(0, 0);
-        Z[r] = mfma32(cat(lo, hi), yf[jp], Z[r]);
+        for (int e = 0; e < 4; ++e) sx[e] = elt(xv, e) * fexp2((REV ? cum[I][e] : tot - cum[I][e]) * kLog2e);
+        xh[I] = pack4(sx);
       }
     }
-    __syncthreads();
+    float gm[4];   // e^{B} of rows 16 r + 4 (l/16) + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gm[e] = fexp2(__shfl(tot, 4 * g4 + e, kWave) * kLog2e);
+    // Z = diag(e^{B}) Z + X^T Y, K = the chunk's tokens
+#pragma unroll
+    for (int cc = 0; cc < DT; ++cc) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Z[cc][e] *= gm[e];
+#pragma unroll
+      for (int jp = 0; jp < JP; ++jp)
+        Z[cc] = mfma32(kslots<MT>(xh, jp), tr_pair<MT>(tY, QS, jp, 16 * cc, g4, rowoff, coloff), Z[cc]);
+    }
+    lds_barrier();
+  };
+
+  Rows fa, fb;
+  fetch(fa, REV ? N - 1 : 0);
+  if (N > 1) fetch(fb, REV ? N - 2 : 1);
+  for (int it = 0; it < N; it += 2) {
+    step(fa, it);
+    if (it + 1 < N) step(fb, it + 1);
   }
   if (REV && P.ds0) {
 #pragma unroll
-    for (int r = 0; r < DT; ++r)
+    for (int cc = 0; cc < DT; ++cc)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * r + 4 * g4 + e, j = n0 + l16;
-        if (i < dk && j < dv) P.ds0[((int64_t)unit * dk + i) * dv + j] = Z[r][e];
+        const int i = 16 * r + 4 * g4 + e, j = 16 * cc + l16;
+        if (i < dk && j < dv) P.ds0[((int64_t)unit * dk + i) * dv + j] = Z[cc][e];
       }
   }
 }
@@ -240,25 +280,32 @@ template <int DP, int M>
 struct BwdLds {
   static constexpr int QS = BwdRow<DP>::QS;
   static constexpr int SA = M + 8;                     // row stride of the M x M tiles
-  static constexpr int TILE = M * QS * 2;
-  static constexpr int oQ = 0, oK = TILE, oV = 2 * TILE, oO = 3 * TILE;   // raw q, k, v, do
-  static constexpr int oQt = 4 * TILE, oKt = 5 * TILE;  // q e^{b}, k e^{-b}; extreme chunks: fp32 dq sums
-  static constexpr int oKh = 6 * TILE;                  // gates, then k e^{B - b}
-  static constexpr int oB = 7 * TILE;                   // [M][DP] fp32 b (log2 units)
-  static constexpr int oA = oB + M * DP * 4;            // [M][SA] bf16 A = dO V^T (causal)
-  static constexpr int oP = oA + M * SA * 2;            // [M][SA] bf16 P (causal)
-  static constexpr int oR = oP + M * SA * 2;            // [M][DP] fp32 q dq - k dk (extreme: dk sums first)
-  static constexpr int oBt = oR + M * DP * 4;           // [DP] B (log2 units)
-  static constexpr int oGam = oBt + DP * 4;             // [DP] e^{B}
-  static constexpr int oSuf = oGam + DP * 4;            // [DP/16][DP] rowsum(S_out (.) D), per column tile
-  static constexpr int oTok = oSuf + (DP / 16) * DP * 4;   // [M] canonical token, -1 past T
-  static constexpr int oFlag = oTok + M * 4;            // bit pattern of max |b|
+  static constexpr int TILE = M * QS * 2;              // token-major [M][QS] bf16
+  static constexpr int STB = DP * QS * 2;              // transposed state [DP (j)][QS] bf16
+  static constexpr int oQ = 0, oK = TILE;              // q, k; then q e^{b}, k e^{-b}
+  static constexpr int oG = 2 * TILE;                  // gates, then k e^{B - b}
+  static constexpr int oV = 3 * TILE, oO = 4 * TILE;   // v, do
+  static constexpr int oS = 5 * TILE, oD = oS + STB;   // S_in^T, D^T
+  static constexpr int oA = oD + STB;                  // [M][SA] bf16 A = dO V^T (causal)
+  static constexpr int oP = oA + M * SA * 2;           // [M][SA] bf16 P (causal)
+  static constexpr int oB = oP + M * SA * 2;           // [M][DP] fp32 b (log2 units), extreme chunks
+  static constexpr int oTok = oB + M * DP * 4;         // [M] canonical token, -1 past T
+  static constexpr int oFlag = oTok + M * 4;           // any |b| beyond the factorised range
   static constexpr int bytes = oFlag + 16;
-  static_assert(2 * TILE >= M * DP * 4, "the fp32 dq sums of extreme chunks overlay the q~, k~ tiles");
 };
 
 constexpr int kChunkWaves = 8;
 
+// Persistent: workgroup w takes chunks w, w + grid, ...; the next chunk's
+// rows and both state blocks are loaded into registers while the current one
+// is computed.  Wave r < DT owns key-channel tile r from the gate cumsum to
+// its dq, dk and dlog_alpha (b, raw and scaled q, k and the rowsum of
+// S_out (.) D stay in its registers); the other waves compute A and P, and
+// all share dv.
+//   phase 1: cumsum, range check, raw q, k (channel waves) | A tiles
+//   phase 2: scaled rows into LDS, rowsum(S_out (.) D) (channel waves)
+//   phase 3: dq, dk, dlog_alpha (channel waves, token tiles last to first) | P tiles
+//   phase 4: dv
 template <int DP, int M>
 __global__ void __launch_bounds__(kChunkWaves * kWave)
 gla_bwd_chunk(BwdParams P) {
@@ -267,227 +314,349 @@ gla_bwd_chunk(BwdParams P) {
   constexpr int K32 = DP / 32;
   constexpr bool KH = (DP % 32) != 0;
   constexpr int QS = L::QS, SA = L::SA, CG = DP / 8;
+  constexpr int ITT = (M * CG + NT - 1) / NT, ITS = (DP * CG + NT - 1) / NT;
+  constexpr int NTRI = MT * (MT + 1) / 2;   // token tile pairs (I, J), J <= I
+  static_assert(DT <= kChunkWaves, "one wave per key-channel tile");
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t *tQ = reinterpret_cast<uint16_t *>(smem + L::oQ), *tK = reinterpret_cast<uint16_t *>(smem + L::oK);
+  uint16_t *tG = reinterpret_cast<uint16_t *>(smem + L::oG);
   uint16_t *tV = reinterpret_cast<uint16_t *>(smem + L::oV), *tO = reinterpret_cast<uint16_t *>(smem + L::oO);
-  uint16_t *tQt = reinterpret_cast<uint16_t *>(smem + L::oQt), *tKt = reinterpret_cast<uint16_t *>(smem + L::oKt);
-  uint16_t *tKh = reinterpret_cast<uint16_t *>(smem + L::oKh);
-  float *bL = reinterpret_cast<float *>(smem + L::oB);
+  uint16_t *tS = reinterpret_cast<uint16_t *>(smem + L::oS), *tD = reinterpret_cast<uint16_t *>(smem + L::oD);
   uint16_t *tA = reinterpret_cast<uint16_t *>(smem + L::oA), *tP = reinterpret_cast<uint16_t *>(smem + L::oP);
-  float *E1 = reinterpret_cast<float *>(smem + L::oQt);   // extreme chunks only
-  float *R = reinterpret_cast<float *>(smem + L::oR);
-  float *gam = reinterpret_cast<float *>(smem + L::oGam), *suf = reinterpret_cast<float *>(smem + L::oSuf);
-  float *Bt = reinterpret_cast<float *>(smem + L::oBt);
+  float *bL = reinterpret_cast<float *>(smem + L::oB);
   int *tok = reinterpret_cast<int *>(smem + L::oTok);
   unsigned *flag = reinterpret_cast<unsigned *>(smem + L::oFlag);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
-  const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
-  const int N = P.nchunks;
-  const int unit = blockIdx.x / N, c = blockIdx.x - unit * N;
-  const int bb = unit / P.H, hh = unit - bb * P.H;
+  const int tid0 = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+  const int N = P.nchunks, total = P.B * P.H * N;
   const int T = P.T, dk = P.dk, dv = P.dv, H = P.H;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(P.q + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.k + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(P.g + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.v + bb * P.v_sb + hh * P.v_sh, P.v_span);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(P.dout + bb * P.do_sb + hh * P.do_sh, P.do_span);
-  const int64_t blk = ((int64_t)unit * N + c) * DP * DP;
-  const uint16_t *Sin = P.st_s + blk, *Dm = P.st_d + blk, *Dt = P.st_dt + blk;
+  const bool chan = wave < DT;
+  const int r = wave;                                          // key-channel tile of a channel wave
+  const int wslot = (wave + kChunkWaves - DT) % kChunkWaves;   // A, P, dv: the other waves first
 
-  // ---- 1. the chunk's rows (q, k, gates, v canonical; do in scan order)
-  if (tid < M) {
-    const int p = c * M + tid;
-    tok[tid] = p < T ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
-  }
-  if (tid == 0) *flag = 0u;
-  __syncthreads();
-  for (int idx = tid; idx < M * CG; idx += NT) {
-    const int tl = idx / CG, cg = idx - tl * CG;
-    const int n = tok[tl];
-    const unsigned oqk = (n >= 0 && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
-    const unsigned ov = (n >= 0 && 8 * cg < dv) ? (unsigned)(((int64_t)n * P.v_st + 8 * cg) * 2) : kOOB;
-    const unsigned oo = (n >= 0 && 8 * cg < dv) ? (unsigned)((((int64_t)c * M + tl) * P.do_st + 8 * cg) * 2) : kOOB;
-    const int at = tl * QS + 8 * cg;
-    *reinterpret_cast<uint4 *>(tQ + at) = bload16(rq, oqk);
-    *reinterpret_cast<uint4 *>(tK + at) = bload16(rk, oqk);
-    *reinterpret_cast<uint4 *>(tKh + at) = bload16(rg, oqk);
-    *reinterpret_cast<uint4 *>(tV + at) = bload16(rv, ov);
-    *reinterpret_cast<uint4 *>(tO + at) = bload16(ro, oo);
-  }
-  __syncthreads();
+  // tiles above the diagonal of A and P stay zero
+  for (int x = tid0; x < 2 * M * SA / 8; x += NT) reinterpret_cast<uint4 *>(tA)[x] = make_uint4(0, 0, 0, 0);
 
-  // ---- 2. cumulative gates (log2 units; ones-triangle MFMA over the gate
-  //         tile) and the scaled rows
-  for (int tt = wave; tt < MT * DT; tt += kChunkWaves) {
-    const int I = tt / DT, r = tt - I * DT;
-    const f32x4_t cum = tile_cumsum<MT, QS>(tKh, I, r, l16, g4);
-    const int i = 16 * r + l16;
-    float mx = 0.f;
+  uint4 fq[ITT], fk[ITT], fg[ITT], fv[ITT], fo[ITT], fs[ITS], fd[ITS];
+  auto fetch = [&](int w) {
+    const int unit = w / N, c = w - unit * N, bb = unit / H, hh = unit - bb * H;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(P.q + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.k + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(P.g + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.v + bb * P.v_sb + hh * P.v_sh, P.v_span);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(P.dout + bb * P.do_sb + hh * P.do_sh, P.do_span);
+    const int64_t blk = ((int64_t)unit * N + c) * DP * DP;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.st_s + blk, DP * DP * 2);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(P.st_d + blk, DP * DP * 2);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float b = cum[e] * kLog2e;
-      bL[(16 * I + 4 * g4 + e) * DP + i] = b;
-      mx = fmaxf(mx, fabsf(b));
+    for (int kq = 0; kq < ITT; ++kq) {
+      const int idx = tid0 + kq * NT;
+      const int tl = idx / CG, cg = idx - tl * CG;
+      const int p = c * M + tl;
+      const bool ok = idx < M * CG && p < T;
+      const int n = ok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
+      const unsigned oqk = (ok && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
+      const unsigned ov = (ok && 8 * cg < dv) ? (unsigned)(((int64_t)n * P.v_st + 8 * cg) * 2) : kOOB;
+      const unsigned oo = (ok && 8 * cg < dv) ? (unsigned)(((int64_t)p * P.do_st + 8 * cg) * 2) : kOOB;
+      fq[kq] = bload16(rq, oqk);
+      fk[kq] = bload16(rk, oqk);
+      fg[kq] = bload16(rg, oqk);
+      fv[kq] = bload16(rv, ov);
+      fo[kq] = bload16(ro, oo);
     }
-    if (I == MT - 1 && g4 == 3) Bt[i] = cum[3] * kLog2e;   // token M-1
-    if (!(mx <= kBwdFastRange)) atomicOr(flag, 1u);          // NaN / inf too
-  }
-  __syncthreads();
-  for (int x = tid; x < M * DP; x += NT) {
-    const int t = x / DP, i = x - t * DP;
-    const float b = bL[x], B = Bt[i];
-    const float q = bf_at(tQ + t * QS + i), k = bf_at(tK + t * QS + i);
-    tQt[t * QS + i] = to_bf(q * fexp2(b));
-    tKt[t * QS + i] = to_bf(k * fexp2(-b));
-    tKh[t * QS + i] = to_bf(k * fexp2(B - b));
-  }
-  if (tid < DP) gam[tid] = fexp2(Bt[tid]);
-  __syncthreads();
-  const bool fast = *flag == 0u;
+#pragma unroll
+    for (int kq = 0; kq < ITS; ++kq) {
+      const int idx = tid0 + kq * NT;
+      const unsigned off = idx < DP * CG ? (unsigned)idx * 16u : kOOB;
+      fs[kq] = bload16(rs, off);
+      fd[kq] = bload16(rd, off);
+    }
+  };
 
-  // ---- 3. A = dO V^T and (factorised chunks) P = Q~ K~^T on s <= t, zero above
-  for (int tt = wave; tt < MT * MT; tt += kChunkWaves) {
-    const int I = tt / MT, J = tt - I * MT;   // rows t (tile I), columns s (tile J)
-    f32x4_t a = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
-    if (J <= I) {
-      const uint16_t *orow = tO + (16 * I + l16) * QS, *vrow = tV + (16 * J + l16) * QS;
+  int w = blockIdx.x;
+  if (w < total) fetch(w);
+  for (; w < total; w += gridDim.x) {
+    const int unit = w / N, c = w - unit * N, bb = unit / H, hh = unit - bb * H;
+    // The lane index is hidden from the optimiser here, so the per-lane LDS
+    // addresses are formed inside each chunk's code rather than hoisted out
+    // of the loop (hundreds of them, which would not fit in registers).
+    int lane = tid0 & 63;
+    asm volatile("" : "+v"(lane));
+    const int tid = wave * kWave + lane, l16 = lane & 15, g4 = lane >> 4;
+    const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
+    // ---- 0. this chunk's rows (q, k, gates, v canonical; do in scan order)
+    //         and state blocks into LDS; the next chunk's loads go out
 #pragma unroll
-      for (int kb = 0; kb < K32; ++kb) a = mfma32(lds4(orow + 32 * kb + 8 * g4), lds4(vrow + 32 * kb + 8 * g4), a);
-      if (KH) a = mfma16(lds2(orow + 32 * K32 + 4 * g4), lds2(vrow + 32 * K32 + 4 * g4), a);
-      if (fast) {
-        const uint16_t *qrow = tQt + (16 * I + l16) * QS, *krow = tKt + (16 * J + l16) * QS;
-#pragma unroll
-        for (int kb = 0; kb < K32; ++kb)
-          pp = mfma32(lds4(qrow + 32 * kb + 8 * g4), lds4(krow + 32 * kb + 8 * g4), pp);
-        if (KH) pp = mfma16(lds2(qrow + 32 * K32 + 4 * g4), lds2(krow + 32 * K32 + 4 * g4), pp);
-      }
-      if (J == I) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (l16 > 4 * g4 + e) { a[e] = 0.f; pp[e] = 0.f; }   // causal: s > t
+    for (int kq = 0; kq < ITT; ++kq) {
+      const int idx = tid + kq * NT;
+      if (idx < M * CG) {
+        const int tl = idx / CG, cg = idx - tl * CG;
+        const int at = tl * QS + 8 * cg;
+        *reinterpret_cast<uint4 *>(tQ + at) = fq[kq];
+        *reinterpret_cast<uint4 *>(tK + at) = fk[kq];
+        *reinterpret_cast<uint4 *>(tG + at) = fg[kq];
+        *reinterpret_cast<uint4 *>(tV + at) = fv[kq];
+        *reinterpret_cast<uint4 *>(tO + at) = fo[kq];
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int at = (16 * I + 4 * g4 + e) * SA + 16 * J + l16;
-      tA[at] = to_bf(a[e]);
-      if (fast) tP[at] = to_bf(pp[e]);
+    for (int kq = 0; kq < ITS; ++kq) {
+      const int idx = tid + kq * NT;
+      if (idx < DP * CG) {
+        const int j = idx / CG, cg = idx - j * CG;
+        *reinterpret_cast<uint4 *>(tS + j * QS + 8 * cg) = fs[kq];
+        *reinterpret_cast<uint4 *>(tD + j * QS + 8 * cg) = fd[kq];
+      }
     }
-  }
-  __syncthreads();
+    if (tid < M) {
+      const int p = c * M + tid;
+      tok[tid] = p < T ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
+    }
+    if (tid == 0) *flag = 0u;
+    lds_barrier();
+    if (w + (int)gridDim.x < total) fetch(w + gridDim.x);
 
-  // ---- 3b. chunks beyond the factorised range: exact exponent differences
-  if (!fast) {
-    for (int x = tid; x < M * M; x += NT) {
-      const int t = x / M, s = x - t * M;
-      float acc = 0.f;
-      if (s <= t)
-        for (int i = 0; i < dk; ++i)
-          acc += bf_at(tQ + t * QS + i) * bf_at(tK + s * QS + i) * fexp2(bL[t * DP + i] - bL[s * DP + i]);
-      tP[t * SA + s] = to_bf(acc);
-    }
-    for (int x = tid; x < M * DP; x += NT) {
-      const int t = x / DP, i = x - t * DP;
-      float aq = 0.f, ak = 0.f;
-      if (i < dk) {
-        for (int s = 0; s <= t; ++s)   // dq sums: keys s <= t
-          aq += bf_at(tA + t * SA + s) * bf_at(tK + s * QS + i) * fexp2(bL[t * DP + i] - bL[s * DP + i]);
-        for (int u = t; u < M; ++u)    // dk sums: queries u >= t (t as the key)
-          ak += bf_at(tA + u * SA + t) * bf_at(tQ + u * QS + i) * fexp2(bL[u * DP + i] - bL[t * DP + i]);
-      }
-      E1[t * DP + i] = aq;
-      R[t * DP + i] = ak;
-    }
-    __syncthreads();
-  }
-
-  // ---- 4. dq, dk (unit (I, r): tokens of tile I, key channels of tile r) and
-  //         dv (unit (I, cc): tokens of tile I, value channels of tile cc)
-  for (int u = wave; u < 2 * MT * DT; u += kChunkWaves) {
-    const bool is_v = u >= MT * DT;
-    const int uu = is_v ? u - MT * DT : u;
-    const int I = uu / DT, r = uu - I * DT;
-    const uint16_t *orow = tO + (16 * I + l16) * QS;
-    if (!is_v) {
-      // dO S_in^T and V D^T: K = value channels; B operands straight from the
-      // state blocks (rows i of S_in and D)
-      f32x4_t x1 = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t *vrow = tV + (16 * I + l16) * QS;
-      const uint16_t *srow = Sin + (16 * r + l16) * DP, *drow = Dm + (16 * r + l16) * DP;
+    // ---- 1. cumulative gates (log2 units) and raw q, k of tile r, in
+    //         accumulator layout (token 16 I + 4 (l/16) + e, channel 16 r + l%16)
+    float bl[MT][4];
+    float Bt = 0.f;
+    uint2 qa[MT], ka[MT];
+    if (chan) {
+      float mx = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < K32; ++kb) {
-        x1 = mfma32(lds4(orow + 32 * kb + 8 * g4), gload16(srow + 32 * kb + 8 * g4), x1);
-        x2 = mfma32(lds4(vrow + 32 * kb + 8 * g4), gload16(drow + 32 * kb + 8 * g4), x2);
-      }
-      if (KH) {
-        x1 = mfma16(lds2(orow + 32 * K32 + 4 * g4), gload8(srow + 32 * K32 + 4 * g4), x1);
-        x2 = mfma16(lds2(vrow + 32 * K32 + 4 * g4), gload8(drow + 32 * K32 + 4 * g4), x2);
-      }
-      // A K~ and A^T Q~ (K = tokens): only the blocks on the causal side
-      f32x4_t y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
-      if (fast) {
-        const uint16_t *arow = tA + (16 * I + l16) * SA;
+      for (int I = 0; I < MT; ++I) {
+        const f32x4_t cum = tile_cumsum<MT, QS>(tG, I, r, l16, g4);
 #pragma unroll
-        for (int jp = 0; jp < JP; ++jp) {
-          const bool hi_ok = 2 * jp + 1 < MT;
-          if (32 * jp <= 16 * I + 15) {   // keys s <= t
-            const uint4 af = cat(lds2(arow + 32 * jp + 4 * g4), hi_ok ? lds2(arow + 32 * jp + 16 + 4 * g4) : make_uint2(0, 0));
-            const uint2 lo = lds_tr(tKt + (32 * jp + 4 * g4 + rowoff) * QS + 16 * r + coloff);
-            const uint2 hi = hi_ok ? lds_tr(tKt + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * r + coloff) : make_uint2(0, 0);
-            y1 = mfma32(af, cat(lo, hi), y1);
-          }
-          if (32 * jp + 31 >= 16 * I) {   // queries u >= t
-            const uint2 alo = lds_tr(tA + (32 * jp + 4 * g4 + rowoff) * SA + 16 * I + coloff);
-            const uint2 ahi = hi_ok ? lds_tr(tA + (32 * jp + 16 + 4 * g4 + rowoff) * SA + 16 * I + coloff) : make_uint2(0, 0);
-            const uint2 qlo = lds_tr(tQt + (32 * jp + 4 * g4 + rowoff) * QS + 16 * r + coloff);
-            const uint2 qhi = hi_ok ? lds_tr(tQt + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * r + coloff) : make_uint2(0, 0);
-            y2 = mfma32(cat(alo, ahi), cat(qlo, qhi), y2);
-          }
+        for (int e = 0; e < 4; ++e) {
+          bl[I][e] = cum[e] * kLog2e;
+          mx = fmaxf(mx, fabsf(bl[I][e]));
         }
+        qa[I] = lds_tr(tQ + (16 * I + 4 * g4 + rowoff) * QS + 16 * r + coloff);
+        ka[I] = lds_tr(tK + (16 * I + 4 * g4 + rowoff) * QS + 16 * r + coloff);
       }
-      // combine, store, and keep q dq - k dk for the gate gradient
-      const int i = 16 * r + l16;
+      Bt = __shfl(bl[MT - 1][3], 48 + l16, kWave);   // token M-1: lane group 3, e = 3
+      if (!(mx <= kBwdFastRange)) atomicOr(flag, 1u);   // NaN / inf too
+    }
+    //         A = dO V^T on tiles J <= I, the diagonal masked to s <= t
+    for (int a = wslot; a < NTRI; a += kChunkWaves) {
+      int I = 0;
+      while ((I + 1) * (I + 2) / 2 <= a) ++I;
+      const int J = a - I * (I + 1) / 2;
+      const uint16_t *orow = tO + (16 * I + l16) * QS, *vrow = tV + (16 * J + l16) * QS;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < K32; ++kb) acc = mfma32(lds4(orow + 32 * kb + 8 * g4), lds4(vrow + 32 * kb + 8 * g4), acc);
+      if (KH) acc = mfma16(lds2(orow + 32 * K32 + 4 * g4), lds2(vrow + 32 * K32 + 4 * g4), acc);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + 4 * g4 + e;
-        const float b = bL[t * DP + i], B = bL[(M - 1) * DP + i];
-        float dqv, dkv;
-        if (fast) {
-          dqv = fexp2(b) * (x1[e] + y1[e]);
-          dkv = fexp2(-b) * y2[e] + fexp2(B - b) * x2[e];
-        } else {
-          dqv = fexp2(b) * x1[e] + E1[t * DP + i];
-          dkv = R[t * DP + i] + fexp2(B - b) * x2[e];
+        const bool keep = J < I || l16 <= 4 * g4 + e;
+        tA[(16 * I + 4 * g4 + e) * SA + 16 * J + l16] = to_bf(keep ? acc[e] : 0.f);
+      }
+    }
+    lds_barrier();
+
+    // ---- 2. scaled rows of tile r into LDS (k e^{B - b} always; q e^{b},
+    //         k e^{-b} where factorised, else b itself), and rowsum(S_out (.) D)
+    //         with S_out = diag(e^{B}) S_in + K^^T V
+    const bool fast = *flag == 0u;
+    uint2 qt[MT], kt[MT];
+    float sufS = 0.f;   // rowsum(S_out (.) D) of channel 16 r + l%16
+    if (chan) {
+      uint2 kh[MT];
+      const int i = 16 * r + l16;
+#pragma unroll
+      for (int I = 0; I < MT; ++I) {
+        const float4 q4 = unpack4(qa[I]), k4 = unpack4(ka[I]);
+        f32x4_t a1, a2, a3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float b = bl[I][e];
+          a1[e] = elt(q4, e) * fexp2(b);
+          a2[e] = elt(k4, e) * fexp2(-b);
+          a3[e] = elt(k4, e) * fexp2(Bt - b);
         }
-        R[t * DP + i] = bf_at(tQ + t * QS + i) * dqv - bf_at(tK + t * QS + i) * dkv;
-        const int n = tok[t];
-        if (n >= 0 && i < dk) {
-          const int64_t o = (((int64_t)bb * T + n) * H + hh) * dk + i;
-          P.gq[o] = to_bf(dqv);
-          P.gk[o] = to_bf(dkv);
+        qt[I] = pack4(a1);
+        kt[I] = pack4(a2);
+        kh[I] = pack4(a3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int at = (16 * I + 4 * g4 + e) * QS + i;
+          const int sh = (e & 1) * 16;
+          tG[at] = (uint16_t)((e < 2 ? kh[I].x : kh[I].y) >> sh);
+          if (fast) {
+            tQ[at] = (uint16_t)((e < 2 ? qt[I].x : qt[I].y) >> sh);
+            tK[at] = (uint16_t)((e < 2 ? kt[I].x : kt[I].y) >> sh);
+          } else {
+            bL[(16 * I + 4 * g4 + e) * DP + i] = bl[I][e];
+          }
         }
       }
-    } else {
-      // dv = P^T dO + K^ D: K = tokens for the first (transposing reads), key
-      // channels for the second (rows of D^T)
-      const int cc = r;
+      float gm[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gm[e] = fexp2(__shfl(Bt, 4 * g4 + e, kWave));
+#pragma unroll
+      for (int cc = 0; cc < DT; ++cc) {
+        f32x4_t so = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jp = 0; jp < JP; ++jp)
+          so = mfma32(kslots<MT>(kh, jp), tr_pair<MT>(tV, QS, jp, 16 * cc, g4, rowoff, coloff), so);
+        // rows 16 r + 4 (l/16) + e, column 16 cc + l%16 of S_in and D
+        const float4 s4 = unpack4(lds2(tS + (16 * cc + l16) * QS + 16 * r + 4 * g4));
+        const float4 d4 = unpack4(lds2(tD + (16 * cc + l16) * QS + 16 * r + 4 * g4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(fmaf(gm[e], elt(s4, e), so[e]), elt(d4, e), acc[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) acc[e] += __shfl_xor(acc[e], off, kWave);
+      // row 16 r + m sits in lane group m / 4, element m % 4
+      const int src = 16 * (l16 >> 2);
+      const float v0 = __shfl(acc[0], src, kWave), v1 = __shfl(acc[1], src, kWave);
+      const float v2 = __shfl(acc[2], src, kWave), v3 = __shfl(acc[3], src, kWave);
+      const int m4 = l16 & 3;
+      sufS = m4 == 0 ? v0 : m4 == 1 ? v1 : m4 == 2 ? v2 : v3;
+    }
+    lds_barrier();
+
+    // ---- 3. (chunks beyond the factorised range) P with exact exponent differences
+    if (!fast) {
+      for (int x = tid; x < M * M; x += NT) {
+        const int t = x / M, s = x - t * M;
+        float acc = 0.f;
+        if (s <= t)
+          for (int i = 0; i < dk; ++i)
+            acc += bf_at(tQ + t * QS + i) * bf_at(tK + s * QS + i) * fexp2(bL[t * DP + i] - bL[s * DP + i]);
+        tP[t * SA + s] = to_bf(acc);
+      }
+    }
+    //         dq, dk, dlog_alpha of tile r, token tiles last to first (the
+    //         reverse sum over the chunk runs in registers)
+    if (chan) {
+      const int i = 16 * r + l16;
+      // S_in^T and D^T columns i as B operands (K = value channels, lds_tr order)
+      uint4 sB[K32 > 0 ? K32 : 1], dB[K32 > 0 ? K32 : 1];
+      uint2 sBh = make_uint2(0, 0), dBh = make_uint2(0, 0);
+#pragma unroll
+      for (int kb = 0; kb < K32; ++kb) {
+        sB[kb] = tr_pair<2>(tS + 32 * kb * QS, QS, 0, 16 * r, g4, rowoff, coloff);
+        dB[kb] = tr_pair<2>(tD + 32 * kb * QS, QS, 0, 16 * r, g4, rowoff, coloff);
+      }
+      if (KH) {
+        sBh = lds_tr(tS + (32 * K32 + 4 * g4 + rowoff) * QS + 16 * r + coloff);
+        dBh = lds_tr(tD + (32 * K32 + 4 * g4 + rowoff) * QS + 16 * r + coloff);
+      }
+      float run = sufS;
+#pragma unroll
+      for (int I = MT - 1; I >= 0; --I) {
+        const uint16_t *orow = tO + (16 * I + l16) * QS, *vrow = tV + (16 * I + l16) * QS;
+        f32x4_t x1 = {0.f, 0.f, 0.f, 0.f}, x2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < K32; ++kb) {
+          x1 = mfma32(cat(lds2(orow + 32 * kb + 4 * g4), lds2(orow + 32 * kb + 16 + 4 * g4)), sB[kb], x1);
+          x2 = mfma32(cat(lds2(vrow + 32 * kb + 4 * g4), lds2(vrow + 32 * kb + 16 + 4 * g4)), dB[kb], x2);
+        }
+        if (KH) {
+          x1 = mfma16(lds2(orow + 32 * K32 + 4 * g4), sBh, x1);
+          x2 = mfma16(lds2(vrow + 32 * K32 + 4 * g4), dBh, x2);
+        }
+        f32x4_t y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
+        if (fast) {
+          const uint16_t *arow = tA + (16 * I + l16) * SA;
+#pragma unroll
+          for (int jp = 0; jp < JP; ++jp) {
+            const bool hi_ok = 2 * jp + 1 < MT;
+            if (32 * jp <= 16 * I + 15) {   // keys s <= t: A K~
+              const uint4 af = cat(lds2(arow + 32 * jp + 4 * g4), hi_ok ? lds2(arow + 32 * jp + 16 + 4 * g4) : make_uint2(0, 0));
+              y1 = mfma32(af, kslots<MT>(kt, jp), y1);
+            }
+            if (32 * jp + 31 >= 16 * I)     // queries u >= t: A^T Q~
+              y2 = mfma32(tr_pair<MT>(tA, SA, jp, 16 * I, g4, rowoff, coloff), kslots<MT>(qt, jp), y2);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * I + 4 * g4 + e;
+            const float bt = bl[I][e];
+            float a1 = 0.f, a2 = 0.f;
+            for (int s = 0; s <= t; ++s)
+              a1 += bf_at(tA + t * SA + s) * bf_at(tK + s * QS + i) * fexp2(bt - bL[s * DP + i]);
+            for (int u = t; u < M; ++u)
+              a2 += bf_at(tA + u * SA + t) * bf_at(tQ + u * QS + i) * fexp2(bL[u * DP + i] - bt);
+            y1[e] = a1;
+            y2[e] = a2;
+          }
+        }
+        const float4 q4 = unpack4(qa[I]), k4 = unpack4(ka[I]);
+        float R[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float b = bl[I][e];
+          float dqv, dkv;
+          if (fast) {
+            dqv = fexp2(b) * (x1[e] + y1[e]);
+            dkv = fexp2(-b) * y2[e] + fexp2(Bt - b) * x2[e];
+          } else {
+            dqv = fexp2(b) * x1[e] + y1[e];
+            dkv = y2[e] + fexp2(Bt - b) * x2[e];
+          }
+          R[e] = elt(q4, e) * dqv - elt(k4, e) * dkv;
+          const int n = tok[16 * I + 4 * g4 + e];
+          if (n >= 0 && i < dk) {
+            const int64_t o = (((int64_t)bb * T + n) * H + hh) * dk + i;
+            P.gq[o] = to_bf(dqv);
+            P.gk[o] = to_bf(dkv);
+          }
+        }
+        // reverse sum: inside the lane's 4 tokens, then over the later lane groups
+        const float s3 = R[3], s2 = R[2] + s3, s1 = R[1] + s2, s0 = R[0] + s1;
+        const float L0 = __shfl(s0, l16, kWave), L1 = __shfl(s0, 16 + l16, kWave);
+        const float L2 = __shfl(s0, 32 + l16, kWave), L3 = __shfl(s0, 48 + l16, kWave);
+        const float after = run + (g4 < 1 ? L1 : 0.f) + (g4 < 2 ? L2 : 0.f) + (g4 < 3 ? L3 : 0.f);
+        const float sv[4] = {s0, s1, s2, s3};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = tok[16 * I + 4 * g4 + e];
+          if (n >= 0 && i < dk) P.dg[(((int64_t)bb * T + n) * H + hh) * dk + i] = after + sv[e];
+        }
+        run += ((L0 + L1) + L2) + L3;
+      }
+    }
+    //         P = Q~ K~^T on tiles J <= I (factorised chunks)
+    if (fast) {
+      for (int a = wslot; a < NTRI; a += kChunkWaves) {
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= a) ++I;
+        const int J = a - I * (I + 1) / 2;
+        const uint16_t *qrow = tQ + (16 * I + l16) * QS, *krow = tK + (16 * J + l16) * QS;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < K32; ++kb) acc = mfma32(lds4(qrow + 32 * kb + 8 * g4), lds4(krow + 32 * kb + 8 * g4), acc);
+        if (KH) acc = mfma16(lds2(qrow + 32 * K32 + 4 * g4), lds2(krow + 32 * K32 + 4 * g4), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool keep = J < I || l16 <= 4 * g4 + e;
+          tP[(16 * I + 4 * g4 + e) * SA + 16 * J + l16] = to_bf(keep ? acc[e] : 0.f);
+        }
+      }
+    }
+    lds_barrier();
+
+    // ---- 4. dv = P^T dO + K^ D (unit (I, cc): tokens of tile I, value
+    //         channels of tile cc); K = tokens (transposing reads), then key
+    //         channels (rows of D^T)
+    for (int u = wslot; u < MT * DT; u += kChunkWaves) {
+      const int I = u / DT, cc = u - I * DT;
       f32x4_t y3 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jp = 0; jp < JP; ++jp) {
-        const bool hi_ok = 2 * jp + 1 < MT;
-        if (32 * jp + 31 >= 16 * I) {   // queries t >= s
-          const uint2 plo = lds_tr(tP + (32 * jp + 4 * g4 + rowoff) * SA + 16 * I + coloff);
-          const uint2 phi = hi_ok ? lds_tr(tP + (32 * jp + 16 + 4 * g4 + rowoff) * SA + 16 * I + coloff) : make_uint2(0, 0);
-          const uint2 olo = lds_tr(tO + (32 * jp + 4 * g4 + rowoff) * QS + 16 * cc + coloff);
-          const uint2 ohi = hi_ok ? lds_tr(tO + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * cc + coloff) : make_uint2(0, 0);
-          y3 = mfma32(cat(plo, phi), cat(olo, ohi), y3);
-        }
-      }
-      const uint16_t *hrow = tKh + (16 * I + l16) * QS, *dtrow = Dt + (16 * cc + l16) * DP;
+      for (int jp = 0; jp < JP; ++jp)
+        if (32 * jp + 31 >= 16 * I)   // queries t >= s
+          y3 = mfma32(tr_pair<MT>(tP, SA, jp, 16 * I, g4, rowoff, coloff),
+                      tr_pair<MT>(tO, QS, jp, 16 * cc, g4, rowoff, coloff), y3);
+      const uint16_t *hrow = tG + (16 * I + l16) * QS, *drow = tD + (16 * cc + l16) * QS;
 #pragma unroll
-      for (int kb = 0; kb < K32; ++kb) y3 = mfma32(lds4(hrow + 32 * kb + 8 * g4), gload16(dtrow + 32 * kb + 8 * g4), y3);
-      if (KH) y3 = mfma16(lds2(hrow + 32 * K32 + 4 * g4), gload8(dtrow + 32 * K32 + 4 * g4), y3);
+      for (int kb = 0; kb < K32; ++kb) y3 = mfma32(lds4(hrow + 32 * kb + 8 * g4), lds4(drow + 32 * kb + 8 * g4), y3);
+      if (KH) y3 = mfma16(lds2(hrow + 32 * K32 + 4 * g4), lds2(drow + 32 * K32 + 4 * g4), y3);
       const int j = 16 * cc + l16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -495,46 +664,7 @@ gla_bwd_chunk(BwdParams P) {
         if (n >= 0 && j < dv) P.gv[(((int64_t)bb * T + n) * H + hh) * dv + j] = to_bf(y3[e]);
       }
     }
-  }
-
-  // ---- 5. rowsum(S_out (.) D): S_out = diag(e^{B}) S_in + K^^T V
-  for (int u = wave; u < DT * DT; u += kChunkWaves) {
-    const int r = u / DT, cc = u - r * DT;
-    f32x4_t so = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jp = 0; jp < JP; ++jp) {
-      const bool hi_ok = 2 * jp + 1 < MT;
-      const uint2 klo = lds_tr(tKh + (32 * jp + 4 * g4 + rowoff) * QS + 16 * r + coloff);
-      const uint2 khi = hi_ok ? lds_tr(tKh + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * r + coloff) : make_uint2(0, 0);
-      const uint2 vlo = lds_tr(tV + (32 * jp + 4 * g4 + rowoff) * QS + 16 * cc + coloff);
-      const uint2 vhi = hi_ok ? lds_tr(tV + (32 * jp + 16 + 4 * g4 + rowoff) * QS + 16 * cc + coloff) : make_uint2(0, 0);
-      so = mfma32(cat(klo, khi), cat(vlo, vhi), so);
-    }
-    const int j = 16 * cc + l16;
-    const uint2 dd = gload8(Dt + j * DP + 16 * r + 4 * g4);   // D[i][j], i = 16 r + 4 g + e
-    const float dval[4] = {bf16lo(dd.x), bf16hi(dd.x), bf16lo(dd.y), bf16hi(dd.y)};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * r + 4 * g4 + e;
-      float x = (gam[i] * bf_at(Sin + i * DP + j) + so[e]) * dval[e];
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);   // over the 16 columns
-      if (l16 == 0) suf[cc * DP + i] = x;   // summed over the column tiles in a fixed order below
-    }
-  }
-  __syncthreads();
-
-  // ---- 6. dlog_alpha: reverse sum over the chunk plus the later chunks' total
-  if (tid < dk) {
-    const int i = tid;
-    float run = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < DT; ++cc) run += suf[cc * DP + i];
-    for (int t = M - 1; t >= 0; --t) {
-      run += R[t * DP + i];
-      const int n = tok[t];
-      if (n >= 0) P.dg[(((int64_t)bb * T + n) * H + hh) * dk + i] = run;
-    }
+    lds_barrier();
   }
 }
 
@@ -542,37 +672,47 @@ gla_bwd_chunk(BwdParams P) {
 int bwd_pad(int d) { return d <= 32 ? 32 : d <= 64 ? 64 : d <= 80 ? 80 : d <= 96 ? 96 : 128; }
 
 template <int DP, int M>
-hipError_t launch_bwd(const BwdParams &p, hipStream_t s) {
-  constexpr int QS = BwdRow<DP>::QS;
-  const size_t scan_lds = (size_t)3 * M * QS * 2 + DP * 4 + M * 4;
-  const size_t chunk_lds = BwdLds<DP, M>::bytes;
+hipError_t launch_bwd(const BwdParams &p, int num_cu, hipStream_t s) {
+  constexpr int scan_lds = ScanLds<DP, M>::bytes;
+  constexpr int chunk_lds = BwdLds<DP, M>::bytes;
+  static int per_cu = 0;   // resident chunk workgroups per CU; the same on every gfx950
   hipError_t e;
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_scan<DP, M, false>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_lds);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_scan<DP, M, true>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_lds);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_chunk<DP, M>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_lds);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, chunk_lds);
   if (e != hipSuccess) return e;
+  if (per_cu == 0) {
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(gla_bwd_chunk<DP, M>),
+                                                     kChunkWaves * kWave, chunk_lds);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+  }
   const int units = p.B * p.H;
-  hipLaunchKernelGGL((gla_bwd_scan<DP, M, false>), dim3(units), dim3(DP / 16 * kWave), scan_lds, s, p);
+  const int scan_grid = (units * (DP / 16) + 7) / 8 * 8;   // whole XCD groups for xcd_linear_block
+  hipLaunchKernelGGL((gla_bwd_scan<DP, M, false>), dim3(scan_grid), dim3(kWave), scan_lds, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((gla_bwd_scan<DP, M, true>), dim3(units), dim3(DP / 16 * kWave), scan_lds, s, p);
+  hipLaunchKernelGGL((gla_bwd_scan<DP, M, true>), dim3(scan_grid), dim3(kWave), scan_lds, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((gla_bwd_chunk<DP, M>), dim3((int64_t)units * p.nchunks), dim3(kChunkWaves * kWave),
-                     chunk_lds, s, p);
+  const int64_t chunks = (int64_t)units * p.nchunks;
+  const int64_t resident = (int64_t)(num_cu > 0 ? num_cu : 1) * per_cu;
+  const int grid = (int)(chunks < resident ? chunks : resident);
+  hipLaunchKernelGGL((gla_bwd_chunk<DP, M>), dim3(grid), dim3(kChunkWaves * kWave), chunk_lds, s, p);
   return hipGetLastError();
 }
 
 template <int DP>
-hipError_t launch_bwd_m(const BwdParams &p, int M, hipStream_t s) {
+hipError_t launch_bwd_m(const BwdParams &p, int M, int num_cu, hipStream_t s) {
   switch (M) {
-    case 16: return launch_bwd<DP, 16>(p, s);
-    case 32: return launch_bwd<DP, 32>(p, s);
+    case 16: return launch_bwd<DP, 16>(p, num_cu, s);
+    case 32: return launch_bwd<DP, 32>(p, num_cu, s);
     case 64:
-      if constexpr (DP <= 80) return launch_bwd<DP, 64>(p, s);
+      if constexpr (DP <= 80) return launch_bwd<DP, 64>(p, num_cu, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -590,7 +730,7 @@ size_t dig_gla_bwd_workspace(int B, int T, int H, int dk, int dv, int chunk) {
   const int DP = dig::bwd_pad(dk > dv ? dk : dv);
   const int M = dig_gla_bwd_chunk(dk, dv, chunk);
   const size_t N = ((size_t)T + M - 1) / M;
-  return 3 * (size_t)B * H * N * DP * DP * 2;
+  return 2 * (size_t)B * H * N * DP * DP * 2;
 }
 
 hipError_t dig_launch_gla_bwd(const DigGlaBwdArgs &a, hipStream_t s) {
@@ -619,7 +759,6 @@ hipError_t dig_launch_gla_bwd(const DigGlaBwdArgs &a, hipStream_t s) {
   unsigned char *ws = static_cast<unsigned char *>(a.workspace);
   p.st_s = reinterpret_cast<uint16_t *>(ws);
   p.st_d = reinterpret_cast<uint16_t *>(ws + blkb);
-  p.st_dt = reinterpret_cast<uint16_t *>(ws + 2 * blkb);
   auto span = [](int64_t st, int d, int T_) {
     return (unsigned)(((int64_t)(T_ - 1) * st + d) * 2);
   };
@@ -627,10 +766,10 @@ hipError_t dig_launch_gla_bwd(const DigGlaBwdArgs &a, hipStream_t s) {
   p.v_span = span(a.v_st, a.dv, a.T);
   p.do_span = span(a.do_st, a.dv, a.T);
   switch (DP) {
-    case 32: return launch_bwd_m<32>(p, M, s);
-    case 64: return launch_bwd_m<64>(p, M, s);
-    case 80: return launch_bwd_m<80>(p, M, s);
-    case 96: return launch_bwd_m<96>(p, M, s);
-    default: return launch_bwd_m<128>(p, M, s);
+    case 32: return launch_bwd_m<32>(p, M, a.num_cu, s);
+    case 64: return launch_bwd_m<64>(p, M, a.num_cu, s);
+    case 80: return launch_bwd_m<80>(p, M, a.num_cu, s);
+    case 96: return launch_bwd_m<96>(p, M, a.num_cu, s);
+    default: return launch_bwd_m<128>(p, M, a.num_cu, s);
   }
 }

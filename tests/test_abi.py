@@ -136,5 +136,5 @@ def test_bwd_rejects_bad_arguments(L, bad):
 
 def test_bwd_workspace_size(L):
     n = L.gla_bwd_workspace_size(1, 8, 4096, 16, 72, 72, 0)
-    assert n == 3 * 8 * 16 * 64 * 80 * 80 * 2          # three bf16 [units][chunks][80][80] state sets
+    assert n == 2 * 8 * 16 * 64 * 80 * 80 * 2          # two bf16 [units][chunks][80][80] state sets
     assert L.gla_bwd_workspace_size(0, 8, 4096, 16, 72, 72, 0) == ctypes.c_size_t(-1).value
