@@ -206,6 +206,8 @@ int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha, 
         ((int64_t)(T - 1) * v_st + dv) * 2 >= ((int64_t)1 << 31) ||
         ((int64_t)(T - 1) * do_st + dv) * 2 >= ((int64_t)1 << 31))
       return fail(DIG_EINVAL, "gla_bwd: one (batch, head) slice of an input spans 2 GiB or more");
+    if ((int64_t)T * H * dk * 4 >= ((int64_t)1 << 31) || (int64_t)T * H * dv * 2 >= ((int64_t)1 << 31))
+      return fail(DIG_EINVAL, "gla_bwd: one batch of an output spans 2 GiB or more");
     const void *outs[5] = {dq, dk_out, dv_out, dlog_alpha, ds0};
     const void *ins[5] = {q, k, v, log_alpha, d_o};
     for (const void *o : outs)

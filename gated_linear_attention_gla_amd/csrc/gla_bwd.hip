@@ -48,7 +48,8 @@ struct BwdParams {
   uint16_t *gq, *gk, *gv;   // dq, dk, dv: [B, T, H, dk | dv] contiguous, canonical order
   float *dg;                // [B, T, H, dk] contiguous, canonical order
   float *ds0;               // nullable [B, H, dk, dv]
-  uint16_t *st_s;           // [units][N][DP (j)][DP (i)] bf16: state entering chunk c, transposed
+  uint16_t *st_s;           // [units][N] blocks of DP x DP bf16: state entering chunk c, transposed,
+                            // in 16 x 16 tiles (see gla_bwd_scan)
   uint16_t *st_d;           // the same layout: gradient of the state leaving chunk c
   int B, T, H, dk, dv, gh, gw, dir, nchunks;
   unsigned qk_span, v_span, do_span;   // bytes addressable in one (batch, head) slice
@@ -119,39 +120,38 @@ __device__ __forceinline__ uint4 tr_pair(const uint16_t *tile, int stride, int j
 }
 
 // ============================== state scans ==================================
-// One wave per (batch-head unit, key-channel tile r): rows i = 16 r .. 16 r +
-// 15 of the dk x dv state in DT accumulators (rows 16 r + 4 (l/16) + e,
-// columns 16 cc + l%16).  The rows are independent in the recurrence, so the
-// DT waves of a unit never wait for each other; they read the same Y rows
-// (a unit's waves sit on one XCD, so the repeats are L2 hits).  Forward:
-// X = k, Y = v, Z from s0, stores the state entering each chunk.  Reverse:
-// X = q, Y = do (scan order), Z from ds_final, stores the gradient of the
-// state leaving each chunk, then ds0.  The gate cumsum, the scaling of X and
-// X as the MFMA's A operand stay in registers; rows arrive two chunks ahead.
+// One workgroup of DT waves per (batch, head) unit; wave r holds rows i =
+// 16 r .. 16 r + 15 of the dk x dv state in DT accumulators (rows 16 r +
+// 4 (l/16) + e, columns 16 cc + l%16).  The waves load each chunk's rows
+// together (two chunks ahead, in registers) and share them through LDS;
+// otherwise each works on its own rows: the cumsum of its key channels'
+// gates, X scaled in registers and used directly as the MFMA's A operand.
+// Forward: X = k, Y = v, Z from s0, stores the state entering each chunk.
+// Reverse: X = q, Y = do (scan order), Z from ds_final, stores the gradient
+// of the state leaving each chunk, then ds0.  States are stored tile-major:
+// 16 x 16 tile (cc, r) of the transposed state ([j][i]) at (cc DT + r) 256,
+// so each wave's store is 512 contiguous bytes.
 template <int DP, int M>
 struct ScanLds {
   static constexpr int QS = BwdRow<DP>::QS;
-  static constexpr int XS = BwdRow<32>::QS;   // [M][XS]: X channels in columns 0..15, gates in 16..31
-  static constexpr int bytes = M * QS * 2 + M * XS * 2;
+  static constexpr int bytes = 3 * M * QS * 2;   // X, gates, Y: token-major [M][QS]
 };
 
 template <int DP, int M, bool REV>
-__global__ void __launch_bounds__(kWave)
+__global__ void __launch_bounds__(DP / 16 * kWave)
 gla_bwd_scan(BwdParams P) {
-  constexpr int DT = DP / 16, MT = M / 16, JP = (MT + 1) / 2;
-  constexpr int QS = ScanLds<DP, M>::QS, XS = ScanLds<DP, M>::XS, CG = DP / 8;
-  constexpr int ITY = (M * CG + kWave - 1) / kWave, ITX = (2 * M + kWave - 1) / kWave;
-  static_assert(M <= kWave, "one token per lane for the canonical index");
+  constexpr int DT = DP / 16, MT = M / 16, JP = (MT + 1) / 2, NT = DT * kWave;
+  constexpr int QS = ScanLds<DP, M>::QS, CG = DP / 8;
+  constexpr int IT = (M * CG + NT - 1) / NT;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t *tY = reinterpret_cast<uint16_t *>(smem);
-  uint16_t *tXG = tY + M * QS;
+  uint16_t *tX = reinterpret_cast<uint16_t *>(smem);
+  uint16_t *tG = tX + M * QS;
+  uint16_t *tY = tG + M * QS;
 
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int r = __builtin_amdgcn_readfirstlane(tid >> 6);   // key-channel tile of this wave
   const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
-  const int lb = xcd_linear_block(blockIdx.x, gridDim.x);
-  const int unit = lb / DT, r = lb - unit * DT;
-  if (unit >= P.B * P.H) return;
-  const int bb = unit / P.H, hh = unit - bb * P.H;
+  const int unit = blockIdx.x, bb = unit / P.H, hh = unit - bb * P.H;
   const int T = P.T, dk = P.dk, dv = P.dv, N = P.nchunks;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc((REV ? P.q : P.k) + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(P.g + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
@@ -170,44 +170,33 @@ gla_bwd_scan(BwdParams P) {
     }
 
   struct Rows {
-    uint4 y[ITY], x[ITX], g[ITX];
+    uint4 x[IT], g[IT], y[IT];
   };
   auto fetch = [&](Rows &f, int c) {
-    const int pl = c * M + (lane < M ? lane : 0);
-    const int nl = (lane < M && pl < T) ? scan_to_canon(P.dir, P.gh, P.gw, T, pl) : -1;
 #pragma unroll
-    for (int kq = 0; kq < ITY; ++kq) {
-      const int idx = lane + kq * kWave;
+    for (int kq = 0; kq < IT; ++kq) {
+      const int idx = tid + kq * NT;
       const int tl = idx / CG, cg = idx - tl * CG;
-      const int n = __shfl(nl, tl < M ? tl : 0, kWave);
-      const bool ok = idx < M * CG && n >= 0 && 8 * cg < dv;
-      const int64_t yrow = REV ? (int64_t)c * M + tl : (int64_t)n;
-      f.y[kq] = bload16(ry, ok ? (unsigned)((yrow * y_st + 8 * cg) * 2) : kOOB);
-    }
-#pragma unroll
-    for (int kq = 0; kq < ITX; ++kq) {
-      const int idx = lane + kq * kWave;
-      const int tl = idx >> 1, ch = 16 * r + 8 * (idx & 1);
-      const int n = __shfl(nl, tl < M ? tl : 0, kWave);
-      const unsigned off = (idx < 2 * M && n >= 0 && ch < dk) ? (unsigned)(((int64_t)n * P.qk_st + ch) * 2) : kOOB;
-      f.x[kq] = bload16(rx, off);
-      f.g[kq] = bload16(rg, off);
+      const int p = c * M + tl;
+      const bool ok = idx < M * CG && p < T;
+      const int n = ok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
+      const int64_t yrow = REV ? (int64_t)p : (int64_t)n;
+      const unsigned oxg = (ok && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
+      const unsigned oy = (ok && 8 * cg < dv) ? (unsigned)((yrow * y_st + 8 * cg) * 2) : kOOB;
+      f.x[kq] = bload16(rx, oxg);
+      f.g[kq] = bload16(rg, oxg);
+      f.y[kq] = bload16(ry, oy);
     }
   };
   auto stash = [&](const Rows &f) {
 #pragma unroll
-    for (int kq = 0; kq < ITY; ++kq) {
-      const int idx = lane + kq * kWave;
+    for (int kq = 0; kq < IT; ++kq) {
+      const int idx = tid + kq * NT;
       const int tl = idx / CG, cg = idx - tl * CG;
-      if (idx < M * CG) *reinterpret_cast<uint4 *>(tY + tl * QS + 8 * cg) = f.y[kq];
-    }
-#pragma unroll
-    for (int kq = 0; kq < ITX; ++kq) {
-      const int idx = lane + kq * kWave;
-      const int tl = idx >> 1, h = idx & 1;
-      if (idx < 2 * M) {
-        *reinterpret_cast<uint4 *>(tXG + tl * XS + 8 * h) = f.x[kq];
-        *reinterpret_cast<uint4 *>(tXG + tl * XS + 16 + 8 * h) = f.g[kq];
+      if ((M * CG) % NT == 0 || idx < M * CG) {
+        *reinterpret_cast<uint4 *>(tX + tl * QS + 8 * cg) = f.x[kq];
+        *reinterpret_cast<uint4 *>(tG + tl * QS + 8 * cg) = f.g[kq];
+        *reinterpret_cast<uint4 *>(tY + tl * QS + 8 * cg) = f.y[kq];
       }
     }
   };
@@ -215,27 +204,28 @@ gla_bwd_scan(BwdParams P) {
   uint16_t *zbase = (REV ? P.st_d : P.st_s) + (int64_t)unit * N * DP * DP;
   auto step = [&](Rows &f, int it) {
     const int c = REV ? N - 1 - it : it;
-    // the state for chunk c, transposed ([j][i]), padding included (zero)
-    uint16_t *zt = zbase + (int64_t)c * DP * DP;
+    // the state for chunk c (transposed, tile-major; padding included, zero)
+    uint16_t *zt = zbase + (int64_t)c * DP * DP + r * 256 + l16 * 16 + 4 * g4;
 #pragma unroll
-    for (int cc = 0; cc < DT; ++cc)
-      *reinterpret_cast<uint2 *>(zt + (16 * cc + l16) * DP + 16 * r + 4 * g4) = pack4(Z[cc]);
+    for (int cc = 0; cc < DT; ++cc) *reinterpret_cast<uint2 *>(zt + cc * DT * 256) = pack4(Z[cc]);
     stash(f);
     lds_barrier();
-    if (it + 2 < N) fetch(f, REV ? c - 2 : c + 2);
-    // cumulative gates (accumulator layout: token 16 I + 4 (l/16) + e,
-    // channel 16 r + l%16) and X scaled by e^{B - b} (forward) or e^{b}
-    // (reverse), both <= 1
+    // issued on every step (past the ends: the last chunk again, unused) so
+    // the wait before each stash covers exactly the rows it needs
+    fetch(f, REV ? max(c - 2, 0) : min(c + 2, N - 1));
+    // cumulative gates of key-channel tile r (accumulator layout: token
+    // 16 I + 4 (l/16) + e, channel 16 r + l%16) and X scaled by e^{B - b}
+    // (forward) or e^{b} (reverse), both <= 1
     uint2 xh[MT];
     float tot;
     {
       f32x4_t cum[MT];
 #pragma unroll
-      for (int I = 0; I < MT; ++I) cum[I] = tile_cumsum<MT, XS>(tXG + 16, I, 0, l16, g4);
+      for (int I = 0; I < MT; ++I) cum[I] = tile_cumsum<MT, QS>(tG, I, r, l16, g4);
       tot = __shfl(cum[MT - 1][3], 48 + l16, kWave);   // token M-1: lane group 3, e = 3
 #pragma unroll
       for (int I = 0; I < MT; ++I) {
-        const float4 xv = unpack4(lds_tr(tXG + (16 * I + 4 * g4 + rowoff) * XS + coloff));
+        const float4 xv = unpack4(lds_tr(tX + (16 * I + 4 * g4 + rowoff) * QS + 16 * r + coloff));
         f32x4_t sx;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sx[e] = elt(xv, e) * fexp2((REV ? cum[I][e] : tot - cum[I][e]) * kLog2e);
@@ -259,11 +249,15 @@ gla_bwd_scan(BwdParams P) {
 
   Rows fa, fb;
   fetch(fa, REV ? N - 1 : 0);
-  if (N > 1) fetch(fb, REV ? N - 2 : 1);
-  for (int it = 0; it < N; it += 2) {
+  fetch(fb, REV ? max(N - 2, 0) : min(1, N - 1));
+  // whole pairs in the loop (no conditional step, so each stash waits for
+  // exactly its own rows), an odd last chunk after it
+  int it = 0;
+  for (; it + 1 < N; it += 2) {
     step(fa, it);
-    if (it + 1 < N) step(fb, it + 1);
+    step(fb, it + 1);
   }
+  if (it < N) step(fa, it);
   if (REV && P.ds0) {
 #pragma unroll
     for (int cc = 0; cc < DT; ++cc)
@@ -288,15 +282,15 @@ struct BwdLds {
   static constexpr int oS = 5 * TILE, oD = oS + STB;   // S_in^T, D^T
   static constexpr int oA = oD + STB;                  // [M][SA] bf16 A = dO V^T (causal)
   static constexpr int oP = oA + M * SA * 2;           // [M][SA] bf16 P (causal)
-  static constexpr int oB = oP + M * SA * 2;           // [M][DP] fp32 b (log2 units), extreme chunks
-  static constexpr int oTok = oB + M * DP * 4;         // [M] canonical token, -1 past T
-  static constexpr int oFlag = oTok + M * 4;           // any |b| beyond the factorised range
+  static constexpr int oB = oP + M * SA * 2;           // [M][DP] fp32: b (log2 units) of extreme chunks, then d log alpha
+  static constexpr int oTok = oB + M * DP * 4;         // [2][M] canonical token, -1 past T (this chunk, the one before)
+  static constexpr int oFlag = oTok + 2 * M * 4;       // any |b| beyond the factorised range
   static constexpr int bytes = oFlag + 16;
 };
 
 constexpr int kChunkWaves = 8;
 
-// Persistent: workgroup w takes chunks w, w + grid, ...; the next chunk's
+// Persistent: each workgroup takes a run of consecutive chunks; the next chunk's
 // rows and both state blocks are loaded into registers while the current one
 // is computed.  Wave r < DT owns key-channel tile r from the gate cumsum to
 // its dq, dk and dlog_alpha (b, raw and scaled q, k and the rowsum of
@@ -305,7 +299,11 @@ constexpr int kChunkWaves = 8;
 //   phase 1: cumsum, range check, raw q, k (channel waves) | A tiles
 //   phase 2: scaled rows into LDS, rowsum(S_out (.) D) (channel waves)
 //   phase 3: dq, dk, dlog_alpha (channel waves, token tiles last to first) | P tiles
-//   phase 4: dv
+//   phase 4: dq, dk staged in LDS; dv
+//   phase 5: the staged outputs into registers
+// The outputs leave as 16-byte rows after the next chunk's rows are in LDS,
+// behind that chunk's prefetch, so neither waits for the other; both are
+// long complete when the next chunk's rows are needed.
 template <int DP, int M>
 __global__ void __launch_bounds__(kChunkWaves * kWave)
 gla_bwd_chunk(BwdParams P) {
@@ -337,33 +335,46 @@ gla_bwd_chunk(BwdParams P) {
   // tiles above the diagonal of A and P stay zero
   for (int x = tid0; x < 2 * M * SA / 8; x += NT) reinterpret_cast<uint4 *>(tA)[x] = make_uint4(0, 0, 0, 0);
 
+  // prefetch registers, filled in three groups spread over the chunk before
+  // (the rows' canonical tokens are kept from the first group for the second)
   uint4 fq[ITT], fk[ITT], fg[ITT], fv[ITT], fo[ITT], fs[ITS], fd[ITS];
-  auto fetch = [&](int w) {
+  int pn[ITT];
+  auto fetch_qkg = [&](int w) {
     const int unit = w / N, c = w - unit * N, bb = unit / H, hh = unit - bb * H;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(P.q + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.k + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(P.g + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.v + bb * P.v_sb + hh * P.v_sh, P.v_span);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(P.dout + bb * P.do_sb + hh * P.do_sh, P.do_span);
-    const int64_t blk = ((int64_t)unit * N + c) * DP * DP;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.st_s + blk, DP * DP * 2);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(P.st_d + blk, DP * DP * 2);
 #pragma unroll
     for (int kq = 0; kq < ITT; ++kq) {
       const int idx = tid0 + kq * NT;
       const int tl = idx / CG, cg = idx - tl * CG;
       const int p = c * M + tl;
-      const bool ok = idx < M * CG && p < T;
-      const int n = ok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
-      const unsigned oqk = (ok && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
-      const unsigned ov = (ok && 8 * cg < dv) ? (unsigned)(((int64_t)n * P.v_st + 8 * cg) * 2) : kOOB;
-      const unsigned oo = (ok && 8 * cg < dv) ? (unsigned)(((int64_t)p * P.do_st + 8 * cg) * 2) : kOOB;
+      const int n = (idx < M * CG && p < T) ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
+      pn[kq] = n;
+      const unsigned oqk = (n >= 0 && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
       fq[kq] = bload16(rq, oqk);
       fk[kq] = bload16(rk, oqk);
       fg[kq] = bload16(rg, oqk);
-      fv[kq] = bload16(rv, ov);
-      fo[kq] = bload16(ro, oo);
     }
+  };
+  auto fetch_vo = [&](int w) {
+    const int unit = w / N, c = w - unit * N, bb = unit / H, hh = unit - bb * H;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.v + bb * P.v_sb + hh * P.v_sh, P.v_span);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(P.dout + bb * P.do_sb + hh * P.do_sh, P.do_span);
+#pragma unroll
+    for (int kq = 0; kq < ITT; ++kq) {
+      const int idx = tid0 + kq * NT;
+      const int tl = idx / CG, cg = idx - tl * CG;
+      const int n = pn[kq];
+      const bool ok = n >= 0 && 8 * cg < dv;
+      fv[kq] = bload16(rv, ok ? (unsigned)(((int64_t)n * P.v_st + 8 * cg) * 2) : kOOB);
+      fo[kq] = bload16(ro, ok ? (unsigned)((((int64_t)c * M + tl) * P.do_st + 8 * cg) * 2) : kOOB);
+    }
+  };
+  auto fetch_states = [&](int w) {
+    const int64_t blk = (int64_t)w * DP * DP;   // chunk w of unit w / N
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P.st_s + blk, DP * DP * 2);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(P.st_d + blk, DP * DP * 2);
 #pragma unroll
     for (int kq = 0; kq < ITS; ++kq) {
       const int idx = tid0 + kq * NT;
@@ -373,10 +384,50 @@ gla_bwd_chunk(BwdParams P) {
     }
   };
 
-  int w = blockIdx.x;
-  if (w < total) fetch(w);
-  for (; w < total; w += gridDim.x) {
-    const int unit = w / N, c = w - unit * N, bb = unit / H, hh = unit - bb * H;
+  // one chunk's outputs, read back from the LDS staging (phase 5) and stored
+  // to memory once the next chunk's first barrier has passed
+  constexpr int ITO = (M * CG + NT - 1) / NT, ITG = (M * (DP / 4) + NT - 1) / NT;
+  uint4 oq[ITO], ok[ITO], ov[ITO], og[ITG];
+  auto store_outputs = [&](int wp, const int *tk, bool valid) {
+    const int unit = wp / N, bb = unit / H, hh = unit - bb * H;
+    const int64_t row0 = (int64_t)bb * T * H + hh;   // token 0 of this (batch, head), in rows of H
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(P.gq + row0 * dk, (unsigned)(((int64_t)(T - 1) * H * dk + dk) * 2));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.gk + row0 * dk, (unsigned)(((int64_t)(T - 1) * H * dk + dk) * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(P.gv + row0 * dv, (unsigned)(((int64_t)(T - 1) * H * dv + dv) * 2));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(P.dg + row0 * dk, (unsigned)(((int64_t)(T - 1) * H * dk + dk) * 4));
+#pragma unroll
+    for (int kq = 0; kq < ITO; ++kq) {
+      const int idx = tid0 + kq * NT;
+      const int t = idx / CG, cg = idx - t * CG;
+      const int n = (valid && idx < M * CG) ? tk[t] : -1;
+      const unsigned oqk = (n >= 0 && 8 * cg < dk) ? (unsigned)(((int64_t)n * H * dk + 8 * cg) * 2) : kOOB;
+      const unsigned ovv = (n >= 0 && 8 * cg < dv) ? (unsigned)(((int64_t)n * H * dv + 8 * cg) * 2) : kOOB;
+      bstore16(rq, oqk, oq[kq]);
+      bstore16(rk, oqk, ok[kq]);
+      bstore16(rv, ovv, ov[kq]);
+    }
+#pragma unroll
+    for (int kq = 0; kq < ITG; ++kq) {
+      const int idx = tid0 + kq * NT;
+      const int t = idx / (DP / 4), cg = idx - t * (DP / 4);
+      const int n = (valid && idx < M * (DP / 4)) ? tk[t] : -1;
+      const unsigned og4 = (n >= 0 && 4 * cg < dk) ? (unsigned)(((int64_t)n * H * dk + 4 * cg) * 4) : kOOB;
+      bstore16(rg, og4, og[kq]);
+    }
+  };
+
+  // a contiguous run of chunks per workgroup: consecutive chunks of one
+  // (batch, head) share memory pages
+  const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int wend = min(total, ((int)blockIdx.x + 1) * per);
+  int w = blockIdx.x * per, wprev = -1, par = 0;
+  if (w < wend) {
+    fetch_qkg(w);
+    fetch_vo(w);
+    fetch_states(w);
+  }
+  for (; w < wend; wprev = w, ++w, par ^= 1) {
+    const int c = w - (w / N) * N;
     // The lane index is hidden from the optimiser here, so the per-lane LDS
     // addresses are formed inside each chunk's code rather than hoisted out
     // of the loop (hundreds of them, which would not fit in registers).
@@ -403,18 +454,27 @@ gla_bwd_chunk(BwdParams P) {
     for (int kq = 0; kq < ITS; ++kq) {
       const int idx = tid + kq * NT;
       if (idx < DP * CG) {
-        const int j = idx / CG, cg = idx - j * CG;
-        *reinterpret_cast<uint4 *>(tS + j * QS + 8 * cg) = fs[kq];
-        *reinterpret_cast<uint4 *>(tD + j * QS + 8 * cg) = fd[kq];
+        // tile-major blocks: 16-byte group idx is row jj, columns ii .. ii+7
+        // of tile (cc, r) = (tile / DT, tile % DT)
+        const int tile = idx >> 5, cc = tile / DT, rr = tile - cc * DT;
+        const int at = (16 * cc + ((idx & 31) >> 1)) * QS + 16 * rr + 8 * (idx & 1);
+        *reinterpret_cast<uint4 *>(tS + at) = fs[kq];
+        *reinterpret_cast<uint4 *>(tD + at) = fd[kq];
       }
     }
+    int *tk = tok + par * M;   // this chunk's canonical tokens; the other half: the chunk before
     if (tid < M) {
       const int p = c * M + tid;
-      tok[tid] = p < T ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
+      tk[tid] = p < T ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
     }
     if (tid == 0) *flag = 0u;
     lds_barrier();
-    if (w + (int)gridDim.x < total) fetch(w + gridDim.x);
+    // every memory operation below is issued on every chunk (the last chunk
+    // refetches itself; the first stores nothing), so the compiler's waits
+    // before the next chunk's rows are exact
+    const int wn = min(w + 1, wend - 1);
+    fetch_qkg(wn);
+    store_outputs(wprev >= 0 ? wprev : w, tok + (par ^ 1) * M, wprev >= 0);
 
     // ---- 1. cumulative gates (log2 units) and raw q, k of tile r, in
     //         accumulator layout (token 16 I + 4 (l/16) + e, channel 16 r + l%16)
@@ -458,6 +518,7 @@ gla_bwd_chunk(BwdParams P) {
     // ---- 2. scaled rows of tile r into LDS (k e^{B - b} always; q e^{b},
     //         k e^{-b} where factorised, else b itself), and rowsum(S_out (.) D)
     //         with S_out = diag(e^{B}) S_in + K^^T V
+    fetch_vo(wn);
     const bool fast = *flag == 0u;
     uint2 qt[MT], kt[MT];
     float sufS = 0.f;   // rowsum(S_out (.) D) of channel 16 r + l%16
@@ -519,6 +580,7 @@ gla_bwd_chunk(BwdParams P) {
     }
     lds_barrier();
 
+    fetch_states(wn);
     // ---- 3. (chunks beyond the factorised range) P with exact exponent differences
     if (!fast) {
       for (int x = tid; x < M * M; x += NT) {
@@ -529,6 +591,7 @@ gla_bwd_chunk(BwdParams P) {
             acc += bf_at(tQ + t * QS + i) * bf_at(tK + s * QS + i) * fexp2(bL[t * DP + i] - bL[s * DP + i]);
         tP[t * SA + s] = to_bf(acc);
       }
+      lds_barrier();   // every b read for P before d log alpha replaces it
     }
     //         dq, dk, dlog_alpha of tile r, token tiles last to first (the
     //         reverse sum over the chunk runs in registers)
@@ -547,6 +610,7 @@ gla_bwd_chunk(BwdParams P) {
         dBh = lds_tr(tD + (32 * K32 + 4 * g4 + rowoff) * QS + 16 * r + coloff);
       }
       float run = sufS;
+      f32x4_t dgx[MT];   // extreme chunks: d log alpha held until the exact sums are done
 #pragma unroll
       for (int I = MT - 1; I >= 0; --I) {
         const uint16_t *orow = tO + (16 * I + l16) * QS, *vrow = tV + (16 * I + l16) * QS;
@@ -589,25 +653,21 @@ gla_bwd_chunk(BwdParams P) {
         }
         const float4 q4 = unpack4(qa[I]), k4 = unpack4(ka[I]);
         float R[4];
+        f32x4_t dq4, dk4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float b = bl[I][e];
-          float dqv, dkv;
           if (fast) {
-            dqv = fexp2(b) * (x1[e] + y1[e]);
-            dkv = fexp2(-b) * y2[e] + fexp2(Bt - b) * x2[e];
+            dq4[e] = fexp2(b) * (x1[e] + y1[e]);
+            dk4[e] = fexp2(-b) * y2[e] + fexp2(Bt - b) * x2[e];
           } else {
-            dqv = fexp2(b) * x1[e] + y1[e];
-            dkv = y2[e] + fexp2(Bt - b) * x2[e];
+            dq4[e] = fexp2(b) * x1[e] + y1[e];
+            dk4[e] = y2[e] + fexp2(Bt - b) * x2[e];
           }
-          R[e] = elt(q4, e) * dqv - elt(k4, e) * dkv;
-          const int n = tok[16 * I + 4 * g4 + e];
-          if (n >= 0 && i < dk) {
-            const int64_t o = (((int64_t)bb * T + n) * H + hh) * dk + i;
-            P.gq[o] = to_bf(dqv);
-            P.gk[o] = to_bf(dkv);
-          }
+          R[e] = elt(q4, e) * dq4[e] - elt(k4, e) * dk4[e];
         }
+        qa[I] = pack4(dq4);   // the raw q, k of tile I are no longer needed
+        ka[I] = pack4(dk4);
         // reverse sum: inside the lane's 4 tokens, then over the later lane groups
         const float s3 = R[3], s2 = R[2] + s3, s1 = R[1] + s2, s0 = R[0] + s1;
         const float L0 = __shfl(s0, l16, kWave), L1 = __shfl(s0, 16 + l16, kWave);
@@ -616,10 +676,16 @@ gla_bwd_chunk(BwdParams P) {
         const float sv[4] = {s0, s1, s2, s3};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int n = tok[16 * I + 4 * g4 + e];
-          if (n >= 0 && i < dk) P.dg[(((int64_t)bb * T + n) * H + hh) * dk + i] = after + sv[e];
+          if (fast) bL[(16 * I + 4 * g4 + e) * DP + i] = after + sv[e];
+          else dgx[I][e] = after + sv[e];
         }
         run += ((L0 + L1) + L2) + L3;
+      }
+      if (!fast) {
+#pragma unroll
+        for (int I = 0; I < MT; ++I)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bL[(16 * I + 4 * g4 + e) * DP + i] = dgx[I][e];
       }
     }
     //         P = Q~ K~^T on tiles J <= I (factorised chunks)
@@ -642,9 +708,22 @@ gla_bwd_chunk(BwdParams P) {
     }
     lds_barrier();
 
-    // ---- 4. dv = P^T dO + K^ D (unit (I, cc): tokens of tile I, value
-    //         channels of tile cc); K = tokens (transposing reads), then key
-    //         channels (rows of D^T)
+    // ---- 4. dq, dk into the q, k tiles (free once P is formed), and
+    //         dv = P^T dO + K^ D into the v tile (unit (I, cc): tokens of tile I,
+    //         value channels of tile cc; K = tokens by transposing reads, then
+    //         key channels along rows of D^T)
+    if (chan) {
+      const int i = 16 * r + l16;
+#pragma unroll
+      for (int I = 0; I < MT; ++I)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int at = (16 * I + 4 * g4 + e) * QS + i;
+          const int sh = (e & 1) * 16;
+          tQ[at] = (uint16_t)((e < 2 ? qa[I].x : qa[I].y) >> sh);
+          tK[at] = (uint16_t)((e < 2 ? ka[I].x : ka[I].y) >> sh);
+        }
+    }
     for (int u = wslot; u < MT * DT; u += kChunkWaves) {
       const int I = u / DT, cc = u - I * DT;
       f32x4_t y3 = {0.f, 0.f, 0.f, 0.f};
@@ -659,13 +738,30 @@ gla_bwd_chunk(BwdParams P) {
       if (KH) y3 = mfma16(lds2(hrow + 32 * K32 + 4 * g4), lds2(drow + 32 * K32 + 4 * g4), y3);
       const int j = 16 * cc + l16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n = tok[16 * I + 4 * g4 + e];
-        if (n >= 0 && j < dv) P.gv[(((int64_t)bb * T + n) * H + hh) * dv + j] = to_bf(y3[e]);
-      }
+      for (int e = 0; e < 4; ++e) tV[(16 * I + 4 * g4 + e) * QS + j] = to_bf(y3[e]);
+    }
+    lds_barrier();
+
+    // ---- 5. the staged outputs into registers; they are stored after the
+    //         next chunk's first barrier
+#pragma unroll
+    for (int kq = 0; kq < ITO; ++kq) {
+      const int idx = tid + kq * NT;
+      const int t = idx / CG, cg = idx - t * CG;
+      const int at = (idx < M * CG ? t : 0) * QS + 8 * cg;
+      oq[kq] = *reinterpret_cast<const uint4 *>(tQ + at);
+      ok[kq] = *reinterpret_cast<const uint4 *>(tK + at);
+      ov[kq] = *reinterpret_cast<const uint4 *>(tV + at);
+    }
+#pragma unroll
+    for (int kq = 0; kq < ITG; ++kq) {
+      const int idx = tid + kq * NT;
+      const int t = idx / (DP / 4), cg = idx - t * (DP / 4);
+      og[kq] = *reinterpret_cast<const uint4 *>(bL + (idx < M * (DP / 4) ? t : 0) * DP + 4 * cg);
     }
     lds_barrier();
   }
+  if (wprev >= 0) store_outputs(wprev, tok + (par ^ 1) * M, true);
 }
 
 // ------------------------------ host side -----------------------------------
@@ -694,10 +790,9 @@ hipError_t launch_bwd(const BwdParams &p, int num_cu, hipStream_t s) {
     per_cu = nb > 0 ? nb : 1;
   }
   const int units = p.B * p.H;
-  const int scan_grid = (units * (DP / 16) + 7) / 8 * 8;   // whole XCD groups for xcd_linear_block
-  hipLaunchKernelGGL((gla_bwd_scan<DP, M, false>), dim3(scan_grid), dim3(kWave), scan_lds, s, p);
+  hipLaunchKernelGGL((gla_bwd_scan<DP, M, false>), dim3(units), dim3(DP / 16 * kWave), scan_lds, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((gla_bwd_scan<DP, M, true>), dim3(scan_grid), dim3(kWave), scan_lds, s, p);
+  hipLaunchKernelGGL((gla_bwd_scan<DP, M, true>), dim3(units), dim3(DP / 16 * kWave), scan_lds, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t chunks = (int64_t)units * p.nchunks;
   const int64_t resident = (int64_t)(num_cu > 0 ? num_cu : 1) * per_cu;

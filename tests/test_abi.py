@@ -127,6 +127,9 @@ def _bwd(L, **kw):
     dict(q=None), dict(do=None), dict(dq=None), dict(dg=None), dict(dtype=0), dict(B=0), dict(dk=0),
     dict(dv=136), dict(dk=12, dv=12), dict(gh=7), dict(dir=4), dict(chunk=48), dict(dk=96, dv=96, chunk=64),
     dict(q=18), dict(do=88), dict(dos=(4096 * 64, 60, 8)), dict(qk=(-8, 64, 8)), dict(dq=16),
+    # d log alpha of one batch (T * H * dk fp32) would span 2 GiB
+    dict(T=65536, gh=256, gw=256, H=64, dk=128, dv=128, qk=(65536 * 128, 128, 8), vs=(65536 * 128, 128, 8),
+         dos=(65536 * 128, 128, 8)),
 ])
 def test_bwd_rejects_bad_arguments(L, bad):
     rc = _bwd(L, **bad)
