@@ -23,10 +23,10 @@
 // of all gates after a point by a constant only rescales the state at that
 // point (so the later tokens' total is rowsum(S (.) dL/dS) there).
 //
-// Three launches:
-//   gla_bwd_scan<.., false>  S_in of every chunk (forward over chunks);
-//   gla_bwd_scan<.., true>   D of every chunk (reverse over chunks), and ds0;
-//   gla_bwd_chunk            the chunks, independently: dq, dk, dv, dlog_alpha.
+// Two launches:
+//   gla_bwd_scan   S_in of every chunk (forward over chunks) and, side by
+//                  side, D of every chunk (reverse over chunks), and ds0;
+//   gla_bwd_chunk  the chunks, independently: dq, dk, dv, dlog_alpha.
 // Both state sets are kept transposed ([value channel j][key channel i],
 // bf16).  The scans use only factors e^{B - b} and e^{b} (<= 1 for gates <=
 // 0).  The chunk kernel factorises e^{b_t - b_s} as e^{b_t} e^{-b_s} when
@@ -138,8 +138,7 @@ struct ScanLds {
 };
 
 template <int DP, int M, bool REV>
-__global__ void __launch_bounds__(DP / 16 * kWave)
-gla_bwd_scan(BwdParams P) {
+__device__ __forceinline__ void scan_unit(const BwdParams &P, int unit) {
   constexpr int DT = DP / 16, MT = M / 16, JP = (MT + 1) / 2, NT = DT * kWave;
   constexpr int QS = ScanLds<DP, M>::QS, CG = DP / 8;
   constexpr int IT = (M * CG + NT - 1) / NT;
@@ -151,7 +150,7 @@ gla_bwd_scan(BwdParams P) {
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
   const int r = __builtin_amdgcn_readfirstlane(tid >> 6);   // key-channel tile of this wave
   const int rowoff = l16 >> 2, coloff = 4 * (l16 & 3);
-  const int unit = blockIdx.x, bb = unit / P.H, hh = unit - bb * P.H;
+  const int bb = unit / P.H, hh = unit - bb * P.H;
   const int T = P.T, dk = P.dk, dv = P.dv, N = P.nchunks;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc((REV ? P.q : P.k) + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(P.g + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
@@ -267,6 +266,16 @@ gla_bwd_scan(BwdParams P) {
         if (i < dk && j < dv) P.ds0[((int64_t)unit * dk + i) * dv + j] = Z[cc][e];
       }
   }
+}
+
+// Both scans in one launch (they are independent): workgroups [0, units)
+// run the forward scan, [units, 2 units) the reverse one.
+template <int DP, int M>
+__global__ void __launch_bounds__(DP / 16 * kWave)
+gla_bwd_scan(BwdParams P) {
+  const int units = P.B * P.H;
+  if ((int)blockIdx.x < units) scan_unit<DP, M, false>(P, blockIdx.x);
+  else scan_unit<DP, M, true>(P, blockIdx.x - units);
 }
 
 // ============================ chunk gradients ================================
@@ -773,10 +782,7 @@ hipError_t launch_bwd(const BwdParams &p, int num_cu, hipStream_t s) {
   constexpr int chunk_lds = BwdLds<DP, M>::bytes;
   static int per_cu = 0;   // resident chunk workgroups per CU; the same on every gfx950
   hipError_t e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_scan<DP, M, false>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_scan<DP, M, true>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_scan<DP, M>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_chunk<DP, M>),
@@ -790,9 +796,7 @@ hipError_t launch_bwd(const BwdParams &p, int num_cu, hipStream_t s) {
     per_cu = nb > 0 ? nb : 1;
   }
   const int units = p.B * p.H;
-  hipLaunchKernelGGL((gla_bwd_scan<DP, M, false>), dim3(units), dim3(DP / 16 * kWave), scan_lds, s, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((gla_bwd_scan<DP, M, true>), dim3(units), dim3(DP / 16 * kWave), scan_lds, s, p);
+  hipLaunchKernelGGL((gla_bwd_scan<DP, M>), dim3(2 * units), dim3(DP / 16 * kWave), scan_lds, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t chunks = (int64_t)units * p.nchunks;
   const int64_t resident = (int64_t)(num_cu > 0 ? num_cu : 1) * per_cu;
