@@ -240,7 +240,7 @@ def bench_bwd(a, dg, gen, torch) -> int:
                    "directions": list(cfg.dirs), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gla_bwd (gla_bwd_scan x2 + gla_bwd_chunk)", "alg_bytes_per_launch": abytes,
+                     "kernel": "gla_bwd (gla_bwd_scan, both directions in one launch, + gla_bwd_chunk)", "alg_bytes_per_launch": abytes,
                      "avg_launch_us": avg * 1e3},
         "gla_bwd": {"tflops_alg": aflops / (avg * 1e-3) / 1e12,
                     "mfma_frac": aflops / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
