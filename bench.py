@@ -170,9 +170,9 @@ def cpu_baseline_bwd(cfg, x_cpu, do_cpu, budget_s: float = 20.0):
 
 
 def bench_bwd(a, dg, gen, torch) -> int:
-    """gla_bwd on the workload's shape: one step = one backward call (three launches on one
-    stream: forward state scan, reverse state-gradient scan, chunk gradients) over rotating
-    input sets, timed with HIP events on that stream."""
+    """gla_bwd on the workload's shape: one step = one backward call (two launches on one
+    stream: the forward state scan and the reverse state-gradient scan side by side, then the
+    chunk gradients) over rotating input sets, timed with HIP events on that stream."""
     dev = torch.device("cuda:0")
     cfg = gen.CONFIGS[a.config]
     if cfg.adaln:
