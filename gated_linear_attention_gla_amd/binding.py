@@ -41,12 +41,22 @@ def lib() -> ctypes.CDLL:
                                   i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                   p, p, i64, i64, i64, p, p, sz, p]
             L.gla_fwd.restype = i32
+            L.gla_fwd_ordered.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
+                                          i32, i32, i32, i32, i32, p, i32,
+                                          p, p, i64, i64, i64, p, p, sz, p]
+            L.gla_fwd_ordered.restype = i32
             L.gla_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
             L.gla_fwd_workspace_size.restype = sz
             L.gla_bwd.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
                                   i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                   p, p, i64, i64, i64, p, p, p, p, p, p, p, sz, p]
             L.gla_bwd.restype = i32
+            L.gla_bwd_ordered.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
+                                          i32, i32, i32, i32, i32, p, i32,
+                                          p, p, i64, i64, i64, p, p, p, p, p, p, p, sz, p]
+            L.gla_bwd_ordered.restype = i32
+            L.dig_gather_rows.argtypes = [p, i32, i32, i32, i32, p, p, p]
+            L.dig_gather_rows.restype = i32
             L.gla_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
             L.gla_bwd_workspace_size.restype = sz
             L.srem_dwconv.argtypes = [p, i32, i32, i32, i32, i64, i64, p, i32, i32, i32, p, i64, i64, p]
@@ -89,6 +99,14 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _order(order, T: int, device: torch.device):
+    """A scan-order table for the *_ordered calls: int32 [T], contiguous, on `device`."""
+    if order.dtype != torch.int32 or tuple(order.shape) != (T,) or not order.is_contiguous() \
+            or order.device != device:
+        raise DigError(f"order must be a contiguous int32 [{T}] tensor on {device}")
+    return order
+
+
 def workspace_bytes(dtype_code: int, B: int, T: int, H: int, dk: int, dv: int, chunk: int = 0) -> int:
     n = lib().gla_fwd_workspace_size(dtype_code, B, T, H, dk, dv, chunk)
     if n == ctypes.c_size_t(-1).value:
@@ -112,11 +130,14 @@ def get_workspace(device: torch.device, nbytes: int, key: str = "fwd") -> torch.
 
 
 def gla_fwd(q, k, v, log_alpha, grid, direction, chunk: int = 0, s0=None, out=None,
-            s_final: bool | torch.Tensor = True, workspace=None):
+            s_final: bool | torch.Tensor = True, workspace=None, order=None):
     """GLA forward over one scan direction.
 
     q, k, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; canonical token order,
     innermost dim contiguous, all on one GPU, same dtype (bf16 or fp32).
+    order: optional int32 [T] device table (scan position -> canonical token,
+    see scan_orders.py); when given, grid and direction are not used
+    (gla_fwd_ordered).
     Returns (o [B, T, H, dv] in SCAN order, s_final [B, H, dk, dv] fp32 or None).
     """
     B, T, H, dk = q.shape
@@ -143,6 +164,14 @@ def gla_fwd(q, k, v, log_alpha, grid, direction, chunk: int = 0, s0=None, out=No
     if workspace is None:
         workspace = get_workspace(dev, workspace_bytes(dc, B, T, H, dk, dv, chunk))
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if order is not None:
+        rc = lib().gla_fwd_ordered(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), dc,
+                                   q.stride(0), q.stride(1), q.stride(2), v.stride(0), v.stride(1), v.stride(2),
+                                   B, T, H, dk, dv, _ptr(_order(order, T, dev)), chunk,
+                                   _ptr(s0), _ptr(out), out.stride(0), out.stride(1), out.stride(2),
+                                   _ptr(sf), _ptr(workspace), wsb, _stream(dev))
+        _check(rc, "gla_fwd_ordered")
+        return out, sf
     gh, gw = grid
     rc = lib().gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), dc,
                        q.stride(0), q.stride(1), q.stride(2), v.stride(0), v.stride(1), v.stride(2),
@@ -154,9 +183,10 @@ def gla_fwd(q, k, v, log_alpha, grid, direction, chunk: int = 0, s0=None, out=No
 
 
 def gla_bwd(q, k, v, log_alpha, grid, direction, d_o, chunk: int = 0, s0=None, ds_final=None,
-            need_ds0: bool = True, workspace=None):
+            need_ds0: bool = True, workspace=None, order=None):
     """Gradients of gla_fwd (bf16): d_o [B, T, H, dv] in SCAN order (the
-    gradient of o), ds_final fp32 [B, H, dk, dv] or None (zero).
+    gradient of o), ds_final fp32 [B, H, dk, dv] or None (zero).  order: as
+    for gla_fwd (gla_bwd_ordered).
 
     Returns (dq, dk, dv, dlog_alpha, ds0): dq, dk bf16 [B, T, H, dk], dv bf16
     [B, T, H, dv], dlog_alpha fp32 [B, T, H, dk], all canonical token order;
@@ -188,6 +218,15 @@ def gla_bwd(q, k, v, log_alpha, grid, direction, d_o, chunk: int = 0, s0=None, d
             raise DigError("gla_bwd: invalid sizes: " + lib().dig_last_error().decode(errors="replace"))
         workspace = get_workspace(dev, n, key="bwd")
     wsb = workspace.numel() * workspace.element_size()
+    if order is not None:
+        rc = lib().gla_bwd_ordered(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), DIG_BF16,
+                                   q.stride(0), q.stride(1), q.stride(2), v.stride(0), v.stride(1), v.stride(2),
+                                   B, T, H, dk, dv, _ptr(_order(order, T, dev)), chunk, _ptr(s0),
+                                   _ptr(d_o), d_o.stride(0), d_o.stride(1), d_o.stride(2), _ptr(ds_final),
+                                   _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(ds0), _ptr(workspace), wsb,
+                                   _stream(dev))
+        _check(rc, "gla_bwd_ordered")
+        return dq, dk_, dv_, dg, ds0
     rc = lib().gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), DIG_BF16,
                        q.stride(0), q.stride(1), q.stride(2), v.stride(0), v.stride(1), v.stride(2),
                        B, T, H, dk, dv, grid[0], grid[1], _dir(direction), chunk, _ptr(s0),
@@ -224,6 +263,20 @@ def srem_remap(x, grid, src, dst, out=None):
     rc = lib().srem_remap(_ptr(x), _dtype_code(x), B, T, C, grid[0], grid[1], _dir(src), _dir(dst),
                           _ptr(out), _stream(x.device))
     _check(rc, "srem_remap")
+    return out
+
+
+def gather_rows(x, index, out=None):
+    """Contiguous x [B, T, C] -> y with y[:, p] = x[:, index[p]] (index int32 [T] on the device;
+    an entry outside [0, T) gives a zero row)."""
+    B, T, C = x.shape
+    if not x.is_contiguous():
+        raise DigError("gather_rows: x must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib().dig_gather_rows(_ptr(x), _dtype_code(x), B, T, C, _ptr(_order(index, T, x.device)), _ptr(out),
+                               _stream(x.device))
+    _check(rc, "dig_gather_rows")
     return out
 
 

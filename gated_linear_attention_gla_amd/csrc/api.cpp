@@ -115,15 +115,24 @@ size_t gla_fwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, in
   return dig_gla_bf16_workspace(B, T, H, dk, dv, auto_chunk(dtype, chunk, dk, dv), num_cu);
 }
 
-int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
-            int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
-            int B, int T, int H, int dk, int dv, int gh, int gw, int dir, int chunk,
-            const float *s0, void *o, int64_t o_sb, int64_t o_st, int64_t o_sh, float *s_final,
-            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// gla_fwd and gla_fwd_ordered: the scan order is either (gh, gw, dir) or the
+// table `order` (non-null).
+int gla_fwd_impl(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+                 int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+                 int B, int T, int H, int dk, int dv, int gh, int gw, int dir, const int32_t *order, int chunk,
+                 const float *s0, void *o, int64_t o_sb, int64_t o_st, int64_t o_sh, float *s_final,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
   try {
     int rc = check_gla_sizes(dtype, B, T, H, dk, dv, chunk);
     if (rc) return rc;
     if (!q || !k || !v || !log_alpha || !o) return fail(DIG_EINVAL, "gla_fwd: q, k, v, log_alpha and o are required");
+    if (order) {
+      if (reinterpret_cast<uintptr_t>(order) & 3u) return fail(DIG_EINVAL, "gla_fwd_ordered: order must be 4-byte aligned");
+      gh = 1; gw = T; dir = DIG_L2R;
+    }
     if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
       return fail(DIG_EINVAL, "gla_fwd: grid %dx%d does not hold T=%d tokens", gh, gw, T);
     if (dir < DIG_L2R || dir > DIG_B2T) return fail(DIG_EINVAL, "gla_fwd: dir must be 0..3");
@@ -162,6 +171,7 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, 
     a.o_sb = o_sb; a.o_st = o_st; a.o_sh = o_sh;
     a.o = o; a.s0 = s0; a.s_final = s_final;
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.gh = gh; a.gw = gw; a.dir = dir; a.chunk = M;
+    a.order = order;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     // launch tag for the workspace flags: 1 .. 2^29-1 (never 0, the zero-filled state)
@@ -174,6 +184,28 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, 
     return fail(DIG_EHIP, "gla_fwd: unexpected C++ exception");
   }
 }
+}  // namespace
+
+extern "C" {
+
+int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+            int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+            int B, int T, int H, int dk, int dv, int gh, int gw, int dir, int chunk,
+            const float *s0, void *o, int64_t o_sb, int64_t o_st, int64_t o_sh, float *s_final,
+            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return gla_fwd_impl(q, k, v, log_alpha, dtype, qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, B, T, H, dk, dv, gh, gw,
+                      dir, nullptr, chunk, s0, o, o_sb, o_st, o_sh, s_final, workspace, workspace_bytes, stream);
+}
+
+int gla_fwd_ordered(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+                    int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+                    int B, int T, int H, int dk, int dv, const int32_t *order, int chunk,
+                    const float *s0, void *o, int64_t o_sb, int64_t o_st, int64_t o_sh, float *s_final,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!order) return fail(DIG_EINVAL, "gla_fwd_ordered: order is required");
+  return gla_fwd_impl(q, k, v, log_alpha, dtype, qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, B, T, H, dk, dv, 1, T,
+                      DIG_L2R, order, chunk, s0, o, o_sb, o_st, o_sh, s_final, workspace, workspace_bytes, stream);
+}
 
 
 size_t gla_bwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
@@ -181,17 +213,24 @@ size_t gla_bwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, in
   return dig_gla_bwd_workspace(B, T, H, dk, dv, chunk);
 }
 
-int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
-            int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
-            int B, int T, int H, int dk, int dv, int gh, int gw, int dir, int chunk,
-            const float *s0, const void *d_o, int64_t do_sb, int64_t do_st, int64_t do_sh,
-            const float *ds_final, void *dq, void *dk_out, void *dv_out, float *dlog_alpha, float *ds0,
-            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+int gla_bwd_impl(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+                 int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+                 int B, int T, int H, int dk, int dv, int gh, int gw, int dir, const int32_t *order, int chunk,
+                 const float *s0, const void *d_o, int64_t do_sb, int64_t do_st, int64_t do_sh,
+                 const float *ds_final, void *dq, void *dk_out, void *dv_out, float *dlog_alpha, float *ds0,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
   try {
     int rc = check_bwd_sizes(dtype, B, T, H, dk, dv, chunk);
     if (rc) return rc;
     if (!q || !k || !v || !log_alpha || !d_o || !dq || !dk_out || !dv_out || !dlog_alpha)
       return fail(DIG_EINVAL, "gla_bwd: q, k, v, log_alpha, d_o, dq, dk, dv and dlog_alpha are required");
+    if (order) {
+      if (reinterpret_cast<uintptr_t>(order) & 3u) return fail(DIG_EINVAL, "gla_bwd_ordered: order must be 4-byte aligned");
+      gh = 1; gw = T; dir = DIG_L2R;
+    }
     if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
       return fail(DIG_EINVAL, "gla_bwd: grid %dx%d does not hold T=%d tokens", gh, gw, T);
     if (dir < DIG_L2R || dir > DIG_B2T) return fail(DIG_EINVAL, "gla_bwd: dir must be 0..3");
@@ -229,6 +268,7 @@ int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha, 
     a.s0 = s0; a.ds_final = ds_final;
     a.dq = dq; a.dk_out = dk_out; a.dv_out = dv_out; a.dlog_alpha = dlog_alpha; a.ds0 = ds0;
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.gh = gh; a.gw = gw; a.dir = dir; a.chunk = chunk;
+    a.order = order;
     a.workspace = workspace;
     a.num_cu = di.num_cu;
     const hipError_t e = dig_launch_gla_bwd(a, stream);
@@ -237,6 +277,32 @@ int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha, 
   } catch (...) {
     return fail(DIG_EHIP, "gla_bwd: unexpected C++ exception");
   }
+}
+}  // namespace
+
+extern "C" {
+
+int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+            int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+            int B, int T, int H, int dk, int dv, int gh, int gw, int dir, int chunk,
+            const float *s0, const void *d_o, int64_t do_sb, int64_t do_st, int64_t do_sh,
+            const float *ds_final, void *dq, void *dk_out, void *dv_out, float *dlog_alpha, float *ds0,
+            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return gla_bwd_impl(q, k, v, log_alpha, dtype, qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, B, T, H, dk, dv, gh, gw,
+                      dir, nullptr, chunk, s0, d_o, do_sb, do_st, do_sh, ds_final, dq, dk_out, dv_out, dlog_alpha,
+                      ds0, workspace, workspace_bytes, stream);
+}
+
+int gla_bwd_ordered(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+                    int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+                    int B, int T, int H, int dk, int dv, const int32_t *order, int chunk,
+                    const float *s0, const void *d_o, int64_t do_sb, int64_t do_st, int64_t do_sh,
+                    const float *ds_final, void *dq, void *dk_out, void *dv_out, float *dlog_alpha, float *ds0,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!order) return fail(DIG_EINVAL, "gla_bwd_ordered: order is required");
+  return gla_bwd_impl(q, k, v, log_alpha, dtype, qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, B, T, H, dk, dv, 1, T,
+                      DIG_L2R, order, chunk, s0, d_o, do_sb, do_st, do_sh, ds_final, dq, dk_out, dv_out,
+                      dlog_alpha, ds0, workspace, workspace_bytes, stream);
 }
 
 int srem_dwconv(const void *x_scan, int dtype, int B, int T, int C, int64_t x_sb, int64_t x_st,
@@ -292,6 +358,28 @@ int srem_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw, in
     return DIG_OK;
   } catch (...) {
     return fail(DIG_EHIP, "srem_remap: unexpected C++ exception");
+  }
+}
+
+int dig_gather_rows(const void *x, int dtype, int B, int T, int C, const int32_t *index, void *y,
+                    hipStream_t stream) {
+  try {
+    if (dtype != DIG_F32 && dtype != DIG_BF16) return fail(DIG_EINVAL, "dig_gather_rows: bad dtype");
+    if (!x || !y || !index) return fail(DIG_EINVAL, "dig_gather_rows: x, index and y are required");
+    if (B <= 0 || T <= 0 || C <= 0) return fail(DIG_EINVAL, "dig_gather_rows: B, T, C must be positive");
+    const int vec = dtype == DIG_BF16 ? 8 : 4;
+    if (C % vec) return fail(DIG_EINVAL, "dig_gather_rows: C must be a multiple of %d", vec);
+    if (!aligned16(x) || !aligned16(y)) return fail(DIG_EINVAL, "dig_gather_rows: x and y must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(index) & 3u) return fail(DIG_EINVAL, "dig_gather_rows: index must be 4-byte aligned");
+    if (x == y) return fail(DIG_EINVAL, "dig_gather_rows: in-place is not allowed");
+    DevInfo di;
+    int rc = current_device(di);
+    if (rc) return rc;
+    const hipError_t e = dig_launch_gather_rows(x, dtype, B, T, C, index, y, di.num_cu, stream);
+    if (e != hipSuccess) return hip_fail(e, "dig_gather_rows launch");
+    return DIG_OK;
+  } catch (...) {
+    return fail(DIG_EHIP, "dig_gather_rows: unexpected C++ exception");
   }
 }
 

@@ -78,6 +78,7 @@ struct DigGlaArgs {
   const float *s0;
   float *s_final;
   int B, T, H, dk, dv, gh, gw, dir, chunk;
+  const int *order;   // nullable: scan position -> canonical token [T]; replaces (gh, gw, dir)
   void *workspace;
   size_t workspace_bytes;
   uint32_t epoch;
@@ -95,6 +96,7 @@ struct DigGlaBwdArgs {
   void *dq, *dk_out, *dv_out;
   float *dlog_alpha, *ds0;
   int B, T, H, dk, dv, gh, gw, dir, chunk;
+  const int *order;   // nullable: scan position -> canonical token [T]; replaces (gh, gw, dir)
   void *workspace;
   int num_cu;   // compute units of the device (the chunk kernel's persistent grid)
 };
@@ -106,6 +108,8 @@ size_t dig_gla_f32_lds_bytes(int dk, int dv, int chunk);
 hipError_t dig_launch_dwconv(const void *x, int dtype, int B, int T, int C, int64_t x_sb, int64_t x_st,
                              const float *w, int gh, int gw, int dir, void *y, int64_t y_sb,
                              int64_t y_st, int num_cu, hipStream_t s);
+hipError_t dig_launch_gather_rows(const void *x, int dtype, int B, int T, int C, const int *index, void *y,
+                                  int num_cu, hipStream_t s);
 hipError_t dig_launch_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw, int from,
                             int to, void *y, int num_cu, hipStream_t s);
 hipError_t dig_launch_adaln(const void *x, int dtype, int64_t N, int C, int64_t x_sn, const float *scale,

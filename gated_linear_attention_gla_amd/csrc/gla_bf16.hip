@@ -81,6 +81,7 @@ struct Params {
   float *s_final;
   int64_t qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
   int B, T, H, dk, dv, gh, gw, dir, nchunks, units;
+  const int *order;                // scan position -> canonical token table [T] (the kernel's ORD path)
   int seg_chunks, nseg, per_xcd;   // chunks per segment, segments per scan, scans per XCD
   int split_L, split_K;            // two-segment split (split_K > 0): see the kernel
   int cgr;                         // 16-byte channel groups holding data: ceil(max(dk, dv) / 8)
@@ -140,7 +141,9 @@ struct Occ {
   static constexpr int waves_per_simd = (2 * (DP / 16) + 3) / 4 < 2 ? 2 : (2 * (DP / 16) + 3) / 4;
 };
 
-template <int DP, int M>
+// ORD: the scan order comes from the caller's table P.order instead of one of
+// the four grid orders.
+template <int DP, int M, bool ORD>
 __global__ void __launch_bounds__(Shape<DP>::NT) __attribute__((amdgpu_waves_per_eu(Occ<DP>::waves_per_simd)))
 gla_fwd_bf16_kernel(Params P) {
   constexpr int NT = Shape<DP>::NT, NTP = Shape<DP>::NTP;
@@ -270,23 +273,45 @@ gla_fwd_bf16_kernel(Params P) {
   // token offsets of chunk x (scan order -> canonical token) into parity
   // buffer x & 1; kOOB past the end of the sequence and for chunks after the
   // segment (their loads then return zeros without touching memory)
+  // ORD: this producer thread's table entry for the next token table, loaded
+  // one table ahead (by every producer lane, out-of-range entries reading 0,
+  // so the count of memory operations does not depend on the lane)
+  const __amdgpu_buffer_rsrc_t rord = make_rsrc(ORD ? P.order : nullptr, ORD ? (unsigned)T * 4u : 0u);
+  unsigned ord_next = 0;
+  auto ord_load = [&](int x) {
+    if constexpr (ORD) {
+      const int p = x * M + ptid;
+      const bool ok = ptid >= 0 && ptid < M && p < T;
+      ord_next = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rord, ok ? (int)(p * 4) : (int)kOOB, 0, 0);
+    }
+  };
   auto fill_tok = [&](int x) {
+    const unsigned ord_cur = ord_next;
+    ord_load(x + 1);
     if (ptid >= 0 && ptid < M) {
       const int p = x * M + ptid;
       unsigned oqk = kOOB, ov = kOOB;
       if (x < c_end && p < T) {
-        // scan position -> canonical token (the four orders of scan_to_canon),
-        // the quotient by gh from a magic multiplier held in scalar registers
-        const unsigned s_ = (P.dir & 1) ? (unsigned)(T - 1 - p) : (unsigned)p;
-        unsigned n = s_;
-        if (P.dir >= 2) {
-          unsigned col = __umulhi(2u * s_, P.gh_magic);   // floor(s/gh) or one more
-          int row = (int)(s_ - col * (unsigned)P.gh);
-          if (row < 0) { --col; row += P.gh; }
-          n = (unsigned)row * (unsigned)P.gw + col;
+        unsigned n;
+        if constexpr (ORD) {
+          n = ord_cur;   // entries outside [0, T) address past the slice and read zeros
+        } else {
+          // scan position -> canonical token (the four orders of scan_to_canon),
+          // the quotient by gh from a magic multiplier held in scalar registers
+          const unsigned s_ = (P.dir & 1) ? (unsigned)(T - 1 - p) : (unsigned)p;
+          n = s_;
+          if (P.dir >= 2) {
+            unsigned col = __umulhi(2u * s_, P.gh_magic);   // floor(s/gh) or one more
+            int row = (int)(s_ - col * (unsigned)P.gh);
+            if (row < 0) { --col; row += P.gh; }
+            n = (unsigned)row * (unsigned)P.gw + col;
+          }
         }
         oqk = n * (unsigned)P.qk_st * 2u;
         ov = n * (unsigned)P.v_st * 2u;
+        if constexpr (ORD) {
+          if (n >= (unsigned)T) oqk = ov = kOOB;
+        }
       }
       unsigned *tb = sTok + (x & 3) * 2 * M;
       tb[ptid] = oqk;
@@ -625,6 +650,7 @@ gla_fwd_bf16_kernel(Params P) {
     // stage chunk c+1 (k, v, gates -> k^, e^{b_last}) while the consumers
     // fold chunk c into the aggregate
     if (do_pass1) {
+      ord_load(c_begin);
       fill_tok(c_begin);
       fill_tok(c_begin + 1);
       fill_tok(c_begin + 2);
@@ -677,6 +703,7 @@ gla_fwd_bf16_kernel(Params P) {
     // the first two output chunks' loads are issued before it
     c_begin = out_begin;
     c_end = out_end;
+    ord_load(c_begin);
     fill_tok(c_begin);
     fill_tok(c_begin + 1);
     fill_tok(c_begin + 2);
@@ -1016,7 +1043,7 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
 template <int DP, int M>
 hipError_t launch(const Params &p, int grid, hipStream_t s) {
   const size_t lds = Lds<DP, M>::bytes;
-  auto *fn = gla_fwd_bf16_kernel<DP, M>;
+  auto *fn = p.order ? gla_fwd_bf16_kernel<DP, M, true> : gla_fwd_bf16_kernel<DP, M, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -1059,6 +1086,7 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   p.o_sb = a.o_sb; p.o_st = a.o_st; p.o_sh = a.o_sh;
   p.B = a.B; p.T = a.T; p.H = a.H; p.dk = a.dk; p.dv = a.dv;
   p.gh = a.gh; p.gw = a.gw; p.dir = a.dir;
+  p.order = a.order;
   p.nchunks = pl.nchunks;
   p.units = pl.units;
   p.seg_chunks = pl.seg_chunks;

@@ -52,8 +52,15 @@ struct BwdParams {
                             // in 16 x 16 tiles (see gla_bwd_scan)
   uint16_t *st_d;           // the same layout: gradient of the state leaving chunk c
   int B, T, H, dk, dv, gh, gw, dir, nchunks;
+  const int *order;         // scan position -> canonical token [T] (the kernels' ORD path)
   unsigned qk_span, v_span, do_span;   // bytes addressable in one (batch, head) slice
 };
+
+// ORD path: table entry p (0 for p outside the table), loaded through a
+// buffer descriptor so that the load is issued by every lane.
+__device__ __forceinline__ int ord_entry(__amdgpu_buffer_rsrc_t r, bool ok, int p) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? p * 4 : (int)kOOB, 0, 0);
+}
 
 template <int DP>
 struct BwdRow {
@@ -137,7 +144,7 @@ struct ScanLds {
   static constexpr int bytes = 3 * M * QS * 2;   // X, gates, Y: token-major [M][QS]
 };
 
-template <int DP, int M, bool REV>
+template <int DP, int M, bool REV, bool ORD>
 __device__ __forceinline__ void scan_unit(const BwdParams &P, int unit) {
   constexpr int DT = DP / 16, MT = M / 16, JP = (MT + 1) / 2, NT = DT * kWave;
   constexpr int QS = ScanLds<DP, M>::QS, CG = DP / 8;
@@ -168,17 +175,36 @@ __device__ __forceinline__ void scan_unit(const BwdParams &P, int unit) {
       Z[cc][e] = (z0 && i < dk && j < dv) ? z0[((int64_t)unit * dk + i) * dv + j] : 0.f;
     }
 
+  // ORD: a set's table entries for the chunk it fetches next, loaded by the
+  // fetch before
+  const __amdgpu_buffer_rsrc_t rord = make_rsrc(ORD ? P.order : nullptr, ORD ? (unsigned)T * 4u : 0u);
   struct Rows {
     uint4 x[IT], g[IT], y[IT];
+    int ord[IT];
   };
-  auto fetch = [&](Rows &f, int c) {
+  auto ord_rows = [&](Rows &f, int c) {
+    if constexpr (ORD) {
+#pragma unroll
+      for (int kq = 0; kq < IT; ++kq) {
+        const int idx = tid + kq * NT, tl = idx / CG;
+        f.ord[kq] = ord_entry(rord, idx < M * CG && c * M + tl < T, c * M + tl);
+      }
+    }
+  };
+  auto fetch = [&](Rows &f, int c, int c_next) {
 #pragma unroll
     for (int kq = 0; kq < IT; ++kq) {
       const int idx = tid + kq * NT;
       const int tl = idx / CG, cg = idx - tl * CG;
       const int p = c * M + tl;
-      const bool ok = idx < M * CG && p < T;
-      const int n = ok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
+      bool ok = idx < M * CG && p < T;
+      int n;
+      if constexpr (ORD) {
+        n = f.ord[kq];
+        ok = ok && n >= 0 && n < T;
+      } else {
+        n = ok ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : 0;
+      }
       const int64_t yrow = REV ? (int64_t)p : (int64_t)n;
       const unsigned oxg = (ok && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
       const unsigned oy = (ok && 8 * cg < dv) ? (unsigned)((yrow * y_st + 8 * cg) * 2) : kOOB;
@@ -186,6 +212,7 @@ __device__ __forceinline__ void scan_unit(const BwdParams &P, int unit) {
       f.g[kq] = bload16(rg, oxg);
       f.y[kq] = bload16(ry, oy);
     }
+    ord_rows(f, c_next);
   };
   auto stash = [&](const Rows &f) {
 #pragma unroll
@@ -211,7 +238,10 @@ __device__ __forceinline__ void scan_unit(const BwdParams &P, int unit) {
     lds_barrier();
     // issued on every step (past the ends: the last chunk again, unused) so
     // the wait before each stash covers exactly the rows it needs
-    fetch(f, REV ? max(c - 2, 0) : min(c + 2, N - 1));
+    {
+      const int cf = REV ? max(c - 2, 0) : min(c + 2, N - 1);
+      fetch(f, cf, REV ? max(cf - 2, 0) : min(cf + 2, N - 1));
+    }
     // cumulative gates of key-channel tile r (accumulator layout: token
     // 16 I + 4 (l/16) + e, channel 16 r + l%16) and X scaled by e^{B - b}
     // (forward) or e^{b} (reverse), both <= 1
@@ -247,8 +277,13 @@ __device__ __forceinline__ void scan_unit(const BwdParams &P, int unit) {
   };
 
   Rows fa, fb;
-  fetch(fa, REV ? N - 1 : 0);
-  fetch(fb, REV ? max(N - 2, 0) : min(1, N - 1));
+  {
+    const int ca = REV ? N - 1 : 0, cb = REV ? max(N - 2, 0) : min(1, N - 1);
+    ord_rows(fa, ca);
+    ord_rows(fb, cb);
+    fetch(fa, ca, REV ? max(ca - 2, 0) : min(ca + 2, N - 1));
+    fetch(fb, cb, REV ? max(cb - 2, 0) : min(cb + 2, N - 1));
+  }
   // whole pairs in the loop (no conditional step, so each stash waits for
   // exactly its own rows), an odd last chunk after it
   int it = 0;
@@ -270,12 +305,12 @@ __device__ __forceinline__ void scan_unit(const BwdParams &P, int unit) {
 
 // Both scans in one launch (they are independent): workgroups [0, units)
 // run the forward scan, [units, 2 units) the reverse one.
-template <int DP, int M>
+template <int DP, int M, bool ORD>
 __global__ void __launch_bounds__(DP / 16 * kWave)
 gla_bwd_scan(BwdParams P) {
   const int units = P.B * P.H;
-  if ((int)blockIdx.x < units) scan_unit<DP, M, false>(P, blockIdx.x);
-  else scan_unit<DP, M, true>(P, blockIdx.x - units);
+  if ((int)blockIdx.x < units) scan_unit<DP, M, false, ORD>(P, blockIdx.x);
+  else scan_unit<DP, M, true, ORD>(P, blockIdx.x - units);
 }
 
 // ============================ chunk gradients ================================
@@ -313,7 +348,7 @@ constexpr int kChunkWaves = 8;
 // The outputs leave as 16-byte rows after the next chunk's rows are in LDS,
 // behind that chunk's prefetch, so neither waits for the other; both are
 // long complete when the next chunk's rows are needed.
-template <int DP, int M>
+template <int DP, int M, bool ORD>
 __global__ void __launch_bounds__(kChunkWaves * kWave)
 gla_bwd_chunk(BwdParams P) {
   using L = BwdLds<DP, M>;
@@ -348,23 +383,44 @@ gla_bwd_chunk(BwdParams P) {
   // (the rows' canonical tokens are kept from the first group for the second)
   uint4 fq[ITT], fk[ITT], fg[ITT], fv[ITT], fo[ITT], fs[ITS], fd[ITS];
   int pn[ITT];
-  auto fetch_qkg = [&](int w) {
+  // ORD: table entries of the rows the next fetch_qkg loads (ordq) and of
+  // the tokens of the chunk just fetched (ordt, threads < M), one fetch ahead
+  const __amdgpu_buffer_rsrc_t rord = make_rsrc(ORD ? P.order : nullptr, ORD ? (unsigned)T * 4u : 0u);
+  int ordq[ITT], ordt = -1;
+  auto ord_rows = [&](int w) {
+    if constexpr (ORD) {
+      const int c = w - (w / N) * N;
+#pragma unroll
+      for (int kq = 0; kq < ITT; ++kq) {
+        const int idx = tid0 + kq * NT, tl = idx / CG;
+        ordq[kq] = ord_entry(rord, idx < M * CG && c * M + tl < T, c * M + tl);
+      }
+    }
+  };
+  auto fetch_qkg = [&](int w, int w_next) {
     const int unit = w / N, c = w - unit * N, bb = unit / H, hh = unit - bb * H;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(P.q + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(P.k + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(P.g + bb * P.qk_sb + hh * P.qk_sh, P.qk_span);
+    if constexpr (ORD) ordt = ord_entry(rord, tid0 < M && c * M + tid0 < T, c * M + tid0);
 #pragma unroll
     for (int kq = 0; kq < ITT; ++kq) {
       const int idx = tid0 + kq * NT;
       const int tl = idx / CG, cg = idx - tl * CG;
       const int p = c * M + tl;
-      const int n = (idx < M * CG && p < T) ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
+      int n;
+      if constexpr (ORD) {
+        n = (idx < M * CG && p < T && ordq[kq] >= 0 && ordq[kq] < T) ? ordq[kq] : -1;
+      } else {
+        n = (idx < M * CG && p < T) ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
+      }
       pn[kq] = n;
       const unsigned oqk = (n >= 0 && 8 * cg < dk) ? (unsigned)(((int64_t)n * P.qk_st + 8 * cg) * 2) : kOOB;
       fq[kq] = bload16(rq, oqk);
       fk[kq] = bload16(rk, oqk);
       fg[kq] = bload16(rg, oqk);
     }
+    ord_rows(w_next);
   };
   auto fetch_vo = [&](int w) {
     const int unit = w / N, c = w - unit * N, bb = unit / H, hh = unit - bb * H;
@@ -431,7 +487,8 @@ gla_bwd_chunk(BwdParams P) {
   const int wend = min(total, ((int)blockIdx.x + 1) * per);
   int w = blockIdx.x * per, wprev = -1, par = 0;
   if (w < wend) {
-    fetch_qkg(w);
+    ord_rows(w);
+    fetch_qkg(w, min(w + 1, wend - 1));
     fetch_vo(w);
     fetch_states(w);
   }
@@ -474,7 +531,8 @@ gla_bwd_chunk(BwdParams P) {
     int *tk = tok + par * M;   // this chunk's canonical tokens; the other half: the chunk before
     if (tid < M) {
       const int p = c * M + tid;
-      tk[tid] = p < T ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
+      if constexpr (ORD) tk[tid] = (p < T && ordt >= 0 && ordt < T) ? ordt : -1;
+      else tk[tid] = p < T ? scan_to_canon(P.dir, P.gh, P.gw, T, p) : -1;
     }
     if (tid == 0) *flag = 0u;
     lds_barrier();
@@ -482,7 +540,7 @@ gla_bwd_chunk(BwdParams P) {
     // refetches itself; the first stores nothing), so the compiler's waits
     // before the next chunk's rows are exact
     const int wn = min(w + 1, wend - 1);
-    fetch_qkg(wn);
+    fetch_qkg(wn, min(wn + 1, wend - 1));
     store_outputs(wprev >= 0 ? wprev : w, tok + (par ^ 1) * M, wprev >= 0);
 
     // ---- 1. cumulative gates (log2 units) and raw q, k of tile r, in
@@ -782,26 +840,27 @@ hipError_t launch_bwd(const BwdParams &p, int num_cu, hipStream_t s) {
   constexpr int chunk_lds = BwdLds<DP, M>::bytes;
   static int per_cu = 0;   // resident chunk workgroups per CU; the same on every gfx950
   hipError_t e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_scan<DP, M>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
+  const bool ord = p.order != nullptr;
+  auto *scan = ord ? gla_bwd_scan<DP, M, true> : gla_bwd_scan<DP, M, false>;
+  auto *chunk = ord ? gla_bwd_chunk<DP, M, true> : gla_bwd_chunk<DP, M, false>;
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(scan), hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void *>(gla_bwd_chunk<DP, M>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, chunk_lds);
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk), hipFuncAttributeMaxDynamicSharedMemorySize, chunk_lds);
   if (e != hipSuccess) return e;
-  if (per_cu == 0) {
+  if (per_cu == 0) {   // the same for both variants (same LDS, same block)
     int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(gla_bwd_chunk<DP, M>),
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(gla_bwd_chunk<DP, M, false>),
                                                      kChunkWaves * kWave, chunk_lds);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
   const int units = p.B * p.H;
-  hipLaunchKernelGGL((gla_bwd_scan<DP, M>), dim3(2 * units), dim3(DP / 16 * kWave), scan_lds, s, p);
+  hipLaunchKernelGGL(scan, dim3(2 * units), dim3(DP / 16 * kWave), scan_lds, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t chunks = (int64_t)units * p.nchunks;
   const int64_t resident = (int64_t)(num_cu > 0 ? num_cu : 1) * per_cu;
   const int grid = (int)(chunks < resident ? chunks : resident);
-  hipLaunchKernelGGL((gla_bwd_chunk<DP, M>), dim3(grid), dim3(kChunkWaves * kWave), chunk_lds, s, p);
+  hipLaunchKernelGGL(chunk, dim3(grid), dim3(kChunkWaves * kWave), chunk_lds, s, p);
   return hipGetLastError();
 }
 
@@ -853,6 +912,7 @@ hipError_t dig_launch_gla_bwd(const DigGlaBwdArgs &a, hipStream_t s) {
   p.ds0 = a.ds0;
   p.B = a.B; p.T = a.T; p.H = a.H; p.dk = a.dk; p.dv = a.dv;
   p.gh = a.gh; p.gw = a.gw; p.dir = a.dir;
+  p.order = a.order;
   p.nchunks = (a.T + M - 1) / M;
   const size_t blkb = (size_t)a.B * a.H * p.nchunks * DP * DP * 2;
   unsigned char *ws = static_cast<unsigned char *>(a.workspace);

@@ -27,7 +27,18 @@ struct Params {
   float *s_final;
   int64_t qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, o_sb, o_st, o_sh;
   int T, H, dk, dv, gh, gw, dir, M, nchunks, units;
+  const int *order;   // nullable: scan position -> canonical token [T]
 };
+
+// Canonical token at scan position p (p < T), or -1 for a table entry
+// outside [0, T) (that token then reads as zeros).
+__device__ __forceinline__ int64_t token_at(const Params &P, int p) {
+  if (P.order) {
+    const int n = P.order[p];
+    return (n >= 0 && n < P.T) ? n : -1;
+  }
+  return scan_to_canon(P.dir, P.gh, P.gw, P.T, p);
+}
 
 __global__ void __launch_bounds__(kNT) gla_fwd_f32_kernel(Params P) {
   extern __shared__ __align__(16) float sm[];
@@ -55,8 +66,8 @@ __global__ void __launch_bounds__(kNT) gla_fwd_f32_kernel(Params P) {
     __syncthreads();
     for (int x = tid; x < M * dk; x += kNT) {
       const int t = x / dk, i = x - t * dk, p = c * M + t;
-      if (p < T) {
-        const int64_t n = scan_to_canon(P.dir, P.gh, P.gw, T, p);
+      const int64_t n = p < T ? token_at(P, p) : -1;
+      if (n >= 0) {
         sq[x] = qb[n * P.qk_st + i];
         sk[x] = kb[n * P.qk_st + i];
         sb[x] = gb[n * P.qk_st + i] * kLog2e;
@@ -66,7 +77,8 @@ __global__ void __launch_bounds__(kNT) gla_fwd_f32_kernel(Params P) {
     }
     for (int x = tid; x < M * dv; x += kNT) {
       const int t = x / dv, j = x - t * dv, p = c * M + t;
-      sv[x] = (p < T) ? vb[(int64_t)scan_to_canon(P.dir, P.gh, P.gw, T, p) * P.v_st + j] : 0.f;
+      const int64_t n = p < T ? token_at(P, p) : -1;
+      sv[x] = n >= 0 ? vb[n * P.v_st + j] : 0.f;
     }
     __syncthreads();
     if (tid < dk) {
@@ -128,6 +140,7 @@ hipError_t dig_launch_gla_f32(const DigGlaArgs &a, hipStream_t s) {
   p.o_sb = a.o_sb; p.o_st = a.o_st; p.o_sh = a.o_sh;
   p.T = a.T; p.H = a.H; p.dk = a.dk; p.dv = a.dv;
   p.gh = a.gh; p.gw = a.gw; p.dir = a.dir;
+  p.order = a.order;
   p.M = a.chunk;
   p.nchunks = (a.T + a.chunk - 1) / a.chunk;
   p.units = a.B * a.H;

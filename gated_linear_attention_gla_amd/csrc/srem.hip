@@ -246,8 +246,49 @@ srem_remap_kernel(const unsigned char *x, unsigned char *y, int B, int T, int C,
   }
 }
 
+// Row gather by a table: y[b, p] = x[b, index[p]] (16-byte copies); a table
+// entry outside [0, T) gives a zero row.  Arranging rows into any scan order
+// and back (an order's inverse as the table) is this one copy.
+template <int ES>
+__global__ void __launch_bounds__(kNT)
+gather_rows_kernel(const unsigned char *x, unsigned char *y, int B, int T, int C, const int *index) {
+  const int CV = C * ES / 16;
+  const int64_t total = (int64_t)B * T * CV;
+  const int64_t stride = (int64_t)gridDim.x * kNT;
+  for (int64_t i = (int64_t)xcd_linear_block(blockIdx.x, gridDim.x) * kNT + threadIdx.x; i < total;
+       i += stride) {
+    const int cv = (int)(i % CV);
+    const int64_t bt = i / CV;
+    const int bb = (int)(bt / T);
+    const int pt = (int)(bt - (int64_t)bb * T);
+    const int ps = index[pt];
+    const int64_t rowb = (int64_t)C * ES;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (ps >= 0 && ps < T) v = *reinterpret_cast<const uint4 *>(x + ((int64_t)bb * T + ps) * rowb + 16 * cv);
+    *reinterpret_cast<uint4 *>(y + ((int64_t)bb * T + pt) * rowb + 16 * cv) = v;
+  }
+}
+
 }  // namespace
 }  // namespace dig
+
+hipError_t dig_launch_gather_rows(const void *x, int dtype, int B, int T, int C, const int *index, void *y,
+                                  int num_cu, hipStream_t s) {
+  using namespace dig;
+  const int ES = dtype == 1 ? 2 : 4;
+  const int64_t total = (int64_t)B * T * (C * ES / 16);
+  int64_t grid = (total + kNT - 1) / kNT;
+  const int64_t cap = (int64_t)num_cu * 16;
+  if (grid > cap) grid = cap;
+  grid = (grid + 7) / 8 * 8;
+  const auto *xp = static_cast<const unsigned char *>(x);
+  auto *yp = static_cast<unsigned char *>(y);
+  if (ES == 2)
+    hipLaunchKernelGGL(gather_rows_kernel<2>, dim3(grid), dim3(kNT), 0, s, xp, yp, B, T, C, index);
+  else
+    hipLaunchKernelGGL(gather_rows_kernel<4>, dim3(grid), dim3(kNT), 0, s, xp, yp, B, T, C, index);
+  return hipGetLastError();
+}
 
 hipError_t dig_launch_dwconv(const void *x, int dtype, int B, int T, int C, int64_t x_sb, int64_t x_st,
                              const float *w, int gh, int gw, int dir, void *y, int64_t y_sb,

@@ -133,6 +133,35 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
             void *workspace, size_t workspace_bytes,
             hipStream_t stream);
 
+/*
+ * gla_fwd_ordered -- gla_fwd over a caller-given scan order: any permutation
+ * of the T tokens, e.g. ZigMa's zigzag (snake) space-filling scans (ZigMa
+ * notes, 关键设计 / Zigzag 扫描方案) or DiG's bidirectional scan (DiG notes,
+ * ablation table: a forward and a reversed order).
+ *
+ *   order   device int32 [T]: order[p] = canonical index of the token scanned
+ *           at position p; 4-byte aligned; read on the stream, so it must stay
+ *           valid until the call completes.  It should be a permutation of
+ *           0..T-1: an entry outside that range reads as a zero token (its
+ *           output row is still written); repeated entries are allowed and
+ *           simply scan that token again.
+ * All other arguments, outputs (o in SCAN order, S_final), constraints,
+ * workspace and errors as gla_fwd; (gh, gw, dir) are replaced by `order`.
+ * With the table of one of the four grid orders it returns exactly what
+ * gla_fwd returns for that direction.
+ */
+int gla_fwd_ordered(const void *q, const void *k, const void *v, const void *log_alpha,
+                    int dtype,
+                    int64_t qk_sb, int64_t qk_st, int64_t qk_sh,
+                    int64_t v_sb, int64_t v_st, int64_t v_sh,
+                    int B, int T, int H, int dk, int dv,
+                    const int32_t *order, int chunk,
+                    const float *s0,
+                    void *o, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                    float *s_final,
+                    void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
 /* Bytes of workspace gla_fwd needs for these sizes on the current device
  * (state hand-off records between sequence segments, their flags and a
  * ticket counter).  Returns 0 when no workspace is needed; (size_t)-1 for
@@ -186,6 +215,28 @@ int gla_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
             void *workspace, size_t workspace_bytes,
             hipStream_t stream);
 
+/*
+ * gla_bwd_ordered -- gla_bwd of gla_fwd_ordered: the same scan order table
+ * `order` (device int32 [T], as for gla_fwd_ordered) in place of (gh, gw,
+ * dir); d_o in that scan order; gradients in canonical order.  The table
+ * must be a permutation for the gradients to be defined: a token listed twice
+ * has one of its occurrences' gradients stored (they are not summed), and an
+ * entry outside [0, T) is a zero token whose gradients are not written
+ * (memory outside the outputs is never touched).  Everything else as gla_bwd.
+ */
+int gla_bwd_ordered(const void *q, const void *k, const void *v, const void *log_alpha,
+                    int dtype,
+                    int64_t qk_sb, int64_t qk_st, int64_t qk_sh,
+                    int64_t v_sb, int64_t v_st, int64_t v_sh,
+                    int B, int T, int H, int dk, int dv,
+                    const int32_t *order, int chunk,
+                    const float *s0,
+                    const void *d_o, int64_t do_sb, int64_t do_st, int64_t do_sh,
+                    const float *ds_final,
+                    void *dq, void *dk_out, void *dv_out, float *dlog_alpha, float *ds0,
+                    void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
 /* Bytes of workspace gla_bwd needs for these sizes ((size_t)-1 for invalid
  * sizes or dtypes). */
 size_t gla_bwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk);
@@ -222,6 +273,19 @@ int srem_dwconv(const void *x_scan, int dtype, int B, int T, int C,
  */
 int srem_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw,
                int from, int to, void *y, hipStream_t stream);
+
+/*
+ * dig_gather_rows -- y[b, p, :] = x[b, index[p], :] for p < T: arranging a
+ * token tensor into a scan order (index = the order table) or back to the
+ * canonical order (index = its inverse), the arrange / arrange-back steps of
+ * ZigMa's scans (ZigMa notes, 关键设计 / 异构逐层扫描).
+ * x, y: contiguous [B, T, C], element size from dtype (DIG_BF16 or DIG_F32),
+ * 16-byte aligned; C % 8 == 0 (bf16) or C % 4 == 0 (fp32).  index: device
+ * int32 [T], 4-byte aligned; an entry outside [0, T) gives a zero row.
+ * Bitwise copy.  y must not overlap x.
+ */
+int dig_gather_rows(const void *x, int dtype, int B, int T, int C,
+                    const int32_t *index, void *y, hipStream_t stream);
 
 /*
  * dig_adaln_modulate -- adaLN modulation of N rows (tokens) of C channels:

@@ -121,6 +121,11 @@ int oracle_scan_perm(int dir, int64_t gh, int64_t gw, int64_t *perm)
  *
  * nthreads <= 0 means "let OpenMP decide".  Returns 0, or -1 on bad args.
  */
+static int gla_fwd_perm(const double *q, const double *k, const double *v,
+                        const double *log_alpha, int64_t B, int64_t T, int64_t H,
+                        int64_t dk, int64_t dv, int64_t *perm,
+                        const double *s0, double *o, double *s_final, int nthreads);
+
 int oracle_gla_fwd(const double *q, const double *k, const double *v,
                    const double *log_alpha, int64_t B, int64_t T, int64_t H,
                    int64_t dk, int64_t dv, int64_t gh, int64_t gw, int dir,
@@ -133,6 +138,45 @@ int oracle_gla_fwd(const double *q, const double *k, const double *v,
     int64_t *perm = (int64_t *)malloc((size_t)T * sizeof(int64_t));
     if (!perm) return -1;
     oracle_scan_perm(dir, gh, gw, perm);
+    return gla_fwd_perm(q, k, v, log_alpha, B, T, H, dk, dv, perm, s0, o, s_final, nthreads);
+}
+
+/* A scan order given as a table: order[p] = canonical index of the token at
+ * scan position p, a permutation of 0..T-1 (ZigMa notes, 关键设计 / Zigzag
+ * 扫描方案: any space-filling order; DiG notes: the four SREM orders are the
+ * special cases).  Same recurrence and outputs as oracle_gla_fwd. */
+static int copy_order(const int64_t *order, int64_t T, int64_t **perm)
+{
+    char *seen = (char *)calloc((size_t)T, 1);
+    *perm = (int64_t *)malloc((size_t)T * sizeof(int64_t));
+    if (!seen || !*perm) { free(seen); free(*perm); return -1; }
+    for (int64_t p = 0; p < T; ++p) {
+        const int64_t n = order[p];
+        if (n < 0 || n >= T || seen[n]) { free(seen); free(*perm); return -1; }
+        seen[n] = 1;
+        (*perm)[p] = n;
+    }
+    free(seen);
+    return 0;
+}
+
+int oracle_gla_fwd_order(const double *q, const double *k, const double *v,
+                         const double *log_alpha, int64_t B, int64_t T, int64_t H,
+                         int64_t dk, int64_t dv, const int64_t *order,
+                         const double *s0, double *o, double *s_final, int nthreads)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0 || !order) return -1;
+    int64_t *perm;
+    if (copy_order(order, T, &perm)) return -1;
+    return gla_fwd_perm(q, k, v, log_alpha, B, T, H, dk, dv, perm, s0, o, s_final, nthreads);
+}
+
+/* Takes ownership of perm (freed on return). */
+static int gla_fwd_perm(const double *q, const double *k, const double *v,
+                        const double *log_alpha, int64_t B, int64_t T, int64_t H,
+                        int64_t dk, int64_t dv, int64_t *perm,
+                        const double *s0, double *o, double *s_final, int nthreads)
+{
 
     const int64_t units = B * H;
     int failed = 0;
@@ -206,6 +250,13 @@ int oracle_gla_fwd(const double *q, const double *k, const double *v,
  * sqrt(T) positions from states stored at block starts (the same operations
  * in the same order, so the same values) to keep memory at O(sqrt(T) d^2).
  */
+static int gla_bwd_perm(const double *q, const double *k, const double *v,
+                        const double *log_alpha, int64_t B, int64_t T, int64_t H,
+                        int64_t dk, int64_t dv, int64_t *perm,
+                        const double *s0, const double *do_scan, const double *ds_final,
+                        double *dq, double *dk_out, double *dv_out, double *dlog_alpha,
+                        double *ds0, int nthreads);
+
 int oracle_gla_bwd(const double *q, const double *k, const double *v,
                    const double *log_alpha, int64_t B, int64_t T, int64_t H,
                    int64_t dk, int64_t dv, int64_t gh, int64_t gw, int dir,
@@ -220,6 +271,34 @@ int oracle_gla_bwd(const double *q, const double *k, const double *v,
     int64_t *perm = (int64_t *)malloc((size_t)T * sizeof(int64_t));
     if (!perm) return -1;
     oracle_scan_perm(dir, gh, gw, perm);
+    return gla_bwd_perm(q, k, v, log_alpha, B, T, H, dk, dv, perm, s0, do_scan, ds_final, dq, dk_out,
+                        dv_out, dlog_alpha, ds0, nthreads);
+}
+
+/* The backward over a scan order given as a table (a permutation, as for
+ * oracle_gla_fwd_order); do_scan in that order. */
+int oracle_gla_bwd_order(const double *q, const double *k, const double *v,
+                         const double *log_alpha, int64_t B, int64_t T, int64_t H,
+                         int64_t dk, int64_t dv, const int64_t *order,
+                         const double *s0, const double *do_scan, const double *ds_final,
+                         double *dq, double *dk_out, double *dv_out, double *dlog_alpha,
+                         double *ds0, int nthreads)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0 || !order) return -1;
+    int64_t *perm;
+    if (copy_order(order, T, &perm)) return -1;
+    return gla_bwd_perm(q, k, v, log_alpha, B, T, H, dk, dv, perm, s0, do_scan, ds_final, dq, dk_out,
+                        dv_out, dlog_alpha, ds0, nthreads);
+}
+
+/* Takes ownership of perm (freed on return). */
+static int gla_bwd_perm(const double *q, const double *k, const double *v,
+                        const double *log_alpha, int64_t B, int64_t T, int64_t H,
+                        int64_t dk, int64_t dv, int64_t *perm,
+                        const double *s0, const double *do_scan, const double *ds_final,
+                        double *dq, double *dk_out, double *dv_out, double *dlog_alpha,
+                        double *ds0, int nthreads)
+{
 
     int64_t K = 1;
     while (K * K < T) ++K;                 /* block length ~ sqrt(T) */

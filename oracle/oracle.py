@@ -51,6 +51,11 @@ def _load():
             lib.oracle_gla_bwd.argtypes = [d, d, d, d, i64, i64, i64, i64, i64, i64, i64, i32, d, d, d,
                                            d, d, d, d, d, i32]
             lib.oracle_gla_bwd.restype = i32
+            lib.oracle_gla_fwd_order.argtypes = [d, d, d, d, i64, i64, i64, i64, i64, d, d, d, d, i32]
+            lib.oracle_gla_fwd_order.restype = i32
+            lib.oracle_gla_bwd_order.argtypes = [d, d, d, d, i64, i64, i64, i64, i64, d, d, d, d,
+                                                 d, d, d, d, d, i32]
+            lib.oracle_gla_bwd_order.restype = i32
             lib.oracle_srem_dwconv.argtypes = [d, i64, i64, i64, d, i64, i64, i32, d, i32]
             lib.oracle_srem_dwconv.restype = i32
             lib.oracle_remap.argtypes = [d, i64, i64, i64, i64, i32, i32, d]
@@ -93,10 +98,46 @@ def scan_perm(direction, gh: int, gw: int) -> np.ndarray:
     return out
 
 
-def gla_fwd(q, k, v, log_alpha, grid, direction, s0=None, nthreads: int = 0):
+def zigzag_order(j: int, gh: int, gw: int) -> np.ndarray:
+    """ZigMa's snake scan S_j (ZigMa notes, 关键设计 / Zigzag 扫描方案): lines
+    (rows for j < 4, columns for j >= 4) walked one after the other, each in
+    the direction opposite to the one before, starting at corner j % 4 =
+    top-left, top-right, bottom-left, bottom-right.  Written out as walks."""
+    if not 0 <= j < 8:
+        raise ValueError("zigzag scheme must be in [0, 8)")
+    columns, corner = j >= 4, j % 4
+    from_bottom, from_right = corner >= 2, corner % 2 == 1
+    out = []
+    if not columns:
+        rows = range(gh - 1, -1, -1) if from_bottom else range(gh)
+        rightward = not from_right
+        for r in rows:
+            cols = range(gw) if rightward else range(gw - 1, -1, -1)
+            out += [r * gw + c for c in cols]
+            rightward = not rightward
+    else:
+        cols = range(gw - 1, -1, -1) if from_right else range(gw)
+        downward = not from_bottom
+        for c in cols:
+            rows = range(gh) if downward else range(gh - 1, -1, -1)
+            out += [r * gw + c for r in rows]
+            downward = not downward
+    return np.array(out, dtype=np.int64)
+
+
+def _order_arg(order, T):
+    o = np.ascontiguousarray(np.asarray(order), dtype=np.int64)
+    if o.shape != (T,):
+        raise ValueError("order must have T entries")
+    return o
+
+
+def gla_fwd(q, k, v, log_alpha, grid, direction, s0=None, nthreads: int = 0, order=None):
     """Token-by-token fp64 GLA forward.
 
     q, k, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; canonical token order.
+    order: optional table (order[p] = canonical token at scan position p, a
+    permutation) used instead of (grid, direction).
     Returns (o_scan [B, T, H, dv] in scan order, s_final [B, H, dk, dv]).
     """
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(log_alpha)
@@ -104,21 +145,27 @@ def gla_fwd(q, k, v, log_alpha, grid, direction, s0=None, nthreads: int = 0):
     dv = v.shape[3]
     if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H):
         raise ValueError("shape mismatch")
-    gh, gw = grid
     o = np.empty((B, T, H, dv), dtype=np.float64)
     sf = np.empty((B, H, dk, dv), dtype=np.float64)
     s0a = None if s0 is None else _f64(s0)
     if s0a is not None and s0a.shape != (B, H, dk, dv):
         raise ValueError("s0 shape")
-    rc = _load().oracle_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), B, T, H, dk, dv, gh, gw,
-                                _dir(direction), None if s0a is None else _ptr(s0a),
-                                _ptr(o), _ptr(sf), int(nthreads))
+    if order is not None:
+        ordv = _order_arg(order, T)
+        rc = _load().oracle_gla_fwd_order(_ptr(q), _ptr(k), _ptr(v), _ptr(g), B, T, H, dk, dv, _ptr(ordv),
+                                          None if s0a is None else _ptr(s0a), _ptr(o), _ptr(sf), int(nthreads))
+    else:
+        gh, gw = grid
+        rc = _load().oracle_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), B, T, H, dk, dv, gh, gw,
+                                    _dir(direction), None if s0a is None else _ptr(s0a),
+                                    _ptr(o), _ptr(sf), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_gla_fwd rejected its arguments")
     return o, sf
 
 
-def gla_bwd(q, k, v, log_alpha, grid, direction, do_scan, ds_final=None, s0=None, nthreads: int = 0):
+def gla_bwd(q, k, v, log_alpha, grid, direction, do_scan, ds_final=None, s0=None, nthreads: int = 0,
+            order=None):
     """Token-by-token fp64 GLA backward (reverse-mode derivative of gla_fwd).
 
     do_scan [B, T, H, dv] in scan order (the gradient of o), ds_final
@@ -139,10 +186,17 @@ def gla_bwd(q, k, v, log_alpha, grid, direction, do_scan, ds_final=None, s0=None
     dq, dkk, dg = (np.empty((B, T, H, dk)) for _ in range(3))
     dvv = np.empty((B, T, H, dv))
     ds0 = np.empty((B, H, dk, dv))
-    rc = _load().oracle_gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), B, T, H, dk, dv, grid[0], grid[1],
-                                _dir(direction), None if s0a is None else _ptr(s0a), _ptr(dO),
-                                None if dsf is None else _ptr(dsf), _ptr(dq), _ptr(dkk), _ptr(dvv),
-                                _ptr(dg), _ptr(ds0), int(nthreads))
+    if order is not None:
+        ordv = _order_arg(order, T)
+        rc = _load().oracle_gla_bwd_order(_ptr(q), _ptr(k), _ptr(v), _ptr(g), B, T, H, dk, dv, _ptr(ordv),
+                                          None if s0a is None else _ptr(s0a), _ptr(dO),
+                                          None if dsf is None else _ptr(dsf), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                                          _ptr(dg), _ptr(ds0), int(nthreads))
+    else:
+        rc = _load().oracle_gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), B, T, H, dk, dv, grid[0], grid[1],
+                                    _dir(direction), None if s0a is None else _ptr(s0a), _ptr(dO),
+                                    None if dsf is None else _ptr(dsf), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                                    _ptr(dg), _ptr(ds0), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_gla_bwd rejected its arguments")
     return dq, dkk, dvv, dg, ds0
