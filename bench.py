@@ -135,7 +135,7 @@ def cpu_baseline(cfg, x_cpu, budget_s: float = 20.0):
     }
 
 
-def cpu_baseline_bwd(cfg, x_cpu, do_cpu, budget_s: float = 20.0):
+def cpu_baseline_bwd(cfg, x_cpu, do_cpu, budget_s: float = 20.0, order=None):
     """The fp64 oracle's backward on a bounded sample of (b, h) units, scaled to tokens/s of the
     whole batch."""
     from oracle import oracle
@@ -151,7 +151,7 @@ def cpu_baseline_bwd(cfg, x_cpu, do_cpu, budget_s: float = 20.0):
             hs = [h for bb, h in sample if bb == b]
             sl = lambda t: t[b:b + 1][:, :, hs].contiguous()
             oracle.gla_bwd(sl(x_cpu["q"]), sl(x_cpu["k"]), sl(x_cpu["v"]), sl(x_cpu["log_alpha"]), grid,
-                           direction, sl(do_cpu), nthreads=threads)
+                           direction, sl(do_cpu), nthreads=threads, order=order)
         return time.perf_counter() - t0
 
     probe = units[:min(len(units), threads)]
@@ -165,8 +165,95 @@ def cpu_baseline_bwd(cfg, x_cpu, do_cpu, budget_s: float = 20.0):
             n = want
     est_full = tp * len(units) / n
     return {"value": cfg.B * cfg.T / est_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {len(units)} (batch, head) units of {cfg.key} (GLA backward, dir "
-                      f"{direction}, fp64, {threads} OpenMP threads): {tp:.2f} s, scaled to the whole batch"}
+            "sample": f"{n} of {len(units)} (batch, head) units of {cfg.key} (GLA backward, "
+                      + ("zigzag order S_0" if order is not None else f"dir {direction}")
+                      + f", fp64, {threads} OpenMP threads): {tp:.2f} s, scaled to the whole batch"}
+
+
+def zigzag_tables(cfg, dev):
+    """ZigMa's eight zigzag scan orders of the workload's grid as device tables."""
+    from gated_linear_attention_gla_amd import scan_orders
+    return [scan_orders.to_device(scan_orders.zigzag(j, cfg.gh, cfg.gw), dev) for j in range(8)]
+
+
+def bench_fwd_ordered(a, dg, gen, torch) -> int:
+    """gla_fwd over table scan orders (ZigMa's zigzag S_0..S_7, cycled): one step = one
+    gla_fwd_ordered launch over rotating input sets, HIP events on the launch stream.  (The SREM
+    conv is defined in the frame of the four grid orders, so it is not part of this step.)"""
+    import numpy as np
+    from oracle import oracle
+
+    dev = torch.device("cuda:0")
+    cfg = gen.CONFIGS[a.config]
+    if cfg.adaln:
+        print("bench.py --order zigzag: runs the GLA-only workloads (C1, C2, C3)", file=sys.stderr)
+        return 2
+    B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.d
+    chunk = a.chunk or cfg.chunk
+    nsets = a.sets or max(1, math.ceil(512e6 / gla_alg_bytes(cfg)))
+    log(f"[bench] gla_fwd zigzag {cfg.key} {cfg.name}: B={B} H={H} T={T} ({cfg.gh}x{cfg.gw}) d={d}; {nsets} sets")
+    sets = [gen.make_inputs(cfg.key, set_index=i, device=dev) for i in range(nsets)]
+    o = torch.empty(B, T, H, d, dtype=torch.bfloat16, device=dev)
+    sf = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    ws = dg.get_workspace(dev, dg.workspace_bytes(dg.DIG_BF16, B, T, H, d, d, chunk))
+    tables = zigzag_tables(cfg, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        x = sets[i % nsets]
+        dg.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], None, None, chunk=chunk, out=o, s_final=sf,
+                   workspace=ws, order=tables[i % 8])
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = []
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(a.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(a.warmup + i)
+        e1.record(stream)
+        evs.append((e0, e1))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / a.steps
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    avg = sum(ms) / len(ms)
+    abytes, aflops = gla_alg_bytes(cfg), gla_alg_flops(cfg, chunk)
+    achieved = abytes / (avg * 1e-3) / 1e9
+    log(f"[bench] gla_fwd zigzag avg {avg * 1e3:.1f} us (median {ms[len(ms) // 2] * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s alg")
+    cpu = None
+    if not a.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        x0 = {k_: v_.cpu() for k_, v_ in sets[0].items() if isinstance(v_, torch.Tensor)}
+        order0 = tables[0].cpu().numpy().astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.gla_fwd(x0["q"], x0["k"], x0["v"], x0["log_alpha"], None, None, nthreads=threads, order=order0)
+        tc = time.perf_counter() - t0
+        cpu = {"value": B * T / tc, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"all {B * H} (batch, head) units of {cfg.key} (GLA fwd, zigzag order S_0, fp64, "
+                         f"{threads} OpenMP threads): {tc:.2f} s"}
+        log(f"[bench] cpu oracle: {cpu['value']:.3e} tokens/s on {threads} cores")
+    rec = {
+        "metric": "GLA fwd tokens/sec over zigzag scan orders, DiG-XL/2 shape T=4096 d=72",
+        "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian activations of the DiG latent-grid shape)",
+        "config": {"workload": f"{cfg.key} {cfg.name}: GLA forward over ZigMa's zigzag scans S_0..S_7 "
+                               f"(order tables, chunk {chunk})",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "grid": [cfg.gh, cfg.gw],
+                   "directions": ["zigzag S_0..S_7"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gla_fwd_bf16_kernel (order table)",
+                     "alg_bytes_per_launch": abytes, "avg_launch_us": avg * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def bench_bwd(a, dg, gen, torch) -> int:
@@ -194,11 +281,12 @@ def bench_bwd(a, dg, gen, torch) -> int:
     nbytes = dg.lib().gla_bwd_workspace_size(dg.DIG_BF16, B, T, H, d, d, chunk)
     ws = dg.get_workspace(dev, nbytes, key="bwd")
     stream = torch.cuda.current_stream(dev)
+    tables = zigzag_tables(cfg, dev) if a.order == "zigzag" else None
 
     def step(i):
         x, do = sets[i % nsets]
         dg.gla_bwd(x["q"], x["k"], x["v"], x["log_alpha"], grid, cfg.direction(i), do, chunk=chunk,
-                   need_ds0=False, workspace=ws)
+                   need_ds0=False, workspace=ws, order=None if tables is None else tables[i % 8])
 
     for i in range(a.warmup):
         step(i)
@@ -227,17 +315,20 @@ def bench_bwd(a, dg, gen, torch) -> int:
         log("[bench] timing the fp64 CPU oracle backward on a bounded sample ...")
         x0, do0 = sets[0]
         x_cpu = {k_: v_.cpu() for k_, v_ in x0.items() if isinstance(v_, torch.Tensor)}
-        cpu = cpu_baseline_bwd(cfg, x_cpu, do0.cpu())
+        cpu = cpu_baseline_bwd(cfg, x_cpu, do0.cpu(), order=None if tables is None else tables[0].cpu().numpy())
         log(f"[bench] cpu oracle bwd: {cpu['value']:.3e} tokens/s on {cpu['cores']} cores")
+    zz = tables is not None
     rec = {
-        "metric": "GLA bwd tokens/sec (training backward), DiG-XL/2 shape T=4096 d=72",
+        "metric": "GLA bwd tokens/sec (training backward" + (", zigzag scan orders" if zz else "")
+                  + "), DiG-XL/2 shape T=4096 d=72",
         "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Gaussian activations and output gradients of the DiG latent-grid shape)",
-        "config": {"workload": f"{cfg.key} {cfg.name}: GLA backward (chunk {chunk}; dq, dk, dv, dlog_alpha)",
+        "config": {"workload": f"{cfg.key} {cfg.name}: GLA backward (chunk {chunk}; dq, dk, dv, dlog_alpha)"
+                               + (" over ZigMa's zigzag scans S_0..S_7 (order tables)" if zz else ""),
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "grid": list(grid),
-                   "directions": list(cfg.dirs), "parallelism": "single GPU"},
+                   "directions": ["zigzag S_0..S_7"] if zz else list(cfg.dirs), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "gla_bwd (gla_bwd_scan, both directions in one launch, + gla_bwd_chunk)", "alg_bytes_per_launch": abytes,
@@ -335,6 +426,8 @@ def main(argv=None) -> int:
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = the workload's, 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bwd", action="store_true", help="time gla_bwd (the training backward) instead")
+    ap.add_argument("--order", default="grid", choices=["grid", "zigzag"],
+                    help="scan orders: the workload's grid directions, or ZigMa's zigzag tables (GLA only)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the launches the PMC passes count: 3 plain copies, 3 gla_fwd")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
@@ -362,6 +455,8 @@ def main(argv=None) -> int:
         return traffic_probe(a.config, a.chunk)
     if a.bwd:
         return bench_bwd(a, dg, gen, torch)
+    if a.order == "zigzag":
+        return bench_fwd_ordered(a, dg, gen, torch)
     dev = torch.device("cuda:0")
     cfg = gen.CONFIGS[a.config]
     B, T, H, d, C = cfg.B, cfg.T, cfg.H, cfg.d, cfg.C
