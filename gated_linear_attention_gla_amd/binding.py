@@ -57,6 +57,14 @@ def lib() -> ctypes.CDLL:
             L.gla_bwd_ordered.restype = i32
             L.dig_gather_rows.argtypes = [p, i32, i32, i32, i32, p, p, p]
             L.dig_gather_rows.restype = i32
+            L.dig_linear_workspace_size.argtypes = []
+            L.dig_linear_workspace_size.restype = sz
+            L.dig_linear.argtypes = [p, p, p, i32, i32, i32, p, sz, p]
+            L.dig_linear.restype = i32
+            L.dig_block_workspace_size.argtypes = [i32, i32, i32, i32]
+            L.dig_block_workspace_size.restype = sz
+            L.dig_block_fwd.argtypes = [p] * 13 + [i32] * 7 + [p, p, sz, p]
+            L.dig_block_fwd.restype = i32
             L.gla_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
             L.gla_bwd_workspace_size.restype = sz
             L.srem_dwconv.argtypes = [p, i32, i32, i32, i32, i64, i64, p, i32, i32, i32, p, i64, i64, p]
@@ -277,6 +285,56 @@ def gather_rows(x, index, out=None):
     rc = lib().dig_gather_rows(_ptr(x), _dtype_code(x), B, T, C, _ptr(_order(index, T, x.device)), _ptr(out),
                                _stream(x.device))
     _check(rc, "dig_gather_rows")
+    return out
+
+
+BLOCK_WEIGHTS = ("w_ada", "b_ada", "w_in", "b_in", "w_out", "b_out", "w_ff1", "b_ff1", "w_ff2", "b_ff2", "w_conv")
+
+
+def linear(x, w, out=None, workspace=None):
+    """y = x w^T for bf16 x [M, K] and w [N, K] (rows contiguous), y [M, N] bf16 (fp32 accumulation)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 \
+            or not x.is_contiguous() or not w.is_contiguous():
+        raise DigError("linear: contiguous bf16 x [M, K] and w [N, K] needed")
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = get_workspace(x.device, int(lib().dig_linear_workspace_size()), key="gemm")
+    rc = lib().dig_linear(_ptr(x), _ptr(w), _ptr(out), M, N, K, _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(x.device))
+    _check(rc, "dig_linear")
+    return out
+
+
+def block_fwd(x, c, weights: dict, grid, direction, H: int, out=None, workspace=None):
+    """One DiG block forward (dig_block_fwd): x bf16 [B, T, C] canonical, c fp32 [B, C], weights
+    a dict with the keys of BLOCK_WEIGHTS (bf16 w_*, fp32 b_* and w_conv).  Returns y [B, T, C]."""
+    B, T, C = x.shape
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise DigError("block_fwd: x must be contiguous bf16 [B, T, C]")
+    if c.dtype != torch.float32 or tuple(c.shape) != (B, C) or not c.is_contiguous():
+        raise DigError("block_fwd: c must be contiguous fp32 [B, C]")
+    shapes = {"w_ada": (6 * C, C), "b_ada": (6 * C,), "w_in": (4 * C, C), "b_in": (4 * C,), "w_out": (C, C),
+              "b_out": (C,), "w_ff1": (4 * C, C), "b_ff1": (4 * C,), "w_ff2": (C, 4 * C), "b_ff2": (C,),
+              "w_conv": (C, 3, 3)}
+    for n in BLOCK_WEIGHTS:
+        t = weights[n]
+        want = torch.bfloat16 if n.startswith("w_") and n != "w_conv" else torch.float32
+        if t.dtype != want or tuple(t.shape) != shapes[n] or not t.is_contiguous() or t.device != x.device:
+            raise DigError(f"block_fwd: {n} must be contiguous {want} {shapes[n]} on {x.device}")
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        n = lib().dig_block_workspace_size(B, T, C, H)
+        if n == ctypes.c_size_t(-1).value:
+            raise DigError("block_fwd: invalid sizes")
+        workspace = get_workspace(x.device, int(n), key="block")
+    rc = lib().dig_block_fwd(_ptr(x), _ptr(c), *[_ptr(weights[n]) for n in BLOCK_WEIGHTS], B, T, C, H, grid[0],
+                             grid[1], _dir(direction), _ptr(out), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(x.device))
+    _check(rc, "dig_block_fwd")
     return out
 
 

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libdig_gla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gla_bf16.hip", "gla_bwd.hip", "gla_f32.hip", "srem.hip", "adaln.hip"]
+SOURCES = ["api.cpp", "gla_bf16.hip", "gla_bwd.hip", "gla_f32.hip", "srem.hip", "adaln.hip", "block.hip"]
 HEADERS = ["dig_internal.h", "dig_mfma.h", os.path.join("..", "..", "include", "dig_gla.h")]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-function",
@@ -54,7 +54,8 @@ def build(force: bool = False, jobs: int | None = None) -> str:
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, force), SOURCES))
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < max(os.path.getmtime(o) for o in objs):
-        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs,
+               "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -383,6 +383,80 @@ int dig_gather_rows(const void *x, int dtype, int B, int T, int C, const int32_t
   }
 }
 
+size_t dig_linear_workspace_size(void) { return DIG_GEMM_SCRATCH; }
+
+int dig_linear(const void *x, const void *w, void *y, int M, int N, int K, void *workspace, size_t workspace_bytes,
+               hipStream_t stream) {
+  try {
+    if (!x || !w || !y) return fail(DIG_EINVAL, "dig_linear: x, w and y are required");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(DIG_EINVAL, "dig_linear: M, N, K must be positive");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(DIG_EINVAL, "dig_linear: 16-byte alignment needed");
+    if (y == x || y == w) return fail(DIG_EINVAL, "dig_linear: y aliases an input");
+    if (!workspace || workspace_bytes < DIG_GEMM_SCRATCH)
+      return fail(DIG_EWORKSPACE, "dig_linear: workspace of %zu bytes needed, %zu given", (size_t)DIG_GEMM_SCRATCH,
+                  workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(DIG_EINVAL, "dig_linear: workspace must be 256-byte aligned");
+    DevInfo di;
+    int rc = current_device(di);
+    if (rc) return rc;
+    const hipError_t e = dig_launch_linear(x, w, y, M, N, K, workspace, DIG_GEMM_SCRATCH, stream);
+    if (e != hipSuccess) return hip_fail(e, "dig_linear");
+    return DIG_OK;
+  } catch (...) {
+    return fail(DIG_EHIP, "dig_linear: unexpected C++ exception");
+  }
+}
+
+size_t dig_block_workspace_size(int B, int T, int C, int H) {
+  if (B <= 0 || T <= 0 || C <= 0 || H <= 0 || C % H || C % 8) return (size_t)-1;
+  DevInfo di;
+  const int num_cu = (current_device(di) == DIG_OK) ? di.num_cu : 256;
+  return dig_block_workspace(B, T, C, H, num_cu);
+}
+
+int dig_block_fwd(const void *x, const float *c, const void *w_ada, const float *b_ada, const void *w_in,
+                  const float *b_in, const void *w_out, const float *b_out, const void *w_ff1, const float *b_ff1,
+                  const void *w_ff2, const float *b_ff2, const float *w_conv, int B, int T, int C, int H, int gh,
+                  int gw, int dir, void *y, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    if (!x || !c || !w_ada || !b_ada || !w_in || !b_in || !w_out || !b_out || !w_ff1 || !b_ff1 || !w_ff2 || !b_ff2 ||
+        !w_conv || !y)
+      return fail(DIG_EINVAL, "dig_block_fwd: every input, weight and y is required");
+    if (B <= 0 || T <= 0 || C <= 0 || H <= 0 || C % H) return fail(DIG_EINVAL, "dig_block_fwd: bad B, T, C, H");
+    const int d = C / H;
+    if (d % 8 || d > 128) return fail(DIG_EINVAL, "dig_block_fwd: head dim C/H must be a multiple of 8, at most 128");
+    if (C > 16384) return fail(DIG_EINVAL, "dig_block_fwd: C must be at most 16384");
+    if ((int64_t)B * T * 4 * C >= ((int64_t)1 << 31) / 2)
+      return fail(DIG_EINVAL, "dig_block_fwd: B*T*4C too large for one product");
+    if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
+      return fail(DIG_EINVAL, "dig_block_fwd: grid %dx%d does not hold T=%d tokens", gh, gw, T);
+    if (dir < DIG_L2R || dir > DIG_B2T) return fail(DIG_EINVAL, "dig_block_fwd: dir must be 0..3");
+    const void *al[] = {x, w_ada, w_in, w_out, w_ff1, w_ff2, y};
+    for (const void *p : al)
+      if (!aligned16(p)) return fail(DIG_EINVAL, "dig_block_fwd: bf16 tensors must be 16-byte aligned");
+    if (y == x) return fail(DIG_EINVAL, "dig_block_fwd: y aliases x");
+    DevInfo di;
+    int rc = current_device(di);
+    if (rc) return rc;
+    const size_t need = dig_block_workspace(B, T, C, H, di.num_cu);
+    if (!workspace || workspace_bytes < need)
+      return fail(DIG_EWORKSPACE, "dig_block_fwd: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(DIG_EINVAL, "dig_block_fwd: workspace must be 256-byte aligned");
+    DigBlockArgs a;
+    a.x = x; a.c = c; a.w_ada = w_ada; a.b_ada = b_ada; a.w_in = w_in; a.b_in = b_in; a.w_out = w_out;
+    a.b_out = b_out; a.w_ff1 = w_ff1; a.b_ff1 = b_ff1; a.w_ff2 = w_ff2; a.b_ff2 = b_ff2; a.w_conv = w_conv;
+    a.y = y; a.B = B; a.T = T; a.C = C; a.H = H; a.gh = gh; a.gw = gw; a.dir = dir; a.chunk = 0;
+    a.workspace = workspace;
+    a.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed) % 0x1fffffffu + 1u;
+    a.num_cu = di.num_cu;
+    const hipError_t e = dig_launch_block(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "dig_block_fwd");
+    return DIG_OK;
+  } catch (...) {
+    return fail(DIG_EHIP, "dig_block_fwd: unexpected C++ exception");
+  }
+}
+
 int dig_adaln_modulate(const void *x, int dtype, int64_t N, int C, int64_t x_sn, const float *scale,
                        const float *shift, float eps, float out_scale, void *y, int64_t y_sn,
                        hipStream_t stream) {

@@ -108,6 +108,32 @@ size_t dig_gla_f32_lds_bytes(int dk, int dv, int chunk);
 hipError_t dig_launch_dwconv(const void *x, int dtype, int B, int T, int C, int64_t x_sb, int64_t x_st,
                              const float *w, int gh, int gw, int dir, void *y, int64_t y_sb,
                              int64_t y_st, int num_cu, hipStream_t s);
+// One DiG block forward (block.hip).
+struct DigBlockArgs {
+  const void *x;          // bf16 [B, T, C] canonical (residual stream in)
+  const float *c;         // [B, C] conditioning (timestep + class embedding)
+  const void *w_ada;      // bf16 [6C, C]
+  const float *b_ada;     // [6C]
+  const void *w_in;       // bf16 [4C, C]: q | k | v | gate rows
+  const float *b_in;      // [4C]
+  const void *w_out;      // bf16 [C, C]
+  const float *b_out;     // [C]
+  const void *w_ff1;      // bf16 [4C, C]
+  const float *b_ff1;     // [4C]
+  const void *w_ff2;      // bf16 [C, 4C]
+  const float *b_ff2;     // [C]
+  const float *w_conv;    // [C, 3, 3]
+  void *y;                // bf16 [B, T, C] canonical (block output)
+  int B, T, C, H, gh, gw, dir, chunk;
+  void *workspace;
+  uint32_t epoch;
+  int num_cu;
+};
+constexpr size_t DIG_GEMM_SCRATCH = size_t(64) << 20;   // bytes of rocBLAS scratch a product may use
+size_t dig_block_workspace(int B, int T, int C, int H, int num_cu);
+hipError_t dig_launch_block(const DigBlockArgs &a, hipStream_t s);
+hipError_t dig_launch_linear(const void *x, const void *w, void *y, int M, int N, int K, void *scratch,
+                             size_t scratch_bytes, hipStream_t s);
 hipError_t dig_launch_gather_rows(const void *x, int dtype, int B, int T, int C, const int *index, void *y,
                                   int num_cu, hipStream_t s);
 hipError_t dig_launch_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw, int from,

@@ -200,7 +200,7 @@ gla_fwd_bf16_kernel(Params P) {
   const int xcd = lid & 7, kslot = lid >> 3;
   const int unit = xcd * P.per_xcd + kslot / P.nseg;
   const int seg = kslot % P.nseg;
-  if (unit >= P.units) return;
+  if ((unsigned)unit >= (unsigned)P.units) return;   // (a workspace that was not zero-filled gives wild tickets)
   // Chunk ranges.  Uniform segments: segment g aggregates and then outputs
   // its own chunks.  Two-segment split (split_K > 0): segment 0 outputs
   // chunks [0, L+K) straight from s0 and publishes the state entering chunk L

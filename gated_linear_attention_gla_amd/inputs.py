@@ -143,3 +143,29 @@ def make_inputs(key: str, set_index: int = 0, device="cpu") -> dict:
         out["ada_out_scale"] = cfg.qkv_scale
     out["w"] = conv_weight(H * d, cfg.conv_perturb, gen, device)
     return out
+
+
+def block_inputs(B: int, T: int, C: int, seed: int = 0, device="cpu", conv_perturb: float = 0.01) -> dict:
+    """Seeded synthetic inputs and weights of one DiG block (no trained weights
+    exist here): the residual stream x [B, T, C] ~ N(0, 1) (bf16), the
+    conditioning c [B, C] ~ N(0, 1) (fp32), the linear weights ~ N(0, 1/fan_in)
+    (bf16; the adaLN regression ~ N(0, 0.25/C) so that shifts, scales and gates
+    stay O(0.5)), biases ~ N(0, 0.02^2) (fp32) and the conv near identity."""
+    g = _gen(seed, device)
+
+    def w(rows, cols, s=1.0):
+        return (torch.randn(rows, cols, generator=g, device=device) * (s / math.sqrt(cols))).to(torch.bfloat16)
+
+    def bias(n):
+        return torch.randn(n, generator=g, device=device) * 0.02
+
+    x = torch.randn(B, T, C, generator=g, device=device).to(torch.bfloat16)
+    c = torch.randn(B, C, generator=g, device=device)
+    out = {"x": x, "c": c,
+           "w_ada": w(6 * C, C, 0.5), "b_ada": bias(6 * C),
+           "w_in": w(4 * C, C), "b_in": bias(4 * C),
+           "w_out": w(C, C), "b_out": bias(C),
+           "w_ff1": w(4 * C, C), "b_ff1": bias(4 * C),
+           "w_ff2": w(C, 4 * C), "b_ff2": bias(C)}
+    out["w_conv"] = conv_weight(C, conv_perturb, g, device)
+    return out

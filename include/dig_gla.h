@@ -288,6 +288,60 @@ int dig_gather_rows(const void *x, int dtype, int B, int T, int C,
                     const int32_t *index, void *y, hipStream_t stream);
 
 /*
+ * dig_linear -- y = x w^T for row-major bf16 x [M, K], w [N, K] (a PyTorch
+ * Linear weight), y [M, N] bf16; fp32 accumulation.  A plain dense product,
+ * run by rocBLAS on `stream` with its scratch in `workspace` (at least
+ * dig_linear_workspace_size() bytes, 256-byte aligned, not shared by calls in
+ * flight at once).  The first call on a device creates that device's rocBLAS
+ * handle, which the library keeps.  Errors: DIG_EINVAL (null, sizes,
+ * alignment, aliasing), DIG_EWORKSPACE, DIG_EHIP.
+ */
+size_t dig_linear_workspace_size(void);
+int dig_linear(const void *x, const void *w, void *y, int M, int N, int K,
+               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dig_block_fwd -- one DiG block forward (DiG notes, 关键设计 / DiG Block设计:
+ * adaLN -> GLA, adaLN -> FFN, the sequence as a 2-D grid through the 3x3
+ * depthwise conv, the next block in another direction; adaLN-Zero
+ * conditioning as DiT, DiT notes 3.2).  For each batch element b:
+ *   [s1|a1|g1|s2|a2|g2] = SiLU(c[b]) w_ada^T + b_ada           (6 vectors of C)
+ *   h  = LN(x)(1 + a1) + s1                                     (LN: no affine, eps 1e-6)
+ *   [q|k|v|u] = h w_in^T + b_in;  q /= sqrt(C/H);  log_alpha = logsigmoid(u) / 16
+ *   o  = gla_fwd over (gh, gw, dir) with H heads of C/H channels (scan order)
+ *   x1 = x + g1 (.) canon(o w_out^T + b_out)                    (canon: back to canonical order)
+ *   h2 = LN(x1)(1 + a2) + s2
+ *   x2 = x1 + g2 (.) (GELU_tanh(h2 w_ff1^T + b_ff1) w_ff2^T + b_ff2)
+ *   y  = srem_dwconv(x2 arranged in the scan order of dir, w_conv)  (canonical order)
+ *
+ *   x, y     bf16 [B, T, C] contiguous, canonical token order; y must not
+ *            overlap x or the workspace.
+ *   c        fp32 [B, C]: the conditioning (timestep + class embedding).
+ *   w_ada    bf16 [6C, C], b_ada fp32 [6C]; w_in bf16 [4C, C] (rows q, k, v,
+ *            u), b_in fp32 [4C]; w_out bf16 [C, C], b_out fp32 [C]; w_ff1 bf16
+ *            [4C, C], b_ff1 fp32 [4C]; w_ff2 bf16 [C, 4C], b_ff2 fp32 [C];
+ *            w_conv fp32 [C, 3, 3].  All contiguous; bf16 ones 16-byte aligned.
+ *   C = H * d with d a multiple of 8, at most 128; C <= 16384.
+ *   workspace  at least dig_block_workspace_size(B, T, C, H) bytes, 256-byte
+ *            aligned, any contents (the call clears the part it needs
+ *            cleared), not shared by calls in flight at once.  Products run on rocBLAS with
+ *            their scratch inside it; the first call on a device creates that
+ *            device's rocBLAS handle.
+ * Errors as gla_fwd.
+ */
+size_t dig_block_workspace_size(int B, int T, int C, int H);
+int dig_block_fwd(const void *x, const float *c,
+                  const void *w_ada, const float *b_ada,
+                  const void *w_in, const float *b_in,
+                  const void *w_out, const float *b_out,
+                  const void *w_ff1, const float *b_ff1,
+                  const void *w_ff2, const float *b_ff2,
+                  const float *w_conv,
+                  int B, int T, int C, int H, int gh, int gw, int dir,
+                  void *y, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/*
  * dig_adaln_modulate -- adaLN modulation of N rows (tokens) of C channels:
  *   y = ((x - mean) / sqrt(var + eps) * (1 + scale) + shift) * out_scale
  * with the population mean and variance of the row, computed in fp32.

@@ -239,3 +239,59 @@ def adaln_modulate(x, scale, shift, eps: float = 1e-6, out_scale: float = 1.0, n
     if rc != 0:
         raise ValueError("oracle_adaln_modulate rejected its arguments")
     return y
+
+
+BLOCK_WEIGHTS = ("w_ada", "b_ada", "w_in", "b_in", "w_out", "b_out", "w_ff1", "b_ff1", "w_ff2", "b_ff2", "w_conv")
+
+
+def block_fwd(x, c, w, grid, direction, H: int, nthreads: int = 0):
+    """One DiG block forward in fp64, the steps in the order the pages give
+    them (DiG notes, 关键设计 / DiG Block设计; adaLN-Zero from DiT notes, 3.2):
+
+      (1) conditioning c -> SiLU -> linear -> six vectors per batch element:
+          shift, scale, gate of the mixer branch, then of the FFN branch;
+      (2) x -> LN (no affine, eps 1e-6) -> (1 + scale) * . + shift -> the q, k,
+          v, gate projections -> GLA over the block's scan direction (q scaled
+          by 1/sqrt(d), log gate = logsigmoid(u) / 16) -> out projection ->
+          added to x times the gate, back in canonical token order;
+      (3) the same adaLN -> FFN (C -> 4C, tanh GELU, 4C -> C) -> gated residual;
+      (4) the tokens in the scan order of the direction, as that scan's 2-D
+          frame, through the 3x3 depthwise conv, stored in canonical order.
+
+    x [B, T, C] (canonical), c [B, C]; w: dict of the weights in
+    BLOCK_WEIGHTS (PyTorch Linear layout [out, in]).  Returns y [B, T, C]."""
+    x = _f64(x)
+    c = _f64(c)
+    W = {n: _f64(w[n]) for n in BLOCK_WEIGHTS}
+    B, T, C = x.shape
+    d = C // H
+    gh, gw = grid
+    # (1) adaLN-Zero parameters
+    silu = c / (1.0 + np.exp(-c))
+    ada = silu @ W["w_ada"].T + W["b_ada"]                              # [B, 6C]
+    s1, a1, g1, s2, a2, g2 = (ada[:, i * C:(i + 1) * C][:, None, :] for i in range(6))
+
+    def ln(z):
+        mu = z.mean(axis=-1, keepdims=True)
+        var = ((z - mu) ** 2).mean(axis=-1, keepdims=True)
+        return (z - mu) / np.sqrt(var + 1e-6)
+
+    # (2) token mixer
+    h = ln(x) * (1.0 + a1) + s1
+    qkvu = h @ W["w_in"].T + W["b_in"]                                 # [B, T, 4C]
+    q, k, v, u = (qkvu[..., i * C:(i + 1) * C].reshape(B, T, H, d) for i in range(4))
+    q = q / np.sqrt(d)
+    log_alpha = (np.minimum(u, 0.0) - np.log1p(np.exp(-np.abs(u)))) / 16.0
+    o, _ = gla_fwd(q, k, v, log_alpha, grid, direction, nthreads=nthreads)   # scan order
+    o2 = o.reshape(B, T, C) @ W["w_out"].T + W["b_out"]
+    perm = scan_perm(direction, gh, gw)                                # perm[p] = canonical token
+    o2c = np.empty_like(o2)
+    o2c[:, perm] = o2
+    x1 = x + g1 * o2c
+    # (3) FFN
+    h2 = ln(x1) * (1.0 + a2) + s2
+    z = h2 @ W["w_ff1"].T + W["b_ff1"]
+    z = 0.5 * z * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (z + 0.044715 * z ** 3)))
+    x2 = x1 + g2 * (z @ W["w_ff2"].T + W["b_ff2"])
+    # (4) SREM conv in the scan frame of the direction
+    return srem_dwconv(x2[:, perm], W["w_conv"], grid, direction, nthreads=nthreads)

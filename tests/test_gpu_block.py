@@ -1,0 +1,87 @@
+"""GPU parity of the DiG block forward (dig_block_fwd, through the C ABI)
+against the fp64 oracle (oracle.block_fwd, pinned in test_oracle_block.py).
+
+The GPU rounds every intermediate to bf16 (the modulated rows, the four
+projections, the GLA output, the out-projection, the residual after the
+mixer, the FFN's hidden layer and output, the residual after the FFN) with
+fp32 accumulation inside each product, so about eight bf16 roundings
+(2^-9 relative each) stand between input and output: the block output is
+compared at 2e-2 normwise per batch element (as the bf16 GLA), and its
+update y - x, which carries all of that rounding, at 4e-2.  Zero adaLN
+weights with the identity conv give the identity map exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_linear_attention_gla_amd import binding as dg
+from gated_linear_attention_gla_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+TOL_Y, TOL_UPDATE = 2e-2, 4e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dg.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(x, grid, direction, H):
+    w = {n: x[n].to("cuda").contiguous() for n in dg.BLOCK_WEIGHTS}
+    y = dg.block_fwd(x["x"].to("cuda"), x["c"].to("cuda"), w, grid, direction, H)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def _check(y, ref, x, what):
+    y = y.double().numpy()
+    x0 = x["x"].double().numpy()
+    for b in range(y.shape[0]):
+        e = np.linalg.norm(y[b] - ref[b]) / np.linalg.norm(ref[b])
+        u = np.linalg.norm((y[b] - x0[b]) - (ref[b] - x0[b])) / np.linalg.norm(ref[b] - x0[b])
+        assert e <= TOL_Y, f"{what} b={b}: y rel err {e:.3e}"
+        assert u <= TOL_UPDATE, f"{what} b={b}: update rel err {u:.3e}"
+
+
+@pytest.mark.parametrize("shape", [(2, 8, 8, 128, 2), (1, 11, 9, 144, 2), (2, 6, 10, 256, 4)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_block_vs_oracle(orc, shape):
+    """Small shapes (ragged chunks, 72-channel heads) in all four directions."""
+    B, gh, gw, C, H = shape
+    x = gen.block_inputs(B, gh * gw, C, seed=80 + C)
+    w = {n: x[n] for n in orc.BLOCK_WEIGHTS}
+    for d in gen.DIRS:
+        _check(_run(x, (gh, gw), d, H), orc.block_fwd(x["x"], x["c"], w, (gh, gw), d, H=H), x, f"{shape} {d}")
+
+
+def test_block_adaln_zero_is_identity():
+    x = gen.block_inputs(2, 64, 128, seed=81, conv_perturb=0.0)
+    x["w_ada"].zero_()
+    x["b_ada"].zero_()
+    for d in gen.DIRS:
+        assert torch.equal(_run(x, (8, 8), d, 2), x["x"]), d
+
+
+def test_block_c2_shape_sampled(orc):
+    """The DiG-XL/2 block at 1024 px (B=8, 64x64 tokens, C=1152, 16 heads):
+    the GPU over the whole batch, the oracle on batch elements 0 and 5."""
+    B, gh, gw, C, H = 8, 64, 64, 1152, 16
+    x = gen.block_inputs(B, gh * gw, C, seed=82)
+    y = _run(x, (gh, gw), "t2b", H)
+    assert torch.isfinite(y.float()).all()
+    w = {n: x[n] for n in orc.BLOCK_WEIGHTS}
+    for b in (0, 5):
+        ref = orc.block_fwd(x["x"][b:b + 1], x["c"][b:b + 1], w, (gh, gw), "t2b", H=H)
+        _check(y[b:b + 1], ref, {"x": x["x"][b:b + 1]}, f"C2 block b={b}")
+
+
+def test_linear_vs_matmul():
+    g = torch.Generator().manual_seed(83)
+    x = torch.randn(300, 256, generator=g).to(torch.bfloat16)
+    w = torch.randn(200, 256, generator=g).to(torch.bfloat16) / 16
+    y = dg.linear(x.to("cuda"), w.to("cuda")).cpu().double()
+    ref = x.double() @ w.double().T
+    assert float((y - ref).norm() / ref.norm()) <= 4e-3
