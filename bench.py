@@ -256,6 +256,102 @@ def bench_fwd_ordered(a, dg, gen, torch) -> int:
     return 0
 
 
+def block_alg_flops(B, T, C, H, M=64) -> int:
+    """Dense products of one block per token: q/k/v/gate (C -> 4C), out (C -> C), FFN (C -> 4C -> C):
+    2 C^2 (4 + 1 + 8); plus the GLA's chunk-wise flops (4 M d + 4 d^2 per head and token)."""
+    d = C // H
+    return B * T * (2 * C * C * 13 + H * (4 * M * d + 4 * d * d))
+
+
+def bench_block(a, dg, gen, torch) -> int:
+    """One DiG-XL/2 block forward (dig_block_fwd) at the C2 latent grid (B=8, 64x64 tokens, C=1152,
+    16 heads) on seeded synthetic weights: one step = one block call, directions cycled.  The MFMA
+    roofline is taken on the block's largest product (tokens x 4C x C, the q/k/v/gate projection and
+    the FFN's first layer), timed through dig_linear with HIP events on the same stream."""
+    import numpy as np
+    from oracle import oracle
+
+    dev = torch.device("cuda:0")
+    cfg = gen.CONFIGS["C2"]
+    B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.d
+    C = H * d
+    grid = (cfg.gh, cfg.gw)
+    log(f"[bench] DiG block C2 shape: B={B} T={T} ({cfg.gh}x{cfg.gw}) C={C} H={H}")
+    x = gen.block_inputs(B, T, C, seed=cfg.seed, device=dev)
+    w = {n: x[n] for n in dg.BLOCK_WEIGHTS}
+    y = torch.empty_like(x["x"])
+    n = dg.lib().dig_block_workspace_size(B, T, C, H)
+    ws = dg.get_workspace(dev, int(n), key="block")
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        dg.block_fwd(x["x"], x["c"], w, grid, cfg.direction(i), H, out=y, workspace=ws)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(a.steps):
+        step(a.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / a.steps
+    aflops = block_alg_flops(B, T, C, H)
+    # the largest product on its own, same operand sizes as inside the block
+    xa = torch.randn(B * T, C, device=dev).to(torch.bfloat16)
+    wa = (torch.randn(4 * C, C, device=dev) / math.sqrt(C)).to(torch.bfloat16)
+    ya = torch.empty(B * T, 4 * C, dtype=torch.bfloat16, device=dev)
+    gws = dg.get_workspace(dev, int(dg.lib().dig_linear_workspace_size()), key="gemm")
+    for _ in range(5):
+        dg.linear(xa, wa, out=ya, workspace=gws)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(a.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dg.linear(xa, wa, out=ya, workspace=gws)
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    g_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    g_flops = 2 * B * T * 4 * C * C
+    g_tflops = g_flops / (g_ms * 1e-3) / 1e12
+    log(f"[bench] block {ms_step * 1e3:.1f} us, {aflops / (ms_step * 1e-3) / 1e12:.0f} TFLOP/s alg; "
+        f"largest product {g_ms * 1e3:.1f} us = {g_tflops:.0f} TFLOP/s")
+    cpu = None
+    if not a.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        xc = {k_: v_[:1].cpu() if k_ in ("x", "c") else v_.cpu() for k_, v_ in x.items()}
+        tc0 = time.perf_counter()
+        oracle.block_fwd(xc["x"], xc["c"], {n_: xc[n_] for n_ in dg.BLOCK_WEIGHTS}, grid, "l2r", H=H,
+                         nthreads=threads)
+        tc = time.perf_counter() - tc0
+        cpu = {"value": T / tc, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"batch element 0 of 8 (T={T}, C={C}, fp64 numpy products + the C GLA and conv "
+                         f"oracles, {threads} threads): {tc:.2f} s"}
+        log(f"[bench] cpu oracle block: {cpu['value']:.3e} tokens/s on {threads} cores")
+    rec = {
+        "metric": "DiG block forward tokens/sec (adaLN-Zero, projections, GLA, FFN, SREM conv), DiG-XL/2 at 1024px",
+        "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian activations, conditioning and weights of the DiG-XL/2 block shape)",
+        "config": {"workload": f"DiG-XL/2 block forward at the C2 latent grid (B={B}, {cfg.gh}x{cfg.gw} tokens, "
+                               f"C={C}, {H} heads)",
+                   "global_batch": B, "seq_len": T, "hidden": C, "heads": H, "grid": list(grid),
+                   "directions": list(cfg.dirs), "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": g_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": g_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": f"largest product of the block (rocBLAS gemm, {B * T} x {4 * C} x {C}, bf16)",
+                     "alg_flops_per_launch": g_flops, "avg_launch_us": g_ms * 1e3},
+        "block": {"tflops_alg": aflops / (ms_step * 1e-3) / 1e12, "alg_flops_per_step": aflops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def bench_bwd(a, dg, gen, torch) -> int:
     """gla_bwd on the workload's shape: one step = one backward call (two launches on one
     stream: the forward state scan and the reverse state-gradient scan side by side, then the
@@ -426,6 +522,7 @@ def main(argv=None) -> int:
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = the workload's, 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bwd", action="store_true", help="time gla_bwd (the training backward) instead")
+    ap.add_argument("--block", action="store_true", help="time one DiG block forward (DiG-XL/2, C2 grid)")
     ap.add_argument("--order", default="grid", choices=["grid", "zigzag"],
                     help="scan orders: the workload's grid directions, or ZigMa's zigzag tables (GLA only)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -455,6 +552,8 @@ def main(argv=None) -> int:
         return traffic_probe(a.config, a.chunk)
     if a.bwd:
         return bench_bwd(a, dg, gen, torch)
+    if a.block:
+        return bench_block(a, dg, gen, torch)
     if a.order == "zigzag":
         return bench_fwd_ordered(a, dg, gen, torch)
     dev = torch.device("cuda:0")
