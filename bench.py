@@ -343,7 +343,7 @@ def bench_block(a, dg, gen, torch) -> int:
                    "directions": list(cfg.dirs), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": g_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": g_tflops / BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": f"largest product of the block (rocBLAS gemm, {B * T} x {4 * C} x {C}, bf16)",
+                     "kernel": f"largest product of the block (hipBLASLt matmul, {B * T} x {4 * C} x {C}, bf16)",
                      "alg_flops_per_launch": g_flops, "avg_launch_us": g_ms * 1e3},
         "block": {"tflops_alg": aflops / (ms_step * 1e-3) / 1e12, "alg_flops_per_step": aflops},
         "cpu_baseline": cpu,

@@ -431,9 +431,11 @@ int dig_block_fwd(const void *x, const float *c, const void *w_ada, const float 
     if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
       return fail(DIG_EINVAL, "dig_block_fwd: grid %dx%d does not hold T=%d tokens", gh, gw, T);
     if (dir < DIG_L2R || dir > DIG_B2T) return fail(DIG_EINVAL, "dig_block_fwd: dir must be 0..3");
-    const void *al[] = {x, w_ada, w_in, w_out, w_ff1, w_ff2, y};
+    const void *al[] = {x, w_ada, w_in, w_out, w_ff1, w_ff2, y, b_in, b_out, b_ff1, b_ff2};
     for (const void *p : al)
-      if (!aligned16(p)) return fail(DIG_EINVAL, "dig_block_fwd: bf16 tensors must be 16-byte aligned");
+      if (!aligned16(p))
+        return fail(DIG_EINVAL, "dig_block_fwd: bf16 tensors and the fp32 biases b_in, b_out, b_ff1, b_ff2 must be "
+                                "16-byte aligned");
     if (y == x) return fail(DIG_EINVAL, "dig_block_fwd: y aliases x");
     DevInfo di;
     int rc = current_device(di);

@@ -16,11 +16,14 @@
 //   y  = DWConv3x3(x2 in the scan frame of dir), stored in canonical order.
 // The residual stream stays in canonical token order; the mixer's scan-order
 // output is gathered back inside the residual kernel.  Dense products run
-// on rocBLAS (bf16 operands, fp32 accumulation) with its scratch in the
-// caller's workspace; the elementwise steps are the kernels below.
-#include <rocblas/rocblas.h>
+// on hipBLASLt (bf16 operands, fp32 accumulation; the biases and the FFN's
+// GELU in its epilogues) with its scratch in the caller's workspace; the
+// other elementwise steps are the kernels below.
+#include <hipblaslt/hipblaslt.h>
 
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "dig_internal.h"
 
@@ -41,6 +44,19 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
                     pack_bf16x2(f[6], f[7]));
 }
 
+__device__ __forceinline__ void ld8f(const float *p, float (&f)[8]) {
+  const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// log sigmoid(z) = min(z, 0) - log(1 + e^{-|z|}); the log1p by its series
+// below e = 0.01 (truncation < e^4 / 4), else the hardware log of 1 + e.
+__device__ __forceinline__ float log_sigmoid(float z) {
+  const float e = __expf(-fabsf(z));
+  const float l = e < 0.01f ? e * (1.0f - e * (0.5f - e * (1.0f / 3.0f))) : __logf(1.0f + e);
+  return fminf(z, 0.f) - l;
+}
+
 // SiLU(c) as the bf16 operand of the conditioning product.
 __global__ void __launch_bounds__(kBT) silu_kernel(const float *c, uint16_t *cs, int n) {
   const int i = blockIdx.x * kBT + threadIdx.x;
@@ -51,12 +67,12 @@ __global__ void __launch_bounds__(kBT) silu_kernel(const float *c, uint16_t *cs,
 }
 
 // y = LN(x) (1 + scale[b]) + shift[b] per row of C channels (population
-// variance, eps), scale/shift = ada[b][off..] + b_ada[off..]; one wave per
-// row, VPL 16-byte vectors per lane, the row held in registers.
+// variance, eps), scale/shift = ada[b][off..] (b_ada already added); one wave
+// per row, VPL 16-byte vectors per lane, the row held in registers.
 template <int VPL>
 __global__ void __launch_bounds__(kBT)
-modulate_kernel(const uint16_t *x, uint16_t *y, int64_t N, int T, int C, const float *ada, const float *b_ada,
-                int shift_off, int scale_off, float eps) {
+modulate_kernel(const uint16_t *x, uint16_t *y, int64_t N, int T, int C, const float *ada, int shift_off,
+                int scale_off, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kBT / 64) + (threadIdx.x >> 6);
   if (row >= N) return;
@@ -97,85 +113,54 @@ modulate_kernel(const uint16_t *x, uint16_t *y, int64_t N, int T, int C, const f
   for (int j = 0; j < VPL; ++j) {
     const int cv = lane + 64 * j;
     if (cv < CV) {
-      float f[8];
+      float f[8], sc[8], sh[8];
       unpack8(raw[j], f);
+      ld8f(ab + scale_off + 8 * cv, sc);
+      ld8f(ab + shift_off + 8 * cv, sh);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ch = 8 * cv + e;
-        const float sc = ab[scale_off + ch] + b_ada[scale_off + ch];
-        const float sh = ab[shift_off + ch] + b_ada[shift_off + ch];
-        f[e] = (f[e] - mean) * rstd * (1.0f + sc) + sh;
-      }
+      for (int e = 0; e < 8; ++e) f[e] = (f[e] - mean) * rstd * (1.0f + sc[e]) + sh[e];
       st16(y + row * C + 8 * cv, pack8(f));
     }
   }
 }
 
-// The projected q, k, v, u (one [N][4C] product) in place: + b_in, q / sqrt(d),
-// u -> logsigmoid(u) / 16 (the log gate).
-__global__ void __launch_bounds__(kBT)
-gla_prep_kernel(uint16_t *qkvu, int64_t N, int C, const float *b_in, float q_scale) {
-  const int C4 = 4 * C, V = C4 / 8;
-  const int64_t total = N * V;
-  for (int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBT) {
-    const int64_t row = i / V;
-    const int col = 8 * (int)(i - row * V);
-    const int part = col / C;   // 0 q, 1 k, 2 v, 3 u (8 columns never straddle a part: C % 8 == 0)
-    uint16_t *p = qkvu + row * C4 + col;
+// The gate quarter u (bias already added by the product) of the projected
+// [N][4C] q | k | v | u rows, in place: u -> logsigmoid(u) / 16 (the log gate).
+__global__ void __launch_bounds__(kBT) gate_prep_kernel(uint16_t *qkvu, uint32_t total, uint32_t V, int C) {
+  for (uint32_t i = blockIdx.x * kBT + threadIdx.x; i < total; i += gridDim.x * kBT) {
+    const uint32_t row = i / V;
+    uint16_t *p = qkvu + (size_t)row * 4 * C + 3 * C + 8 * (i - row * V);
     float f[8];
     unpack8(ld16(p), f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float z = f[e] + b_in[col + e];
-      if (part == 0) z *= q_scale;
-      if (part == 3) z = (fminf(z, 0.f) - log1pf(expf(-fabsf(z)))) * (1.0f / 16.0f);
-      f[e] = z;
-    }
+    for (int e = 0; e < 8; ++e) f[e] = log_sigmoid(f[e]) * (1.0f / 16.0f);
     st16(p, pack8(f));
   }
 }
 
-// out[b, n] = x[b, n] + gate[b] (.) (y[b, src] + bias), gate = ada[b][gate_off..]
-// + b_ada[gate_off..]; src = the scan position of canonical token n under
-// dir when gather (the mixer's scan-order output), else n.
+// out[b, n'] = x[b, n] + gate[b] (.) (y[b, n''] + bias), gate = ada[b][gate_off..]
+// (b_ada already added).  With p the scan position of canonical token n under
+// dir: gather (the mixer's scan-order output) reads y at n'' = p, scatter
+// (the conv's scan-frame input) writes out at n' = p; otherwise n' = n'' = n.
 __global__ void __launch_bounds__(kBT)
-gated_residual_kernel(const uint16_t *x, const uint16_t *y, const float *bias, const float *ada, const float *b_ada,
-                      int gate_off, uint16_t *out, int B, int T, int C, bool gather, int dir, int gh, int gw) {
-  const int V = C / 8;
-  const int64_t total = (int64_t)B * T * V;
-  for (int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBT) {
-    const int64_t row = i / V;
+gated_residual_kernel(const uint16_t *x, const uint16_t *y, const float *bias, const float *ada, int gate_off,
+                      uint16_t *out, uint32_t total, int T, int C, bool gather, bool scatter, int dir, int gh,
+                      int gw) {
+  const uint32_t V = C / 8;
+  for (uint32_t i = blockIdx.x * kBT + threadIdx.x; i < total; i += gridDim.x * kBT) {
+    const uint32_t row = i / V;
     const int col = 8 * (int)(i - row * V);
-    const int b = (int)(row / T), n = (int)(row - (int64_t)b * T);
-    const int src = gather ? canon_to_scan(dir, gh, gw, T, n) : n;
-    float fx[8], fy[8];
-    unpack8(ld16(x + row * C + col), fx);
-    unpack8(ld16(y + ((int64_t)b * T + src) * C + col), fy);
-    const float *ab = ada + (int64_t)b * 6 * C + gate_off + col;
-    const float *bb = b_ada + gate_off + col;
+    const uint32_t b = row / T, n = row - b * T;
+    const uint32_t p = (gather || scatter) ? (uint32_t)canon_to_scan(dir, gh, gw, T, (int)n) : n;
+    const size_t base = (size_t)b * T;
+    float fx[8], fy[8], g[8], bb[8];
+    unpack8(ld16(x + (size_t)row * C + col), fx);
+    unpack8(ld16(y + (base + (gather ? p : n)) * C + col), fy);
+    ld8f(ada + (size_t)b * 6 * C + gate_off + col, g);
+    ld8f(bias + col, bb);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) fx[e] += (ab[e] + bb[e]) * (fy[e] + bias[col + e]);
-    st16(out + row * C + col, pack8(fx));
-  }
-}
-
-// In place: f = GELU(f + b) with the tanh form DiT's MLP uses.
-__global__ void __launch_bounds__(kBT)
-bias_gelu_kernel(uint16_t *f, int64_t N, int F, const float *bias) {
-  const int V = F / 8;
-  const int64_t total = N * V;
-  for (int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBT) {
-    const int64_t row = i / V;
-    const int col = 8 * (int)(i - row * V);
-    uint16_t *p = f + row * F + col;
-    float v[8];
-    unpack8(ld16(p), v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float z = v[e] + bias[col + e];
-      v[e] = 0.5f * z * (1.0f + tanhf(0.7978845608028654f * (z + 0.044715f * z * z * z)));
-    }
-    st16(p, pack8(v));
+    for (int e = 0; e < 8; ++e) fx[e] += g[e] * (fy[e] + bb[e]);
+    st16(out + (base + (scatter ? p : n)) * C + col, pack8(fx));
   }
 }
 
@@ -191,29 +176,94 @@ int ew_grid(int64_t items, int num_cu) {
   return (int)(g < cap ? (g < 1 ? 1 : g) : cap);
 }
 
-// one rocBLAS handle per device, created on first use and kept
-std::mutex g_handle_mu;
-rocblas_handle g_handle[64] = {};
+// Dense products on hipBLASLt: one handle per device and one plan (matmul
+// descriptor, layouts, the heuristic's first algorithm) per shape, output
+// type and epilogue, created on first use and kept.  The mutex also covers
+// the per-call bias and launch, since a plan's descriptor holds the bias
+// pointer.
+enum class Epi { none, bias, gelu_bias };
+struct Plan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+};
+std::mutex g_lt_mu;
+hipblasLtHandle_t g_lt[64] = {};
+std::map<std::tuple<int, int, int, int, bool, int, size_t>, Plan> g_plans;
 
-hipError_t handle_for(rocblas_handle &h) {
+hipError_t make_plan(hipblasLtHandle_t h, int M, int N, int K, bool y_f32, Epi epi, size_t scratch_bytes,
+                     Plan &P) {
+  // Row-major Y[M][N] = X[M][K] W[N][K]^T is column-major D (N x M) = op(A) B with
+  // A = W seen as a K x N column-major matrix (op = transpose) and B = X as K x M;
+  // the bias runs along D's rows, the output features.
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  const hipDataType yt = y_f32 ? HIP_R_32F : HIP_R_16BF, bt = HIP_R_32F;
+  const uint32_t e = epi == Epi::none ? HIPBLASLT_EPILOGUE_DEFAULT
+                     : epi == Epi::bias ? HIPBLASLT_EPILOGUE_BIAS
+                                        : HIPBLASLT_EPILOGUE_GELU_BIAS;
+  bool ok = hipblasLtMatmulDescCreate(&P.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatmulDescSetAttribute(P.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) ==
+                HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatmulDescSetAttribute(P.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) ==
+                HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatmulDescSetAttribute(P.desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &e, sizeof(e)) ==
+                HIPBLAS_STATUS_SUCCESS;
+  if (ok && epi != Epi::none)
+    ok = hipblasLtMatmulDescSetAttribute(P.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bt, sizeof(bt)) ==
+         HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&P.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS &&
+       hipblasLtMatrixLayoutCreate(&P.lb, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS &&
+       hipblasLtMatrixLayoutCreate(&P.ld, yt, N, M, N) == HIPBLAS_STATUS_SUCCESS;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+       hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &scratch_bytes,
+                                             sizeof(scratch_bytes)) == HIPBLAS_STATUS_SUCCESS;
+  hipblasLtMatmulHeuristicResult_t res[1];
+  int got = 0;
+  ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, P.desc, P.la, P.lb, P.ld, P.ld, pref, 1, res, &got) ==
+                 HIPBLAS_STATUS_SUCCESS &&
+       got > 0 && res[0].state == HIPBLAS_STATUS_SUCCESS;
+  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+  if (!ok) {
+    if (P.la) hipblasLtMatrixLayoutDestroy(P.la);
+    if (P.lb) hipblasLtMatrixLayoutDestroy(P.lb);
+    if (P.ld) hipblasLtMatrixLayoutDestroy(P.ld);
+    if (P.desc) hipblasLtMatmulDescDestroy(P.desc);
+    P = Plan{};
+    return hipErrorNotSupported;
+  }
+  P.algo = res[0].algo;
+  return hipSuccess;
+}
+
+// Y[M][N] = alpha X[M][K] W[N][K]^T (+ bias[N], then GELU per epi), row-major,
+// bf16 operands, fp32 accumulation, Y bf16 or fp32; scratch: the library's
+// workspace (device memory of scratch_bytes).
+hipError_t gemm(const void *X, const void *W, void *Y, bool y_f32, int M, int N, int K, Epi epi, const float *bias,
+                float alpha, void *scratch, size_t scratch_bytes, hipStream_t s) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lk(g_handle_mu);
-  if (!g_handle[dev] && rocblas_create_handle(&g_handle[dev]) != rocblas_status_success) return hipErrorUnknown;
-  h = g_handle[dev];
-  return hipSuccess;
-}
-
-// Y[M][N] = X[M][K] W[N][K]^T (row-major), bf16 operands, fp32 accumulation,
-// Y bf16 or fp32.  rocBLAS is column-major: Y^T = W (K x N, transposed) X^T.
-rocblas_status gemm(rocblas_handle h, const void *X, const void *W, void *Y, bool y_f32, int M, int N, int K) {
-  const float one = 1.f, zero = 0.f;
-  const rocblas_datatype yt = y_f32 ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
-  return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &one, W,
-                         rocblas_datatype_bf16_r, K, X, rocblas_datatype_bf16_r, K, &zero, Y, yt, N, Y, yt, N,
-                         rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  std::lock_guard<std::mutex> lk(g_lt_mu);
+  if (!g_lt[dev] && hipblasLtCreate(&g_lt[dev]) != HIPBLAS_STATUS_SUCCESS) return hipErrorUnknown;
+  const auto key = std::make_tuple(dev, M, N, K, y_f32, (int)epi, scratch_bytes);
+  auto it = g_plans.find(key);
+  if (it == g_plans.end()) {
+    Plan P;
+    if ((e = make_plan(g_lt[dev], M, N, K, y_f32, epi, scratch_bytes, P)) != hipSuccess) return e;
+    it = g_plans.emplace(key, P).first;
+  }
+  const Plan &P = it->second;
+  if (epi != Epi::none &&
+      hipblasLtMatmulDescSetAttribute(P.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) !=
+          HIPBLAS_STATUS_SUCCESS)
+    return hipErrorUnknown;
+  const float beta = 0.f;
+  return hipblasLtMatmul(g_lt[dev], P.desc, &alpha, W, P.la, X, P.lb, &beta, Y, P.ld, Y, P.ld, &P.algo, scratch,
+                         scratch_bytes, s) == HIPBLAS_STATUS_SUCCESS
+             ? hipSuccess
+             : hipErrorUnknown;
 }
 
 }  // namespace
@@ -221,13 +271,13 @@ rocblas_status gemm(rocblas_handle h, const void *X, const void *W, void *Y, boo
 
 // ------------------------------------------------------------------ host side
 namespace {
-constexpr size_t kGemmScratch = DIG_GEMM_SCRATCH;   // rocBLAS scratch inside the workspace
+constexpr size_t kGemmScratch = DIG_GEMM_SCRATCH;   // hipBLASLt scratch inside the workspace
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 // the bf16 GLA's chunk for this head size (64 while its LDS plan holds it)
 int block_chunk(int d) { return d <= 96 ? 64 : 32; }
 
 struct BlockLayout {
-  size_t ada, cs, h, qkvu, o, o2, x1, x2, xs, gla, gemm, bytes;
+  size_t ada, cs, h, qkvu, o, o2, x1, x2, gla, gemm, bytes;
 };
 BlockLayout block_layout(int B, int T, int C, int H, int num_cu) {
   BlockLayout L{};
@@ -241,8 +291,7 @@ BlockLayout block_layout(int B, int T, int C, int H, int num_cu) {
   L.o = take(tok * C * e);          // GLA output (scan order), then the FFN output
   L.o2 = take(tok * C * e);         // out-projection (scan order)
   L.x1 = take(tok * C * e);
-  L.x2 = take(tok * C * e);
-  L.xs = take(tok * C * e);         // x2 in the scan order of dir (conv input)
+  L.x2 = take(tok * C * e);         // x2 in the scan order of dir (the conv's input)
   const int d = C / H;
   L.gla = take(dig_gla_bf16_workspace(B, T, H, d, d, block_chunk(d), num_cu));
   L.gemm = take(kGemmScratch);
@@ -257,13 +306,7 @@ size_t dig_block_workspace(int B, int T, int C, int H, int num_cu) {
 
 hipError_t dig_launch_linear(const void *x, const void *w, void *y, int M, int N, int K, void *scratch,
                              size_t scratch_bytes, hipStream_t s) {
-  using namespace dig;
-  rocblas_handle h;
-  hipError_t e = handle_for(h);
-  if (e != hipSuccess) return e;
-  if (rocblas_set_stream(h, s) != rocblas_status_success) return hipErrorUnknown;
-  if (rocblas_set_workspace(h, scratch, scratch_bytes) != rocblas_status_success) return hipErrorUnknown;
-  return gemm(h, x, w, y, false, M, N, K) == rocblas_status_success ? hipSuccess : hipErrorUnknown;
+  return dig::gemm(x, w, y, false, M, N, K, dig::Epi::none, nullptr, 1.0f, scratch, scratch_bytes, s);
 }
 
 hipError_t dig_launch_block(const DigBlockArgs &a, hipStream_t s) {
@@ -277,24 +320,20 @@ hipError_t dig_launch_block(const DigBlockArgs &a, hipStream_t s) {
   uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h), *qkvu = reinterpret_cast<uint16_t *>(ws + L.qkvu);
   uint16_t *o = reinterpret_cast<uint16_t *>(ws + L.o), *o2 = reinterpret_cast<uint16_t *>(ws + L.o2);
   uint16_t *x1 = reinterpret_cast<uint16_t *>(ws + L.x1), *x2 = reinterpret_cast<uint16_t *>(ws + L.x2);
-  uint16_t *xs = reinterpret_cast<uint16_t *>(ws + L.xs);
   const uint16_t *x = static_cast<const uint16_t *>(a.x);
 
-  rocblas_handle hb;
-  hipError_t e = handle_for(hb);
-  if (e != hipSuccess) return e;
-  if (rocblas_set_stream(hb, s) != rocblas_status_success) return hipErrorUnknown;
-  if (rocblas_set_workspace(hb, ws + L.gemm, kGemmScratch) != rocblas_status_success) return hipErrorUnknown;
-  auto G = [&](const void *X, const void *W, void *Y, bool f32, int M, int Nn, int K) {
-    return gemm(hb, X, W, Y, f32, M, Nn, K) == rocblas_status_success ? hipSuccess : hipErrorUnknown;
+  hipError_t e;
+  auto G = [&](const void *X, const void *W, void *Y, bool f32, int M, int Nn, int K, Epi epi, const float *bias,
+               float alpha = 1.0f) {
+    return gemm(X, W, Y, f32, M, Nn, K, epi, bias, alpha, ws + L.gemm, kGemmScratch, s);
   };
   const int vpl = (C / 8 + 63) / 64;
   auto modulate = [&](const uint16_t *in, uint16_t *out, int shift_off, int scale_off) {
     const int grid = (int)((N + 3) / 4);
 #define DIG_MOD_CASE(V)                                                                                   \
   if (vpl <= V) {                                                                                         \
-    hipLaunchKernelGGL((modulate_kernel<V>), dim3(grid), dim3(kBT), 0, s, in, out, N, T, C, ada, a.b_ada, \
-                       shift_off, scale_off, 1e-6f);                                                      \
+    hipLaunchKernelGGL((modulate_kernel<V>), dim3(grid), dim3(kBT), 0, s, in, out, N, T, C, ada, shift_off, \
+                       scale_off, 1e-6f);                                                                 \
     return hipGetLastError();                                                                             \
   }
     DIG_MOD_CASE(1)
@@ -317,15 +356,17 @@ hipError_t dig_launch_block(const DigBlockArgs &a, hipStream_t s) {
                        reinterpret_cast<uint4 *>(ws + L.gla), n16);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // (1) conditioning -> [s1 | a1 | g1 | s2 | a2 | g2] (fp32; b_ada added where used)
+  // (1) conditioning -> [s1 | a1 | g1 | s2 | a2 | g2] (fp32, b_ada added by the product)
   hipLaunchKernelGGL(silu_kernel, dim3((B * C + kBT - 1) / kBT), dim3(kBT), 0, s, a.c, cs, B * C);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = G(cs, a.w_ada, ada, true, B, 6 * C, C)) != hipSuccess) return e;
+  if ((e = G(cs, a.w_ada, ada, true, B, 6 * C, C, Epi::bias, a.b_ada)) != hipSuccess) return e;
   // (2) mixer: adaLN, projections, GLA over dir, out-projection, gated residual
   if ((e = modulate(x, h, 0, C)) != hipSuccess) return e;
-  if ((e = G(h, a.w_in, qkvu, false, (int)N, 4 * C, C)) != hipSuccess) return e;
-  hipLaunchKernelGGL(gla_prep_kernel, dim3(ew_grid(N * C / 2, a.num_cu)), dim3(kBT), 0, s, qkvu, N, C, a.b_in,
-                     1.0f / sqrtf((float)d));
+  // q | k | v | u + b_in; q's 1 / sqrt(d) is taken by the out-projection's alpha
+  // (the mixer's output is linear in q)
+  if ((e = G(h, a.w_in, qkvu, false, (int)N, 4 * C, C, Epi::bias, a.b_in)) != hipSuccess) return e;
+  hipLaunchKernelGGL(gate_prep_kernel, dim3(ew_grid(N * C / 8, a.num_cu)), dim3(kBT), 0, s, qkvu,
+                     (uint32_t)(N * C / 8), (uint32_t)(C / 8), C);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   DigGlaArgs g{};
   g.q = qkvu; g.k = qkvu + C; g.v = qkvu + 2 * C; g.g = qkvu + 3 * C;
@@ -338,27 +379,22 @@ hipError_t dig_launch_block(const DigBlockArgs &a, hipStream_t s) {
   g.workspace = ws + L.gla; g.workspace_bytes = L.gemm - L.gla;
   g.epoch = a.epoch; g.num_cu = a.num_cu;
   if ((e = dig_launch_gla_bf16(g, s)) != hipSuccess) return e;
-  if ((e = G(o, a.w_out, o2, false, (int)N, C, C)) != hipSuccess) return e;
+  if ((e = G(o, a.w_out, o2, false, (int)N, C, C, Epi::none, nullptr, 1.0f / sqrtf((float)d))) != hipSuccess)
+    return e;
   const int egrid = ew_grid(N * C / 8, a.num_cu);
-  hipLaunchKernelGGL(gated_residual_kernel, dim3(egrid), dim3(kBT), 0, s, x, o2, a.b_out, ada, a.b_ada, 2 * C, x1, B,
-                     T, C, true, a.dir, a.gh, a.gw);
+  hipLaunchKernelGGL(gated_residual_kernel, dim3(egrid), dim3(kBT), 0, s, x, o2, a.b_out, ada, 2 * C, x1,
+                     (uint32_t)(N * C / 8), T, C, true, false, a.dir, a.gh, a.gw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // (3) FFN: adaLN, C -> 4C, GELU, 4C -> C, gated residual
   if ((e = modulate(x1, h, 3 * C, 4 * C)) != hipSuccess) return e;
-  if ((e = G(h, a.w_ff1, qkvu, false, (int)N, 4 * C, C)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bias_gelu_kernel, dim3(ew_grid(N * C / 2, a.num_cu)), dim3(kBT), 0, s, qkvu, N, 4 * C, a.b_ff1);
+  if ((e = G(h, a.w_ff1, qkvu, false, (int)N, 4 * C, C, Epi::gelu_bias, a.b_ff1)) != hipSuccess) return e;
+  if ((e = G(qkvu, a.w_ff2, o, false, (int)N, C, 4 * C, Epi::none, nullptr)) != hipSuccess) return e;
+  // x2 goes out in the scan order of dir: the conv's input
+  hipLaunchKernelGGL(gated_residual_kernel, dim3(egrid), dim3(kBT), 0, s, x1, o, a.b_ff2, ada, 5 * C, x2,
+                     (uint32_t)(N * C / 8), T, C, false, true, a.dir, a.gh, a.gw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = G(qkvu, a.w_ff2, o, false, (int)N, C, 4 * C)) != hipSuccess) return e;
-  hipLaunchKernelGGL(gated_residual_kernel, dim3(egrid), dim3(kBT), 0, s, x1, o, a.b_ff2, ada, a.b_ada, 5 * C, x2, B,
-                     T, C, false, a.dir, a.gh, a.gw);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // (4) SREM: x2 in the scan order of dir, then the 3x3 depthwise conv of its
-  //     scan frame, stored in canonical order
-  const uint16_t *conv_in = x2;
-  if (a.dir != 0) {
-    if ((e = dig_launch_remap(x2, 1, B, T, C, a.gh, a.gw, 0, a.dir, xs, a.num_cu, s)) != hipSuccess) return e;
-    conv_in = xs;
-  }
-  return dig_launch_dwconv(conv_in, 1, B, T, C, (int64_t)T * C, C, a.w_conv, a.gh, a.gw, a.dir, a.y,
+  // (4) SREM: the 3x3 depthwise conv of the scan frame of dir, stored in
+  //     canonical order
+  return dig_launch_dwconv(x2, 1, B, T, C, (int64_t)T * C, C, a.w_conv, a.gh, a.gw, a.dir, a.y,
                            (int64_t)T * C, C, a.num_cu, s);
 }

@@ -290,10 +290,11 @@ int dig_gather_rows(const void *x, int dtype, int B, int T, int C,
 /*
  * dig_linear -- y = x w^T for row-major bf16 x [M, K], w [N, K] (a PyTorch
  * Linear weight), y [M, N] bf16; fp32 accumulation.  A plain dense product,
- * run by rocBLAS on `stream` with its scratch in `workspace` (at least
+ * run by hipBLASLt on `stream` with its scratch in `workspace` (at least
  * dig_linear_workspace_size() bytes, 256-byte aligned, not shared by calls in
- * flight at once).  The first call on a device creates that device's rocBLAS
- * handle, which the library keeps.  Errors: DIG_EINVAL (null, sizes,
+ * flight at once).  The first call on a device creates that device's
+ * hipBLASLt handle, and the first call of a shape its plan (descriptor and
+ * algorithm), which the library keeps.  Errors: DIG_EINVAL (null, sizes,
  * alignment, aliasing), DIG_EWORKSPACE, DIG_EHIP.
  */
 size_t dig_linear_workspace_size(void);
@@ -320,13 +321,15 @@ int dig_linear(const void *x, const void *w, void *y, int M, int N, int K,
  *   w_ada    bf16 [6C, C], b_ada fp32 [6C]; w_in bf16 [4C, C] (rows q, k, v,
  *            u), b_in fp32 [4C]; w_out bf16 [C, C], b_out fp32 [C]; w_ff1 bf16
  *            [4C, C], b_ff1 fp32 [4C]; w_ff2 bf16 [C, 4C], b_ff2 fp32 [C];
- *            w_conv fp32 [C, 3, 3].  All contiguous; bf16 ones 16-byte aligned.
+ *            w_conv fp32 [C, 3, 3].  All contiguous; bf16 ones and b_in,
+ *            b_out, b_ff1, b_ff2 16-byte aligned.
  *   C = H * d with d a multiple of 8, at most 128; C <= 16384.
  *   workspace  at least dig_block_workspace_size(B, T, C, H) bytes, 256-byte
  *            aligned, any contents (the call clears the part it needs
- *            cleared), not shared by calls in flight at once.  Products run on rocBLAS with
+ *            cleared), not shared by calls in flight at once.  Products run on
+ *            hipBLASLt (the biases and the FFN's GELU in its epilogues) with
  *            their scratch inside it; the first call on a device creates that
- *            device's rocBLAS handle.
+ *            device's hipBLASLt handle and the first call of a shape its plans.
  * Errors as gla_fwd.
  */
 size_t dig_block_workspace_size(int B, int T, int C, int H);
