@@ -177,10 +177,11 @@ int ew_grid(int64_t items, int num_cu) {
 }
 
 // Dense products on hipBLASLt: one handle per device and one plan (matmul
-// descriptor, layouts, the heuristic's first algorithm) per shape, output
-// type and epilogue, created on first use and kept.  The mutex also covers
-// the per-call bias and launch, since a plan's descriptor holds the bias
-// pointer.
+// descriptor, layouts, algorithm) per shape, output type and epilogue,
+// created on first use and kept.  The plan's algorithm is the fastest of the
+// heuristic's candidates, each timed on the first call's own operands and
+// stream (that first call waits for the stream).  The mutex also covers the
+// per-call bias and launch, since a plan's descriptor holds the bias pointer.
 enum class Epi { none, bias, gelu_bias };
 struct Plan {
   hipblasLtMatmulDesc_t desc = nullptr;
@@ -191,7 +192,10 @@ std::mutex g_lt_mu;
 hipblasLtHandle_t g_lt[64] = {};
 std::map<std::tuple<int, int, int, int, bool, int, size_t>, Plan> g_plans;
 
-hipError_t make_plan(hipblasLtHandle_t h, int M, int N, int K, bool y_f32, Epi epi, size_t scratch_bytes,
+constexpr int kCandidates = 8;
+
+hipError_t make_plan(hipblasLtHandle_t h, int M, int N, int K, bool y_f32, Epi epi, const void *X, const void *W,
+                     void *Y, const float *bias, float alpha, void *scratch, size_t scratch_bytes, hipStream_t s,
                      Plan &P) {
   // Row-major Y[M][N] = X[M][K] W[N][K]^T is column-major D (N x M) = op(A) B with
   // A = W seen as a K x N column-major matrix (op = transpose) and B = X as K x M;
@@ -218,11 +222,40 @@ hipError_t make_plan(hipblasLtHandle_t h, int M, int N, int K, bool y_f32, Epi e
   ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
        hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &scratch_bytes,
                                              sizeof(scratch_bytes)) == HIPBLAS_STATUS_SUCCESS;
-  hipblasLtMatmulHeuristicResult_t res[1];
+  hipblasLtMatmulHeuristicResult_t res[kCandidates];
   int got = 0;
-  ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, P.desc, P.la, P.lb, P.ld, P.ld, pref, 1, res, &got) ==
+  ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, P.desc, P.la, P.lb, P.ld, P.ld, pref, kCandidates, res, &got) ==
                  HIPBLAS_STATUS_SUCCESS &&
        got > 0 && res[0].state == HIPBLAS_STATUS_SUCCESS;
+  if (ok && epi != Epi::none)
+    ok = hipblasLtMatmulDescSetAttribute(P.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) ==
+         HIPBLAS_STATUS_SUCCESS;
+  int best = 0;
+  if (ok && got > 1) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    float best_ms = 3.4e38f;
+    const float beta = 0.f;
+    if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+      for (int c = 0; c < got; ++c) {
+        if (res[c].state != HIPBLAS_STATUS_SUCCESS) continue;
+        bool run = true;
+        for (int r = 0; r < 4 && run; ++r) {
+          if (r == 1) run = hipEventRecord(e0, s) == hipSuccess;
+          run = run && hipblasLtMatmul(h, P.desc, &alpha, W, P.la, X, P.lb, &beta, Y, P.ld, Y, P.ld, &res[c].algo,
+                                       scratch, scratch_bytes, s) == HIPBLAS_STATUS_SUCCESS;
+        }
+        float ms = 0.f;
+        if (run && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+            hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms < best_ms) {
+          best_ms = ms;
+          best = c;
+        }
+      }
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipGetLastError();
+  }
   if (pref) hipblasLtMatmulPreferenceDestroy(pref);
   if (!ok) {
     if (P.la) hipblasLtMatrixLayoutDestroy(P.la);
@@ -232,7 +265,7 @@ hipError_t make_plan(hipblasLtHandle_t h, int M, int N, int K, bool y_f32, Epi e
     P = Plan{};
     return hipErrorNotSupported;
   }
-  P.algo = res[0].algo;
+  P.algo = res[best].algo;
   return hipSuccess;
 }
 
@@ -251,7 +284,9 @@ hipError_t gemm(const void *X, const void *W, void *Y, bool y_f32, int M, int N,
   auto it = g_plans.find(key);
   if (it == g_plans.end()) {
     Plan P;
-    if ((e = make_plan(g_lt[dev], M, N, K, y_f32, epi, scratch_bytes, P)) != hipSuccess) return e;
+    if ((e = make_plan(g_lt[dev], M, N, K, y_f32, epi, X, W, Y, bias, alpha, scratch, scratch_bytes, s, P)) !=
+        hipSuccess)
+      return e;
     it = g_plans.emplace(key, P).first;
   }
   const Plan &P = it->second;

@@ -294,7 +294,8 @@ int dig_gather_rows(const void *x, int dtype, int B, int T, int C,
  * dig_linear_workspace_size() bytes, 256-byte aligned, not shared by calls in
  * flight at once).  The first call on a device creates that device's
  * hipBLASLt handle, and the first call of a shape its plan (descriptor and
- * algorithm), which the library keeps.  Errors: DIG_EINVAL (null, sizes,
+ * the fastest of the library's candidate algorithms, timed on that call's
+ * operands; that call waits for the stream), which the library keeps.  Errors: DIG_EINVAL (null, sizes,
  * alignment, aliasing), DIG_EWORKSPACE, DIG_EHIP.
  */
 size_t dig_linear_workspace_size(void);
@@ -329,7 +330,9 @@ int dig_linear(const void *x, const void *w, void *y, int M, int N, int K,
  *            cleared), not shared by calls in flight at once.  Products run on
  *            hipBLASLt (the biases and the FFN's GELU in its epilogues) with
  *            their scratch inside it; the first call on a device creates that
- *            device's hipBLASLt handle and the first call of a shape its plans.
+ *            device's hipBLASLt handle and the first call of a shape its plans
+ *            (candidate algorithms timed on that call's operands; that call
+ *            waits for the stream).
  * Errors as gla_fwd.
  */
 size_t dig_block_workspace_size(int B, int T, int C, int H);
