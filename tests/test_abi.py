@@ -141,3 +141,39 @@ def test_bwd_workspace_size(L):
     n = L.gla_bwd_workspace_size(1, 8, 4096, 16, 72, 72, 0)
     assert n == 2 * 8 * 16 * 64 * 80 * 80 * 2          # two bf16 [units][chunks][80][80] state sets
     assert L.gla_bwd_workspace_size(0, 8, 4096, 16, 72, 72, 0) == ctypes.c_size_t(-1).value
+
+
+def _block(L, **kw):
+    a = dict(x=256, c=512, w=[768 + 256 * i for i in range(10)], w_conv=4096, B=1, T=64, C=128, H=2, gh=8, gw=8,
+             dir=0, y=8192)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    w = [p(v) for v in a["w"]]
+    return L.dig_block_fwd(p(a["x"]), p(a["c"]), *w, p(a["w_conv"]), a["B"], a["T"], a["C"], a["H"], a["gh"],
+                           a["gw"], a["dir"], p(a["y"]), None, 0, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(x=None), dict(c=None), dict(y=None), dict(w_conv=None), dict(w=[768] * 9 + [None]), dict(B=0),
+    dict(C=130), dict(H=3), dict(C=136, H=1), dict(C=24, H=2), dict(C=16392, H=2), dict(gh=7), dict(dir=4),
+    dict(x=264), dict(y=256),
+    dict(w=[768 + 256 * i for i in range(3)] + [1032] + [768 + 256 * i for i in range(4, 10)]),   # b_in misaligned
+    dict(B=64, T=4096, gh=64, gw=64, C=1024, H=8),                                                 # B*T*4C >= 2^30
+])
+def test_block_rejects_bad_arguments(L, bad):
+    """Checked before any device query: nulls, head size (C/H a multiple of
+    8, at most 128), C <= 16384, the grid, the direction, alignment of the
+    bf16 tensors and of b_in/b_out/b_ff1/b_ff2, y aliasing x, the product size."""
+    assert _block(L, **bad) == -1, bad
+    assert L.dig_last_error()
+
+
+@pytest.mark.parametrize("bad", [dict(x=None), dict(M=0), dict(K=-1), dict(x=264), dict(y=256), dict(y=512),
+                                 dict(ws=None), dict(wsb=1024), dict(ws=4096 + 16)])
+def test_linear_rejects_bad_arguments(L, bad):
+    a = dict(x=256, w=512, y=768, M=4, N=8, K=16, ws=4096, wsb=L.dig_linear_workspace_size())
+    a.update(bad)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = L.dig_linear(p(a["x"]), p(a["w"]), p(a["y"]), a["M"], a["N"], a["K"], p(a["ws"]), a["wsb"], None)
+    assert rc in (-1, -2), bad
+    assert L.dig_last_error()
