@@ -262,6 +262,7 @@ hipblasLtHandle_t g_lt[64] = {};
 std::map<std::tuple<int, int, int, int, bool, int, size_t>, Plan> g_plans;
 
 constexpr int kCandidates = 8;
+constexpr double kTimeFlops = 1e10;
 constexpr int kTimedRuns = 10;   // after one untimed run; short products need several to rise above launch jitter
 
 hipError_t make_plan(hipblasLtHandle_t h, int M, int N, int K, bool y_f32, Epi epi, const void *X, const void *W,
@@ -300,8 +301,14 @@ hipError_t make_plan(hipblasLtHandle_t h, int M, int N, int K, bool y_f32, Epi e
   if (ok && epi != Epi::none)
     ok = hipblasLtMatmulDescSetAttribute(P.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) ==
          HIPBLAS_STATUS_SUCCESS;
+  // Products under kTimeFlops run for about as long as their launch takes, so
+  // event timing would measure the host, not the candidates: the heuristic's
+  // first choice then.  No timing either while the stream is being captured
+  // into a graph (the trial products would become graph nodes).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
   int best = 0;
-  if (ok && got > 1) {
+  if (ok && got > 1 && cap == hipStreamCaptureStatusNone && 2.0 * M * N * K >= kTimeFlops) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
     float best_ms = 3.4e38f;
     const float beta = 0.f;

@@ -295,7 +295,9 @@ int dig_gather_rows(const void *x, int dtype, int B, int T, int C,
  * flight at once).  The first call on a device creates that device's
  * hipBLASLt handle, and the first call of a shape its plan (descriptor and
  * the fastest of the library's candidate algorithms, timed on that call's
- * operands; that call waits for the stream), which the library keeps.  Errors: DIG_EINVAL (null, sizes,
+ * operands; that call waits for the stream; under graph capture, and for
+ * products under 1e10 flops, the library's first choice, untimed), which the
+ * library keeps.  Errors: DIG_EINVAL (null, sizes,
  * alignment, aliasing), DIG_EWORKSPACE, DIG_EHIP.
  */
 size_t dig_linear_workspace_size(void);
