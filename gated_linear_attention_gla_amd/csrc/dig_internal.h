@@ -129,7 +129,7 @@ struct DigBlockArgs {
   uint32_t epoch;
   int num_cu;
 };
-constexpr size_t DIG_GEMM_SCRATCH = size_t(64) << 20;   // bytes of rocBLAS scratch a product may use
+constexpr size_t DIG_GEMM_SCRATCH = size_t(64) << 20;   // bytes of hipBLASLt scratch a product may use
 size_t dig_block_workspace(int B, int T, int C, int H, int num_cu);
 hipError_t dig_launch_block(const DigBlockArgs &a, hipStream_t s);
 hipError_t dig_launch_linear(const void *x, const void *w, void *y, int M, int N, int K, void *scratch,
