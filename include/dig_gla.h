@@ -26,7 +26,11 @@
  *     device memory) unless stated otherwise.  The caller owns every buffer
  *     and keeps it alive until the work queued on `stream` has finished.
  *   - The library never allocates or frees device memory and never
- *     synchronises the stream.  Work is queued on `stream` (NULL = the
+ *     synchronises the stream, with one exception: the dense products of
+ *     dig_linear and dig_block_fwd run on hipBLASLt, whose handle (created
+ *     on a device's first such call) may hold library-internal memory, and
+ *     the first call of each product shape times candidate algorithms,
+ *     waiting for the stream.  Work is queued on `stream` (NULL = the
  *     default stream of the current device); errors raised by a kernel while
  *     it runs surface at the caller's next synchronisation.
  *   - Strides are in ELEMENTS; the innermost (channel) dimension is contiguous.
@@ -36,7 +40,7 @@
  *     DIG_ENODEV when the current device is not a gfx950.  After a non-zero
  *     return, dig_last_error() describes it.  No C++ exception crosses the ABI.
  *   - Calls on different streams are thread-safe, except that two calls in
- *     flight at the same time must not share a gla_fwd workspace.
+ *     flight at the same time must not share a workspace.
  */
 #ifndef DIG_GLA_H
 #define DIG_GLA_H
