@@ -66,26 +66,15 @@ __global__ void __launch_bounds__(kBT) silu_kernel(const float *c, uint16_t *cs,
   }
 }
 
-// y = LN(x) (1 + scale[b]) + shift[b] per row of C channels (population
-// variance, eps), scale/shift = ada[b][off..] (b_ada already added); one wave
-// per row, VPL 16-byte vectors per lane, the row held in registers.
+// LN statistics (mean, 1 / std with population variance) of one token row
+// held as VPL 16-byte vectors per lane (vector cv = lane + 64 j, valid below CV).
 template <int VPL>
-__global__ void __launch_bounds__(kBT)
-modulate_kernel(const uint16_t *x, uint16_t *y, int64_t N, int T, int C, const float *ada, int shift_off,
-                int scale_off, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kBT / 64) + (threadIdx.x >> 6);
-  if (row >= N) return;
-  const int CV = C / 8;
-  const int b = (int)(row / T);
-  const uint16_t *xr = x + row * C;
-  uint4 raw[VPL];
+__device__ __forceinline__ void row_stats(const uint4 (&raw)[VPL], int lane, int CV, int C, float eps, float &mean,
+                                          float &rstd) {
   float sum = 0.f;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
-    const int cv = lane + 64 * j;
-    raw[j] = ld16(xr + 8 * (cv < CV ? cv : 0));
-    if (cv < CV) {
+    if (lane + 64 * j < CV) {
       float f[8];
       unpack8(raw[j], f);
 #pragma unroll
@@ -94,7 +83,7 @@ modulate_kernel(const uint16_t *x, uint16_t *y, int64_t N, int T, int C, const f
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  const float mean = sum / (float)C;
+  mean = sum / (float)C;
   float sq = 0.f;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
@@ -107,21 +96,83 @@ modulate_kernel(const uint16_t *x, uint16_t *y, int64_t N, int T, int C, const f
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off, 64);
-  const float rstd = 1.0f / sqrtf(sq / (float)C + eps);
-  const float *ab = ada + (int64_t)b * 6 * C;
+  rstd = 1.0f / sqrtf(sq / (float)C + eps);
+}
+
+// y[row] = (x - mean) rstd (1 + scale[b]) + shift[b] for the RPW rows of a
+// wave; a lane loads its channels' scale and shift once for rows of one batch
+// element (b_ada already in ada).
+template <int VPL, int RPW>
+__device__ __forceinline__ void modulate_out(const uint4 (&raw)[RPW][VPL], const float (&mean)[RPW],
+                                             const float (&rstd)[RPW], const bool (&live)[RPW], const int (&bs)[RPW],
+                                             const int64_t (&rows)[RPW], const float *ada, int C, int shift_off,
+                                             int scale_off, uint16_t *__restrict__ y, int lane, int CV) {
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int cv = lane + 64 * j;
     if (cv < CV) {
-      float f[8], sc[8], sh[8];
-      unpack8(raw[j], f);
-      ld8f(ab + scale_off + 8 * cv, sc);
-      ld8f(ab + shift_off + 8 * cv, sh);
+      float sc[8], sh[8];
+      int cur = bs[0];
+      ld8f(ada + (int64_t)cur * 6 * C + scale_off + 8 * cv, sc);
+      ld8f(ada + (int64_t)cur * 6 * C + shift_off + 8 * cv, sh);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = (f[e] - mean) * rstd * (1.0f + sc[e]) + sh[e];
-      st16(y + row * C + 8 * cv, pack8(f));
+      for (int r = 0; r < RPW; ++r) {
+        if (!live[r]) continue;
+        if (bs[r] != cur) {
+          cur = bs[r];
+          ld8f(ada + (int64_t)cur * 6 * C + scale_off + 8 * cv, sc);
+          ld8f(ada + (int64_t)cur * 6 * C + shift_off + 8 * cv, sh);
+        }
+        float f[8];
+        unpack8(raw[r][j], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (f[e] - mean[r]) * rstd[r] * (1.0f + sc[e]) + sh[e];
+        st16(y + rows[r] * C + 8 * cv, pack8(f));
+      }
     }
   }
+}
+
+// The rows of a wave: RPW consecutive token rows from row0 (past N: not live,
+// clamped to row0 for loads), with their batch indices.
+template <int RPW>
+__device__ __forceinline__ void wave_rows(int64_t row0, int64_t N, int T, int64_t (&rows)[RPW], int (&bs)[RPW],
+                                          bool (&live)[RPW]) {
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    live[r] = row0 + r < N;
+    rows[r] = live[r] ? row0 + r : row0;
+    bs[r] = (int)(rows[r] / T);
+  }
+}
+
+// h = LN(x) (1 + scale[b]) + shift[b] per row of C channels (eps), scale/shift
+// = ada[b][off..] (b_ada already added); RPW rows per wave, VPL 16-byte
+// vectors per lane, the rows held in registers.
+template <int VPL, int RPW>
+__global__ void __launch_bounds__(kBT)
+modulate_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int64_t N, int T, int C,
+                const float *__restrict__ ada, int shift_off, int scale_off, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * (kBT / 64) + (threadIdx.x >> 6)) * RPW;
+  if (row0 >= N) return;
+  const int CV = C / 8;
+  int64_t rows[RPW];
+  int bs[RPW];
+  bool live[RPW];
+  wave_rows<RPW>(row0, N, T, rows, bs, live);
+  uint4 raw[RPW][VPL];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int cv = lane + 64 * j;
+      raw[r][j] = ld16(x + rows[r] * C + 8 * (cv < CV ? cv : 0));
+    }
+  float mean[RPW], rstd[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) row_stats<VPL>(raw[r], lane, CV, C, eps, mean[r], rstd[r]);
+  modulate_out<VPL, RPW>(raw, mean, rstd, live, bs, rows, ada, C, shift_off, scale_off, y, lane, CV);
 }
 
 // The gate quarter u (bias already added by the product) of the projected
@@ -164,73 +215,64 @@ gated_residual_kernel(const uint16_t *x, const uint16_t *y, const float *bias, c
   }
 }
 
-// The mixer's residual and the FFN's adaLN in one pass, one wave per token row
-// held in registers: x1 = x + g1 (.) (y[b, p] + bias) with p the scan position
-// of the row's token under dir (the mixer's scan-order output), stored; then
-// h = LN(x1) (1 + a2) + s2 over the stored (bf16) x1, as modulate_kernel.
-template <int VPL>
+// The mixer's residual and the FFN's adaLN in one pass, RPW token rows per
+// wave held in registers: x1 = x + g1 (.) (y[b, p] + bias) with p the scan
+// position of the row's token under dir (the mixer's scan-order output),
+// stored; then h = LN(x1) (1 + a2) + s2 over the stored (bf16) x1, as
+// modulate_kernel.
+template <int VPL, int RPW>
 __global__ void __launch_bounds__(kBT)
-residual_modulate_kernel(const uint16_t *x, const uint16_t *y, const float *bias, const float *ada, int gate_off,
-                         int shift_off, int scale_off, float eps, uint16_t *x1, uint16_t *h, int64_t N, int T, int C,
-                         int dir, int gh, int gw) {
+residual_modulate_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ y,
+                         const float *__restrict__ bias, const float *__restrict__ ada, int gate_off, int shift_off,
+                         int scale_off, float eps, uint16_t *__restrict__ x1, uint16_t *__restrict__ h, int64_t N,
+                         int T, int C, int dir, int gh, int gw) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kBT / 64) + (threadIdx.x >> 6);
-  if (row >= N) return;
+  const int64_t row0 = ((int64_t)blockIdx.x * (kBT / 64) + (threadIdx.x >> 6)) * RPW;
+  if (row0 >= N) return;
   const int CV = C / 8;
-  const int b = (int)(row / T), n = (int)(row - (int64_t)b * T);
-  const int64_t src = (int64_t)b * T + canon_to_scan(dir, gh, gw, T, n);
-  const float *ab = ada + (int64_t)b * 6 * C;
-  uint4 raw[VPL];
-  float sum = 0.f;
+  int64_t rows[RPW], src[RPW];
+  int bs[RPW];
+  bool live[RPW];
+  wave_rows<RPW>(row0, N, T, rows, bs, live);
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = (int)(rows[r] - (int64_t)bs[r] * T);
+    src[r] = (int64_t)bs[r] * T + canon_to_scan(dir, gh, gw, T, n);
+  }
+  uint4 raw[RPW][VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int cv = lane + 64 * j;
     const int c8 = 8 * (cv < CV ? cv : 0);
-    float fx[8], fy[8], g[8], bb[8];
-    unpack8(ld16(x + row * C + c8), fx);
-    unpack8(ld16(y + src * C + c8), fy);
-    ld8f(ab + gate_off + c8, g);
+    uint4 ux[RPW], uy[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      ux[r] = ld16(x + rows[r] * C + c8);
+      uy[r] = ld16(y + src[r] * C + c8);
+    }
+    float g[8], bb[8];
+    int cur = bs[0];
+    ld8f(ada + (int64_t)cur * 6 * C + gate_off + c8, g);
     ld8f(bias + c8, bb);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) fx[e] += g[e] * (fy[e] + bb[e]);
-    raw[j] = pack8(fx);
-    if (cv < CV) {
-      st16(x1 + row * C + c8, raw[j]);
-      float f[8];
-      unpack8(raw[j], f);
+    for (int r = 0; r < RPW; ++r) {
+      if (bs[r] != cur) {
+        cur = bs[r];
+        ld8f(ada + (int64_t)cur * 6 * C + gate_off + c8, g);
+      }
+      float fx[8], fy[8];
+      unpack8(ux[r], fx);
+      unpack8(uy[r], fy);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sum += f[e];
+      for (int e = 0; e < 8; ++e) fx[e] += g[e] * (fy[e] + bb[e]);
+      raw[r][j] = pack8(fx);
+      if (cv < CV && live[r]) st16(x1 + rows[r] * C + c8, raw[r][j]);
     }
   }
+  float mean[RPW], rstd[RPW];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  const float mean = sum / (float)C;
-  float sq = 0.f;
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    if (lane + 64 * j < CV) {
-      float f[8];
-      unpack8(raw[j], f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { const float d = f[e] - mean; sq = fmaf(d, d, sq); }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off, 64);
-  const float rstd = 1.0f / sqrtf(sq / (float)C + eps);
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    const int cv = lane + 64 * j;
-    if (cv < CV) {
-      float f[8], sc[8], sh[8];
-      unpack8(raw[j], f);
-      ld8f(ab + scale_off + 8 * cv, sc);
-      ld8f(ab + shift_off + 8 * cv, sh);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = (f[e] - mean) * rstd * (1.0f + sc[e]) + sh[e];
-      st16(h + row * C + 8 * cv, pack8(f));
-    }
-  }
+  for (int r = 0; r < RPW; ++r) row_stats<VPL>(raw[r], lane, CV, C, eps, mean[r], rstd[r]);
+  modulate_out<VPL, RPW>(raw, mean, rstd, live, bs, rows, ada, C, shift_off, scale_off, h, lane, CV);
 }
 
 // Zero fill (uint4 granules) -- a kernel rather than a memset node.
@@ -440,39 +482,40 @@ hipError_t dig_launch_block(const DigBlockArgs &a, hipStream_t s) {
     return gemm(X, W, Y, f32, M, Nn, K, epi, bias, alpha, ws + L.gemm, kGemmScratch, s);
   };
   const int vpl = (C / 8 + 63) / 64;
+  // two rows per wave while the rows fit the registers (VPL <= 4: C <= 2048)
   auto modulate = [&](const uint16_t *in, uint16_t *out, int shift_off, int scale_off) {
-    const int grid = (int)((N + 3) / 4);
-#define DIG_MOD_CASE(V)                                                                                   \
-  if (vpl <= V) {                                                                                         \
-    hipLaunchKernelGGL((modulate_kernel<V>), dim3(grid), dim3(kBT), 0, s, in, out, N, T, C, ada, shift_off, \
-                       scale_off, 1e-6f);                                                                 \
-    return hipGetLastError();                                                                             \
+#define DIG_MOD_CASE(V, R)                                                                                  \
+  if (vpl <= V) {                                                                                           \
+    const int grid = (int)((N + 4 * R - 1) / (4 * R));                                                      \
+    hipLaunchKernelGGL((modulate_kernel<V, R>), dim3(grid), dim3(kBT), 0, s, in, out, N, T, C, ada, shift_off, \
+                       scale_off, 1e-6f);                                                                   \
+    return hipGetLastError();                                                                               \
   }
-    DIG_MOD_CASE(1)
-    DIG_MOD_CASE(2)
-    DIG_MOD_CASE(3)
-    DIG_MOD_CASE(4)
-    DIG_MOD_CASE(8)
-    DIG_MOD_CASE(16)
-    DIG_MOD_CASE(32)
+    DIG_MOD_CASE(1, 2)
+    DIG_MOD_CASE(2, 2)
+    DIG_MOD_CASE(3, 2)
+    DIG_MOD_CASE(4, 2)
+    DIG_MOD_CASE(8, 1)
+    DIG_MOD_CASE(16, 1)
+    DIG_MOD_CASE(32, 1)
 #undef DIG_MOD_CASE
     return hipErrorInvalidValue;
   };
   auto residual_modulate = [&]() {
-    const int grid = (int)((N + 3) / 4);
-#define DIG_RM_CASE(V)                                                                                      \
-  if (vpl <= V) {                                                                                           \
-    hipLaunchKernelGGL((residual_modulate_kernel<V>), dim3(grid), dim3(kBT), 0, s, x, o2, a.b_out, ada, 2 * C, \
-                       3 * C, 4 * C, 1e-6f, x1, h, N, T, C, a.dir, a.gh, a.gw);                             \
-    return hipGetLastError();                                                                               \
+#define DIG_RM_CASE(V, R)                                                                                    \
+  if (vpl <= V) {                                                                                            \
+    const int grid = (int)((N + 4 * R - 1) / (4 * R));                                                       \
+    hipLaunchKernelGGL((residual_modulate_kernel<V, R>), dim3(grid), dim3(kBT), 0, s, x, o2, a.b_out, ada, 2 * C, \
+                       3 * C, 4 * C, 1e-6f, x1, h, N, T, C, a.dir, a.gh, a.gw);                              \
+    return hipGetLastError();                                                                                \
   }
-    DIG_RM_CASE(1)
-    DIG_RM_CASE(2)
-    DIG_RM_CASE(3)
-    DIG_RM_CASE(4)
-    DIG_RM_CASE(8)
-    DIG_RM_CASE(16)
-    DIG_RM_CASE(32)
+    DIG_RM_CASE(1, 2)
+    DIG_RM_CASE(2, 2)
+    DIG_RM_CASE(3, 2)
+    DIG_RM_CASE(4, 2)
+    DIG_RM_CASE(8, 1)
+    DIG_RM_CASE(16, 1)
+    DIG_RM_CASE(32, 1)
 #undef DIG_RM_CASE
     return hipErrorInvalidValue;
   };
