@@ -67,11 +67,13 @@ def conv_alg_bytes(cfg) -> int:
     return 2 * cfg.B * cfg.T * cfg.C * el + cfg.C * 9 * 4
 
 
-def traffic_record(cfg_key: str):
-    """Measured HBM bytes per gla_fwd launch from a committed rocprofv3 PMC summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"gla_fwd_{cfg_key.lower()}_traffic.json")
-    src = os.path.join(ROOT, "gated_linear_attention_gla_amd", "csrc", "gla_bf16.hip")
+def traffic_record(cfg_key: str, kind: str = "fwd"):
+    """Measured HBM bytes per gla_fwd launch (kind "fwd") or per gla_bwd call (kind "bwd": both
+    kernels) from a committed rocprofv3 PMC summary, if it was taken on the current kernel source;
+    else None."""
+    path = os.path.join(ROOT, "profiles", f"gla_{kind}_{cfg_key.lower()}_traffic.json")
+    src = os.path.join(ROOT, "gated_linear_attention_gla_amd", "csrc",
+                       "gla_bwd.hip" if kind == "bwd" else "gla_bf16.hip")
     try:
         rec = json.load(open(path))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -426,7 +428,7 @@ def bench_bwd(a, dg, gen, torch) -> int:
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "grid": list(grid),
                    "directions": ["zigzag S_0..S_7"] if zz else list(cfg.dirs), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None if zz else traffic_record(cfg.key, "bwd"),
                      "kernel": "gla_bwd (gla_bwd_scan, both directions in one launch, + gla_bwd_chunk)", "alg_bytes_per_launch": abytes,
                      "avg_launch_us": avg * 1e3},
         "gla_bwd": {"tflops_alg": aflops / (avg * 1e-3) / 1e12,
@@ -441,9 +443,10 @@ def bench_bwd(a, dg, gen, torch) -> int:
 COPY_PROBE_BYTES = 256 << 20   # the plain copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
 
 
-def traffic_probe(cfg_key: str, chunk: int) -> int:
+def traffic_probe(cfg_key: str, chunk: int, bwd: bool = False) -> int:
     """Launch sequence for the two rocprofv3 PMC passes: three plain device copies of
-    COPY_PROBE_BYTES (read + write of known size), then three gla_fwd launches of the workload."""
+    COPY_PROBE_BYTES (read + write of known size), then three gla_fwd launches of the workload
+    (with bwd: three gla_bwd calls)."""
     import torch
 
     from gated_linear_attention_gla_amd import binding as dg
@@ -462,17 +465,26 @@ def traffic_probe(cfg_key: str, chunk: int) -> int:
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
+    if bwd:
+        gen_do = torch.Generator(device=dev)
+        gen_do.manual_seed(cfg.seed + 4409)
+        do = torch.randn(cfg.B, cfg.T, cfg.H, cfg.d, generator=gen_do, device=dev).to(torch.bfloat16)
     torch.cuda.synchronize()
     for i in range(3):
-        dg.gla_fwd(q, k, v, x["log_alpha"], (cfg.gh, cfg.gw), cfg.direction(i), chunk=chunk)
+        if bwd:
+            dg.gla_bwd(q, k, v, x["log_alpha"], (cfg.gh, cfg.gw), cfg.direction(i), do, chunk=chunk or cfg.chunk,
+                       need_ds0=False)
+        else:
+            dg.gla_fwd(q, k, v, x["log_alpha"], (cfg.gh, cfg.gw), cfg.direction(i), chunk=chunk)
     torch.cuda.synchronize()
-    log(f"[bench] traffic probe done: {cfg.key}, 3 copies of {COPY_PROBE_BYTES} B, 3 gla_fwd launches")
+    log(f"[bench] traffic probe done: {cfg.key}, 3 copies of {COPY_PROBE_BYTES} B, 3 gla_{'bwd' if bwd else 'fwd'} calls")
     return 0
 
 
-def write_traffic(cfg_key: str, fetch_dir: str, write_dir: str, command: str) -> int:
+def write_traffic(cfg_key: str, fetch_dir: str, write_dir: str, command: str, bwd: bool = False) -> int:
     """Turn the counter CSVs of the two PMC passes over --traffic-probe into the per-launch HBM
-    traffic record read by traffic_record().  Each counter is scaled by bytes / counter of the copy."""
+    traffic record read by traffic_record().  Each counter is scaled by bytes / counter of the copy.
+    With bwd, a call's traffic is the sum of its two kernels' (medians over the three calls)."""
     import csv
     import glob
     import statistics
@@ -485,30 +497,33 @@ def write_traffic(cfg_key: str, fetch_dir: str, write_dir: str, command: str) ->
         rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
-        gla = [float(r["Counter_Value"]) * 1024 for r in rows if "gla_fwd_bf16_kernel" in r["Kernel_Name"]]
+        names = ("gla_bwd_scan", "gla_bwd_chunk") if bwd else ("gla_fwd_bf16_kernel",)
+        per = [[float(r["Counter_Value"]) * 1024 for r in rows if n in r["Kernel_Name"]] for n in names]
         # torch's same-dtype device copy is the runtime's blit kernel
         cp = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        if len(gla) < 1 or len(cp) < 1:
+        if min(len(g) for g in per) < 1 or len(cp) < 1:
             raise SystemExit(f"write_traffic: no gla/copy dispatches with {counter} under {d}")
-        return statistics.median(gla), statistics.median(cp), len(gla), len(cp)
+        return sum(statistics.median(g) for g in per), statistics.median(cp), len(per[-1]), len(cp)
 
     gf, cf, ng, nc = per_dispatch(fetch_dir, "FETCH_SIZE")
     gw, cw, _, _ = per_dispatch(write_dir, "WRITE_SIZE")
     kf, kw = COPY_PROBE_BYTES / cf, COPY_PROBE_BYTES / cw
     total = gf * kf + gw * kw
-    src = os.path.join(ROOT, "gated_linear_attention_gla_amd", "csrc", "gla_bf16.hip")
-    rec = {"kernel": "gla_fwd_bf16_kernel", "workload": cfg_key,
+    kind = "bwd" if bwd else "fwd"
+    src = os.path.join(ROOT, "gated_linear_attention_gla_amd", "csrc", "gla_bwd.hip" if bwd else "gla_bf16.hip")
+    alg = bwd_alg_bytes(cfg) if bwd else gla_alg_bytes(cfg)
+    rec = {"kernel": "gla_bwd_scan + gla_bwd_chunk" if bwd else "gla_fwd_bf16_kernel", "workload": cfg_key,
            "kernel_src_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
            "bytes_per_launch": total, "fetch_bytes_raw": gf, "write_bytes_raw": gw,
            "copy_scale_fetch": kf, "copy_scale_write": kw, "copy_bytes": COPY_PROBE_BYTES,
-           "alg_bytes_per_launch": gla_alg_bytes(cfg), "gla_dispatches": ng, "copy_dispatches": nc,
+           "alg_bytes_per_launch": alg, "gla_dispatches": ng, "copy_dispatches": nc,
            "command": command}
-    out = os.path.join(ROOT, "profiles", f"gla_fwd_{cfg_key.lower()}_traffic.json")
+    out = os.path.join(ROOT, "profiles", f"gla_{kind}_{cfg_key.lower()}_traffic.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     log(f"[bench] {out}: {total / 1e6:.1f} MB per launch "
-        f"(alg {gla_alg_bytes(cfg) / 1e6:.1f} MB; copy scale fetch {kf:.3f}, write {kw:.3f})")
+        f"(alg {alg / 1e6:.1f} MB; copy scale fetch {kf:.3f}, write {kw:.3f})")
     return 0
 
 
@@ -532,7 +547,7 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
 
     if a.write_traffic:
-        return write_traffic(a.config, *a.write_traffic)
+        return write_traffic(a.config, *a.write_traffic, bwd=a.bwd)
 
     if a.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {a.gpus} is not supported "
@@ -549,7 +564,7 @@ def main(argv=None) -> int:
         return 1
     dg.lib()
     if a.traffic_probe:
-        return traffic_probe(a.config, a.chunk)
+        return traffic_probe(a.config, a.chunk, bwd=a.bwd)
     if a.bwd:
         return bench_bwd(a, dg, gen, torch)
     if a.block:
