@@ -192,7 +192,7 @@ def bench_fwd_ordered(a, dg, gen, torch) -> int:
         return 2
     B, T, H, d = cfg.B, cfg.T, cfg.H, cfg.d
     chunk = a.chunk or cfg.chunk
-    nsets = a.sets or max(1, math.ceil(512e6 / gla_alg_bytes(cfg)))
+    nsets = a.sets or max(2, math.ceil(512e6 / gla_alg_bytes(cfg)))
     log(f"[bench] gla_fwd zigzag {cfg.key} {cfg.name}: B={B} H={H} T={T} ({cfg.gh}x{cfg.gw}) d={d}; {nsets} sets")
     sets = [gen.make_inputs(cfg.key, set_index=i, device=dev) for i in range(nsets)]
     o = torch.empty(B, T, H, d, dtype=torch.bfloat16, device=dev)
@@ -367,7 +367,7 @@ def bench_bwd(a, dg, gen, torch) -> int:
     grid = (cfg.gh, cfg.gw)
     chunk = a.chunk or cfg.chunk
     per_set = B * T * H * d * 2 * 5
-    nsets = a.sets or max(1, math.ceil(512e6 / per_set))
+    nsets = a.sets or max(2, math.ceil(512e6 / per_set))
     log(f"[bench] gla_bwd {cfg.key} {cfg.name}: B={B} H={H} T={T} ({cfg.gh}x{cfg.gw}) d={d}; {nsets} input sets")
     gen_do = torch.Generator(device=dev)
     sets = []
@@ -578,7 +578,7 @@ def main(argv=None) -> int:
     chunk = a.chunk or cfg.chunk
 
     ws_bytes = gla_alg_bytes(cfg) + conv_alg_bytes(cfg)
-    nsets = a.sets or max(1, math.ceil(512e6 / ws_bytes))
+    nsets = a.sets or max(2, math.ceil(512e6 / ws_bytes))
     log(f"[bench] {cfg.key} {cfg.name}: B={B} H={H} T={T} ({cfg.gh}x{cfg.gw}) d={d}; {nsets} input sets")
     sets = []
     for i in range(nsets):

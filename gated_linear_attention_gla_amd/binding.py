@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
             L.gla_fwd_ordered.restype = i32
             L.gla_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
             L.gla_fwd_workspace_size.restype = sz
+            L.gla_fwd_workspace_status.argtypes = [p, sz, p]
+            L.gla_fwd_workspace_status.restype = i32
             L.gla_bwd.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
                                   i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                   p, p, i64, i64, i64, p, p, p, p, p, p, p, sz, p]
@@ -188,6 +190,14 @@ def gla_fwd(q, k, v, log_alpha, grid, direction, chunk: int = 0, s0=None, out=No
                        _ptr(sf), _ptr(workspace), wsb, _stream(dev))
     _check(rc, "gla_fwd")
     return out, sf
+
+
+def workspace_status(workspace) -> None:
+    """Synchronise the current stream and raise DigError if a gla_fwd call that used
+    `workspace` had a wait between workgroups give up (gla_fwd_workspace_status)."""
+    rc = lib().gla_fwd_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(workspace.device))
+    _check(rc, "gla_fwd_workspace_status")
 
 
 def gla_bwd(q, k, v, log_alpha, grid, direction, d_o, chunk: int = 0, s0=None, ds_final=None,

@@ -208,6 +208,28 @@ int gla_fwd_ordered(const void *q, const void *k, const void *v, const void *log
 }
 
 
+int gla_fwd_workspace_status(void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    if (!workspace || workspace_bytes < DIG_GLA_ERR_WORD_OFFSET + 4)
+      return fail(DIG_EINVAL, "gla_fwd_workspace_status: a gla_fwd workspace is required");
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "gla_fwd_workspace_status: hipStreamSynchronize");
+    unsigned word = 0;
+    char *p = static_cast<char *>(workspace) + DIG_GLA_ERR_WORD_OFFSET;
+    e = hipMemcpy(&word, p, sizeof(word), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "gla_fwd_workspace_status: hipMemcpy");
+    if (word == 0) return DIG_OK;
+    const unsigned zero = 0;
+    e = hipMemcpy(p, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "gla_fwd_workspace_status: hipMemcpy");
+    return fail(DIG_EHIP, "gla_fwd: a wait between workgroups gave up (error word 0x%x): a call that used this "
+                "workspace returned wrong results (workspace not zero-filled before its first use, or shared "
+                "by calls in flight at the same time)", word);
+  } catch (...) {
+    return fail(DIG_EHIP, "gla_fwd_workspace_status: unexpected C++ exception");
+  }
+}
+
 size_t gla_bwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
   if (check_bwd_sizes(dtype, B, T, H, dk, dv, chunk) != DIG_OK) return (size_t)-1;
   return dig_gla_bwd_workspace(B, T, H, dk, dv, chunk);

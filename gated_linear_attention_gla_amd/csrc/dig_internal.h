@@ -86,6 +86,9 @@ struct DigGlaArgs {
 };
 
 hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s);
+// Byte offset, inside the bf16 forward's workspace, of the error word its
+// kernel sets when a wait between workgroups gives up (bit 0).
+constexpr size_t DIG_GLA_ERR_WORD_OFFSET = 64;
 size_t dig_gla_bf16_workspace(int B, int T, int H, int dk, int dv, int chunk, int num_cu);
 hipError_t dig_launch_gla_f32(const DigGlaArgs &a, hipStream_t s);
 

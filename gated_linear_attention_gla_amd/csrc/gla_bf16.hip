@@ -74,6 +74,25 @@ namespace {
 // products far inside the fp32/bf16 range.
 constexpr float kFastRange = 64.0f;
 
+// Waits between workgroups are bounded: a flag that has not arrived after
+// kWaitTicks of the 100 MHz real-time clock (4 s, far beyond any legitimate
+// wait: a whole segment of the longest sequence the 32-bit slice offsets
+// allow streams in well under a second) sets kErrWait in the workspace's
+// error word and the wait gives up, so the workgroup still finishes.
+constexpr long long kWaitTicks = 400000000ll;
+constexpr unsigned kErrWait = 1u;
+
+__device__ __forceinline__ void wait_flag(const unsigned *flag, unsigned epoch, unsigned *err) {
+  const long long t0 = wall_clock64();
+  while ((__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 2) != epoch) {
+    if (wall_clock64() - t0 > kWaitTicks) {
+      __hip_atomic_fetch_or(err, kErrWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 struct Params {
   const uint16_t *q, *k, *v, *g;
   uint16_t *o;
@@ -89,7 +108,8 @@ struct Params {
   unsigned gh_magic;               // ceil(2^31 / gh): scan-order decode by a scalar multiply (fill_tok)
   unsigned qk_span, v_span, o_span;   // bytes addressable in one (batch, head) slice of q/k/g, v, o
   int blk_floats;                  // floats of one published state block
-  int *ticket;                     // [8] launch-order ticket counters, one per XCD (reset by the last taker)
+  unsigned *ticket;                // [8] launch-order ticket counters, one per XCD (cyclic, see the kernel)
+  unsigned *err;                   // error word: kErrWait when a wait gave up
   unsigned *flags;                 // [units][nseg]: epoch*4 + {1 aggregate, 2 split hand-off}
   float *gam;                      // [units][nseg][DP] product of the segment's gates
   float *agg;                      // [units][nseg][blk_floats] aggregate state
@@ -188,19 +208,27 @@ gla_fwd_bf16_kernel(Params P) {
   // 144-byte rows share 128-byte lines, then meet in one L2.  Within an XCD,
   // tickets taken in start order assign the work, so segment g of a scan
   // always holds a larger ticket than segment g-1 of it and only ever waits
-  // for a workgroup that started before it.
+  // for a workgroup that started before it.  The counter is cyclic (atomic
+  // increment wrapping at gsize - 1): a launch takes exactly gsize tickets,
+  // so it leaves the counter where it found it, and whatever the counter
+  // holds, the gsize tickets of a launch are a permutation of [0, gsize) --
+  // from r < gsize they run r .. gsize-1, 0 .. r-1; from a value >= gsize the
+  // first taker gets that value (read as gsize - 1) and the rest 0 .. gsize-2.
+  // Every piece of work is therefore taken exactly once even on a workspace
+  // that was never zero-filled; only the start order can then be rotated,
+  // which the bounded waits turn into an error rather than a hang.
   if (tid == 0) {
-    const int g = blockIdx.x & 7, gsize = (int)gridDim.x >> 3;
-    const int t = __hip_atomic_fetch_add(P.ticket + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == gsize - 1) __hip_atomic_store(P.ticket + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sMisc[1] = (t << 3) | g;
+    const unsigned g = blockIdx.x & 7, gsize = gridDim.x >> 3;
+    unsigned t = __builtin_amdgcn_atomic_inc32(P.ticket + g, gsize - 1, __ATOMIC_RELAXED, "agent");
+    if (t >= gsize) t = gsize - 1;
+    sMisc[1] = (int)((t << 3) | g);
   }
   __syncthreads();
   const int lid = sMisc[1];
   const int xcd = lid & 7, kslot = lid >> 3;
   const int unit = xcd * P.per_xcd + kslot / P.nseg;
   const int seg = kslot % P.nseg;
-  if ((unsigned)unit >= (unsigned)P.units) return;   // (a workspace that was not zero-filled gives wild tickets)
+  if (unit >= P.units) return;   // the padding slots of the last XCD range
   // Chunk ranges.  Uniform segments: segment g aggregates and then outputs
   // its own chunks.  Two-segment split (split_K > 0): segment 0 outputs
   // chunks [0, L+K) straight from s0 and publishes the state entering chunk L
@@ -805,9 +833,7 @@ gla_fwd_bf16_kernel(Params P) {
     load_s0(S);
   } else if (P.split_K > 0) {
     // split segment 1: the state segment 0 publishes on its way past chunk L
-    if (tid == 0)
-      while ((__hip_atomic_load(P.flags + slot0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 2) != P.epoch)
-        __builtin_amdgcn_s_sleep(2);
+    if (tid == 0) wait_flag(P.flags + slot0, P.epoch, P.err);
     __syncthreads();                                            // B l
     // S(L) folded with this segment's aggregate of chunks [L, L+K)
 #pragma unroll
@@ -825,9 +851,7 @@ gla_fwd_bf16_kernel(Params P) {
     // segment order, so the result does not depend on timing.  The loads of
     // kFoldBatch segments are issued before their folds.
     if (wave == 0)
-      for (int j = lane; j < seg; j += 64)
-        while ((__hip_atomic_load(P.flags + slot0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 2) != P.epoch)
-          __builtin_amdgcn_s_sleep(2);
+      for (int j = lane; j < seg; j += 64) wait_flag(P.flags + slot0 + j, P.epoch, P.err);
     __syncthreads();                                            // B l
     load_s0(S);
     if (has_cols) {
@@ -1027,7 +1051,7 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   pl.blk_floats = DTr * NWv * 64 * 4;
   const size_t slots = (size_t)pl.units * pl.nseg;
   auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
-  size_t off = 256;   // the 8 ticket counters live at offset 0
+  size_t off = 256;   // header: the 8 ticket counters at byte 0, the error word at DIG_GLA_ERR_WORD_OFFSET
   pl.off_flags = off;
   off += up(slots * 4);
   pl.off_gam = off;
@@ -1038,6 +1062,12 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   off += up(slots * pl.blk_floats * 4);
   pl.bytes = off;
   return pl;
+}
+
+// Clears n 32-bit words (the segment flags of a launch that will be replayed
+// from a graph, where every replay carries the same epoch).
+__global__ void __launch_bounds__(256) clear_words_kernel(unsigned *w, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) w[i] = 0u;
 }
 
 template <int DP, int M>
@@ -1104,12 +1134,27 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   p.v_span = (unsigned)(((int64_t)(a.T - 1) * a.v_st + a.dv) * 2);
   p.o_span = (unsigned)(((int64_t)(a.T - 1) * a.o_st + a.dv) * 2);
   char *ws = static_cast<char *>(a.workspace);
-  p.ticket = reinterpret_cast<int *>(ws);
+  p.ticket = reinterpret_cast<unsigned *>(ws);
+  p.err = reinterpret_cast<unsigned *>(ws + DIG_GLA_ERR_WORD_OFFSET);
   p.flags = reinterpret_cast<unsigned *>(ws + pl.off_flags);
   p.gam = reinterpret_cast<float *>(ws + pl.off_gam);
   p.agg = reinterpret_cast<float *>(ws + pl.off_agg);
   p.inc = reinterpret_cast<float *>(ws + pl.off_inc);
   p.epoch = a.epoch;
+  // Flags carry the launch's epoch, so between ordinary calls they need no
+  // clearing.  A launch captured into a graph replays with one epoch, and
+  // the flags of the previous replay would read as published: the flag
+  // words are cleared by a fill kernel queued before the GLA kernel.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cap);
+  if (e != hipSuccess) return e;
+  if (cap == hipStreamCaptureStatusActive && pl.nseg > 1) {
+    const int n = pl.units * pl.nseg;
+    hipLaunchKernelGGL(clear_words_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0, s,
+                       p.flags, n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   switch (pl.DP) {
     case 32: return launch_m<32>(p, a.chunk, pl.grid, s);
     case 64: return launch_m<64>(p, a.chunk, pl.grid, s);

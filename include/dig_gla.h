@@ -118,11 +118,21 @@ extern "C" {
  *                    scan position T-1.  Passing it as s0 of a later call
  *                    continues the scan (state hand-off).
  *   workspace        device memory of at least gla_fwd_workspace_size(...)
- *                    bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST
- *                    USE; the library keeps it consistent afterwards, so it
+ *                    bytes, 256-byte aligned, zero-filled before its first
+ *                    use; the library keeps it consistent afterwards, so it
  *                    can be reused by later calls of any size up to the one
- *                    it was sized for (not by two calls in flight at once).
- *                    May be NULL when the size function returns 0.
+ *                    it was sized for, and by replays of a captured graph
+ *                    (not by two calls in flight at once).  Its header holds
+ *                    cyclic ticket counters (any content gives each piece of
+ *                    work to exactly one workgroup) and launch-tagged flags;
+ *                    every wait between workgroups is bounded (4 s), and a
+ *                    wait that gives up -- possible only on a workspace that
+ *                    was not zero-filled or is shared by calls in flight --
+ *                    sets an error word that gla_fwd_workspace_status
+ *                    reports.  While `stream` is capturing a graph, a small
+ *                    fill kernel that clears the flags is queued before the
+ *                    GLA kernel.  May be NULL when the size function
+ *                    returns 0.
  *   stream           HIP stream to queue on.
  */
 int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
@@ -171,6 +181,18 @@ int gla_fwd_ordered(const void *q, const void *k, const void *v, const void *log
  * ticket counter).  Returns 0 when no workspace is needed; (size_t)-1 for
  * invalid sizes. */
 size_t gla_fwd_workspace_size(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+
+/* gla_fwd_workspace_status -- SYNCHRONISES `stream`, then reads and clears
+ * the error word of a gla_fwd / gla_fwd_ordered workspace.  Returns DIG_OK
+ * when the word is clear: no call that used the workspace since the last
+ * check had a wait between workgroups give up.  Returns DIG_EHIP (with a
+ * message) when one did -- that call's o and s_final are wrong -- and also
+ * on the first check of a workspace that was not zero-filled before its
+ * first use (the word is part of the header; the outputs of such calls are
+ * still right unless a wait gave up).  DIG_EINVAL for a NULL or too small
+ * workspace.  The only call of the library that waits for the stream; it is
+ * meant for tests and for callers that check a workspace. */
+int gla_fwd_workspace_status(void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * gla_bwd -- gradients of gla_fwd (bf16 path) for training.

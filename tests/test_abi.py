@@ -177,3 +177,9 @@ def test_linear_rejects_bad_arguments(L, bad):
     rc = L.dig_linear(p(a["x"]), p(a["w"]), p(a["y"]), a["M"], a["N"], a["K"], p(a["ws"]), a["wsb"], None)
     assert rc in (-1, -2), bad
     assert L.dig_last_error()
+
+
+def test_workspace_status_rejects_missing_workspace(L):
+    assert L.gla_fwd_workspace_status(None, 0, None) == -1
+    assert b"workspace" in L.dig_last_error()
+    assert L.gla_fwd_workspace_status(ctypes.c_void_p(256), 16, None) == -1

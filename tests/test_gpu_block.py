@@ -6,9 +6,11 @@ projections, the GLA output, the out-projection, the residual after the
 mixer, the FFN's hidden layer and output, the residual after the FFN) with
 fp32 accumulation inside each product, so about eight bf16 roundings
 (2^-9 relative each) stand between input and output: the block output is
-compared at 2e-2 normwise per batch element (as the bf16 GLA), and its
-update y - x, which carries all of that rounding, at 4e-2.  Zero adaLN
-weights with the identity conv give the identity map exactly.
+compared element by element at 2e-2 of its largest magnitude per batch
+element (max|y - ref| / max|ref|, as the bf16 GLA), and its update y - x,
+which carries all of that rounding, at 4e-2 of the update's largest
+magnitude.  Zero adaLN weights with the identity conv give the identity map
+exactly.
 """
 import numpy as np
 import pytest
@@ -39,9 +41,11 @@ def _run(x, grid, direction, H):
 def _check(y, ref, x, what):
     y = y.double().numpy()
     x0 = x["x"].double().numpy()
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     for b in range(y.shape[0]):
-        e = np.linalg.norm(y[b] - ref[b]) / np.linalg.norm(ref[b])
-        u = np.linalg.norm((y[b] - x0[b]) - (ref[b] - x0[b])) / np.linalg.norm(ref[b] - x0[b])
+        err = np.abs(y[b] - ref[b])
+        e = err.max() / np.abs(ref[b]).max()
+        u = err.max() / np.abs(ref[b] - x0[b]).max()
         assert e <= TOL_Y, f"{what} b={b}: y rel err {e:.3e}"
         assert u <= TOL_UPDATE, f"{what} b={b}: update rel err {u:.3e}"
 
@@ -67,17 +71,14 @@ def test_block_adaln_zero_is_identity():
         assert torch.equal(_run(x, (8, 8), d, 2), x["x"]), d
 
 
-def test_block_c2_shape_sampled(orc):
+def test_block_c2_shape(orc):
     """The DiG-XL/2 block at 1024 px (B=8, 64x64 tokens, C=1152, 16 heads):
-    the GPU over the whole batch, the oracle on batch elements 0 and 5."""
+    the GPU and the oracle over the whole batch."""
     B, gh, gw, C, H = 8, 64, 64, 1152, 16
     x = gen.block_inputs(B, gh * gw, C, seed=82)
     y = _run(x, (gh, gw), "t2b", H)
-    assert torch.isfinite(y.float()).all()
     w = {n: x[n] for n in orc.BLOCK_WEIGHTS}
-    for b in (0, 5):
-        ref = orc.block_fwd(x["x"][b:b + 1], x["c"][b:b + 1], w, (gh, gw), "t2b", H=H)
-        _check(y[b:b + 1], ref, {"x": x["x"][b:b + 1]}, f"C2 block b={b}")
+    _check(y, orc.block_fwd(x["x"], x["c"], w, (gh, gw), "t2b", H=H), x, "C2 block")
 
 
 def test_linear_vs_matmul():

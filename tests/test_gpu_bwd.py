@@ -51,32 +51,31 @@ def run_bwd(x, grid, direction, chunk=0):
     return tuple(t.cpu() for t in out)
 
 
-def oracle_bwd(orc, x, grid, direction, units=None):
+def oracle_bwd(orc, x, grid, direction):
     f = lambda t: None if t is None else t.double().numpy()
     q, k, v, g, do, dsf, s0 = (x["q"], x["k"], x["v"], x["log_alpha"], x["do"], x["dsf"], x["s0"])
-    if units is None:
-        return orc.gla_bwd(q, k, v, g, grid, direction, do, ds_final=f(dsf), s0=f(s0))
-    outs = []
-    for b, h in units:
-        sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous()
-        st = lambda t: None if t is None else f(t[b:b + 1, h:h + 1].contiguous())
-        outs.append(orc.gla_bwd(sl(q), sl(k), sl(v), sl(g), grid, direction, sl(do), ds_final=st(dsf), s0=st(s0)))
-    return outs
+    return orc.gla_bwd(q, k, v, g, grid, direction, do, ds_final=f(dsf), s0=f(s0))
 
 
-def check(got, ref, tag, x=None, units=None):
-    """dq, dk, dv, ds0: normwise per slice.  dlog_alpha is the chunk sum of
-    q (.) dq - k (.) dk (plus the state term): its rounding is relative to
-    those summands, which cancel where the true value vanishes (alpha -> 0
-    gives exactly 0), so its scale is the larger of |dlog_alpha| and
-    |q (.) dq| per (batch, head) slice."""
+def check(got, ref, tag, x=None):
+    """dq, dk, dv, ds0: normwise per slice (and per 64-token block).
+    dlog_alpha is the chunk sum of q (.) dq - k (.) dk (plus the state term):
+    its rounding is relative to those summands, which cancel where the true
+    value vanishes (alpha -> 0 gives exactly 0), so its gated scale is the
+    larger of |dlog_alpha| and |q (.) dq| per (batch, head) slice.  The error
+    against |dlog_alpha| alone is printed beside it (not gated), so the gap
+    between the two scales is visible in the test log."""
     for n, a, r in zip(NAMES[:3], got[:3], ref[:3]):
         assert_o_close(a, r, TOL_BF16, f"{tag} {n}")
     assert_state_close(got[4], ref[4], TOL_BF16, f"{tag} ds0")
-    gq = to_np(x["q"]) if units is None else to_np(x["q"])[units[0]:units[0] + 1, :, units[1]:units[1] + 1]
+    gq = to_np(x["q"])
     a, r = to_np(got[3]), ref[3]
     scale = np.maximum(np.max(np.abs(r), axis=(1, 3)), np.max(np.abs(gq * ref[0]), axis=(1, 3)))
-    e = np.max(np.abs(a - r), axis=(1, 3)) / np.maximum(scale, 1e-30)
+    num = np.max(np.abs(a - r), axis=(1, 3))
+    e = num / np.maximum(scale, 1e-30)
+    e_self = num / np.maximum(np.max(np.abs(r), axis=(1, 3)), 1e-30)
+    print(f"[dlog_alpha] {tag}: err/max(|dlog_alpha|, |q dq|) = {e.max():.3e}, "
+          f"err/|dlog_alpha| = {e_self.max():.3e}", flush=True)
     assert np.all(np.isfinite(a)), f"{tag} dlog_alpha: non-finite"
     assert e.max() <= TOL_BF16, f"{tag} dlog_alpha: rel err {e.max():.3e} > {TOL_BF16:g}"
 
@@ -159,7 +158,8 @@ def test_bwd_gradient_of_forward_loss(orc):
     assert abs(gd - dd) <= 2e-2 * max(abs(dd), 1e-6), (gd, dd)
 
 
-def _sampled_bwd(orc, key, directions, units):
+def _full_bwd(orc, key, directions):
+    """A named workload at full size, every (batch, head) unit compared."""
     cfg = gen.CONFIGS[key]
     x = gen.make_inputs(key)
     g = torch.Generator().manual_seed(cfg.seed + 77)
@@ -168,16 +168,12 @@ def _sampled_bwd(orc, key, directions, units):
     x["s0"] = None
     for d in directions:
         got = run_bwd(x, (cfg.gh, cfg.gw), d, chunk=cfg.chunk)
-        for t in got[:4]:
-            assert torch.isfinite(t.float()).all()
-        for (b, h), ref in zip(units, oracle_bwd(orc, x, (cfg.gh, cfg.gw), d, units=units)):
-            sub = [t[b:b + 1, :, h:h + 1] for t in got[:4]] + [got[4][b:b + 1, h:h + 1]]
-            check(sub, ref, f"{key} {d} unit {(b, h)}", x, (b, h))
+        check(got, oracle_bwd(orc, x, (cfg.gh, cfg.gw), d), f"{key} {d}", x)
 
 
-def test_bwd_c1_sampled(orc):
-    _sampled_bwd(orc, "C1", DIRS, [(0, 0), (17, 3), (31, 5)])
+def test_bwd_c1_full(orc):
+    _full_bwd(orc, "C1", DIRS)
 
 
-def test_bwd_c2_sampled(orc):
-    _sampled_bwd(orc, "C2", ("l2r", "b2t"), [(0, 0), (7, 15)])
+def test_bwd_c2_full(orc):
+    _full_bwd(orc, "C2", DIRS)
