@@ -111,10 +111,10 @@ struct Params {
   unsigned *ticket;                // [8] launch-order ticket counters, one per XCD (cyclic, see the kernel)
   unsigned *err;                   // error word: kErrWait when a wait gave up
   unsigned *flags;                 // [units][nseg]: epoch*4 + {1 aggregate, 2 split hand-off}
-  float *gam;                      // [units][nseg][DP] product of the segment's gates
-  float *agg;                      // [units][nseg][blk_floats] aggregate state
-  float *inc;                      // [units][nseg][blk_floats]: slot 0 holds the state a
-                                   // two-segment split hands over at chunk L
+  float *gam;                      // [units][nseg][DP] product of the segment's gates (look-back only)
+  float *agg;                      // [units][nseg][blk_floats] aggregate state (look-back only)
+  float *inc;                      // [units][blk_floats]: the state a two-segment split hands
+                                   // over at chunk L (split only)
   unsigned epoch;
 };
 
@@ -266,9 +266,13 @@ gla_fwd_bf16_kernel(Params P) {
   const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;   // tiles present in a state block
   const int64_t slot0 = (int64_t)unit * P.nseg;
   // this scan's published segment aggregates and gate products
-  const __amdgpu_buffer_rsrc_t ragg_ = make_rsrc(P.agg + slot0 * P.blk_floats, (unsigned)(P.nseg * P.blk_floats * 4));
-  const __amdgpu_buffer_rsrc_t rgam_ = make_rsrc(P.gam + slot0 * DP, (unsigned)(P.nseg * DP * 4));
-  const __amdgpu_buffer_rsrc_t rinc_ = make_rsrc(P.inc + slot0 * P.blk_floats, (unsigned)(P.blk_floats * 4));
+  // (regions a segmentation mode does not use are absent: null, zero-sized)
+  const __amdgpu_buffer_rsrc_t ragg_ = make_rsrc(P.agg ? P.agg + slot0 * P.blk_floats : nullptr,
+                                                 P.agg ? (unsigned)(P.nseg * P.blk_floats * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t rgam_ = make_rsrc(P.gam ? P.gam + slot0 * DP : nullptr,
+                                                 P.gam ? (unsigned)(P.nseg * DP * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t rinc_ = make_rsrc(P.inc ? P.inc + (int64_t)unit * P.blk_floats : nullptr,
+                                                 P.inc ? (unsigned)(P.blk_floats * 4) : 0u);
   const int acol = n0 + 4 * g4;             // accumulator-layout channel of this lane (4 channels)
 
   // ---- one-time set-up: e^{b_last} = 1 for channel tiles no wave scans
@@ -1049,17 +1053,20 @@ Plan make_plan(int B, int T, int H, int dk, int dv, int M, int num_cu) {
   pl.grid = 8 * pl.per_xcd * pl.nseg;
   const int DTr = (dk + 15) / 16, NWv = (dv + 15) / 16;
   pl.blk_floats = DTr * NWv * 64 * 4;
+  // Workspace: each region only where the segmentation uses it (one segment
+  // per scan needs the header alone).
   const size_t slots = (size_t)pl.units * pl.nseg;
+  const bool split = pl.split_K > 0, lookback = pl.nseg > 1 && !split;
   auto up = [](size_t x) { return ((x + 255) / 256) * 256; };
   size_t off = 256;   // header: the 8 ticket counters at byte 0, the error word at DIG_GLA_ERR_WORD_OFFSET
   pl.off_flags = off;
-  off += up(slots * 4);
+  off += pl.nseg > 1 ? up(slots * 4) : 0;
   pl.off_gam = off;
-  off += up(slots * pl.DP * 4);
+  off += lookback ? up(slots * pl.DP * 4) : 0;
   pl.off_agg = off;
-  off += up(slots * pl.blk_floats * 4);
+  off += lookback ? up(slots * pl.blk_floats * 4) : 0;
   pl.off_inc = off;
-  off += up(slots * pl.blk_floats * 4);
+  off += split ? up((size_t)pl.units * pl.blk_floats * 4) : 0;
   pl.bytes = off;
   return pl;
 }
@@ -1136,10 +1143,11 @@ hipError_t dig_launch_gla_bf16(const DigGlaArgs &a, hipStream_t s) {
   char *ws = static_cast<char *>(a.workspace);
   p.ticket = reinterpret_cast<unsigned *>(ws);
   p.err = reinterpret_cast<unsigned *>(ws + DIG_GLA_ERR_WORD_OFFSET);
-  p.flags = reinterpret_cast<unsigned *>(ws + pl.off_flags);
-  p.gam = reinterpret_cast<float *>(ws + pl.off_gam);
-  p.agg = reinterpret_cast<float *>(ws + pl.off_agg);
-  p.inc = reinterpret_cast<float *>(ws + pl.off_inc);
+  const bool split = pl.split_K > 0, lookback = pl.nseg > 1 && !split;
+  p.flags = pl.nseg > 1 ? reinterpret_cast<unsigned *>(ws + pl.off_flags) : nullptr;
+  p.gam = lookback ? reinterpret_cast<float *>(ws + pl.off_gam) : nullptr;
+  p.agg = lookback ? reinterpret_cast<float *>(ws + pl.off_agg) : nullptr;
+  p.inc = split ? reinterpret_cast<float *>(ws + pl.off_inc) : nullptr;
   p.epoch = a.epoch;
   // Flags carry the launch's epoch, so between ordinary calls they need no
   // clearing.  A launch captured into a graph replays with one epoch, and
