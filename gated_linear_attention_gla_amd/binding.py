@@ -47,6 +47,10 @@ def lib() -> ctypes.CDLL:
             L.gla_fwd_ordered.restype = i32
             L.gla_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
             L.gla_fwd_workspace_size.restype = sz
+            L.gla_fwd_noalloc.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
+                                          i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          p, p, i64, i64, i64, p, p]
+            L.gla_fwd_noalloc.restype = i32
             L.gla_fwd_workspace_status.argtypes = [p, sz, p]
             L.gla_fwd_workspace_status.restype = i32
             L.gla_bwd.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
@@ -190,6 +194,28 @@ def gla_fwd(q, k, v, log_alpha, grid, direction, chunk: int = 0, s0=None, out=No
                        _ptr(sf), _ptr(workspace), wsb, _stream(dev))
     _check(rc, "gla_fwd")
     return out, sf
+
+
+def gla_fwd_noalloc(q, k, v, log_alpha, grid, direction, chunk: int = 0, s0=None, out=None, s_final=None):
+    """gla_fwd through the allocation-free entry point (its workspace is the
+    library's fixed per-GPU scratch).  out and s_final must be given
+    (preallocated): this wrapper allocates nothing either."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if out is None:
+        raise DigError("gla_fwd_noalloc: out must be preallocated")
+    if k.shape != q.shape or log_alpha.shape != q.shape or tuple(v.shape[:3]) != (B, T, H):
+        raise DigError("gla_fwd_noalloc: shape mismatch")
+    if k.stride() != q.stride() or log_alpha.stride() != q.stride():
+        raise DigError("gla_fwd_noalloc: q, k, log_alpha must share strides")
+    gh, gw = grid
+    rc = lib().gla_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _dtype_code(q),
+                               q.stride(0), q.stride(1), q.stride(2), v.stride(0), v.stride(1), v.stride(2),
+                               B, T, H, dk, dv, gh, gw, _dir(direction), chunk,
+                               _ptr(s0), _ptr(out), out.stride(0), out.stride(1), out.stride(2),
+                               _ptr(s_final), _stream(q.device))
+    _check(rc, "gla_fwd_noalloc")
+    return out, s_final
 
 
 def workspace_status(workspace) -> None:

@@ -58,6 +58,34 @@ int current_device(DevInfo &out) {
 
 std::atomic<uint32_t> g_epoch{1};
 
+// Fixed device scratch of gla_fwd_noalloc: the forward's workspace for callers
+// that cannot allocate.  Each device the library runs on holds its own copy
+// (zero at load) until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is used.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+void *g_scratch_ptr[kMaxDev];
+hipError_t g_scratch_err[kMaxDev];
+std::once_flag g_scratch_once[kMaxDev];
+
+int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) return fail(DIG_ENODEV, "device index %d out of range", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress(scratch)");
+  if (g_scratch_ptr[dev] == nullptr) return fail(DIG_EHIP, "hipGetSymbolAddress(scratch) gave no address");
+  *out = g_scratch_ptr[dev];
+  return DIG_OK;
+}
+
 int auto_chunk(int dtype, int chunk, int dk, int dv) {
   if (chunk != 0) return chunk;
   if (dtype != DIG_BF16) return 16;
@@ -195,6 +223,32 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha, 
             void *workspace, size_t workspace_bytes, hipStream_t stream) {
   return gla_fwd_impl(q, k, v, log_alpha, dtype, qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, B, T, H, dk, dv, gh, gw,
                       dir, nullptr, chunk, s0, o, o_sb, o_st, o_sh, s_final, workspace, workspace_bytes, stream);
+}
+
+int gla_fwd_noalloc(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,
+                    int64_t qk_sb, int64_t qk_st, int64_t qk_sh, int64_t v_sb, int64_t v_st, int64_t v_sh,
+                    int B, int T, int H, int dk, int dv, int gh, int gw, int dir, int chunk,
+                    const float *s0, void *o, int64_t o_sb, int64_t o_st, int64_t o_sh, float *s_final,
+                    hipStream_t stream) {
+  try {
+    int rc = check_gla_sizes(dtype, B, T, H, dk, dv, chunk);
+    if (rc) return rc;
+    DevInfo di;
+    rc = current_device(di);
+    if (rc) return rc;
+    const size_t need =
+        dtype == DIG_BF16 ? dig_gla_bf16_workspace(B, T, H, dk, dv, auto_chunk(dtype, chunk, dk, dv), di.num_cu) : 0;
+    if (need > kScratchBytes)
+      return fail(DIG_EWORKSPACE, "gla_fwd_noalloc: these sizes need %zu bytes of scratch, more than its fixed %zu "
+                  "(use gla_fwd with a workspace)", need, kScratchBytes);
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    return gla_fwd_impl(q, k, v, log_alpha, dtype, qk_sb, qk_st, qk_sh, v_sb, v_st, v_sh, B, T, H, dk, dv, gh, gw,
+                        dir, nullptr, chunk, s0, o, o_sb, o_st, o_sh, s_final, ws, kScratchBytes, stream);
+  } catch (...) {
+    return fail(DIG_EHIP, "gla_fwd_noalloc: unexpected C++ exception");
+  }
 }
 
 int gla_fwd_ordered(const void *q, const void *k, const void *v, const void *log_alpha, int dtype,

@@ -148,6 +148,33 @@ int gla_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
             hipStream_t stream);
 
 /*
+ * gla_fwd_noalloc -- gla_fwd without a workspace argument, for callers that
+ * cannot allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc.  It allocates nothing: the
+ * workspace is a fixed 16 MiB device array inside the library, one per GPU
+ * (zero when the library's code is loaded on that GPU, held until the
+ * process ends), whose address is looked up on the first call on each
+ * device.  Arguments, outputs, constraints and errors as gla_fwd; sizes
+ * whose workspace (gla_fwd_workspace_size) exceeds 16 MiB return
+ * DIG_EWORKSPACE with nothing queued.  Every call on one GPU shares that
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and give wrong results -- serialise them, or use gla_fwd with a workspace
+ * per stream.  The array keeps each call's state; the forward needs nothing
+ * of it cleared between calls (cyclic tickets, launch-tagged flags, cleared
+ * before the kernel under graph capture).
+ */
+int gla_fwd_noalloc(const void *q, const void *k, const void *v, const void *log_alpha,
+                    int dtype,
+                    int64_t qk_sb, int64_t qk_st, int64_t qk_sh,
+                    int64_t v_sb, int64_t v_st, int64_t v_sh,
+                    int B, int T, int H, int dk, int dv,
+                    int gh, int gw, int dir, int chunk,
+                    const float *s0,
+                    void *o, int64_t o_sb, int64_t o_st, int64_t o_sh,
+                    float *s_final,
+                    hipStream_t stream);
+
+/*
  * gla_fwd_ordered -- gla_fwd over a caller-given scan order: any permutation
  * of the T tokens, e.g. ZigMa's zigzag (snake) space-filling scans (ZigMa
  * notes, 关键设计 / Zigzag 扫描方案) or DiG's bidirectional scan (DiG notes,
