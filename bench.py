@@ -304,15 +304,14 @@ def bench_block(a, dg, gen, torch) -> int:
     xa = torch.randn(B * T, C, device=dev).to(torch.bfloat16)
     wa = (torch.randn(4 * C, C, device=dev) / math.sqrt(C)).to(torch.bfloat16)
     ya = torch.empty(B * T, 4 * C, dtype=torch.bfloat16, device=dev)
-    gws = dg.get_workspace(dev, int(dg.lib().dig_linear_workspace_size()), key="gemm")
     for _ in range(5):
-        dg.linear(xa, wa, out=ya, workspace=gws)
+        dg.linear(xa, wa, out=ya)
     torch.cuda.synchronize()
     evs = []
     for _ in range(a.steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        dg.linear(xa, wa, out=ya, workspace=gws)
+        dg.linear(xa, wa, out=ya)
         e1.record(stream)
         evs.append((e0, e1))
     torch.cuda.synchronize()
@@ -345,7 +344,7 @@ def bench_block(a, dg, gen, torch) -> int:
                    "directions": list(cfg.dirs), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": g_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": g_tflops / BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": f"largest product of the block (hipBLASLt matmul, {B * T} x {4 * C} x {C}, bf16)",
+                     "kernel": f"gemm_bf16_kernel: largest product of the block ({B * T} x {4 * C} x {C}, bf16)",
                      "alg_flops_per_launch": g_flops, "avg_launch_us": g_ms * 1e3},
         "block": {"tflops_alg": aflops / (ms_step * 1e-3) / 1e12, "alg_flops_per_step": aflops},
         "cpu_baseline": cpu,
@@ -462,9 +461,16 @@ def traffic_probe(cfg_key: str, chunk: int, bwd: bool = False) -> int:
         q, k, v = (m[j].view(cfg.B, cfg.T, cfg.H, cfg.d) for j in range(3))
     else:
         q, k, v = x["q"], x["k"], x["v"]
+    # the same copy over 144-byte rows at the GLA's head stride: q [B, T, H, d]
+    # rearranged to [B, H, T, d] by torch's strided copy kernel (reads and
+    # writes q's bytes once each), a check that the copy's counter scaling
+    # holds for rows of this size and stride
+    qt = torch.empty(cfg.B, cfg.H, cfg.T, cfg.d, dtype=q.dtype, device=dev)
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
+    for _ in range(3):
+        qt.copy_(q.permute(0, 2, 1, 3))
     if bwd:
         gen_do = torch.Generator(device=dev)
         gen_do.manual_seed(cfg.seed + 4409)
@@ -501,14 +507,21 @@ def write_traffic(cfg_key: str, fetch_dir: str, write_dir: str, command: str, bw
         per = [[float(r["Counter_Value"]) * 1024 for r in rows if n in r["Kernel_Name"]] for n in names]
         # torch's same-dtype device copy is the runtime's blit kernel
         cp = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        # torch's strided copy of q into [B, H, T, d] (elementwise kernel)
+        st = [float(r["Counter_Value"]) * 1024 for r in rows if "direct_copy" in r["Kernel_Name"]]
         if min(len(g) for g in per) < 1 or len(cp) < 1:
             raise SystemExit(f"write_traffic: no gla/copy dispatches with {counter} under {d}")
-        return sum(statistics.median(g) for g in per), statistics.median(cp), len(per[-1]), len(cp)
+        return (sum(statistics.median(g) for g in per), statistics.median(cp), len(per[-1]), len(cp),
+                statistics.median(st) if st else None)
 
-    gf, cf, ng, nc = per_dispatch(fetch_dir, "FETCH_SIZE")
-    gw, cw, _, _ = per_dispatch(write_dir, "WRITE_SIZE")
+    gf, cf, ng, nc, sf_ = per_dispatch(fetch_dir, "FETCH_SIZE")
+    gw, cw, _, _, sw_ = per_dispatch(write_dir, "WRITE_SIZE")
     kf, kw = COPY_PROBE_BYTES / cf, COPY_PROBE_BYTES / cw
     total = gf * kf + gw * kw
+    q_bytes = cfg.B * cfg.T * cfg.H * cfg.d * 2
+    strided = None if sf_ is None or sw_ is None else {
+        "bytes": q_bytes, "fetch_raw": sf_, "write_raw": sw_, "fetch_scaled_over_bytes": sf_ * kf / q_bytes,
+        "write_scaled_over_bytes": sw_ * kw / q_bytes}
     kind = "bwd" if bwd else "fwd"
     src = os.path.join(ROOT, "gated_linear_attention_gla_amd", "csrc", "gla_bwd.hip" if bwd else "gla_bf16.hip")
     alg = bwd_alg_bytes(cfg) if bwd else gla_alg_bytes(cfg)
@@ -517,7 +530,7 @@ def write_traffic(cfg_key: str, fetch_dir: str, write_dir: str, command: str, bw
            "bytes_per_launch": total, "fetch_bytes_raw": gf, "write_bytes_raw": gw,
            "copy_scale_fetch": kf, "copy_scale_write": kw, "copy_bytes": COPY_PROBE_BYTES,
            "alg_bytes_per_launch": alg, "gla_dispatches": ng, "copy_dispatches": nc,
-           "command": command}
+           "strided_copy_check": strided, "command": command}
     out = os.path.join(ROOT, "profiles", f"gla_{kind}_{cfg_key.lower()}_traffic.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)

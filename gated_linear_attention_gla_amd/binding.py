@@ -336,10 +336,8 @@ def linear(x, w, out=None, workspace=None):
         raise DigError("linear: contiguous bf16 x [M, K] and w [N, K] needed")
     if out is None:
         out = torch.empty(M, N, dtype=torch.bfloat16, device=x.device)
-    if workspace is None:
-        workspace = get_workspace(x.device, int(lib().dig_linear_workspace_size()), key="gemm")
-    rc = lib().dig_linear(_ptr(x), _ptr(w), _ptr(out), M, N, K, _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream(x.device))
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().dig_linear(_ptr(x), _ptr(w), _ptr(out), M, N, K, _ptr(workspace), wsb, _stream(x.device))
     _check(rc, "dig_linear")
     return out
 

@@ -459,23 +459,27 @@ int dig_gather_rows(const void *x, int dtype, int B, int T, int C, const int32_t
   }
 }
 
-size_t dig_linear_workspace_size(void) { return DIG_GEMM_SCRATCH; }
+size_t dig_linear_workspace_size(void) { return 0; }
 
 int dig_linear(const void *x, const void *w, void *y, int M, int N, int K, void *workspace, size_t workspace_bytes,
                hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
   try {
     if (!x || !w || !y) return fail(DIG_EINVAL, "dig_linear: x, w and y are required");
     if (M <= 0 || N <= 0 || K <= 0) return fail(DIG_EINVAL, "dig_linear: M, N, K must be positive");
+    if (K % 8 || N % 8) return fail(DIG_EINVAL, "dig_linear: K and N must be multiples of 8");
+    if ((int64_t)M * K >= ((int64_t)1 << 30) || (int64_t)N * K >= ((int64_t)1 << 30))
+      return fail(DIG_EINVAL, "dig_linear: M*K and N*K must stay below 2^30 elements");
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(DIG_EINVAL, "dig_linear: 16-byte alignment needed");
     if (y == x || y == w) return fail(DIG_EINVAL, "dig_linear: y aliases an input");
-    if (!workspace || workspace_bytes < DIG_GEMM_SCRATCH)
-      return fail(DIG_EWORKSPACE, "dig_linear: workspace of %zu bytes needed, %zu given", (size_t)DIG_GEMM_SCRATCH,
-                  workspace_bytes);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(DIG_EINVAL, "dig_linear: workspace must be 256-byte aligned");
     DevInfo di;
     int rc = current_device(di);
     if (rc) return rc;
-    const hipError_t e = dig_launch_linear(x, w, y, M, N, K, workspace, DIG_GEMM_SCRATCH, stream);
+    DigGemmArgs g{};
+    g.X = x; g.W = w; g.Y = y; g.y_f32 = false; g.M = M; g.N = N; g.K = K; g.kind = DIG_EPI_NONE; g.alpha = 1.0f;
+    g.num_cu = di.num_cu;
+    const hipError_t e = dig_launch_gemm(g, stream);
     if (e != hipSuccess) return hip_fail(e, "dig_linear");
     return DIG_OK;
   } catch (...) {
@@ -507,11 +511,11 @@ int dig_block_fwd(const void *x, const float *c, const void *w_ada, const float 
     if (gh <= 0 || gw <= 0 || (int64_t)gh * gw != T)
       return fail(DIG_EINVAL, "dig_block_fwd: grid %dx%d does not hold T=%d tokens", gh, gw, T);
     if (dir < DIG_L2R || dir > DIG_B2T) return fail(DIG_EINVAL, "dig_block_fwd: dir must be 0..3");
-    const void *al[] = {x, w_ada, w_in, w_out, w_ff1, w_ff2, y, b_in, b_out, b_ff1, b_ff2};
+    const void *al[] = {x, w_ada, w_in, w_out, w_ff1, w_ff2, y, b_ada, b_in, b_out, b_ff1, b_ff2};
     for (const void *p : al)
       if (!aligned16(p))
-        return fail(DIG_EINVAL, "dig_block_fwd: bf16 tensors and the fp32 biases b_in, b_out, b_ff1, b_ff2 must be "
-                                "16-byte aligned");
+        return fail(DIG_EINVAL, "dig_block_fwd: bf16 tensors and the fp32 biases b_ada, b_in, b_out, b_ff1, b_ff2 "
+                                "must be 16-byte aligned");
     if (y == x) return fail(DIG_EINVAL, "dig_block_fwd: y aliases x");
     DevInfo di;
     int rc = current_device(di);

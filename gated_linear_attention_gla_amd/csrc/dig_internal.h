@@ -132,11 +132,35 @@ struct DigBlockArgs {
   uint32_t epoch;
   int num_cu;
 };
-constexpr size_t DIG_GEMM_SCRATCH = size_t(64) << 20;   // bytes of hipBLASLt scratch a product may use
 size_t dig_block_workspace(int B, int T, int C, int H, int num_cu);
 hipError_t dig_launch_block(const DigBlockArgs &a, hipStream_t s);
-hipError_t dig_launch_linear(const void *x, const void *w, void *y, int M, int N, int K, void *scratch,
-                             size_t scratch_bytes, hipStream_t s);
+
+// Dense product Y[M][N] = alpha X[M][K] W[N][K]^T (+ bias[N]) with an
+// epilogue (gemm.hip): bf16 operands, fp32 accumulation, Y bf16 or fp32.
+// Needs K and N multiples of 8 and M K, N K below 2^30 (32-bit byte offsets).
+enum {
+  DIG_EPI_NONE = 0,      // alpha acc (+ bias)
+  DIG_EPI_GELU = 1,      // tanh GELU(alpha acc + bias)
+  DIG_EPI_GATE = 2,      // alpha acc + bias; columns >= gate_col -> logsigmoid(.) / 16
+  DIG_EPI_RESIDUAL = 3,  // Y[r'] = res[r'] + gate[b][gate_off + n] (alpha acc + bias), r' the mapped row
+};
+struct DigGemmArgs {
+  const void *X, *W;
+  void *Y;
+  bool y_f32;
+  int M, N, K;
+  int kind;
+  float alpha;
+  const float *bias;     // nullable, 16-byte aligned
+  int gate_col;
+  const void *res;       // RESIDUAL: bf16 [M][N], indexed by the mapped row
+  const float *gate;     // RESIDUAL: fp32, row b at gate + b gate_stride + gate_off
+  int gate_stride, gate_off;
+  int rowmap;            // RESIDUAL: 0 identity; 1 X rows in scan order -> Y canonical; 2 canonical -> scan
+  int T, dir, gh, gw;    // RESIDUAL: tokens per batch element and the scan order (rowmap != 0)
+  int num_cu;
+};
+hipError_t dig_launch_gemm(const DigGemmArgs &a, hipStream_t s);
 hipError_t dig_launch_gather_rows(const void *x, int dtype, int B, int T, int C, const int *index, void *y,
                                   int num_cu, hipStream_t s);
 hipError_t dig_launch_remap(const void *x, int dtype, int B, int T, int C, int gh, int gw, int from,

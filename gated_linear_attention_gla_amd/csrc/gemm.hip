@@ -1,0 +1,301 @@
+// gemm.hip -- the dense products of the DiG block on gfx950 bf16 MFMA.
+//
+// Y[M][N] = alpha * X[M][K] W[N][K]^T with an elementwise epilogue, row-major,
+// bf16 operands, fp32 accumulation (DiG notes, 关键设计 / DiG Block设计: the
+// q/k/v/gate, output and FFN projections around the mixer; DiT notes, 3.2:
+// the adaLN-Zero regression of the conditioning).  Both operands are
+// K-contiguous, so a tile of either is a set of K-rows.
+//
+// Block tile: 256 tokens (M) x BN features (N, 256 or 128), K in steps of 64;
+// eight waves, each owning 64 tokens x BN/2 features.  Tiles go through LDS
+// double-buffered: the next K step's rows are loaded into registers while the
+// current one is multiplied, then written to the other buffer (one barrier
+// per K step).  LDS rows are 36 dwords (64 + 8 bf16): the operand fragments
+// are read 8 bytes per lane from 16 rows at a time, which is conflict free
+// at a stride of 4 * odd dwords on gfx950.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 with W as the A operand and X as B: the
+// accumulator of lane l holds features 4 (l / 16) + e, e = 0..3, of token
+// l % 16 -- four consecutive features of one row of Y -- so results leave as
+// 8-byte row segments (16 bytes for fp32 output), and an epilogue that needs
+// the row (a residual read from another tensor, a permuted row) handles it
+// per lane.  Each 32-wide K block is read as two 8-byte halves in the same
+// order on both operands (the order inside one product is free).
+#include "dig_internal.h"
+#include "dig_mfma.h"
+
+namespace dig {
+namespace {
+
+constexpr int GBM = 256;        // tokens per block tile
+constexpr int GBK = 64;         // K per step
+constexpr int GLD = GBK + 8;    // LDS row stride (elements)
+constexpr int GGM = 8;          // M tiles per group in the block order (L2 reuse)
+
+struct Epi {
+  int kind;            // DIG_EPI_*
+  float alpha;
+  const float *bias;   // [N] fp32 or null
+  int gate_col;        // kind GATE: columns >= gate_col take logsigmoid(.) / 16
+  // kind RESIDUAL: out[r'][n] = res[c][n] + gate[b][gate_off + n] * (alpha acc + bias[n]),
+  // r' the mapped output row, c the canonical row of the token
+  const uint16_t *res;
+  const float *gate;
+  int gate_stride, gate_off;
+  int rowmap;          // 0 identity; 1 rows in scan order -> canonical; 2 canonical -> scan order
+  int T, dir, gh, gw;
+};
+
+// log sigmoid(z) = min(z, 0) - log(1 + e^{-|z|}); log1p by its series below
+// e = 0.01 (truncation < e^4 / 4), else the hardware log of 1 + e.
+__device__ __forceinline__ float log_sigmoid_f(float z) {
+  const float e = __expf(-fabsf(z));
+  const float l = e < 0.01f ? e * (1.0f - e * (0.5f - e * (1.0f / 3.0f))) : __logf(1.0f + e);
+  return fminf(z, 0.f) - l;
+}
+// tanh-form GELU: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), with
+// tanh(u) = 1 - 2 / (e^{2u} + 1) (exact at both saturations).
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float u = 0.7978845608028654f * (z + 0.044715f * z * z * z);
+  const float t = 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f);
+  return 0.5f * z * (1.0f + t);
+}
+
+// Waves: WV = 8 (4 along tokens x 2 along features) or 4 (2 x 2, each wave
+// 128 x 128 outputs: 256 accumulator registers, one wave per SIMD).  PF:
+// register prefetch depth in K steps (1 or 2).
+template <int BN, int WV, int PF, bool F32OUT>
+__global__ void __launch_bounds__(64 * WV, 1)
+gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, void *__restrict__ Y, int M, int N,
+                 int K, int ntm, int ntn, Epi ep) {
+  constexpr int GT = 64 * WV;
+  constexpr int WMW = WV == 8 ? 4 : 2;     // waves along tokens
+  constexpr int WM = GBM / WMW;            // tokens per wave
+  constexpr int WN = BN / 2;               // features per wave
+  constexpr int TN = WN / 16;              // 16-wide feature tiles per wave (A operand)
+  constexpr int TM = WM / 16;              // 16-token tiles per wave (B operand)
+  constexpr int XR = GBM * GBK / 8 / GT;   // 16-byte X chunks per thread per K step
+  constexpr int WR = BN * GBK / 8 / GT;    // and W chunks
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t *xs = reinterpret_cast<uint16_t *>(smem);                  // [2][GBM][GLD]
+  uint16_t *wsh = xs + 2 * GBM * GLD;                                  // [2][BN][GLD]
+
+  // ---- block -> tile (tm, tn): blocks of one XCD (i % 8) take a contiguous
+  // range of the tile order, which walks groups of GGM token tiles across
+  // every feature tile, so concurrently running blocks share X and W rows in L2
+  const int ntiles = ntm * ntn;
+  const int lb = xcd_linear_block(blockIdx.x, gridDim.x);
+  if (lb >= ntiles) return;
+  const int grp = lb / (GGM * ntn), within = lb - grp * GGM * ntn;
+  const int gm = min(GGM, ntm - grp * GGM);
+  const int tm = grp * GGM + within % gm, tn = within / gm;
+  const int m0 = tm * GBM, n0 = tn * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;   // token rows [WM wm, +WM), features [WN wn, +WN)
+
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (unsigned)((int64_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (unsigned)((int64_t)N * K * 2));
+
+  // global -> registers: chunk idx = tid + GT r -> row idx / 8, 8-element column idx % 8;
+  // rows past M / N and columns past K read zeros (offset past the buffer)
+  // PF = 2: two register sets, the rows of K step k+2 are loaded while step k
+  // is multiplied and step k+1's rows (loaded during step k-1) go to LDS, so
+  // a load has two steps to arrive (loads are unconditional: a step past K
+  // reads zeros, which keeps the count of outstanding loads, and so the
+  // waits, exact).  PF = 1: one set, step k+1's rows load during step k.
+  struct Rows { uint4 x[XR], w[WR]; };
+  Rows ra;
+  [[maybe_unused]] Rows rb;
+  // chunk idx = tid + GT r -> row idx / 8, 8-element K column 8 (idx % 8).
+  // Per chunk, computed once: its byte offset at k0 = 0 and its K column (a
+  // row past M / N gets column K, i.e. never loads); a step adds 2 k0.
+  unsigned xo[XR], wo[WR];
+  int xk[XR], wk[WR];
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int idx = tid + GT * r, row = idx >> 3, c = idx & 7;
+    const bool ok = m0 + row < M;
+    xo[r] = ok ? (unsigned)(((int64_t)(m0 + row) * K + 8 * c) * 2) : 0u;
+    xk[r] = ok ? 8 * c : K;
+  }
+#pragma unroll
+  for (int r = 0; r < WR; ++r) {
+    const int idx = tid + GT * r, row = idx >> 3, c = idx & 7;
+    const bool ok = n0 + row < N;
+    wo[r] = ok ? (unsigned)(((int64_t)(n0 + row) * K + 8 * c) * 2) : 0u;
+    wk[r] = ok ? 8 * c : K;
+  }
+  auto load = [&](Rows &rr, int k0) {
+#pragma unroll
+    for (int r = 0; r < XR; ++r) rr.x[r] = bload16(rx, xk[r] + k0 < K ? xo[r] + 2u * k0 : kOOB);
+#pragma unroll
+    for (int r = 0; r < WR; ++r) rr.w[r] = bload16(rw, wk[r] + k0 < K ? wo[r] + 2u * k0 : kOOB);
+  };
+  auto store = [&](const Rows &rr, int buf) {
+    uint16_t *xb = xs + buf * GBM * GLD, *wb = wsh + buf * BN * GLD;
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+      const int idx = tid + GT * r;
+      *reinterpret_cast<uint4 *>(xb + (idx >> 3) * GLD + 8 * (idx & 7)) = rr.x[r];
+    }
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+      const int idx = tid + GT * r;
+      *reinterpret_cast<uint4 *>(wb + (idx >> 3) * GLD + 8 * (idx & 7)) = rr.w[r];
+    }
+  };
+
+  f32x4_t acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one K step from LDS buffer buf: two 32-wide K blocks
+  auto compute = [&](int buf) {
+    const uint16_t *xb = xs + buf * GBM * GLD + (WM * wm + l16) * GLD + 4 * g4;
+    const uint16_t *wb = wsh + buf * BN * GLD + (WN * wn + l16) * GLD + 4 * g4;
+#pragma unroll
+    for (int kb = 0; kb < GBK; kb += 32) {
+      uint4 a[TN], b[TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) a[i] = cat(lds2(wb + 16 * i * GLD + kb), lds2(wb + 16 * i * GLD + kb + 16));
+#pragma unroll
+      for (int j = 0; j < TM; ++j) b[j] = cat(lds2(xb + 16 * j * GLD + kb), lds2(xb + 16 * j * GLD + kb + 16));
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    }
+  };
+
+  const int KT = (K + GBK - 1) / GBK;
+  if constexpr (PF == 2) {
+    load(ra, 0);
+    load(rb, GBK);
+    store(ra, 0);
+    __syncthreads();
+    // steps in pairs (register sets a, b) so the set loaded last is known at
+    // every wait; an odd count runs one step past K on zeros
+    for (int kt = 0; kt < KT; kt += 2) {
+      load(ra, (kt + 2) * GBK);
+      compute(0);
+      store(rb, 1);
+      __syncthreads();
+      if (kt + 1 >= KT) break;
+      load(rb, (kt + 3) * GBK);
+      compute(1);
+      store(ra, 0);
+      __syncthreads();
+    }
+  } else {
+    load(ra, 0);
+    store(ra, 0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const bool more = kt + 1 < KT;
+      if (more) load(ra, (kt + 1) * GBK);
+      compute(kt & 1);
+      if (more) store(ra, (kt + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds features nf .. nf+3 of token m for each tile
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = m0 + WM * wm + 16 * j + l16;
+    if (m >= M) continue;
+    // output row (rowmap) and the canonical row of the residual: rowmap 1 reads
+    // X in scan order and writes canonical rows; rowmap 2 the reverse
+    int64_t orow = m, rrow = m;
+    int bidx = 0;
+    if (ep.kind == DIG_EPI_RESIDUAL) {
+      bidx = m / ep.T;
+      const int t = m - bidx * ep.T;
+      const int t2 = ep.rowmap == 1 ? scan_to_canon(ep.dir, ep.gh, ep.gw, ep.T, t)
+                     : ep.rowmap == 2 ? canon_to_scan(ep.dir, ep.gh, ep.gw, ep.T, t)
+                                      : t;
+      orow = (int64_t)bidx * ep.T + t2;
+      rrow = ep.rowmap == 2 ? m : orow;
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int nf = n0 + WN * wn + 16 * i + 4 * g4;
+      if (nf >= N) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] * ep.alpha;
+      if (ep.bias) {
+        const float4 bb = *reinterpret_cast<const float4 *>(ep.bias + nf);
+        v[0] += bb.x; v[1] += bb.y; v[2] += bb.z; v[3] += bb.w;
+      }
+      if (ep.kind == DIG_EPI_GELU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+      } else if (ep.kind == DIG_EPI_GATE && nf >= ep.gate_col) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = log_sigmoid_f(v[e]) * (1.0f / 16.0f);
+      } else if (ep.kind == DIG_EPI_RESIDUAL) {
+        const uint2 rr = *reinterpret_cast<const uint2 *>(ep.res + rrow * N + nf);
+        const float4 gg = *reinterpret_cast<const float4 *>(ep.gate + (int64_t)bidx * ep.gate_stride + ep.gate_off + nf);
+        v[0] = bf16lo(rr.x) + gg.x * v[0];
+        v[1] = bf16hi(rr.x) + gg.y * v[1];
+        v[2] = bf16lo(rr.y) + gg.z * v[2];
+        v[3] = bf16hi(rr.y) + gg.w * v[3];
+      }
+      if constexpr (F32OUT) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(Y) + orow * N + nf) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + orow * N + nf) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+  }
+}
+
+template <int BN, int WV, int PF, bool F32OUT>
+hipError_t launch_gemm(const void *X, const void *W, void *Y, int M, int N, int K, const Epi &ep, hipStream_t s) {
+  const int ntm = (M + GBM - 1) / GBM, ntn = (N + BN - 1) / BN;
+  const int grid = ((ntm * ntn + 7) / 8) * 8;
+  const size_t lds = (size_t)2 * (GBM + BN) * GLD * 2;
+  auto *fn = gemm_bf16_kernel<BN, WV, PF, F32OUT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * WV), lds, s, static_cast<const uint16_t *>(X),
+                     static_cast<const uint16_t *>(W), Y, M, N, K, ntm, ntn, ep);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace dig
+
+hipError_t dig_launch_gemm(const DigGemmArgs &a, hipStream_t s) {
+  dig::Epi ep{};
+  ep.kind = a.kind;
+  ep.alpha = a.alpha;
+  ep.bias = a.bias;
+  ep.gate_col = a.gate_col;
+  ep.res = static_cast<const uint16_t *>(a.res);
+  ep.gate = a.gate;
+  ep.gate_stride = a.gate_stride;
+  ep.gate_off = a.gate_off;
+  ep.rowmap = a.rowmap;
+  ep.T = a.T > 0 ? a.T : 1;
+  ep.dir = a.dir;
+  ep.gh = a.gh;
+  ep.gw = a.gw;
+  // 128-wide feature tiles when 256-wide ones would leave the chip's CUs
+  // short of tiles or waste a half-empty last tile
+  const int ntm = (a.M + dig::GBM - 1) / dig::GBM;
+  const bool wide = a.N % 256 == 0 && (int64_t)ntm * (a.N / 256) >= 2 * a.num_cu;
+  // (measured at the DiG-XL/2 block's shapes: 256-wide tiles with one step
+  // of prefetch 668 TFLOP/s on 32768 x 4608 x 1152; four waves of 128 x 128
+  // each 519; 128-wide tiles with two steps of prefetch 583)
+  if (a.y_f32) return dig::launch_gemm<128, 8, 1, true>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  if (wide) return dig::launch_gemm<256, 8, 1, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  return dig::launch_gemm<128, 8, 2, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+}

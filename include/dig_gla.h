@@ -25,14 +25,13 @@
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch-owned
  *     device memory) unless stated otherwise.  The caller owns every buffer
  *     and keeps it alive until the work queued on `stream` has finished.
- *   - The library never allocates or frees device memory and never
- *     synchronises the stream, with one exception: the dense products of
- *     dig_linear and dig_block_fwd run on hipBLASLt, whose handle (created
- *     on a device's first such call) may hold library-internal memory, and
- *     the first call of each product shape times candidate algorithms,
- *     waiting for the stream.  Work is queued on `stream` (NULL = the
- *     default stream of the current device); errors raised by a kernel while
- *     it runs surface at the caller's next synchronisation.
+ *   - The library never allocates or frees device memory (gla_fwd_noalloc's
+ *     fixed scratch is a static device array of the library), keeps no
+ *     global mutable state beyond per-device facts looked up once, and never
+ *     synchronises the stream, except gla_fwd_workspace_status, which exists
+ *     to do so.  Work is queued on `stream` (NULL = the default stream of the
+ *     current device); errors raised by a kernel while it runs surface at the
+ *     caller's next synchronisation.
  *   - Strides are in ELEMENTS; the innermost (channel) dimension is contiguous.
  *   - Return value: 0 on success; DIG_EINVAL for invalid arguments (checked
  *     before any HIP call, nothing is queued); DIG_EWORKSPACE when the
@@ -342,16 +341,13 @@ int dig_gather_rows(const void *x, int dtype, int B, int T, int C,
 
 /*
  * dig_linear -- y = x w^T for row-major bf16 x [M, K], w [N, K] (a PyTorch
- * Linear weight), y [M, N] bf16; fp32 accumulation.  A plain dense product,
- * run by hipBLASLt on `stream` with its scratch in `workspace` (at least
- * dig_linear_workspace_size() bytes, 256-byte aligned, not shared by calls in
- * flight at once).  The first call on a device creates that device's
- * hipBLASLt handle, and the first call of a shape its plan (descriptor and
- * the fastest of the library's candidate algorithms, timed on that call's
- * operands; that call waits for the stream; under graph capture, and for
- * products under 1e10 flops, the library's first choice, untimed), which the
- * library keeps.  Errors: DIG_EINVAL (null, sizes,
- * alignment, aliasing), DIG_EWORKSPACE, DIG_EHIP.
+ * Linear weight), y [M, N] bf16; fp32 accumulation.  The plain form of the
+ * library's bf16 MFMA product that the block's projections use (DiG notes,
+ * 关键设计 / DiG Block设计), queued on `stream`.  Needs K and N multiples of 8,
+ * 16-byte aligned pointers and M*K, N*K below 2^30 elements.  It needs no
+ * workspace: dig_linear_workspace_size() returns 0 and `workspace` may be
+ * NULL (the arguments stay for the ABI).  Errors: DIG_EINVAL (null, sizes,
+ * alignment, aliasing), DIG_EHIP.
  */
 size_t dig_linear_workspace_size(void);
 int dig_linear(const void *x, const void *w, void *y, int M, int N, int K,
@@ -378,16 +374,13 @@ int dig_linear(const void *x, const void *w, void *y, int M, int N, int K,
  *            u), b_in fp32 [4C]; w_out bf16 [C, C], b_out fp32 [C]; w_ff1 bf16
  *            [4C, C], b_ff1 fp32 [4C]; w_ff2 bf16 [C, 4C], b_ff2 fp32 [C];
  *            w_conv fp32 [C, 3, 3].  All contiguous; bf16 ones and b_in,
- *            b_out, b_ff1, b_ff2 16-byte aligned.
+ *            b_ada, b_in, b_out, b_ff1, b_ff2 16-byte aligned.
  *   C = H * d with d a multiple of 8, at most 128; C <= 16384.
  *   workspace  at least dig_block_workspace_size(B, T, C, H) bytes, 256-byte
  *            aligned, any contents (the call clears the part it needs
- *            cleared), not shared by calls in flight at once.  Products run on
- *            hipBLASLt (the biases and the FFN's GELU in its epilogues) with
- *            their scratch inside it; the first call on a device creates that
- *            device's hipBLASLt handle and the first call of a shape its plans
- *            (candidate algorithms timed on that call's operands; that call
- *            waits for the stream).
+ *            cleared), not shared by calls in flight at once.  The products
+ *            run on the library's bf16 MFMA GEMM with the biases, the log
+ *            gate, GELU and both gated residuals in its epilogues.
  * Errors as gla_fwd.
  */
 size_t dig_block_workspace_size(int B, int T, int C, int H);

@@ -169,9 +169,13 @@ def test_block_rejects_bad_arguments(L, bad):
 
 
 @pytest.mark.parametrize("bad", [dict(x=None), dict(M=0), dict(K=-1), dict(x=264), dict(y=256), dict(y=512),
-                                 dict(ws=None), dict(wsb=1024), dict(ws=4096 + 16)])
+                                 dict(K=12), dict(N=12), dict(M=1 << 27), dict(N=1 << 27)])
 def test_linear_rejects_bad_arguments(L, bad):
-    a = dict(x=256, w=512, y=768, M=4, N=8, K=16, ws=4096, wsb=L.dig_linear_workspace_size())
+    """Checked before any device query: nulls, sizes (K and N multiples of 8,
+    M*K and N*K below 2^30), 16-byte alignment, y aliasing an input.  The
+    product needs no workspace."""
+    assert L.dig_linear_workspace_size() == 0
+    a = dict(x=256, w=512, y=768, M=4, N=8, K=16, ws=None, wsb=0)
     a.update(bad)
     p = lambda x: None if x is None else ctypes.c_void_p(x)
     rc = L.dig_linear(p(a["x"]), p(a["w"]), p(a["y"]), a["M"], a["N"], a["K"], p(a["ws"]), a["wsb"], None)
