@@ -545,7 +545,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4"])
+    ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "CB"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 512 MB)")
     ap.add_argument("--chunk", type=int, default=0, help="tokens per chunk (0 = the workload's, 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -105,7 +105,8 @@ int check_gla_sizes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
     if (M == 64 && (dk > 96 || dv > 96))
       return fail(DIG_EINVAL, "gla_fwd: bf16 chunk 64 needs dk, dv <= 96 (use 0, 16 or 32)");
   } else {
-    if (M != 16 && M != 32) return fail(DIG_EINVAL, "gla_fwd: fp32 chunk must be 0, 16 or 32");
+    if (M != 16 && M != 32 && M != 64 && M != 128)
+      return fail(DIG_EINVAL, "gla_fwd: fp32 chunk must be 0, 16, 32, 64 or 128");
   }
   return DIG_OK;
 }

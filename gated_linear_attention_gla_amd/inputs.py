@@ -74,6 +74,12 @@ CONFIGS = {
     "C4": Config("C4", "dig-xl2-2048px-mixer-step", B=1, H=16, gh=128, gw=128, d=72, dtype="bf16",
                  qkv_scale=1.0 / math.sqrt(72), gate_mu=2.0, chunk=64, dirs=DIRS, adaln=True,
                  conv_perturb=0.01, seed=1004),
+    # DiG-B/2 at 512^2 (32x32 latent-patch grid).  The pages give the B model's
+    # depth only; its width is read as 12 heads of 64 channels (hidden 768),
+    # between S (6 x 64) and XL (16 x 72), and the image side as 512, between
+    # the S (256) and XL (1024) workloads; the gates as S's.
+    "CB": Config("CB", "dig-b2-512px", B=16, H=12, gh=32, gw=32, d=64, dtype="bf16",
+                 qkv_scale=1.0 / math.sqrt(64), gate_mu=0.0, chunk=64, dirs=DIRS, seed=1005),
 }
 
 

@@ -107,8 +107,11 @@ extern "C" {
  *   gh, gw, dir      the token grid and the scan direction.
  *   chunk            tokens per chunk: 0 = automatic (bf16: 64, or 32 when
  *                    dk or dv exceeds 96; fp32: 16); else 16, 32 or 64
- *                    (bf16; 64 only for dk, dv <= 96) or 16, 32 (fp32).
- *                    The chunk size changes rounding only, never the result.
+ *                    (bf16; 64 only for dk, dv <= 96) or 16, 32, 64, 128
+ *                    (fp32, as long as its LDS plan -- 4 (3 M dk + M dv +
+ *                    M^2 + dk dv) bytes -- fits in 160 KiB, e.g. 128 for
+ *                    dk, dv <= 32).  The chunk size changes rounding only,
+ *                    never the result.
  *   s0               nullable; [B, H, dk, dv] contiguous fp32 initial state.
  *   o                [B, T, H, dv] written in SCAN order (row p is scan
  *                    position p), strides (o_sb, o_st, o_sh).  Must not

@@ -70,6 +70,18 @@ def test_c0_fp32_vs_oracle(orc, direction, chunk):
     assert_state_close(sf, rs, TOL_F32)
 
 
+@pytest.mark.parametrize("d", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
+def test_fp32_chunk_invariance(orc, d, chunk):
+    """The chunk size changes rounding only: chunks of 16, 32, 64 and 128
+    tokens over a ragged 300-token scan (fp32 path) against the oracle."""
+    x = gen.gla_inputs(2, 300, 2, d, d, dtype="f32", seed=23 + d, qkv_scale=1 / np.sqrt(d), gate_div=4.0)
+    o, sf = run_gla(x, (15, 20), "b2t", chunk=chunk)
+    ro, rs = oracle_gla(orc, x, (15, 20), "b2t")
+    assert_o_close(o, ro, TOL_F32)
+    assert_state_close(sf, rs, TOL_F32)
+
+
 def test_fp32_ragged_dk_ne_dv_with_s0(orc):
     x = gen.gla_inputs(2, 35, 3, 24, 40, dtype="f32", seed=21, qkv_scale=0.3, gate_div=4.0)
     s0 = torch.randn(2, 3, 24, 40, generator=torch.Generator().manual_seed(3))
@@ -220,6 +232,11 @@ def test_bf16_segmented_scans_with_s0(orc, shape):
 def test_c2_full_size(orc):
     """DiG-XL/2 at 1024^2 (B=8, H=16, 64x64, d=72): all 128 units, the four directions."""
     _full(orc, "C2", DIRS)
+
+
+def test_cb_full_size(orc):
+    """DiG-B/2 at 512^2 (B=16, H=12, 32x32, d=64): all 192 units, the four directions."""
+    _full(orc, "CB", DIRS)
 
 
 def test_c3_full_size(orc):
