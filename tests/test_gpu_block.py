@@ -82,12 +82,14 @@ def test_block_c2_shape(orc):
 
 
 @pytest.mark.parametrize("shape", [(300, 200, 256), (256, 256, 64), (1, 8, 8), (777, 136, 1160),
-                                   (4096, 1152, 1152), (513, 4608, 72), (32768, 1152, 8)],
+                                   (4096, 1152, 1152), (513, 4608, 72), (32768, 1152, 8), (8, 6912, 1152),
+                                   (16, 40, 4608), (17, 264, 16)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_linear_vs_fp64(shape):
-    """dig_linear (the block's MFMA product, no epilogue) against an fp64
+    """dig_linear (the block's products, no epilogue) against an fp64
     product of the same bf16 operands, element by element: ragged M, N and
-    K tails, a single row, both feature-tile widths, K of one step."""
+    K tails, a single row, both feature-tile widths, K of one step, and the
+    few-row kernel (M <= 16: the conditioning product's shape)."""
     M, N, K = shape
     g = torch.Generator().manual_seed(83 + M + N + K)
     x = torch.randn(M, K, generator=g).to(torch.bfloat16)
