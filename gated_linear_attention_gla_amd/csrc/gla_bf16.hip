@@ -616,7 +616,11 @@ gla_fwd_bf16_kernel(Params P) {
     }
   };
   // o of chunk c for this wave's columns: O^T = S^T q~^T + V^T P^T (S: the
-  // state entering the chunk), stored 8 bytes per lane.
+  // state entering the chunk), stored 8 bytes per lane.  Every token tile is
+  // computed before the first staging store: a store between two tiles would
+  // keep the compiler from issuing the next tile's LDS reads ahead of this
+  // tile's products (it cannot tell the staging tile from the operand tiles),
+  // and the tiles' reads then run one round trip at a time.
   uint16_t *stg = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oStg);
   auto outputs = [&](int c, const f32x4_t *S) {
     const int par = c & 1;
@@ -626,25 +630,44 @@ gla_fwd_bf16_kernel(Params P) {
     uint4 sa[K32];   // S^T (bf16) as the A operand, K = channels
 #pragma unroll
     for (int kb2 = 0; kb2 < K32; ++kb2) sa[kb2] = cat(pack4(S[2 * kb2]), pack4(S[2 * kb2 + 1]));
+    // every operand fragment of the chunk first (q~ rows, P^T tiles), then the products
+    uint4 qf[MT][K32], pf[MT][JP];
+    [[maybe_unused]] uint2 qh[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const uint16_t *qrow = tq + (16 * i + l16) * QS;
-      f32x4_t O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb2 = 0; kb2 < K32; ++kb2)
-        O = mfma32(sa[kb2], cat(lds2(qrow + 32 * kb2 + 4 * g4), lds2(qrow + 32 * kb2 + 16 + 4 * g4)), O);
-      if (KH) O = mfma16(pack4(S[2 * K32]), lds2(qrow + 32 * K32 + 4 * g4), O);
+        qf[i][kb2] = cat(lds2(qrow + 32 * kb2 + 4 * g4), lds2(qrow + 32 * kb2 + 16 + 4 * g4));
+      if (KH) qh[i] = lds2(qrow + 32 * K32 + 4 * g4);
 #pragma unroll
       for (int jp = 0; jp < JP; ++jp) {
         const int j0 = 2 * jp, j1 = 2 * jp + 1;
         if (j0 <= i) {
           const uint2 pt0 = lds2(pt + (i * (i + 1) / 2 + j0) * 256 + lane * 4);
           const uint2 pt1 = (j1 <= i) ? lds2(pt + (i * (i + 1) / 2 + j1) * 256 + lane * 4) : make_uint2(0, 0);
-          O = mfma32(vf[jp], cat(pt0, pt1), O);
+          pf[i][jp] = cat(pt0, pt1);
         }
       }
-      *reinterpret_cast<uint2 *>(stg + (16 * i + l16) * QS + n0 + 4 * g4) = pack4(O);
     }
+    // (keep the scheduler from sinking the reads back between the products,
+    // where the registers allow it: 128-channel tiles and the 64-channel
+    // table-order kernel would spill)
+    if constexpr (DP <= 96 && !(ORD && DP == 64)) __builtin_amdgcn_sched_barrier(0);
+    f32x4_t O[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      O[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb2 = 0; kb2 < K32; ++kb2) O[i] = mfma32(sa[kb2], qf[i][kb2], O[i]);
+      if (KH) O[i] = mfma16(pack4(S[2 * K32]), qh[i], O[i]);
+#pragma unroll
+      for (int jp = 0; jp < JP; ++jp)
+        if (2 * jp <= i) O[i] = mfma32(vf[jp], pf[i][jp], O[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      *reinterpret_cast<uint2 *>(stg + (16 * i + l16) * QS + n0 + 4 * g4) = pack4(O[i]);
   };
   // o of chunk c from the staging tile to memory: whole token rows, 16 bytes
   // per lane (a 64-lane store covers a few complete rows instead of 16-column
