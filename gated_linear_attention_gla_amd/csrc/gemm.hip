@@ -6,21 +6,23 @@
 // the adaLN-Zero regression of the conditioning).  Both operands are
 // K-contiguous, so a tile of either is a set of K-rows.
 //
-// Block tile: 256 tokens (M) x BN features (N, 256 or 128), K in steps of 64;
-// eight waves, each owning 64 tokens x BN/2 features.  Tiles go through LDS
-// double-buffered: the next K step's rows are loaded into registers while the
-// current one is multiplied, then written to the other buffer (one barrier
-// per K step).  LDS rows are 36 dwords (64 + 8 bf16): the operand fragments
-// are read 8 bytes per lane from 16 rows at a time, which is conflict free
-// at a stride of 4 * odd dwords on gfx950.
+// Block tile: 256 tokens (M) x BN features (N, 256 or 128), K in steps of
+// 64; eight waves, 4 along tokens x 2 along features, each owning 64 tokens
+// x BN/2 features as 32 x 32 tiles on v_mfma_f32_32x32x16_bf16 (the 16 x 16
+// shape reads as many operand registers per instruction for half the
+// products: measured 6-17 % slower at the block's shapes).  Tiles go through
+// LDS double-buffered with one barrier per K step: the rows of step k+1 are
+// loaded into registers halfway through step k-1 and written to the other
+// buffer halfway through step k, so a load has a whole step to arrive and
+// the LDS writes overlap products.  LDS rows are 36 dwords (64 + 8 bf16): a
+// fragment is one 16-byte read per lane from 32 rows, conflict free at a
+// stride of 4 * odd dwords.
 //
-// MFMA v_mfma_f32_16x16x32_bf16 with W as the A operand and X as B: the
-// accumulator of lane l holds features 4 (l / 16) + e, e = 0..3, of token
-// l % 16 -- four consecutive features of one row of Y -- so results leave as
-// 8-byte row segments (16 bytes for fp32 output), and an epilogue that needs
-// the row (a residual read from another tensor, a permuted row) handles it
-// per lane.  Each 32-wide K block is read as two 8-byte halves in the same
-// order on both operands (the order inside one product is free).
+// W is the A operand and X the B operand: accumulator register 4 q + e of
+// lane l holds feature 8 q + 4 (l / 32) + e of token l % 32 -- four
+// consecutive features of one row of Y -- so results leave as 8-byte row
+// segments (16 bytes for fp32 output), and an epilogue that needs the row (a
+// residual read from another tensor, a permuted row) handles it per lane.
 #include "dig_internal.h"
 #include "dig_mfma.h"
 
@@ -31,6 +33,15 @@ constexpr int GBM = 256;        // tokens per block tile
 constexpr int GBK = 64;         // K per step
 constexpr int GLD = GBK + 8;    // LDS row stride (elements)
 constexpr int GGM = 8;          // M tiles per group in the block order (L2 reuse)
+
+// v_mfma_f32_32x32x16_bf16: lane l supplies row (A) / column (B) l % 32 and
+// the 8-element K slice l / 32; the accumulator register 4 q + e of lane l
+// holds row 8 q + 4 (l / 32) + e, column l % 32.
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+__device__ __forceinline__ f32x16_t mfma32x32(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
 
 struct Epi {
   int kind;            // DIG_EPI_*
@@ -61,19 +72,15 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return 0.5f * z * (1.0f + t);
 }
 
-// Waves: WV = 8 (4 along tokens x 2 along features) or 4 (2 x 2, each wave
-// 128 x 128 outputs: 256 accumulator registers, one wave per SIMD).  PF:
-// register prefetch depth in K steps (1 or 2).
-template <int BN, int WV, int PF, bool F32OUT>
-__global__ void __launch_bounds__(64 * WV, 1)
+template <int BN, bool F32OUT>
+__global__ void __launch_bounds__(512, 1)
 gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, void *__restrict__ Y, int M, int N,
                  int K, int ntm, int ntn, Epi ep) {
-  constexpr int GT = 64 * WV;
-  constexpr int WMW = WV == 8 ? 4 : 2;     // waves along tokens
-  constexpr int WM = GBM / WMW;            // tokens per wave
+  constexpr int GT = 512;                  // threads: eight waves
+  constexpr int WM = GBM / 4;              // tokens per wave
   constexpr int WN = BN / 2;               // features per wave
-  constexpr int TN = WN / 16;              // 16-wide feature tiles per wave (A operand)
-  constexpr int TM = WM / 16;              // 16-token tiles per wave (B operand)
+  constexpr int TN = WN / 32;              // 32-feature tiles per wave (A operand)
+  constexpr int TM = WM / 32;              // 32-token tiles per wave (B operand)
   constexpr int XR = GBM * GBK / 8 / GT;   // 16-byte X chunks per thread per K step
   constexpr int WR = BN * GBK / 8 / GT;    // and W chunks
   extern __shared__ __align__(16) unsigned char smem[];
@@ -92,25 +99,18 @@ gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W,
   const int m0 = tm * GBM, n0 = tn * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;   // token rows [WM wm, +WM), features [WN wn, +WN)
+  const int l32 = lane & 31, h32 = lane >> 5;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (unsigned)((int64_t)M * K * 2));
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (unsigned)((int64_t)N * K * 2));
 
-  // global -> registers: chunk idx = tid + GT r -> row idx / 8, 8-element column idx % 8;
-  // rows past M / N and columns past K read zeros (offset past the buffer)
-  // PF = 2: two register sets, the rows of K step k+2 are loaded while step k
-  // is multiplied and step k+1's rows (loaded during step k-1) go to LDS, so
-  // a load has two steps to arrive (loads are unconditional: a step past K
-  // reads zeros, which keeps the count of outstanding loads, and so the
-  // waits, exact).  PF = 1: one set, step k+1's rows load during step k.
+  // global -> registers: chunk idx = tid + GT r -> row idx / 8, 8-element K
+  // column 8 (idx % 8).  Per chunk, computed once: its byte offset at k0 = 0
+  // and its K column (a row past M / N gets column K, i.e. never loads: the
+  // offset past the buffer reads zeros); a step adds 2 k0.
   struct Rows { uint4 x[XR], w[WR]; };
   Rows ra;
-  [[maybe_unused]] Rows rb;
-  // chunk idx = tid + GT r -> row idx / 8, 8-element K column 8 (idx % 8).
-  // Per chunk, computed once: its byte offset at k0 = 0 and its K column (a
-  // row past M / N gets column K, i.e. never loads); a step adds 2 k0.
   unsigned xo[XR], wo[WR];
   int xk[XR], wk[WR];
 #pragma unroll
@@ -147,69 +147,62 @@ gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W,
     }
   };
 
-  f32x4_t acc[TN][TM];
+  f32x16_t acc[TN][TM];
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // one K step from LDS buffer buf: two 32-wide K blocks
-  auto compute = [&](int buf) {
-    const uint16_t *xb = xs + buf * GBM * GLD + (WM * wm + l16) * GLD + 4 * g4;
-    const uint16_t *wb = wsh + buf * BN * GLD + (WN * wn + l16) * GLD + 4 * g4;
+  // One 32-wide K block (kh) of the step in LDS buffer buf, as two 16-wide
+  // K slices; lane l reads row l % 32 of each 32-row tile at K offset
+  // 8 (l / 32).  (Issuing the reads ahead of the products by hand, one to
+  // three W fragments deep, measured the same as the compiler's order.)
+  auto compute_half = [&](int buf, int kh) {
+    const uint16_t *xb = xs + buf * GBM * GLD + (WM * wm + l32) * GLD + 8 * h32 + 32 * kh;
+    const uint16_t *wb = wsh + buf * BN * GLD + (WN * wn + l32) * GLD + 8 * h32 + 32 * kh;
+    uint4 a[2][TN], b[2][TM];
 #pragma unroll
-    for (int kb = 0; kb < GBK; kb += 32) {
-      uint4 a[TN], b[TM];
+    for (int sl = 0; sl < 2; ++sl) {
 #pragma unroll
-      for (int i = 0; i < TN; ++i) a[i] = cat(lds2(wb + 16 * i * GLD + kb), lds2(wb + 16 * i * GLD + kb + 16));
+      for (int j = 0; j < TM; ++j) b[sl][j] = lds4(xb + 32 * j * GLD + 16 * sl);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) b[j] = cat(lds2(xb + 16 * j * GLD + kb), lds2(xb + 16 * j * GLD + kb + 16));
+      for (int i = 0; i < TN; ++i) a[sl][i] = lds4(wb + 32 * i * GLD + 16 * sl);
+    }
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-    }
+        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32x32(a[sl][i], b[sl][j], acc[i][j]);
   };
 
   const int KT = (K + GBK - 1) / GBK;
-  if constexpr (PF == 2) {
-    load(ra, 0);
-    load(rb, GBK);
-    store(ra, 0);
-    __syncthreads();
-    // steps in pairs (register sets a, b) so the set loaded last is known at
-    // every wait; an odd count runs one step past K on zeros
-    for (int kt = 0; kt < KT; kt += 2) {
-      load(ra, (kt + 2) * GBK);
-      compute(0);
-      store(rb, 1);
-      __syncthreads();
-      if (kt + 1 >= KT) break;
-      load(rb, (kt + 3) * GBK);
-      compute(1);
-      store(ra, 0);
-      __syncthreads();
+  load(ra, 0);
+  store(ra, 0);
+  if (KT > 1) load(ra, GBK);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    compute_half(kt & 1, 0);
+    // the rows of step kt+1 (loaded halfway through the previous step) go to
+    // the buffer step kt-1 read, which every wave left at the barrier that
+    // ended it; then the rows of step kt+2 are loaded
+    if (kt + 1 < KT) {
+      store(ra, (kt + 1) & 1);
+      if (kt + 2 < KT) load(ra, (kt + 2) * GBK);
     }
-  } else {
-    load(ra, 0);
-    store(ra, 0);
+    compute_half(kt & 1, 1);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const bool more = kt + 1 < KT;
-      if (more) load(ra, (kt + 1) * GBK);
-      compute(kt & 1);
-      if (more) store(ra, (kt + 1) & 1);
-      __syncthreads();
-    }
   }
 
-  // ---- epilogue: lane holds features nf .. nf+3 of token m for each tile
+  // ---- epilogue: per lane, features nf .. nf+3 of token m
+  // output row (rowmap) and the canonical row of the residual: rowmap 1 reads
+  // X in scan order and writes canonical rows; rowmap 2 the reverse
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    const int m = m0 + WM * wm + 16 * j + l16;
+    const int m = m0 + WM * wm + 32 * j + l32;
     if (m >= M) continue;
-    // output row (rowmap) and the canonical row of the residual: rowmap 1 reads
-    // X in scan order and writes canonical rows; rowmap 2 the reverse
     int64_t orow = m, rrow = m;
     int bidx = 0;
     if (ep.kind == DIG_EPI_RESIDUAL) {
@@ -222,50 +215,53 @@ gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W,
       rrow = ep.rowmap == 2 ? m : orow;
     }
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int nf = n0 + WN * wn + 16 * i + 4 * g4;
-      if (nf >= N) continue;
-      float v[4];
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] * ep.alpha;
-      if (ep.bias) {
-        const float4 bb = *reinterpret_cast<const float4 *>(ep.bias + nf);
-        v[0] += bb.x; v[1] += bb.y; v[2] += bb.z; v[3] += bb.w;
-      }
-      if (ep.kind == DIG_EPI_GELU) {
+      for (int q = 0; q < 4; ++q) {
+        const int nf = n0 + WN * wn + 32 * i + 8 * q + 4 * h32;
+        if (nf >= N) continue;
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
-      } else if (ep.kind == DIG_EPI_GATE && nf >= ep.gate_col) {
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * ep.alpha;
+        if (ep.bias) {
+          const float4 bb = *reinterpret_cast<const float4 *>(ep.bias + nf);
+          v[0] += bb.x; v[1] += bb.y; v[2] += bb.z; v[3] += bb.w;
+        }
+        if (ep.kind == DIG_EPI_GELU) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = log_sigmoid_f(v[e]) * (1.0f / 16.0f);
-      } else if (ep.kind == DIG_EPI_RESIDUAL) {
-        const uint2 rr = *reinterpret_cast<const uint2 *>(ep.res + rrow * N + nf);
-        const float4 gg = *reinterpret_cast<const float4 *>(ep.gate + (int64_t)bidx * ep.gate_stride + ep.gate_off + nf);
-        v[0] = bf16lo(rr.x) + gg.x * v[0];
-        v[1] = bf16hi(rr.x) + gg.y * v[1];
-        v[2] = bf16lo(rr.y) + gg.z * v[2];
-        v[3] = bf16hi(rr.y) + gg.w * v[3];
+          for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+        } else if (ep.kind == DIG_EPI_GATE && nf >= ep.gate_col) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = log_sigmoid_f(v[e]) * (1.0f / 16.0f);
+        } else if (ep.kind == DIG_EPI_RESIDUAL) {
+          const uint2 rr = *reinterpret_cast<const uint2 *>(ep.res + rrow * N + nf);
+          const float4 gg =
+              *reinterpret_cast<const float4 *>(ep.gate + (int64_t)bidx * ep.gate_stride + ep.gate_off + nf);
+          v[0] = bf16lo(rr.x) + gg.x * v[0];
+          v[1] = bf16hi(rr.x) + gg.y * v[1];
+          v[2] = bf16lo(rr.y) + gg.z * v[2];
+          v[3] = bf16hi(rr.y) + gg.w * v[3];
+        }
+        if constexpr (F32OUT) {
+          *reinterpret_cast<float4 *>(static_cast<float *>(Y) + orow * N + nf) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + orow * N + nf) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
       }
-      if constexpr (F32OUT) {
-        *reinterpret_cast<float4 *>(static_cast<float *>(Y) + orow * N + nf) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + orow * N + nf) =
-            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
-    }
   }
 }
 
-template <int BN, int WV, int PF, bool F32OUT>
+template <int BN, bool F32OUT>
 hipError_t launch_gemm(const void *X, const void *W, void *Y, int M, int N, int K, const Epi &ep, hipStream_t s) {
   const int ntm = (M + GBM - 1) / GBM, ntn = (N + BN - 1) / BN;
   const int grid = ((ntm * ntn + 7) / 8) * 8;
   const size_t lds = (size_t)2 * (GBM + BN) * GLD * 2;
-  auto *fn = gemm_bf16_kernel<BN, WV, PF, F32OUT>;
+  auto *fn = gemm_bf16_kernel<BN, F32OUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * WV), lds, s, static_cast<const uint16_t *>(X),
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(512), lds, s, static_cast<const uint16_t *>(X),
                      static_cast<const uint16_t *>(W), Y, M, N, K, ntm, ntn, ep);
   return hipGetLastError();
 }
@@ -359,10 +355,7 @@ hipError_t dig_launch_gemm(const DigGemmArgs &a, hipStream_t s) {
   // N = 1152 measured no faster than 128-wide ones)
   const int ntm = (a.M + dig::GBM - 1) / dig::GBM;
   const bool wide = a.N % 256 == 0 && (int64_t)ntm * (a.N / 256) >= 2 * a.num_cu;
-  // (measured at the DiG-XL/2 block's shapes: 256-wide tiles with one step
-  // of prefetch 668 TFLOP/s on 32768 x 4608 x 1152; four waves of 128 x 128
-  // each 519; 128-wide tiles with two steps of prefetch 583)
-  if (a.y_f32) return dig::launch_gemm<128, 8, 1, true>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
-  if (wide) return dig::launch_gemm<256, 8, 1, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
-  return dig::launch_gemm<128, 8, 2, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  if (a.y_f32) return dig::launch_gemm<128, true>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  if (wide) return dig::launch_gemm<256, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  return dig::launch_gemm<128, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
 }
