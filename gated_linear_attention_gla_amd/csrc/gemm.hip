@@ -196,34 +196,33 @@ gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W,
     __syncthreads();
   }
 
-  // ---- epilogue: per lane, features nf .. nf+3 of token m
-  // output row (rowmap) and the canonical row of the residual: rowmap 1 reads
-  // X in scan order and writes canonical rows; rowmap 2 the reverse
+  // ---- epilogue, in two passes through LDS (free once the last step's
+  // barrier has passed): (1) each lane finishes its values -- alpha, bias,
+  // GELU or the log gate -- and writes them into an LDS copy of the tile,
+  // bf16, or fp32 where the output is fp32 or the residual is still to be
+  // added (so the final value is rounded once); (2) the tile leaves as whole
+  // 16-byte pieces of rows, consecutive threads along a row, with the row
+  // permutation and the gated residual applied there.  (Stored straight from
+  // the accumulators, every 128-byte line of Y arrived as eight 16-byte
+  // pieces from as many instructions: 7.8 us of a 46 us tile.)
+  const bool resid = ep.kind == DIG_EPI_RESIDUAL;
+  const bool stage32 = F32OUT || resid;                  // fp32 staging
+  constexpr int RB = BN * 4 + 16;                        // staged row stride, bytes (fp32 rows; bf16 rows use half)
+  const int rb = stage32 ? RB : BN * 2 + 16;
+  unsigned char *stg = smem;
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    const int m = m0 + WM * wm + 32 * j + l32;
-    if (m >= M) continue;
-    int64_t orow = m, rrow = m;
-    int bidx = 0;
-    if (ep.kind == DIG_EPI_RESIDUAL) {
-      bidx = m / ep.T;
-      const int t = m - bidx * ep.T;
-      const int t2 = ep.rowmap == 1 ? scan_to_canon(ep.dir, ep.gh, ep.gw, ep.T, t)
-                     : ep.rowmap == 2 ? canon_to_scan(ep.dir, ep.gh, ep.gw, ep.T, t)
-                                      : t;
-      orow = (int64_t)bidx * ep.T + t2;
-      rrow = ep.rowmap == 2 ? m : orow;
-    }
+    const int ml = WM * wm + 32 * j + l32;
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int nf = n0 + WN * wn + 32 * i + 8 * q + 4 * h32;
-        if (nf >= N) continue;
+        const int nl = WN * wn + 32 * i + 8 * q + 4 * h32;
+        const int nf = n0 + nl;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * ep.alpha;
-        if (ep.bias) {
+        if (ep.bias && nf < N) {
           const float4 bb = *reinterpret_cast<const float4 *>(ep.bias + nf);
           v[0] += bb.x; v[1] += bb.y; v[2] += bb.z; v[3] += bb.w;
         }
@@ -233,22 +232,51 @@ gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W,
         } else if (ep.kind == DIG_EPI_GATE && nf >= ep.gate_col) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = log_sigmoid_f(v[e]) * (1.0f / 16.0f);
-        } else if (ep.kind == DIG_EPI_RESIDUAL) {
-          const uint2 rr = *reinterpret_cast<const uint2 *>(ep.res + rrow * N + nf);
-          const float4 gg =
-              *reinterpret_cast<const float4 *>(ep.gate + (int64_t)bidx * ep.gate_stride + ep.gate_off + nf);
-          v[0] = bf16lo(rr.x) + gg.x * v[0];
-          v[1] = bf16hi(rr.x) + gg.y * v[1];
-          v[2] = bf16lo(rr.y) + gg.z * v[2];
-          v[3] = bf16hi(rr.y) + gg.w * v[3];
         }
-        if constexpr (F32OUT) {
-          *reinterpret_cast<float4 *>(static_cast<float *>(Y) + orow * N + nf) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + orow * N + nf) =
+        if (stage32)
+          *reinterpret_cast<float4 *>(stg + ml * rb + nl * 4) = make_float4(v[0], v[1], v[2], v[3]);
+        else
+          *reinterpret_cast<uint2 *>(stg + ml * rb + nl * 2) =
               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
       }
+  }
+  __syncthreads();
+  // pass 2: OE output elements (16 bytes) per piece, BN / OE pieces per row
+  constexpr int OE = F32OUT ? 4 : 8, CPR = BN / OE;
+  for (int c = tid; c < GBM * CPR; c += GT) {
+    const int row = c / CPR, nl = (c - row * CPR) * OE;
+    const int m = m0 + row, nf = n0 + nl;
+    if (m >= M || nf >= N) continue;   // N is a multiple of 8: a piece is all in or all out
+    int64_t orow = m, rrow = m;
+    int bidx = 0;
+    if (resid) {
+      // rowmap 1 reads X in scan order and writes canonical rows; rowmap 2
+      // the reverse; the residual is read at the token's canonical row
+      bidx = m / ep.T;
+      const int t = m - bidx * ep.T;
+      const int t2 = ep.rowmap == 1 ? scan_to_canon(ep.dir, ep.gh, ep.gw, ep.T, t)
+                     : ep.rowmap == 2 ? canon_to_scan(ep.dir, ep.gh, ep.gw, ep.T, t)
+                                      : t;
+      orow = (int64_t)bidx * ep.T + t2;
+      rrow = ep.rowmap == 2 ? m : orow;
+    }
+    const unsigned char *sp = stg + row * rb + nl * (stage32 ? 4 : 2);
+    if constexpr (F32OUT) {
+      *reinterpret_cast<uint4 *>(static_cast<float *>(Y) + orow * N + nf) = *reinterpret_cast<const uint4 *>(sp);
+    } else if (!resid) {
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(Y) + orow * N + nf) = *reinterpret_cast<const uint4 *>(sp);
+    } else {
+      const float4 v0 = *reinterpret_cast<const float4 *>(sp), v1 = *reinterpret_cast<const float4 *>(sp + 16);
+      const uint4 rr = *reinterpret_cast<const uint4 *>(ep.res + rrow * N + nf);
+      const float *gp = ep.gate + (int64_t)bidx * ep.gate_stride + ep.gate_off + nf;
+      const float4 g0 = *reinterpret_cast<const float4 *>(gp), g1 = *reinterpret_cast<const float4 *>(gp + 4);
+      uint4 o;
+      o.x = pack_bf16x2(bf16lo(rr.x) + g0.x * v0.x, bf16hi(rr.x) + g0.y * v0.y);
+      o.y = pack_bf16x2(bf16lo(rr.y) + g0.z * v0.z, bf16hi(rr.y) + g0.w * v0.w);
+      o.z = pack_bf16x2(bf16lo(rr.z) + g1.x * v1.x, bf16hi(rr.z) + g1.y * v1.y);
+      o.w = pack_bf16x2(bf16lo(rr.w) + g1.z * v1.z, bf16hi(rr.w) + g1.w * v1.w);
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(Y) + orow * N + nf) = o;
+    }
   }
 }
 
@@ -256,7 +284,9 @@ template <int BN, bool F32OUT>
 hipError_t launch_gemm(const void *X, const void *W, void *Y, int M, int N, int K, const Epi &ep, hipStream_t s) {
   const int ntm = (M + GBM - 1) / GBM, ntn = (N + BN - 1) / BN;
   const int grid = ((ntm * ntn + 7) / 8) * 8;
-  const size_t lds = (size_t)2 * (GBM + BN) * GLD * 2;
+  // operand buffers, or the staged output tile (fp32 rows) if larger
+  const size_t lds_ops = (size_t)2 * (GBM + BN) * GLD * 2, lds_out = (size_t)GBM * (BN * 4 + 16);
+  const size_t lds = BN == 256 ? lds_ops : (lds_ops > lds_out ? lds_ops : lds_out);
   auto *fn = gemm_bf16_kernel<BN, F32OUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
@@ -267,56 +297,90 @@ hipError_t launch_gemm(const void *X, const void *W, void *Y, int M, int N, int 
 }
 
 // Few rows (M <= 16, e.g. the conditioning product over the batch): the MFMA
-// tile would be almost all padding, so each wave takes 8 rows of W, reads
-// each row once (16 bytes per lane along K) and dots it with every row of X
-// held in LDS; alpha, bias, fp32 or bf16 output.  (Measured at 8 x 6912 x
-// 1152: 20.9 us against 30.6 on the MFMA tile; four rows at once with all
-// loads issued first measured 24.4.)
-constexpr int SK_MAXM = 16, SK_T = 256, SK_ROWS = 8;
+// tile would be almost all padding, and the product is one pass over W, so
+// the kernel is built for memory-level parallelism: one row of W per wave,
+// eight waves per block, the 16-byte pieces of the row that a lane needs (up
+// to 4 x 512 elements of K ahead) requested before X (M x K) is staged in
+// LDS per block.  A lane's M dot products are summed across the wave by a
+// reduce-scatter (each step exchanges half of the remaining values: 17
+// shuffles for 16 rows rather than 6 per row), after which lanes 4 m ..
+// 4 m + 3 hold row m's sum.  alpha, bias, fp32 or bf16 output.  (8 x 6912 x
+// 1152: 57 us for eight rows per wave walked one after another, 26 us now.)
+constexpr int SK_MAXM = 16, SK_T = 512, SK_KU = 4;
+constexpr int SK_XMAX = 64 * 1024 / 16 / SK_T;   // X pieces per thread at most (64 KiB of LDS)
 template <bool F32OUT>
 __global__ void __launch_bounds__(SK_T)
 gemm_skinny_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, void *__restrict__ Y, int M, int N,
                    int K, float alpha, const float *__restrict__ bias) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t *xs = reinterpret_cast<uint16_t *>(smem);   // [M][K]
-  for (int i = threadIdx.x; i < M * K / 8; i += SK_T)
-    reinterpret_cast<uint4 *>(xs)[i] = reinterpret_cast<const uint4 *>(X)[i];
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * (SK_T / 64) + wave) * SK_ROWS;
-  for (int r = 0; r < SK_ROWS; ++r) {
-    const int n = n0 + r;
-    if (n >= N) break;
-    float acc[SK_MAXM];
+  const int n = blockIdx.x * (SK_T / 64) + wave;
+  const uint16_t *wrow = W + (int64_t)(n < N ? n : N - 1) * K;   // past N: row N-1, never stored
+  // the first SK_KU pieces of the row are requested before X is staged
+  uint4 wv[SK_KU];
+  auto load_w = [&](int k0) {
 #pragma unroll
-    for (int m = 0; m < SK_MAXM; ++m) acc[m] = 0.f;
-    for (int k = 8 * lane; k < K; k += 512) {
-      const uint4 wv = *reinterpret_cast<const uint4 *>(W + (int64_t)n * K + k);
-      const uint32_t wwd[4] = {wv.x, wv.y, wv.z, wv.w};
+    for (int u = 0; u < SK_KU; ++u)
+      if (k0 + 512 * u < K) wv[u] = *reinterpret_cast<const uint4 *>(wrow + k0 + 512 * u);
+  };
+  load_w(8 * lane);
+  {
+    const int nx = M * K / 8;
+    uint4 t[SK_XMAX];
+#pragma unroll
+    for (int r = 0; r < SK_XMAX; ++r) {
+      const int i = threadIdx.x + SK_T * r;
+      if (i < nx) t[r] = reinterpret_cast<const uint4 *>(X)[i];
+    }
+#pragma unroll
+    for (int r = 0; r < SK_XMAX; ++r) {
+      const int i = threadIdx.x + SK_T * r;
+      if (i < nx) reinterpret_cast<uint4 *>(xs)[i] = t[r];
+    }
+  }
+  __syncthreads();
+  float acc[SK_MAXM];
+#pragma unroll
+  for (int m = 0; m < SK_MAXM; ++m) acc[m] = 0.f;
+  for (int k0 = 8 * lane; k0 < K; k0 += 512 * SK_KU) {
+    if (k0 != 8 * lane) load_w(k0);
+#pragma unroll
+    for (int u = 0; u < SK_KU; ++u) {
+      const int k = k0 + 512 * u;
+      if (k >= K) break;
+      const uint32_t ww[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
 #pragma unroll
       for (int m = 0; m < SK_MAXM; ++m) {
         if (m < M) {
           const uint4 xv = *reinterpret_cast<const uint4 *>(xs + m * K + k);
           const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[m] += bf16lo(wwd[e]) * bf16lo(xw[e]) + bf16hi(wwd[e]) * bf16hi(xw[e]);
+          for (int e = 0; e < 4; ++e) acc[m] += bf16lo(ww[e]) * bf16lo(xw[e]) + bf16hi(ww[e]) * bf16hi(xw[e]);
         }
       }
     }
+  }
+  // reduce-scatter over the 64 lanes: at the step across lane bit b, a lane
+  // keeps the half of its values selected by its bit b and adds its
+  // partner's copy of that half
 #pragma unroll
-    for (int m = 0; m < SK_MAXM; ++m) {
-      if (m < M) {
-        float v = acc[m];
+  for (int h = SK_MAXM / 2, b = 32; h >= 1; h >>= 1, b >>= 1) {
+    const bool up = (lane & b) != 0;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-        if (lane == 0) {
-          v = v * alpha + (bias ? bias[n] : 0.f);
-          if constexpr (F32OUT) static_cast<float *>(Y)[(int64_t)m * N + n] = v;
-          else static_cast<uint16_t *>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf(v);
-        }
-      }
+    for (int i = 0; i < h; ++i) {
+      const float send = up ? acc[i] : acc[i + h];
+      const float keep = up ? acc[i + h] : acc[i];
+      acc[i] = keep + __shfl_xor(send, b, 64);
     }
+  }
+  acc[0] += __shfl_xor(acc[0], 2, 64);
+  acc[0] += __shfl_xor(acc[0], 1, 64);
+  const int m = lane >> 2;   // lanes 4 m .. 4 m + 3 hold the sum of row m
+  if ((lane & 3) == 0 && m < M && n < N) {
+    const float v = acc[0] * alpha + (bias ? bias[n] : 0.f);
+    if constexpr (F32OUT) static_cast<float *>(Y)[(int64_t)m * N + n] = v;
+    else static_cast<uint16_t *>(Y)[(int64_t)m * N + n] = (uint16_t)f2bf(v);
   }
 }
 
@@ -339,7 +403,7 @@ hipError_t dig_launch_gemm(const DigGemmArgs &a, hipStream_t s) {
   ep.gh = a.gh;
   ep.gw = a.gw;
   if (a.M <= dig::SK_MAXM && a.kind == DIG_EPI_NONE && (size_t)a.M * a.K * 2 <= 64 * 1024) {
-    const int rows_per_block = (dig::SK_T / 64) * dig::SK_ROWS;
+    const int rows_per_block = dig::SK_T / 64;
     const size_t lds = (size_t)a.M * a.K * 2;
     auto *fn = a.y_f32 ? dig::gemm_skinny_kernel<true> : dig::gemm_skinny_kernel<false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -356,6 +420,8 @@ hipError_t dig_launch_gemm(const DigGemmArgs &a, hipStream_t s) {
   const int ntm = (a.M + dig::GBM - 1) / dig::GBM;
   const bool wide = a.N % 256 == 0 && (int64_t)ntm * (a.N / 256) >= 2 * a.num_cu;
   if (a.y_f32) return dig::launch_gemm<128, true>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
-  if (wide) return dig::launch_gemm<256, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  // (256-wide tiles stage bf16 only: the residual epilogue, staged in fp32,
+  // runs on 128-wide tiles)
+  if (wide && a.kind != DIG_EPI_RESIDUAL) return dig::launch_gemm<256, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
   return dig::launch_gemm<128, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
 }
