@@ -7,10 +7,12 @@
 // K-contiguous, so a tile of either is a set of K-rows.
 //
 // Block tile: 256 tokens (M) x BN features (N, 256 or 128), K in steps of
-// 64; eight waves, 4 along tokens x 2 along features, each owning 64 tokens
-// x BN/2 features as 32 x 32 tiles on v_mfma_f32_32x32x16_bf16 (the 16 x 16
-// shape reads as many operand registers per instruction for half the
-// products: measured 6-17 % slower at the block's shapes).  Tiles go through
+// 64; sixteen waves, 4 along tokens x 4 along features, each owning 64
+// tokens x BN/4 features as 32 x 32 tiles on v_mfma_f32_32x32x16_bf16
+// (four waves per SIMD keep a product ready to issue while others wait on
+// LDS: 3-10 % faster than eight waves of 64 x BN/2; the 16 x 16 shape reads
+// as many operand registers per instruction for half the products: 6-17 %
+// slower at the block's shapes).  Tiles go through
 // LDS double-buffered with one barrier per K step: the rows of step k+1 are
 // loaded into registers halfway through step k-1 and written to the other
 // buffer halfway through step k, so a load has a whole step to arrive and
@@ -72,13 +74,14 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return 0.5f * z * (1.0f + t);
 }
 
-template <int BN, bool F32OUT>
-__global__ void __launch_bounds__(512, 1)
+template <int BN, int WV, bool F32OUT>
+__global__ void __launch_bounds__(64 * WV, 1)
 gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, void *__restrict__ Y, int M, int N,
                  int K, int ntm, int ntn, Epi ep) {
-  constexpr int GT = 512;                  // threads: eight waves
+  constexpr int GT = 64 * WV;              // threads
+  constexpr int WVN = WV / 4;              // waves along features (4 along tokens)
   constexpr int WM = GBM / 4;              // tokens per wave
-  constexpr int WN = BN / 2;               // features per wave
+  constexpr int WN = BN / WVN;             // features per wave
   constexpr int TN = WN / 32;              // 32-feature tiles per wave (A operand)
   constexpr int TM = WM / 32;              // 32-token tiles per wave (B operand)
   constexpr int XR = GBM * GBK / 8 / GT;   // 16-byte X chunks per thread per K step
@@ -99,7 +102,7 @@ gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W,
   const int m0 = tm * GBM, n0 = tn * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;   // token rows [WM wm, +WM), features [WN wn, +WN)
+  const int wm = wave / WVN, wn = wave % WVN;   // token rows [WM wm, +WM), features [WN wn, +WN)
   const int l32 = lane & 31, h32 = lane >> 5;
 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (unsigned)((int64_t)M * K * 2));
@@ -280,18 +283,18 @@ gemm_bf16_kernel(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W,
   }
 }
 
-template <int BN, bool F32OUT>
+template <int BN, int WV, bool F32OUT>
 hipError_t launch_gemm(const void *X, const void *W, void *Y, int M, int N, int K, const Epi &ep, hipStream_t s) {
   const int ntm = (M + GBM - 1) / GBM, ntn = (N + BN - 1) / BN;
   const int grid = ((ntm * ntn + 7) / 8) * 8;
   // operand buffers, or the staged output tile (fp32 rows) if larger
   const size_t lds_ops = (size_t)2 * (GBM + BN) * GLD * 2, lds_out = (size_t)GBM * (BN * 4 + 16);
   const size_t lds = BN == 256 ? lds_ops : (lds_ops > lds_out ? lds_ops : lds_out);
-  auto *fn = gemm_bf16_kernel<BN, F32OUT>;
+  auto *fn = gemm_bf16_kernel<BN, WV, F32OUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(512), lds, s, static_cast<const uint16_t *>(X),
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * WV), lds, s, static_cast<const uint16_t *>(X),
                      static_cast<const uint16_t *>(W), Y, M, N, K, ntm, ntn, ep);
   return hipGetLastError();
 }
@@ -419,9 +422,10 @@ hipError_t dig_launch_gemm(const DigGemmArgs &a, hipStream_t s) {
   // N = 1152 measured no faster than 128-wide ones)
   const int ntm = (a.M + dig::GBM - 1) / dig::GBM;
   const bool wide = a.N % 256 == 0 && (int64_t)ntm * (a.N / 256) >= 2 * a.num_cu;
-  if (a.y_f32) return dig::launch_gemm<128, true>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  if (a.y_f32) return dig::launch_gemm<128, 16, true>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
   // (256-wide tiles stage bf16 only: the residual epilogue, staged in fp32,
   // runs on 128-wide tiles)
-  if (wide && a.kind != DIG_EPI_RESIDUAL) return dig::launch_gemm<256, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
-  return dig::launch_gemm<128, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  if (wide && a.kind != DIG_EPI_RESIDUAL)
+    return dig::launch_gemm<256, 16, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
+  return dig::launch_gemm<128, 16, false>(a.X, a.W, a.Y, a.M, a.N, a.K, ep, s);
 }
