@@ -51,11 +51,13 @@ def _check(y, ref, x, what):
 
 
 @pytest.mark.parametrize("shape", [(2, 8, 8, 128, 2), (1, 11, 9, 144, 2), (2, 6, 10, 256, 4), (1, 6, 7, 256, 2),
-                                   (2, 4, 5, 16, 2)],
+                                   (2, 4, 5, 16, 2), (17, 4, 5, 16, 2)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_block_vs_oracle(orc, shape):
     """Small shapes in all four directions: ragged chunks, 72-channel heads,
-    128-channel heads (32-token chunks) and 8-channel heads."""
+    128-channel heads (32-token chunks) and 8-channel heads; with 17 batch
+    elements the conditioning product (17 rows) runs on the MFMA tile with
+    fp32 output instead of the few-row kernel."""
     B, gh, gw, C, H = shape
     x = gen.block_inputs(B, gh * gw, C, seed=80 + C)
     w = {n: x[n] for n in orc.BLOCK_WEIGHTS}
