@@ -34,6 +34,7 @@
 // other chunks evaluate the decayed intra-chunk sums with exact exponent
 // differences on the vector ALUs.
 #include "dig_mfma.h"
+#include <atomic>
 
 namespace dig {
 namespace {
@@ -838,7 +839,10 @@ template <int DP, int M>
 hipError_t launch_bwd(const BwdParams &p, int num_cu, hipStream_t s) {
   constexpr int scan_lds = ScanLds<DP, M>::bytes;
   constexpr int chunk_lds = BwdLds<DP, M>::bytes;
-  static int per_cu = 0;   // resident chunk workgroups per CU; the same on every gfx950
+  // resident chunk workgroups per CU: the same on every gfx950, so computed
+  // once (concurrent first calls store the same value)
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   hipError_t e;
   const bool ord = p.order != nullptr;
   auto *scan = ord ? gla_bwd_scan<DP, M, true> : gla_bwd_scan<DP, M, false>;
@@ -853,6 +857,7 @@ hipError_t launch_bwd(const BwdParams &p, int num_cu, hipStream_t s) {
                                                      kChunkWaves * kWave, chunk_lds);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
   const int units = p.B * p.H;
   hipLaunchKernelGGL(scan, dim3(2 * units), dim3(DP / 16 * kWave), scan_lds, s, p);

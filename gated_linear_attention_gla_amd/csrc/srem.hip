@@ -17,6 +17,7 @@
 // Workgroups are ordered so that each XCD sweeps neighbouring columns, whose
 // shared cells hit its L2.
 #include "dig_internal.h"
+#include <atomic>
 
 namespace dig {
 namespace {
@@ -199,13 +200,17 @@ hipError_t launch_walkers(const void *x, int B, int T, int C, int64_t x_sb, int6
                           const float *w, int gh, int gw, int dir, void *y, int64_t y_sb,
                           int64_t y_st, int num_cu, hipStream_t s) {
   constexpr int CH = NW * PW, ES = 4 / PW;
-  static int per_cu = 0;   // resident workgroups per CU; the same on every gfx950
+  // resident workgroups per CU: the same on every gfx950, so computed once
+  // (concurrent first calls store the same value)
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &nb, srem_dwconv_kernel<NW, PW, NC>, kNT, 0);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
   int R, Q;
   scan_frame(dir, gh, gw, R, Q);
