@@ -8,23 +8,23 @@
 //
 // Block tile: 256 tokens (M) x BN features (N, 256 or 128), K in steps of
 // 64; sixteen waves, 4 along tokens x 4 along features, each owning 64
-// tokens x BN/4 features as 32 x 32 tiles on v_mfma_f32_32x32x16_bf16
-// (four waves per SIMD keep a product ready to issue while others wait on
-// LDS: 3-10 % faster than eight waves of 64 x BN/2; the 16 x 16 shape reads
-// as many operand registers per instruction for half the products: 6-17 %
-// slower at the block's shapes).  Tiles go through
-// LDS double-buffered with one barrier per K step: the rows of step k+1 are
-// loaded into registers halfway through step k-1 and written to the other
-// buffer halfway through step k, so a load has a whole step to arrive and
-// the LDS writes overlap products.  LDS rows are 36 dwords (64 + 8 bf16): a
-// fragment is one 16-byte read per lane from 32 rows, conflict free at a
-// stride of 4 * odd dwords.
+// tokens x BN/4 features as 32 x 32 tiles on v_mfma_f32_32x32x16_bf16 (four
+// waves per SIMD keep a product ready to issue while others wait on LDS:
+// 3-10 % faster than eight waves of 64 x BN/2; the 16 x 16 shape reads as
+// many operand registers per instruction for half the products: 6-17 %
+// slower at the block's shapes).  Tiles go through LDS double-buffered with
+// one barrier per K step: the rows of step k+1 are loaded into registers
+// halfway through step k-1 and written to the other buffer halfway through
+// step k, so a load has a whole step to arrive and the LDS writes overlap
+// products.  LDS rows are 36 dwords (64 + 8 bf16): a fragment is one 16-byte
+// read per lane from 32 rows, conflict free at a stride of 4 * odd dwords.
 //
 // W is the A operand and X the B operand: accumulator register 4 q + e of
 // lane l holds feature 8 q + 4 (l / 32) + e of token l % 32 -- four
-// consecutive features of one row of Y -- so results leave as 8-byte row
-// segments (16 bytes for fp32 output), and an epilogue that needs the row (a
-// residual read from another tensor, a permuted row) handles it per lane.
+// consecutive features of one row of Y.  The epilogue finishes those values
+// per lane (alpha, bias, GELU, the log gate), stages the tile in LDS, and
+// writes it as 16-byte pieces of whole rows, applying the row permutation
+// and the gated residual on the way out.
 #include "dig_internal.h"
 #include "dig_mfma.h"
 
