@@ -43,7 +43,7 @@
 //     stages a chunk loaded two chunks earlier, scans its gates and forms q~,
 //     k~ (k^ for pairwise chunks); all waves build the causal P^T tiles.  The
 //     producers work one chunk ahead on the other half of double-buffered LDS
-//     tiles, so the two roles overlap (three barriers per chunk);
+//     tiles, so the two roles overlap (two barriers per chunk);
 //   * the scan permutation is applied in the loads (scan position p reads
 //     canonical token scan_to_canon(p)); no permuted copy is ever written;
 //   * all LDS tiles are token-major rows written with 16-byte stores; the
@@ -64,6 +64,8 @@
 // l % 16.  The K order inside one MFMA is free as long as A and B agree, which
 // lets accumulators feed the next product directly (P^T -> B of V^T P^T,
 // S -> A of S^T q~^T) without a trip through LDS.
+#include <type_traits>
+
 #include "dig_mfma.h"
 
 namespace dig {
@@ -413,9 +415,10 @@ gla_fwd_bf16_kernel(Params P) {
     load_chunk(x + 2, with_q, ls, 0, JA);   // the rest in later intervals
   };
   // The loads of chunk x+2 are spread over the intervals of the step (the
-  // producers' vector-memory issue otherwise stalls the first interval):
-  // loads [0, JA) after the staging stores, [JA, JB) after the transform,
-  // the rest and the token table of chunk x+3 after the P^T tiles.
+  // producers' vector-memory issue otherwise stalls the interval it falls
+  // in): loads [0, JA) after the staging stores of chunk x, the rest and
+  // the token table of chunk x+3 after the transform of chunk x, one
+  // interval later.
   auto mid_loads = [&](int x, bool with_q, LoadSet &ls) { load_chunk(x + 2, with_q, ls, JA, JB); };
   auto late_loads = [&](int x, bool with_q, LoadSet &ls) {
     load_chunk(x + 2, with_q, ls, JB, 4 * R);
@@ -589,19 +592,28 @@ gla_fwd_bf16_kernel(Params P) {
   // S = diag(e^{b_last}) (S + k~^T v) (k~ = k e^{-b} in tile 1: the same
   // product as k^^T v, scaled once per row afterwards); pairwise chunks and
   // segment aggregates S = diag(e^{b_last}) S + k^^T v (k^ in tile 2), which
-  // optionally also accumulates the product of the gates in gprod.
-  auto state_update = [&](int par, f32x4_t *S, f32x4_t *gprod, bool fast) {
+  // optionally also accumulates the product of the gates in gprod.  The form
+  // is a template argument (std::true_type: fast), so each copy scales its
+  // rows once instead of selecting a factor per element.
+  auto state_update = [&](int par, f32x4_t *S, f32x4_t *gprod, auto fast_c, const uint4 *vf_in) {
+    constexpr bool fast = decltype(fast_c)::value;
     const uint16_t *th = tile(par, fast ? 1 : 2);
     uint4 vf[JP];
-    v_frags(tile(par, 3), vf);
+    if (vf_in) {
+#pragma unroll
+      for (int jp = 0; jp < JP; ++jp) vf[jp] = vf_in[jp];
+    } else {
+      v_frags(tile(par, 3), vf);
+    }
     const float *gm_ = gam(par);
-    // one code path for both forms: the row scale goes before or after the product
 #pragma unroll
     for (int r = 0; r < DT; ++r) {
       const float4 gm = *reinterpret_cast<const float4 *>(gm_ + 16 * r + 4 * g4);
       const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+      if constexpr (!fast) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[r][e] *= fast ? 1.f : gv[e];
+        for (int e = 0; e < 4; ++e) S[r][e] *= gv[e];
+      }
       if (gprod) { gprod[r][0] *= gm.x; gprod[r][1] *= gm.y; gprod[r][2] *= gm.z; gprod[r][3] *= gm.w; }
 #pragma unroll
       for (int jp = 0; jp < JP; ++jp) {
@@ -611,21 +623,23 @@ gla_fwd_bf16_kernel(Params P) {
                              : make_uint2(0, 0);
         S[r] = mfma32(cat(lo, hi), vf[jp], S[r]);
       }
+      if constexpr (fast) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[r][e] *= fast ? gv[e] : 1.f;
+        for (int e = 0; e < 4; ++e) S[r][e] *= gv[e];
+      }
     }
   };
   // o of chunk c for this wave's columns: O^T = S^T q~^T + V^T P^T (S: the
-  // state entering the chunk), stored 8 bytes per lane.  Every token tile is
+  // state entering the chunk), stored 8 bytes per lane into the staging
+  // tile; the v fragments are left in vf for the state update.  Every token tile is
   // computed before the first staging store: a store between two tiles would
   // keep the compiler from issuing the next tile's LDS reads ahead of this
   // tile's products (it cannot tell the staging tile from the operand tiles),
   // and the tiles' reads then run one round trip at a time.
   uint16_t *stg = reinterpret_cast<uint16_t *>(smem + Lds<DP, M>::oStg);
-  auto outputs = [&](int c, const f32x4_t *S) {
+  auto outputs = [&](int c, const f32x4_t *S, uint4 *vf) {
     const int par = c & 1;
     const uint16_t *tq = tile(par, 0), *pt = ptile(par);
-    uint4 vf[JP];
     v_frags(tile(par, 3), vf);
     uint4 sa[K32];   // S^T (bf16) as the A operand, K = channels
 #pragma unroll
@@ -777,37 +791,41 @@ gla_fwd_bf16_kernel(Params P) {
     if (has_rows) produce2(c_begin, pw_next);
     lds_barrier();                                              // B v
     if (!pw_next) produce3_fast(c_begin); else produce3_pairwise(c_begin);
+    produce1(c_begin + 1, true, lsB);
     lds_barrier();                                              // B w
     if (pw_next) {
       if (has_rows) qtilde(tile(c_begin & 1, 0), bt);
       lds_barrier();                                            // B x
     }
-    // chunk c: stage and transform chunk x = c+1 from register set (x - c_begin) & 1
-    auto out_step = [&](int c, LoadSet &ls) {
+    // Step c (the consumers write o of chunk c): the producers transform
+    // chunk x = c+1 and issue the rest of chunk x+2's loads (register set
+    // ls_tail), then stage chunk x+1 (set ls_stage) while all waves build the
+    // P^T tiles of chunk x.
+    auto out_step = [&](int c, LoadSet &ls_tail, LoadSet &ls_stage) {
       const int x = c + 1;
       const bool live = x < c_end;
-      // interval 1: stage chunk x (the consumers write o of chunk c)
-      produce1(x, true, ls);   // unconditional, as in the aggregate pass
-      lds_barrier();                                            // B loop 1
       const bool pwx = live && chunk_pairwise(x);
-      // interval 2: transform chunk x (the consumers update the state)
+      // interval 1: transform chunk x (the consumers write o of chunk c and
+      // update the state)
       if (has_rows && live) produce2(x, pwx);
-      mid_loads(x, true, ls);
-      lds_barrier();                                            // B loop 2
-      // interval 3: all waves build the P^T tiles of chunk x
+      mid_loads(x, true, ls_tail);
+      late_loads(x, true, ls_tail);
+      lds_barrier();                                            // B loop 1
+      // interval 2: P^T tiles of chunk x; stage chunk x+1 (unconditional, as
+      // in the aggregate pass)
       if (live) {
         if (!pwx) produce3_fast(x); else produce3_pairwise(x);
       }
-      late_loads(x, true, ls);
-      lds_barrier();                                            // B loop 3
+      produce1(x + 1, true, ls_stage);
+      lds_barrier();                                            // B loop 2
       if (pwx) {
         if (has_rows) qtilde(tile(x & 1, 0), bt);
-        lds_barrier();                                          // B loop 4
+        lds_barrier();                                          // B loop 3
       }
     };
     for (int c = c_begin; c < c_end; c += 2) {   // in pairs, as in the aggregate pass
-      out_step(c, lsB);
-      out_step(c + 1, lsA);
+      out_step(c, lsB, lsA);
+      out_step(c + 1, lsA, lsB);
     }
     return;
   }
@@ -827,7 +845,7 @@ gla_fwd_bf16_kernel(Params P) {
     lds_barrier();                                              // B 2
     lds_barrier();                                              // B 3
     for (int c = c_begin; c < c_end; ++c) {
-      if (has_cols) state_update(c & 1, S, gp, false);
+      if (has_cols) state_update(c & 1, S, gp, std::false_type{}, nullptr);
       lds_barrier();                                            // B loop 1
       lds_barrier();                                            // B loop 2
     }
@@ -936,11 +954,11 @@ gla_fwd_bf16_kernel(Params P) {
     }
   }
   // ========================= pass 2: outputs ==================================
-  // Three barrier intervals per chunk c: the producers stage and transform
-  // chunk c+1 while the consumers write o of chunk c, then update its state;
-  // all waves build the P^T tiles of chunk c+1 in the third.  A pairwise
-  // chunk c+1 adds one interval (its q~ may be written only after every
-  // thread has read its raw q).
+  // Two barrier intervals per chunk c: the consumers write o of chunk c and
+  // update the state while the producers transform chunk c+1; then all waves
+  // build the P^T tiles of chunk c+1 while the producers stage chunk c+2 and
+  // the consumers store o of chunk c.  A pairwise chunk c+1 adds one interval
+  // (its q~ may be written only after every thread has read its raw q).
   drain_vmem();
   c_begin = out_begin;
   c_end = out_end;
@@ -956,18 +974,16 @@ gla_fwd_bf16_kernel(Params P) {
   for (int c = c_begin; c < c_end; ++c) {
     const int x = c + 1;
     const bool live = x < c_end;
-    // interval 1: o of chunk c
-    if (has_cols) outputs(c, S);
-    lds_barrier();                                              // B loop 1
-    pw_next = live && chunk_pairwise(x);
-    // interval 2: o of chunk c to memory, the state after chunk c.  Split
-    // segment 0 publishes the state entering chunk L: its stores go out
-    // before the o stores, so the wait that orders them before the flag
-    // (raised right after the barrier) does not cover the o stores.
+    const bool pwx = live && chunk_pairwise(x);
+    // interval 1: o of chunk c into the staging tile, then the state after
+    // chunk c.  Split segment 0 publishes the state entering chunk L; the
+    // flag goes up right after the barrier.
     const bool pub = c + 1 == publish_at;
-    if (!pub) store_stage(c);
     if (has_cols) {
-      state_update(c & 1, S, nullptr, !pw_c);
+      uint4 vf[JP];
+      outputs(c, S, vf);
+      if (pw_c) state_update(c & 1, S, nullptr, std::false_type{}, vf);
+      else state_update(c & 1, S, nullptr, std::true_type{}, vf);
       if (pub) {
 #pragma unroll
         for (int r = 0; r < DT; ++r)
@@ -975,22 +991,21 @@ gla_fwd_bf16_kernel(Params P) {
         drain_vmem();
       }
     }
-    if (pub) store_stage(c);
-    lds_barrier();                                              // B loop 2
+    lds_barrier();                                              // B loop 1
     if (pub && tid == 0)
       __hip_atomic_store(P.flags + slot0, P.epoch * 4u + 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // interval 3: P^T tiles of chunk x
+    // interval 2: P^T tiles of chunk x; o of chunk c to memory
     if (live) {
-      if (!pw_next) produce3_fast(x); else produce3_pairwise(x);
+      if (!pwx) produce3_fast(x); else produce3_pairwise(x);
     }
-    lds_barrier();                                              // B loop 3
-    if (pw_next) lds_barrier();                                 // B loop 4
-    pw_c = pw_next;
+    store_stage(c);
+    lds_barrier();                                              // B loop 2
+    if (pwx) lds_barrier();                                     // B loop 3
+    pw_c = pwx;
   }
   if ((c_end - c_begin) & 1) {   // the producers' step past the segment
     lds_barrier();                                              // B loop 1
     lds_barrier();                                              // B loop 2
-    lds_barrier();                                              // B loop 3
   }
 
   if (last_seg && P.s_final && has_cols) {
