@@ -716,8 +716,8 @@ gla_fwd_bf16_kernel(Params P) {
   // allocated in the other role's code.
   if (producer) {
     // ===================== pass 1: segment aggregate ==========================
-    // stage chunk c+1 (k, v, gates -> k^, e^{b_last}) while the consumers
-    // fold chunk c into the aggregate
+    // transform chunk c+1 (gates -> k^, e^{b_last}) while the consumers fold
+    // chunk c into the aggregate, then stage chunk c+2
     if (do_pass1) {
       ord_load(c_begin);
       fill_tok(c_begin);
@@ -731,39 +731,39 @@ gla_fwd_bf16_kernel(Params P) {
       mid_loads(c_begin, false, lsA);
       late_loads(c_begin, false, lsA);
       lds_barrier();                                            // B 2
-      if (has_rows) {
+      // the gates of chunk x -> b, e^{b_last}, k^ = k e^{b_last - b}
+      auto agg_transform = [&](int x) {
         float gmo[4], bl[4];
-        scan(tile(c_begin & 1, 2), bt);
-        chunk_total(bt, gmo, bl, c_begin & 1);
-        khat_direct(tile(c_begin & 1, 1), tile(c_begin & 1, 2), bt, bl);
-      }
+        scan(tile(x & 1, 2), bt);
+        chunk_total(bt, gmo, bl, x & 1);
+        khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
+      };
+      if (has_rows) agg_transform(c_begin);
+      produce1(c_begin + 1, false, lsB);
       lds_barrier();                                            // B 3
-      // chunk c: stage chunk x = c+1 from register set (x - c_begin) & 1
-      auto agg_step = [&](int c, LoadSet &ls) {
+      // Step c (the consumers fold chunk c into the aggregate): transform
+      // chunk x = c+1 and issue the rest of chunk x+2's loads (register set
+      // ls_tail), then stage chunk x+1 (set ls_stage), which goes to the
+      // buffer chunk c was read from.  The staging is unconditional (past
+      // the segment the token table reads zeros and the stores land in a
+      // buffer nobody reads): a skipped load would make the compiler's count
+      // of outstanding loads, and its waits, conservative for every chunk.
+      auto agg_step = [&](int c, LoadSet &ls_tail, LoadSet &ls_stage) {
         const int x = c + 1;
-        // unconditional (past the segment the token table reads zeros and
-        // the stores land in a buffer nobody reads): a skipped load would
-        // make the compiler's count of outstanding loads, and its waits,
-        // conservative for every chunk
-        produce1(x, false, ls);
+        if (has_rows && x < c_end) agg_transform(x);
+        mid_loads(x, false, ls_tail);
+        late_loads(x, false, ls_tail);
         lds_barrier();                                          // B loop 1
-        if (has_rows && x < c_end) {
-          float gmo[4], bl[4];
-          scan(tile(x & 1, 2), bt);
-          chunk_total(bt, gmo, bl, x & 1);
-          khat_direct(tile(x & 1, 1), tile(x & 1, 2), bt, bl);
-        }
-        mid_loads(x, false, ls);
-        late_loads(x, false, ls);
+        produce1(x + 1, false, ls_stage);
         lds_barrier();                                          // B loop 2
       };
       // Steps in pairs (register sets B, A); an odd count ends with a step
-      // past the segment that only stages zeros, matched by the consumers.
-      // (A conditional second step would leave the compiler unsure which
-      // set was loaded last, and it would wait for both.)
+      // past the segment, matched by the consumers.  (A conditional second
+      // step would leave the compiler unsure which set was loaded last, and
+      // it would wait for both.)
       for (int c = c_begin; c < c_end; c += 2) {
-        agg_step(c, lsB);
-        agg_step(c + 1, lsA);
+        agg_step(c, lsB, lsA);
+        agg_step(c + 1, lsA, lsB);
       }
       drain_vmem();
       __syncthreads();                                          // B e
