@@ -330,7 +330,9 @@ struct BwdLds {
   static constexpr int oB = oP + M * SA * 2;           // [M][DP] fp32: b (log2 units) of extreme chunks, then d log alpha
   static constexpr int oTok = oB + M * DP * 4;         // [2][M] canonical token, -1 past T (this chunk, the one before)
   static constexpr int oFlag = oTok + 2 * M * 4;       // any |b| beyond the factorised range
-  static constexpr int bytes = oFlag + 16;
+  static constexpr int oEB = oFlag + 16;               // [DP] fp32 e^{B} per key channel
+  static constexpr int oSuf = oEB + DP * 4;            // [DP] fp32 rowsum(S_out (.) D) per key channel
+  static constexpr int bytes = oSuf + DP * 4;
 };
 
 constexpr int kChunkWaves = 8;
@@ -369,6 +371,13 @@ gla_bwd_chunk(BwdParams P) {
   float *bL = reinterpret_cast<float *>(smem + L::oB);
   int *tok = reinterpret_cast<int *>(smem + L::oTok);
   unsigned *flag = reinterpret_cast<unsigned *>(smem + L::oFlag);
+  float *tEB = reinterpret_cast<float *>(smem + L::oEB), *tSuf = reinterpret_cast<float *>(smem + L::oSuf);
+  // With waves to spare beyond the channel waves (DT < 8), the rowsum of
+  // S_out (.) D -- a constant of each key channel over the chunk, added to
+  // every d log alpha of it -- is formed by those spare waves in phase 3 and
+  // added to d log alpha in phase 5, off the channel waves' path.
+  constexpr int NH = kChunkWaves - DT;   // spare (non-channel) waves
+  constexpr bool kSpareSuf = NH > 0;
 
   const int tid0 = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const int N = P.nchunks, total = P.B * P.H * N;
@@ -620,31 +629,35 @@ gla_bwd_chunk(BwdParams P) {
           }
         }
       }
-      float gm[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kSpareSuf) {
+        if (g4 == 0) tEB[i] = fexp2(Bt);
+      } else {
+        float gm[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gm[e] = fexp2(__shfl(Bt, 4 * g4 + e, kWave));
+        for (int e = 0; e < 4; ++e) gm[e] = fexp2(__shfl(Bt, 4 * g4 + e, kWave));
 #pragma unroll
-      for (int cc = 0; cc < DT; ++cc) {
-        f32x4_t so = {0.f, 0.f, 0.f, 0.f};
+        for (int cc = 0; cc < DT; ++cc) {
+          f32x4_t so = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jp = 0; jp < JP; ++jp)
-          so = mfma32(kslots<MT>(kh, jp), tr_pair<MT>(tV, QS, jp, 16 * cc, g4, rowoff, coloff), so);
-        // rows 16 r + 4 (l/16) + e, column 16 cc + l%16 of S_in and D
-        const float4 s4 = unpack4(lds2(tS + (16 * cc + l16) * QS + 16 * r + 4 * g4));
-        const float4 d4 = unpack4(lds2(tD + (16 * cc + l16) * QS + 16 * r + 4 * g4));
+          for (int jp = 0; jp < JP; ++jp)
+            so = mfma32(kslots<MT>(kh, jp), tr_pair<MT>(tV, QS, jp, 16 * cc, g4, rowoff, coloff), so);
+          // rows 16 r + 4 (l/16) + e, column 16 cc + l%16 of S_in and D
+          const float4 s4 = unpack4(lds2(tS + (16 * cc + l16) * QS + 16 * r + 4 * g4));
+          const float4 d4 = unpack4(lds2(tD + (16 * cc + l16) * QS + 16 * r + 4 * g4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(fmaf(gm[e], elt(s4, e), so[e]), elt(d4, e), acc[e]);
+          for (int e = 0; e < 4; ++e) acc[e] = fmaf(fmaf(gm[e], elt(s4, e), so[e]), elt(d4, e), acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) acc[e] += __shfl_xor(acc[e], off, kWave);
+        // row 16 r + m sits in lane group m / 4, element m % 4
+        const int src = 16 * (l16 >> 2);
+        const float v0 = __shfl(acc[0], src, kWave), v1 = __shfl(acc[1], src, kWave);
+        const float v2 = __shfl(acc[2], src, kWave), v3 = __shfl(acc[3], src, kWave);
+        const int m4 = l16 & 3;
+        sufS = m4 == 0 ? v0 : m4 == 1 ? v1 : m4 == 2 ? v2 : v3;
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) acc[e] += __shfl_xor(acc[e], off, kWave);
-      // row 16 r + m sits in lane group m / 4, element m % 4
-      const int src = 16 * (l16 >> 2);
-      const float v0 = __shfl(acc[0], src, kWave), v1 = __shfl(acc[1], src, kWave);
-      const float v2 = __shfl(acc[2], src, kWave), v3 = __shfl(acc[3], src, kWave);
-      const int m4 = l16 & 3;
-      sufS = m4 == 0 ? v0 : m4 == 1 ? v1 : m4 == 2 ? v2 : v3;
     }
     lds_barrier();
 
@@ -756,6 +769,37 @@ gla_bwd_chunk(BwdParams P) {
           for (int e = 0; e < 4; ++e) bL[(16 * I + 4 * g4 + e) * DP + i] = dgx[I][e];
       }
     }
+    //         rowsum(S_out (.) D) of key-channel tile rr, on the spare waves:
+    //         the same products and sums as the channel wave's own form
+    //         (k^ from LDS as the A operand, tokens along K)
+    if constexpr (kSpareSuf) {
+      if (!chan) {
+        for (int rr = wslot; rr < DT; rr += NH) {
+          const int i0 = 16 * rr;
+          float gm[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gm[e] = tEB[i0 + 4 * g4 + e];
+#pragma unroll
+          for (int cc = 0; cc < DT; ++cc) {
+            f32x4_t so = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jp = 0; jp < JP; ++jp)
+              so = mfma32(tr_pair<MT>(tG, QS, jp, i0, g4, rowoff, coloff),
+                          tr_pair<MT>(tV, QS, jp, 16 * cc, g4, rowoff, coloff), so);
+            const float4 s4 = unpack4(lds2(tS + (16 * cc + l16) * QS + i0 + 4 * g4));
+            const float4 d4 = unpack4(lds2(tD + (16 * cc + l16) * QS + i0 + 4 * g4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(fmaf(gm[e], elt(s4, e), so[e]), elt(d4, e), acc[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) acc[e] += __shfl_xor(acc[e], off, kWave);
+          if (l16 == 0)
+            *reinterpret_cast<float4 *>(tSuf + i0 + 4 * g4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
+    }
     //         P = Q~ K~^T on tiles J <= I (factorised chunks)
     if (fast) {
       for (int a = wslot; a < NTRI; a += kChunkWaves) {
@@ -825,7 +869,12 @@ gla_bwd_chunk(BwdParams P) {
     for (int kq = 0; kq < ITG; ++kq) {
       const int idx = tid + kq * NT;
       const int t = idx / (DP / 4), cg = idx - t * (DP / 4);
-      og[kq] = *reinterpret_cast<const uint4 *>(bL + (idx < M * (DP / 4) ? t : 0) * DP + 4 * cg);
+      float4 gv4 = *reinterpret_cast<const float4 *>(bL + (idx < M * (DP / 4) ? t : 0) * DP + 4 * cg);
+      if constexpr (kSpareSuf) {
+        const float4 sf = *reinterpret_cast<const float4 *>(tSuf + 4 * cg);
+        gv4.x += sf.x; gv4.y += sf.y; gv4.z += sf.z; gv4.w += sf.w;
+      }
+      og[kq] = __builtin_bit_cast(uint4, gv4);
     }
     lds_barrier();
   }
