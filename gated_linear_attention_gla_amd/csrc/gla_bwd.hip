@@ -596,22 +596,35 @@ gla_bwd_chunk(BwdParams P) {
     //         k e^{-b} where factorised, else b itself), and rowsum(S_out (.) D)
     //         with S_out = diag(e^{B}) S_in + K^^T V
     fetch_vo(wn);
-    const bool fast = *flag == 0u;
+    const bool fast = __builtin_amdgcn_readfirstlane(*flag) == 0u;   // uniform: a scalar branch
     uint2 qt[MT], kt[MT];
     float sufS = 0.f;   // rowsum(S_out (.) D) of channel 16 r + l%16
+    float eB = 1.f;     // e^{B} of channel 16 r + l%16
     if (chan) {
       uint2 kh[MT];
       const int i = 16 * r + l16;
+      eB = fexp2(Bt);
 #pragma unroll
       for (int I = 0; I < MT; ++I) {
         const float4 q4 = unpack4(qa[I]), k4 = unpack4(ka[I]);
         f32x4_t a1, a2, a3;
+        if (fast) {
+          // |b| <= 64: e^{B - b} = e^{B} e^{-b} in fp32 (two exponentials
+          // per element instead of three)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float b = bl[I][e];
-          a1[e] = elt(q4, e) * fexp2(b);
-          a2[e] = elt(k4, e) * fexp2(-b);
-          a3[e] = elt(k4, e) * fexp2(Bt - b);
+          for (int e = 0; e < 4; ++e) {
+            const float b = bl[I][e];
+            a1[e] = elt(q4, e) * fexp2(b);
+            a2[e] = elt(k4, e) * fexp2(-b);
+            a3[e] = a2[e] * eB;
+          }
+        } else {
+          // only k^ is used (with exact exponent differences)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a1[e] = a2[e] = 0.f;
+            a3[e] = elt(k4, e) * fexp2(Bt - bl[I][e]);
+          }
         }
         qt[I] = pack4(a1);
         kt[I] = pack4(a2);
@@ -630,7 +643,7 @@ gla_bwd_chunk(BwdParams P) {
         }
       }
       if constexpr (kSpareSuf) {
-        if (g4 == 0) tEB[i] = fexp2(Bt);
+        if (g4 == 0) tEB[i] = eB;
       } else {
         float gm[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -740,7 +753,7 @@ gla_bwd_chunk(BwdParams P) {
           const float b = bl[I][e];
           if (fast) {
             dq4[e] = fexp2(b) * (x1[e] + y1[e]);
-            dk4[e] = fexp2(-b) * y2[e] + fexp2(Bt - b) * x2[e];
+            dk4[e] = fexp2(-b) * fmaf(eB, x2[e], y2[e]);   // e^{-b} y2 + e^{B - b} x2
           } else {
             dq4[e] = fexp2(b) * x1[e] + y1[e];
             dk4[e] = y2[e] + fexp2(Bt - b) * x2[e];
