@@ -304,14 +304,18 @@ __device__ __forceinline__ void scan_unit(const BwdParams &P, int unit) {
   }
 }
 
-// Both scans in one launch (they are independent): workgroups [0, units)
-// run the forward scan, [units, 2 units) the reverse one.
+// Both scans in one launch (they are independent): work items [0, units)
+// are the forward scans, [units, 2 units) the reverse ones.  Workgroup i
+// runs on XCD i % 8; with a grid of whole XCD rounds each XCD takes a
+// contiguous range of items, so the heads of a batch element, whose
+// 144-byte rows share 128-byte lines, are read through one L2.
 template <int DP, int M, bool ORD>
 __global__ void __launch_bounds__(DP / 16 * kWave)
 gla_bwd_scan(BwdParams P) {
   const int units = P.B * P.H;
-  if ((int)blockIdx.x < units) scan_unit<DP, M, false, ORD>(P, blockIdx.x);
-  else scan_unit<DP, M, true, ORD>(P, blockIdx.x - units);
+  const int item = (gridDim.x & 7) == 0 ? xcd_linear_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  if (item < units) scan_unit<DP, M, false, ORD>(P, item);
+  else scan_unit<DP, M, true, ORD>(P, item - units);
 }
 
 // ============================ chunk gradients ================================
@@ -492,10 +496,15 @@ gla_bwd_chunk(BwdParams P) {
   };
 
   // a contiguous run of chunks per workgroup: consecutive chunks of one
-  // (batch, head) share memory pages
+  // (batch, head) share memory pages.  With a grid of whole XCD rounds
+  // (workgroup i runs on XCD i % 8) each XCD takes a contiguous range of
+  // runs, so the workgroups of the heads of one batch element, which walk
+  // the same token range side by side and whose 144-byte rows share
+  // 128-byte lines, meet in one L2.
+  const int lb = (gridDim.x & 7) == 0 ? xcd_linear_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int wend = min(total, ((int)blockIdx.x + 1) * per);
-  int w = blockIdx.x * per, wprev = -1, par = 0;
+  const int wend = min(total, (lb + 1) * per);
+  int w = lb * per, wprev = -1, par = 0;
   if (w < wend) {
     ord_rows(w);
     fetch_qkg(w, min(w + 1, wend - 1));
