@@ -352,9 +352,9 @@ constexpr int kChunkWaves = 8;
 //   phase 3: dq, dk, dlog_alpha (channel waves, token tiles last to first) | P tiles
 //   phase 4: dq, dk staged in LDS; dv
 //   phase 5: the staged outputs into registers
-// The outputs leave as 16-byte rows after the next chunk's rows are in LDS,
-// behind that chunk's prefetch, so neither waits for the other; both are
-// long complete when the next chunk's rows are needed.
+// The outputs leave as 16-byte rows at the end of the next chunk's phase 2,
+// after that chunk's first prefetch and its own arithmetic of phases 1 and
+// 2; both are long complete when the rows after it are needed.
 template <int DP, int M, bool ORD>
 __global__ void __launch_bounds__(kChunkWaves * kWave)
 gla_bwd_chunk(BwdParams P) {
@@ -464,7 +464,7 @@ gla_bwd_chunk(BwdParams P) {
   };
 
   // one chunk's outputs, read back from the LDS staging (phase 5) and stored
-  // to memory once the next chunk's first barrier has passed
+  // to memory at the end of the next chunk's phase 2
   constexpr int ITO = (M * CG + NT - 1) / NT, ITG = (M * (DP / 4) + NT - 1) / NT;
   uint4 oq[ITO], ok[ITO], ov[ITO], og[ITG];
   auto store_outputs = [&](int wp, const int *tk, bool valid) {
@@ -560,7 +560,6 @@ gla_bwd_chunk(BwdParams P) {
     // before the next chunk's rows are exact
     const int wn = min(w + 1, wend - 1);
     fetch_qkg(wn, min(wn + 1, wend - 1));
-    store_outputs(wprev >= 0 ? wprev : w, tok + (par ^ 1) * M, wprev >= 0);
 
     // ---- 1. cumulative gates (log2 units) and raw q, k of tile r, in
     //         accumulator layout (token 16 I + 4 (l/16) + e, channel 16 r + l%16)
@@ -681,6 +680,12 @@ gla_bwd_chunk(BwdParams P) {
         sufS = m4 == 0 ? v0 : m4 == 1 ? v1 : m4 == 2 ? v2 : v3;
       }
     }
+    // the chunk before's outputs leave here, after this chunk's arithmetic of
+    // phases 1 and 2 rather than before it: a wave whose stores wait for
+    // room in the memory pipeline then waits at the barrier, not in front of
+    // its own work (C2 526 -> 497 us against issuing them at the top of
+    // phase 1)
+    store_outputs(wprev >= 0 ? wprev : w, tok + (par ^ 1) * M, wprev >= 0);
     lds_barrier();
 
     fetch_states(wn);
@@ -876,8 +881,8 @@ gla_bwd_chunk(BwdParams P) {
     }
     lds_barrier();
 
-    // ---- 5. the staged outputs into registers; they are stored after the
-    //         next chunk's first barrier
+    // ---- 5. the staged outputs into registers; they are stored at the end
+    //         of the next chunk's phase 2
 #pragma unroll
     for (int kq = 0; kq < ITO; ++kq) {
       const int idx = tid + kq * NT;
