@@ -101,9 +101,12 @@ int check_gla_sizes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
   const int M = auto_chunk(dtype, chunk, dk, dv);
   if (dtype == DIG_BF16) {
     if (dk % 8 || dv % 8) return fail(DIG_EINVAL, "gla_fwd: bf16 path needs dk, dv multiples of 8");
-    if (M != 16 && M != 32 && M != 64) return fail(DIG_EINVAL, "gla_fwd: bf16 chunk must be 0, 16, 32 or 64");
+    if (M != 16 && M != 32 && M != 64 && M != 128)
+      return fail(DIG_EINVAL, "gla_fwd: bf16 chunk must be 0, 16, 32, 64 or 128");
     if (M == 64 && (dk > 96 || dv > 96))
       return fail(DIG_EINVAL, "gla_fwd: bf16 chunk 64 needs dk, dv <= 96 (use 0, 16 or 32)");
+    if (M == 128 && (dk > 32 || dv > 32))
+      return fail(DIG_EINVAL, "gla_fwd: bf16 chunk 128 needs dk, dv <= 32 (use 0, 16, 32 or 64)");
   } else {
     if (M != 16 && M != 32 && M != 64 && M != 128)
       return fail(DIG_EINVAL, "gla_fwd: fp32 chunk must be 0, 16, 32, 64 or 128");

@@ -140,7 +140,10 @@ struct Lds {
   // 4 * odd dwords; the transposing reads (4 rows x 32 bytes) need the four
   // rows on disjoint 8-bank groups.  DP + 8 satisfies both for 64 and 96
   // channels, DP + 24 for 32, 80 and 128.
-  static constexpr int QS = (DP == 64 || DP == 96) ? DP + 8 : DP + 24;
+  // 128-token chunks (32 channels only) take DP + 8 so that the plan fits
+  // in 160 KiB; their transposing reads then take 1.5x their conflict-free
+  // time.
+  static constexpr int QS = (DP == 64 || DP == 96 || M == 128) ? DP + 8 : DP + 24;
   static constexpr int MT = M / 16;
   static constexpr int NPT = MT * (MT + 1) / 2;        // causal 16x16 tiles of P^T
   static constexpr int TILE = M * QS * 2;
@@ -1029,7 +1032,7 @@ int lds_bytes(int DP, int M) {
 #define DIG_LDS_CASE(D, MM) \
   case D * 1000 + MM:       \
     return Lds<D, MM>::bytes;
-    DIG_LDS_CASE(32, 16) DIG_LDS_CASE(32, 32) DIG_LDS_CASE(32, 64)
+    DIG_LDS_CASE(32, 16) DIG_LDS_CASE(32, 32) DIG_LDS_CASE(32, 64) DIG_LDS_CASE(32, 128)
     DIG_LDS_CASE(64, 16) DIG_LDS_CASE(64, 32) DIG_LDS_CASE(64, 64)
     DIG_LDS_CASE(80, 16) DIG_LDS_CASE(80, 32) DIG_LDS_CASE(80, 64)
     DIG_LDS_CASE(96, 16) DIG_LDS_CASE(96, 32) DIG_LDS_CASE(96, 64)
@@ -1133,6 +1136,9 @@ hipError_t launch_m(const Params &p, int M, int grid, hipStream_t s) {
     case 32: return launch<DP, 32>(p, grid, s);
     case 64:
       if constexpr (DP <= 96) return launch<DP, 64>(p, grid, s);   // 128 channels: LDS holds 32-token chunks
+      return hipErrorInvalidValue;
+    case 128:
+      if constexpr (DP == 32) return launch<DP, 128>(p, grid, s);  // LDS holds 128-token chunks at 32 channels
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

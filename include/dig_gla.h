@@ -106,8 +106,9 @@ extern "C" {
  *                    path takes any layout.
  *   gh, gw, dir      the token grid and the scan direction.
  *   chunk            tokens per chunk: 0 = automatic (bf16: 64, or 32 when
- *                    dk or dv exceeds 96; fp32: 16); else 16, 32 or 64
- *                    (bf16; 64 only for dk, dv <= 96) or 16, 32, 64, 128
+ *                    dk or dv exceeds 96; fp32: 16); else 16, 32, 64 or
+ *                    128 (bf16; 64 only for dk, dv <= 96, 128 only for dk,
+ *                    dv <= 32, where its LDS plan fits) or 16, 32, 64, 128
  *                    (fp32, as long as its LDS plan -- 4 (3 M dk + M dv +
  *                    M^2 + dk dv) bytes -- fits in 160 KiB, e.g. 128 for
  *                    dk, dv <= 32).  The chunk size changes rounding only,

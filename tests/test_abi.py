@@ -54,7 +54,7 @@ def _gla(L, **kw):
     dict(q=None), dict(o=None), dict(B=0), dict(T=-1), dict(dk=0), dict(dv=136),
     dict(gh=7), dict(dir=4), dict(dtype=7), dict(chunk=48), dict(dk=12, dv=12),
     dict(q=18), dict(qk=(4096 * 64, 60, 8)), dict(o=16), dict(dtype=0, chunk=256),
-    dict(qk=(-8, 64, 8)), dict(dk=128, dv=128, chunk=64),
+    dict(qk=(-8, 64, 8)), dict(dk=128, dv=128, chunk=64), dict(dk=40, dv=40, chunk=128),
 ])
 def test_gla_rejects_bad_arguments(L, bad):
     rc = _gla(L, **bad)

@@ -120,13 +120,50 @@ def test_bf16_shapes_vs_oracle(orc, shape):
         assert_state_close(sf, rs, TOL_BF16, f"s[{d}]")
 
 
-@pytest.mark.parametrize("chunk", [16, 32, 64])
-def test_bf16_chunk_invariance(orc, chunk):
-    x = gen.gla_inputs(2, 200, 2, 64, 64, dtype="bf16", seed=5, qkv_scale=0.125)
+@pytest.mark.parametrize("d,chunk", [(64, 16), (64, 32), (64, 64), (32, 16), (32, 32), (32, 64), (32, 128)])
+def test_bf16_chunk_invariance(orc, d, chunk):
+    """Every chunk size the bf16 kernel offers for a head width gives the
+    oracle's result (128-token chunks: heads of up to 32 channels)."""
+    x = gen.gla_inputs(2, 200, 2, d, d, dtype="bf16", seed=5, qkv_scale=0.125)
     o, sf = run_gla(x, (10, 20), "t2b", chunk=chunk)
     ro, rs = oracle_gla(orc, x, (10, 20), "t2b")
     assert_o_close(o, ro, TOL_BF16)
     assert_state_close(sf, rs, TOL_BF16)
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 2, 10, 20, 32, False),    # 200 tokens: one 128-token chunk and a ragged 72-token tail
+    (2, 2, 10, 20, 24, False),    # 24 channels: zero-padded channel groups
+    (8, 16, 32, 32, 32, True),    # 128 scans of 8 chunks: two segments, the pipelined split
+    (1, 2, 64, 64, 32, True),     # 2 scans of 32 chunks: eight segments, decoupled look-back
+], ids=lambda s: "x".join(map(str, s)))
+def test_bf16_chunk128(orc, shape):
+    """128-token chunks (heads of up to 32 channels) in every direction, whole
+    outputs against the oracle, with and without an initial state."""
+    B, H, gh, gw, d, with_s0 = shape
+    x = gen.gla_inputs(B, gh * gw, H, d, d, dtype="bf16", seed=40 + d, qkv_scale=0.17)
+    s0 = torch.randn(B, H, d, d, generator=torch.Generator().manual_seed(9)) * 0.5 if with_s0 else None
+    for direction in DIRS:
+        o, sf = run_gla(x, (gh, gw), direction, chunk=128, s0=s0)
+        ro, rs = oracle_gla(orc, x, (gh, gw), direction, s0=None if s0 is None else s0.double().numpy())
+        assert_o_close(o, ro, TOL_BF16, f"o[{direction}]")
+        assert_state_close(sf, rs, TOL_BF16, f"s[{direction}]")
+
+
+def test_bf16_chunk128_pairwise_gates(orc):
+    """128-token chunks whose gates exceed the factorised range (the pairwise
+    intra-chunk path) beside chunks that stay inside it."""
+    gh, gw = 12, 24
+    x = gen.gla_inputs(2, gh * gw, 2, 32, 32, dtype="bf16", seed=41, qkv_scale=0.17)
+    g = x["log_alpha"].float()
+    g[:, 30:33] = -1e4
+    g[:, 150, :, :5] = -40.0
+    x["log_alpha"] = g.to(torch.bfloat16)
+    for d in ("l2r", "t2b"):
+        o, sf = run_gla(x, (gh, gw), d, chunk=128)
+        ro, rs = oracle_gla(orc, x, (gh, gw), d)
+        assert_o_close(o, ro, TOL_BF16, f"o[{d}]")
+        assert_state_close(sf, rs, TOL_BF16, f"s[{d}]")
 
 
 def test_bf16_state_handoff(orc):
