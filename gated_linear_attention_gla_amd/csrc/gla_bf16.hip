@@ -496,7 +496,10 @@ gla_fwd_bf16_kernel(Params P) {
   // (fp32) and k^ = k e^{b_last - b} directly.  bt stays in
   // registers for P3 of a pairwise chunk.
   f32x4_t bt[MT];
-  auto produce2 = [&](int x, bool pairwise) {
+  // (produce2 and produce3_fast are forced inline: left to the compiler, the
+  // 128-token instantiations called them as functions, with their captures
+  // in a stack frame)
+  auto produce2 = [&](int x, bool pairwise) __attribute__((always_inline)) {
     const int par = x & 1;
     uint16_t *tq = tile(par, 0), *tk = tile(par, 1), *tg = tile(par, 2);
     float gmo[4], bl[4];
@@ -527,7 +530,7 @@ gla_fwd_bf16_kernel(Params P) {
   };
   // P3(x), fast chunks: causal P^T tiles (j, i), j <= i, from q~ and k~,
   // spread over all waves (the consumers have nothing else to do then).
-  auto produce3_fast = [&](int x) {
+  auto produce3_fast = [&](int x) __attribute__((always_inline)) {
     const int par = x & 1;
     const uint16_t *tq = tile(par, 0), *tk = tile(par, 1);
     uint16_t *pt = ptile(par);
