@@ -57,6 +57,8 @@ def bitwise(a, b):
     (2, 3, 11, 9, 72, "bf16", 64),
     (1, 8, 64, 64, 64, "bf16", 64),     # eight segments per scan (look-back)
     (6, 16, 32, 32, 64, "bf16", 32),    # the two-segment split
+    (2, 2, 10, 20, 32, "bf16", 128),    # 128-token chunks, ragged tail
+    (8, 16, 32, 32, 32, "bf16", 128),   # 128-token chunks, the two-segment split
     (1, 2, 8, 8, 16, "f32", 16),
 ], ids=lambda c: "x".join(map(str, c)))
 def test_fwd_table_of_a_grid_order_is_that_direction(case):
@@ -91,6 +93,19 @@ def test_fwd_random_permutation_segmented_vs_oracle(orc):
     x = gen.gla_inputs(B, T, H, d, d, seed=62, qkv_scale=1 / 8)
     perm = np.random.default_rng(62).permutation(T)
     o, sf = fwd(x, order=perm)
+    ro, rs = orc.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], None, None, order=perm)
+    assert_o_close(o, ro, TOL_BF16, "random order o")
+    assert_state_close(sf, rs, TOL_BF16, "random order s_final")
+
+
+def test_fwd_random_permutation_chunk128_vs_oracle(orc):
+    """A random order with 128-token chunks (32-channel heads) through the
+    eight-segment look-back."""
+    B, H, gh, gw, d = 1, 2, 64, 64, 32
+    T = gh * gw
+    x = gen.gla_inputs(B, T, H, d, d, seed=63, qkv_scale=0.17)
+    perm = np.random.default_rng(63).permutation(T)
+    o, sf = fwd(x, order=perm, chunk=128)
     ro, rs = orc.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], None, None, order=perm)
     assert_o_close(o, ro, TOL_BF16, "random order o")
     assert_state_close(sf, rs, TOL_BF16, "random order s_final")
