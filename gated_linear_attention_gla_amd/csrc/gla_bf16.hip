@@ -222,14 +222,19 @@ gla_fwd_bf16_kernel(Params P) {
   // Every piece of work is therefore taken exactly once even on a workspace
   // that was never zero-filled; only the start order can then be rotated,
   // which the bounded waits turn into an error rather than a hang.
-  if (tid == 0) {
-    const unsigned g = blockIdx.x & 7, gsize = gridDim.x >> 3;
-    unsigned t = __builtin_amdgcn_atomic_inc32(P.ticket + g, gsize - 1, __ATOMIC_RELAXED, "agent");
-    if (t >= gsize) t = gsize - 1;
-    sMisc[1] = (int)((t << 3) | g);
+  // With one segment per scan no workgroup ever waits for another, so the
+  // launch index assigns the work and no ticket is taken.
+  int lid = (int)blockIdx.x;
+  if (P.nseg > 1) {
+    if (tid == 0) {
+      const unsigned g = blockIdx.x & 7, gsize = gridDim.x >> 3;
+      unsigned t = __builtin_amdgcn_atomic_inc32(P.ticket + g, gsize - 1, __ATOMIC_RELAXED, "agent");
+      if (t >= gsize) t = gsize - 1;
+      sMisc[1] = (int)((t << 3) | g);
+    }
+    __syncthreads();
+    lid = sMisc[1];
   }
-  __syncthreads();
-  const int lid = sMisc[1];
   const int xcd = lid & 7, kslot = lid >> 3;
   const int unit = xcd * P.per_xcd + kslot / P.nseg;
   const int seg = kslot % P.nseg;
