@@ -4,7 +4,9 @@ The bf16 forward kernel's workgroup i runs on XCD i % 8 and takes a ticket
 from that XCD's counter with an atomic increment that wraps at gsize - 1
 (gsize = workgroups per XCD); a ticket t >= gsize reads as gsize - 1; ticket
 t of XCD x is segment t % nseg of unit x * per_xcd + t // nseg (units past
-the last one are padding).  This model replays that logic exactly as the
+the last one are padding).  With one segment per scan no workgroup waits for
+another and the kernel takes no ticket: t = i // 8, the launch index, and the
+counters are never touched.  This model replays that logic exactly as the
 kernel states it, over counters holding any value (zero-filled, a rotation,
 byte-pattern garbage) and random start orders, and checks that
 
@@ -40,9 +42,12 @@ def launch(counters, units, nseg, rng):
     start = {}
     for pos, wg in enumerate(arrival):
         xcd = wg & 7
-        t = atomic_inc(counters, xcd, gsize - 1)
-        if t >= gsize:
-            t = gsize - 1
+        if nseg == 1:
+            t = wg >> 3
+        else:
+            t = atomic_inc(counters, xcd, gsize - 1)
+            if t >= gsize:
+                t = gsize - 1
         unit = xcd * per_xcd + t // nseg
         seg = t % nseg
         if unit >= units:
@@ -69,7 +74,7 @@ def test_tickets_are_a_bijection(units, nseg, init):
         assert gs == gsize
         assert set(taken) == {(u, s) for u in range(units) for s in range(nseg)}
         for x in range(8):
-            if before[x] < gsize:
+            if nseg == 1 or before[x] < gsize:
                 assert counters[x] == before[x]
             else:
                 assert counters[x] == gsize - 1
