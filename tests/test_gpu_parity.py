@@ -166,6 +166,19 @@ def test_bf16_chunk128_pairwise_gates(orc):
         assert_state_close(sf, rs, TOL_BF16, f"s[{d}]")
 
 
+def test_bf16_longest_scan(orc):
+    """One scan of 4095 x 4093 = 16,760,835 tokens (a ragged 3-token last
+    chunk) scanned bottom to top: the plan splits it into hundreds of
+    look-back segments, so the last one folds every earlier aggregate, and
+    the slice offsets run to 268 MB.  Whole output against the oracle."""
+    gh, gw, d = 4095, 4093, 8
+    x = gen.gla_inputs(1, gh * gw, 1, d, d, dtype="bf16", seed=77, qkv_scale=0.35)
+    o, sf = run_gla(x, (gh, gw), "b2t")
+    ro, rs = oracle_gla(orc, x, (gh, gw), "b2t")
+    assert_o_close(o, ro, TOL_BF16, "o[longest]")
+    assert_state_close(sf, rs, TOL_BF16, "s[longest]")
+
+
 def test_bf16_state_handoff(orc):
     """Scan [0, T1) then [T1, T) with s0 = s_final of the first call == one call."""
     T1, T2 = 96, 160
