@@ -442,6 +442,27 @@ def bench_bwd(a, dg, gen, torch) -> int:
 COPY_PROBE_BYTES = 256 << 20   # the plain copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
 
 
+def product_probe() -> int:
+    """Launch sequence for PMC passes over the DiG block's largest product: five dig_linear calls
+    of [B*T, C] x [4C, C]^T at the DiG-XL/2 block shape (B=8, 64x64 tokens, C=1152) on seeded
+    operands."""
+    import torch
+
+    from gated_linear_attention_gla_amd import binding as dg
+
+    dev = torch.device("cuda:0")
+    B, T, C = 8, 64 * 64, 1152
+    g = torch.Generator(device="cpu").manual_seed(0)
+    x = (torch.randn(B * T, C, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    w = (torch.randn(4 * C, C, generator=g) / math.sqrt(C)).to(torch.bfloat16).to(dev)
+    y = torch.empty(B * T, 4 * C, dtype=torch.bfloat16, device=dev)
+    for _ in range(5):
+        dg.linear(x, w, out=y)
+    torch.cuda.synchronize()
+    log("[bench] product probe: 5 x dig_linear 32768 x 4608 x 1152")
+    return 0
+
+
 def traffic_probe(cfg_key: str, chunk: int, bwd: bool = False) -> int:
     """Launch sequence for the two rocprofv3 PMC passes: three plain device copies of
     COPY_PROBE_BYTES (read + write of known size), then three gla_fwd launches of the workload
@@ -553,6 +574,8 @@ def main(argv=None) -> int:
     ap.add_argument("--block", action="store_true", help="time one DiG block forward (DiG-XL/2, C2 grid)")
     ap.add_argument("--order", default="grid", choices=["grid", "zigzag"],
                     help="scan orders: the workload's grid directions, or ZigMa's zigzag tables (GLA only)")
+    ap.add_argument("--product-probe", action="store_true",
+                    help="only five launches of the block's largest product (for PMC passes)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the launches the PMC passes count: 3 plain copies, 3 gla_fwd")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
@@ -576,6 +599,8 @@ def main(argv=None) -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     dg.lib()
+    if a.product_probe:
+        return product_probe()
     if a.traffic_probe:
         return traffic_probe(a.config, a.chunk, bwd=a.bwd)
     if a.bwd:
