@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
 # (B, H, gh, gw, d): two segments per scan (the pipelined split) and eight
 # segments per scan (the look-back over published aggregates)
 SEGMENTED = [(6, 16, 32, 32, 64), (1, 8, 64, 64, 72)]
+# one segment per scan (192 scans of 4 chunks): the work comes from the
+# launch index and the kernel touches no workspace word
+SINGLE = (16, 12, 16, 16, 64)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,7 +55,7 @@ def test_workspace_not_zero_filled(orc):
     ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
     assert ws.data_ptr() % 256 == 0
     for i, (shape, direction) in enumerate([(SEGMENTED[0], "l2r"), (SEGMENTED[1], "b2t"),
-                                            (SEGMENTED[0], "t2b"), (SEGMENTED[1], "r2l")]):
+                                            (SEGMENTED[0], "t2b"), (SEGMENTED[1], "r2l"), (SINGLE, "b2t")]):
         x = _inputs(shape, 90 + i)
         grid = (shape[2], shape[3])
         xd = {k: x[k].to("cuda") for k in ("q", "k", "v", "log_alpha")}
@@ -66,7 +69,7 @@ def test_workspace_not_zero_filled(orc):
         dg.workspace_status(ws)
 
 
-@pytest.mark.parametrize("shape", SEGMENTED, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", SEGMENTED + [SINGLE], ids=lambda s: "x".join(map(str, s)))
 def test_graph_replays_see_new_inputs(orc, shape):
     """gla_fwd captured into a graph: every replay carries the same launch
     tag, so the flags of the previous replay must not read as published.
