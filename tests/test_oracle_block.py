@@ -93,6 +93,33 @@ def test_mixer_plumbing(orc):
         np.testing.assert_allclose(y - x, oc, rtol=1e-10, atol=1e-12)
 
 
+def test_mixer_log_gate(orc):
+    """The gate projection taken as u = LN(x) (not 0, where logsigmoid(u) and
+    logsigmoid(-u) agree): y - x is the pinned GLA oracle with log alpha =
+    logsigmoid(u) / 16 from torch's logsigmoid; the FFN is silenced."""
+    B, gh, gw, C, H = 2, 3, 4, 16, 2
+    T, d = gh * gw, C // H
+    x, c, w = _case(B, gh, gw, C, seed=7)
+    eye = np.eye(C)
+    w["w_ada"][:] = 0.0
+    w["b_ada"][:] = 0.0
+    w["b_ada"][2 * C:3 * C] = 1.0
+    w["w_in"][:] = np.concatenate([eye, eye, eye, eye])
+    w["b_in"][:] = 0.0
+    w["w_out"][:] = eye
+    w["b_out"][:] = 0.0
+    _identity_conv(w)
+    for direction in ("l2r", "b2t"):
+        y = orc.block_fwd(x, c, w, (gh, gw), direction, H=H)
+        ht = F.layer_norm(torch.tensor(x), (C,), eps=1e-6)
+        h = ht.numpy().reshape(B, T, H, d)
+        la = (F.logsigmoid(ht) / 16.0).numpy().reshape(B, T, H, d)
+        o, _ = orc.gla_fwd(h / np.sqrt(d), h, h, la, (gh, gw), direction)
+        oc = np.empty((B, T, C))
+        oc[:, orc.scan_perm(direction, gh, gw)] = o.reshape(B, T, C)
+        np.testing.assert_allclose(y - x, oc, rtol=1e-10, atol=1e-12)
+
+
 def test_ffn_branch(orc):
     """With the mixer gate zero and the FFN gate one, y - x is the FFN of the
     modulated LN(x) (torch's layer_norm, linear and tanh GELU)."""
