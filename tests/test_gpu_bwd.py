@@ -177,3 +177,13 @@ def test_bwd_c1_full(orc):
 
 def test_bwd_c2_full(orc):
     _full_bwd(orc, "C2", DIRS)
+
+
+def test_bwd_c4_shape_full(orc):
+    """The 2048-pixel shape (B = 1, H = 16, 128 x 128 tokens, d = 72, long-memory
+    gates): 16 scans of 256 chunks each, so the scans are the longest the
+    workloads have and every workgroup of the persistent chunk kernel runs a
+    long run of chunks; every unit compared, with s0 and dS_final."""
+    x = make_case(1, 128 * 128, 16, 72, 72, seed=88, gate_mu=2.0)
+    for d in ("l2r", "b2t"):
+        check(run_bwd(x, (128, 128), d), oracle_bwd(orc, x, (128, 128), d), f"C4 shape {d}", x)
